@@ -1,0 +1,200 @@
+"""CPU oracle for ECF8 -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product (``lossless_entropy_coded_ecf8_amd``)
+never imports it, and this package never imports the product: the two are
+independent implementations of the same format so that each can check the other.
+
+The arithmetic lives in ``ecf8_oracle.c`` (plain C, one bit at a time); this
+module only marshals numpy arrays into it and adds the fp64 statistics the
+pages quote (entropy, average code length).
+
+Sources: the ECF8 technical blog (codearts.csdn.net), sections 2.2 (exponent
+entropy), 3.1.1 (Huffman coding of the exponent) and 3.2.1 (chunked parallel
+decode with per-thread gaps); the ECF8 paper abstract (arXiv 2510.02676,
+lossless / bit-exact).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ecf8_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+_intp = ctypes.POINTER(ctypes.c_int)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc into oracle/liboracle.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-shared", "-fPIC",
+                               _SRC, "-o", tmp])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        L.oracle_histogram.argtypes = [_u8p, ctypes.c_uint64, _u64p]
+        L.oracle_huffman_lengths.argtypes = [_u64p, _intp]
+        L.oracle_huffman_lengths.restype = ctypes.c_int
+        L.oracle_canonical_codes.argtypes = [_intp, _u32p]
+        L.oracle_canonical_codes.restype = ctypes.c_int
+        L.oracle_total_bits.argtypes = [_u8p, ctypes.c_uint64, _intp]
+        L.oracle_total_bits.restype = ctypes.c_uint64
+        L.oracle_sizes.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                                   _u64p, _u64p, _u64p, _u64p, _u64p]
+        L.oracle_encode.argtypes = [_u8p, ctypes.c_uint64, _intp, ctypes.c_uint32, ctypes.c_uint32,
+                                    _u8p, _u8p, _u8p, _u64p]
+        L.oracle_encode.restype = ctypes.c_uint64
+        L.oracle_decode_range.argtypes = [_u8p, ctypes.c_uint64, _u8p, _intp, ctypes.c_uint64,
+                                          ctypes.c_uint64, ctypes.c_uint64, _u8p]
+        L.oracle_decode_range.restype = ctypes.c_uint64
+        L.oracle_decode.argtypes = [_u8p, ctypes.c_uint64, _u8p, ctypes.c_uint64, _intp, _u8p]
+        L.oracle_decode.restype = ctypes.c_uint64
+        L.oracle_check_layout.argtypes = [_u8p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                          _intp, ctypes.c_uint32, ctypes.c_uint32, _u8p, _u64p]
+        L.oracle_check_layout.restype = ctypes.c_int64
+        _lib = L
+    return _lib
+
+
+def _p(a, t):
+    return a.ctypes.data_as(t)
+
+
+def _c8(a):
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    return a
+
+
+def histogram(x: np.ndarray) -> np.ndarray:
+    x = _c8(x)
+    f = np.zeros(16, dtype=np.uint64)
+    lib().oracle_histogram(_p(x, _u8p), x.size, _p(f, _u64p))
+    return f
+
+
+def huffman_lengths(freq) -> np.ndarray:
+    f = np.ascontiguousarray(np.asarray(freq, dtype=np.uint64))
+    assert f.size == 16
+    L = np.zeros(16, dtype=np.intc)
+    lib().oracle_huffman_lengths(_p(f, _u64p), _p(L, _intp))
+    return L.astype(np.int64)
+
+
+def canonical_codes(lengths) -> np.ndarray:
+    L = np.ascontiguousarray(np.asarray(lengths, dtype=np.intc))
+    c = np.zeros(16, dtype=np.uint32)
+    rc = lib().oracle_canonical_codes(_p(L, _intp), _p(c, _u32p))
+    if rc != 0:
+        raise ValueError("bad code lengths")
+    return c.astype(np.int64)
+
+
+def sizes(n: int, total_bits: int, chunk_bytes: int, tb: int) -> dict:
+    out = [ctypes.c_uint64() for _ in range(5)]
+    lib().oracle_sizes(n, total_bits, chunk_bytes, tb, *[ctypes.byref(o) for o in out])
+    keys = ["n_chunks", "n_blocks", "stream_bytes", "nibble_bytes", "gap_bytes"]
+    return {k: int(o.value) for k, o in zip(keys, out)}
+
+
+def encode(x: np.ndarray, lengths=None, chunk_bytes: int = 16, tb: int = 256) -> dict:
+    """Histogram -> Huffman lengths (unless given) -> canonical code -> encode."""
+    x = _c8(x).ravel()
+    n = x.size
+    if lengths is None:
+        lengths = huffman_lengths(histogram(x))
+    L = np.ascontiguousarray(np.asarray(lengths, dtype=np.intc))
+    T = int(lib().oracle_total_bits(_p(x, _u8p), n, _p(L, _intp)))
+    sz = sizes(n, T, chunk_bytes, tb)
+    stream = np.zeros(sz["stream_bytes"], dtype=np.uint8)
+    nib = np.zeros(sz["nibble_bytes"], dtype=np.uint8)
+    gaps = np.zeros(sz["gap_bytes"], dtype=np.uint8)
+    blk = np.zeros(sz["n_blocks"] + 1, dtype=np.uint64)
+    T2 = lib().oracle_encode(_p(x, _u8p), n, _p(L, _intp), chunk_bytes, tb,
+                             _p(stream, _u8p), _p(nib, _u8p), _p(gaps, _u8p), _p(blk, _u64p))
+    if T2 == (1 << 64) - 1:
+        raise ValueError("oracle_encode: element with a zero-length code")
+    assert T2 == T
+    return dict(n=n, total_bits=T, lengths=L.astype(np.int64), chunk_bytes=chunk_bytes, tb=tb,
+                stream=stream, nibbles=nib, gaps=gaps, blk_off=blk, **sz)
+
+
+def decode(stream, nibbles, n: int, lengths) -> np.ndarray:
+    stream = _c8(stream)
+    nibbles = _c8(nibbles)
+    L = np.ascontiguousarray(np.asarray(lengths, dtype=np.intc))
+    out = np.zeros(max(n, 1), dtype=np.uint8)
+    r = lib().oracle_decode(_p(stream, _u8p), stream.size, _p(nibbles, _u8p), n, _p(L, _intp),
+                            _p(out, _u8p))
+    if r == (1 << 64) - 1:
+        raise ValueError("oracle_decode: invalid code in stream")
+    return out[:n]
+
+
+def decode_range(stream, nibbles, lengths, start_bit: int, first_elem: int, count: int):
+    """Decode `count` elements starting at codeword bit `start_bit`.
+    Returns (bytes, end_bit)."""
+    stream = _c8(stream)
+    nibbles = _c8(nibbles)
+    L = np.ascontiguousarray(np.asarray(lengths, dtype=np.intc))
+    out = np.zeros(max(count, 1), dtype=np.uint8)
+    r = lib().oracle_decode_range(_p(stream, _u8p), stream.size, _p(nibbles, _u8p), _p(L, _intp),
+                                  start_bit, first_elem, count, _p(out, _u8p))
+    if r == (1 << 64) - 1:
+        raise ValueError("oracle_decode_range: invalid code in stream")
+    return out[:count], int(r)
+
+
+def check_layout(stream, n: int, total_bits: int, lengths, chunk_bytes: int, tb: int,
+                 gaps, blk_off) -> int:
+    """0 if the stored gaps / block offsets match a fresh bit walk."""
+    stream = _c8(stream)
+    gaps = _c8(gaps)
+    blk = np.ascontiguousarray(np.asarray(blk_off, dtype=np.uint64))
+    L = np.ascontiguousarray(np.asarray(lengths, dtype=np.intc))
+    return int(lib().oracle_check_layout(_p(stream, _u8p), stream.size, n, total_bits, _p(L, _intp),
+                                         chunk_bytes, tb, _p(gaps, _u8p), _p(blk, _u64p)))
+
+
+# ---- fp64 statistics quoted by the pages (ECF8 blog §2.2, §3.1.1) ----
+
+def entropy_bits(freq) -> float:
+    """Shannon entropy H = -sum p log2 p of the exponent histogram (fp64)."""
+    f = np.asarray(freq, dtype=np.float64)
+    tot = f.sum()
+    if tot == 0:
+        return 0.0
+    p = f[f > 0] / tot
+    return float(-(p * np.log2(p)).sum())
+
+
+def average_length(freq, lengths) -> float:
+    """Expected code length sum p_s * len_s (fp64)."""
+    f = np.asarray(freq, dtype=np.float64)
+    tot = f.sum()
+    if tot == 0:
+        return 0.0
+    return float((f * np.asarray(lengths, dtype=np.float64)).sum() / tot)
+
+
+def kraft_sum(lengths) -> float:
+    L = [int(l) for l in lengths if int(l) > 0]
+    return float(sum(2.0 ** -l for l in L))
