@@ -197,6 +197,14 @@ int ecf8_decode_prepare(const ecf8_tensor_desc* descs, int count, uint8_t* out_b
  * hip_stream; the return code covers launch errors only. */
 int ecf8_decode_run(const ecf8_plan* plan, void* hip_stream);
 
+/* The two launches of ecf8_decode_run, for callers that schedule or time
+ * them separately: ecf8_build_tables (one workgroup per tensor, ECF8 blog
+ * §3.1.2) must precede ecf8_decode_blocks (the persistent decode dispatch,
+ * ECF8 blog §3.2.1) on the same stream.  Same arguments and errors as
+ * ecf8_decode_run. */
+int ecf8_build_tables(const ecf8_plan* plan, void* hip_stream);
+int ecf8_decode_blocks(const ecf8_plan* plan, void* hip_stream);
+
 /* prepare + run. */
 int ecf8_decode_batched(const ecf8_tensor_desc* descs, int count, uint8_t* out_base,
                         void* workspace, uint64_t workspace_bytes, void* hip_stream);

@@ -1,0 +1,356 @@
+"""ctypes binding of libecf8.so (include/ecf8.h).
+
+Argument marshalling only: every step of encode runs in the library's host
+code and every step of decode runs in its HIP kernels.  PyTorch provides
+device memory and the current HIP stream.  If the library is not built the
+import fails loudly -- there is no Python or CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libecf8.so")
+
+NSYM = 16
+DEFAULT_CHUNK_BYTES = 16
+DEFAULT_THREADS_PER_BLOCK = 256
+
+ERRORS = {0: "ok", -1: "ECF8_ERR_ARG", -2: "ECF8_ERR_SIZE", -3: "ECF8_ERR_META",
+          -4: "ECF8_ERR_UNSUPPORTED", -5: "ECF8_ERR_CORRUPT", -6: "ECF8_ERR_HIP",
+          -7: "ECF8_ERR_WORKSPACE"}
+
+
+class Ecf8Error(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s failed: %s (%d)" % (where, ERRORS.get(code, "?"), code))
+
+
+class Codebook(ctypes.Structure):
+    _fields_ = [("len", ctypes.c_uint8 * NSYM)]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("chunk_bytes", ctypes.c_uint32), ("threads_per_block", ctypes.c_uint32)]
+
+
+class Meta(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_uint64), ("total_bits", ctypes.c_uint64), ("n_chunks", ctypes.c_uint64),
+                ("n_blocks", ctypes.c_uint64), ("stream_bytes", ctypes.c_uint64),
+                ("nibble_bytes", ctypes.c_uint64), ("gap_bytes", ctypes.c_uint64),
+                ("chunk_bytes", ctypes.c_uint32), ("threads_per_block", ctypes.c_uint32),
+                ("cb", Codebook), ("max_len", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+class Stream(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("nibbles", ctypes.c_void_p), ("gaps", ctypes.c_void_p),
+                ("blk_off", ctypes.c_void_p)]
+
+
+class TensorDesc(ctypes.Structure):
+    _fields_ = [("s", Stream), ("meta", Meta), ("out_offset", ctypes.c_uint64)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
+                ("total_blocks", ctypes.c_uint64), ("count", ctypes.c_uint32),
+                ("chunk_bytes", ctypes.c_uint32), ("threads_per_block", ctypes.c_uint32),
+                ("grid", ctypes.c_uint32)]
+
+
+EXPORTS = ["ecf8_histogram", "ecf8_codebook_from_freq", "ecf8_build_codebook", "ecf8_canonical_codes",
+           "ecf8_encode_sizes", "ecf8_encode", "ecf8_validate_meta", "ecf8_workspace_bytes",
+           "ecf8_decode_prepare", "ecf8_decode_run", "ecf8_build_tables", "ecf8_decode_blocks",
+           "ecf8_decode_batched", "ecf8_decode",
+           "ecf8_decode_status", "ecf8_strerror", "ecf8_version"]
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libecf8.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libecf8.so is not built; run `python -m lossless_entropy_coded_ecf8_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    u8p, u64p, u32p, vp = (ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_uint64),
+                           ctypes.POINTER(ctypes.c_uint32), ctypes.c_void_p)
+    i = ctypes.c_int
+    sig = {
+        "ecf8_histogram": (i, [vp, ctypes.c_uint64, u64p]),
+        "ecf8_codebook_from_freq": (i, [u64p, ctypes.c_uint32, ctypes.POINTER(Codebook)]),
+        "ecf8_build_codebook": (i, [vp, ctypes.c_uint64, ctypes.c_uint32, ctypes.POINTER(Codebook)]),
+        "ecf8_canonical_codes": (i, [ctypes.POINTER(Codebook), u32p]),
+        "ecf8_encode_sizes": (i, [vp, ctypes.c_uint64, ctypes.POINTER(Codebook), ctypes.POINTER(Params),
+                                  ctypes.POINTER(Meta)]),
+        "ecf8_encode": (i, [vp, ctypes.c_uint64, ctypes.POINTER(Codebook), ctypes.POINTER(Params),
+                            vp, ctypes.c_uint64, vp, ctypes.c_uint64, vp, ctypes.c_uint64, vp,
+                            ctypes.c_uint64, ctypes.POINTER(Meta)]),
+        "ecf8_validate_meta": (i, [ctypes.POINTER(Meta)]),
+        "ecf8_workspace_bytes": (ctypes.c_uint64, [i]),
+        "ecf8_decode_prepare": (i, [ctypes.POINTER(TensorDesc), i, vp, vp, ctypes.c_uint64, vp,
+                                    ctypes.POINTER(Plan)]),
+        "ecf8_decode_run": (i, [ctypes.POINTER(Plan), vp]),
+        "ecf8_build_tables": (i, [ctypes.POINTER(Plan), vp]),
+        "ecf8_decode_blocks": (i, [ctypes.POINTER(Plan), vp]),
+        "ecf8_decode_batched": (i, [ctypes.POINTER(TensorDesc), i, vp, vp, ctypes.c_uint64, vp]),
+        "ecf8_decode": (i, [ctypes.POINTER(Stream), ctypes.POINTER(Meta), vp, ctypes.c_uint64, vp,
+                            ctypes.c_uint64, vp]),
+        "ecf8_decode_status": (i, [vp, vp, u64p]),
+        "ecf8_strerror": (ctypes.c_char_p, [i]),
+        "ecf8_version": (i, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise Ecf8Error(rc, where)
+
+
+def _u8(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # torch tensor on the CPU
+        x = x.detach().cpu().contiguous().view(-1).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.uint8).reshape(-1))
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data) if a.size else ctypes.c_void_p(0)
+
+
+# ------------------------------------------------------------------ host side
+
+def histogram(x) -> np.ndarray:
+    a = _u8(x)
+    f = (ctypes.c_uint64 * NSYM)()
+    _check(lib().ecf8_histogram(_ptr(a), a.size, f), "ecf8_histogram")
+    return np.array(list(f), dtype=np.uint64)
+
+
+def codebook_from_freq(freq, max_len: int = 16) -> np.ndarray:
+    f = (ctypes.c_uint64 * NSYM)(*[int(v) for v in freq])
+    cb = Codebook()
+    _check(lib().ecf8_codebook_from_freq(f, max_len, ctypes.byref(cb)), "ecf8_codebook_from_freq")
+    return np.array(list(cb.len), dtype=np.int64)
+
+
+def build_codebook(x, max_len: int = 16) -> np.ndarray:
+    a = _u8(x)
+    cb = Codebook()
+    _check(lib().ecf8_build_codebook(_ptr(a), a.size, max_len, ctypes.byref(cb)), "ecf8_build_codebook")
+    return np.array(list(cb.len), dtype=np.int64)
+
+
+def _codebook(lengths) -> Codebook:
+    cb = Codebook()
+    for s, l in enumerate(lengths):
+        cb.len[s] = int(l)
+    return cb
+
+
+def canonical_codes(lengths) -> np.ndarray:
+    out = (ctypes.c_uint32 * NSYM)()
+    cb = _codebook(lengths)
+    _check(lib().ecf8_canonical_codes(ctypes.byref(cb), out), "ecf8_canonical_codes")
+    return np.array(list(out), dtype=np.int64)
+
+
+def meta_dict(m: Meta) -> dict:
+    d = {k: getattr(m, k) for k, _ in Meta._fields_ if k not in ("cb", "reserved")}
+    d["lengths"] = list(m.cb.len)
+    return d
+
+
+def compressed_bytes(m: Meta) -> int:
+    """Bytes one decode must read: stream payload, nibble plane, gaps, block offsets."""
+    return int((m.total_bits + 7) // 8 + (m.n + 1) // 2 + (m.n_chunks + 1) // 2 + 8 * (m.n_blocks + 1))
+
+
+@dataclasses.dataclass
+class Encoded:
+    """Host-side encoded tensor (numpy buffers in the include/ecf8.h layout)."""
+    meta: Meta
+    stream: np.ndarray
+    nibbles: np.ndarray
+    gaps: np.ndarray
+    blk_off: np.ndarray
+    shape: tuple = ()
+
+    @property
+    def n(self) -> int:
+        return int(self.meta.n)
+
+    @property
+    def lengths(self) -> np.ndarray:
+        return np.array(list(self.meta.cb.len), dtype=np.int64)
+
+    def compressed_bytes(self) -> int:
+        return compressed_bytes(self.meta)
+
+    def to(self, device) -> "DeviceEncoded":
+        import torch
+        t = lambda a: torch.from_numpy(a).to(device)
+        return DeviceEncoded(self.meta, t(self.stream), t(self.nibbles), t(self.gaps),
+                             t(self.blk_off.view(np.int64)), self.shape)
+
+
+def encode(x, lengths=None, chunk_bytes: int = DEFAULT_CHUNK_BYTES,
+           threads_per_block: int = DEFAULT_THREADS_PER_BLOCK, max_len: int = 16) -> Encoded:
+    """Histogram -> Huffman code (unless `lengths` given) -> encode, all in libecf8."""
+    shape = tuple(x.shape) if hasattr(x, "shape") else ()
+    a = _u8(x)
+    cb = _codebook(build_codebook(a, max_len) if lengths is None else lengths)
+    p = Params(chunk_bytes, threads_per_block)
+    m = Meta()
+    _check(lib().ecf8_encode_sizes(_ptr(a), a.size, ctypes.byref(cb), ctypes.byref(p), ctypes.byref(m)),
+           "ecf8_encode_sizes")
+    stream = np.empty(m.stream_bytes, dtype=np.uint8)
+    nib = np.empty(m.nibble_bytes, dtype=np.uint8)
+    gaps = np.empty(m.gap_bytes, dtype=np.uint8)
+    blk = np.empty(m.n_blocks + 1, dtype=np.uint64)
+    m2 = Meta()
+    _check(lib().ecf8_encode(_ptr(a), a.size, ctypes.byref(cb), ctypes.byref(p), _ptr(stream), stream.size,
+                             _ptr(nib), nib.size, _ptr(gaps), gaps.size, _ptr(blk), blk.size,
+                             ctypes.byref(m2)), "ecf8_encode")
+    return Encoded(m2, stream, nib, gaps, blk, shape)
+
+
+def validate_meta(m: Meta) -> int:
+    return int(lib().ecf8_validate_meta(ctypes.byref(m)))
+
+
+def workspace_bytes(count: int) -> int:
+    return int(lib().ecf8_workspace_bytes(count))
+
+
+# ------------------------------------------------------------------ device side
+
+@dataclasses.dataclass
+class DeviceEncoded:
+    """Device-resident encoded tensor: four torch uint8/int64 tensors + metadata."""
+    meta: Meta
+    stream: "object"
+    nibbles: "object"
+    gaps: "object"
+    blk_off: "object"
+    shape: tuple = ()
+
+    @property
+    def n(self) -> int:
+        return int(self.meta.n)
+
+    def compressed_bytes(self) -> int:
+        return compressed_bytes(self.meta)
+
+    def c_stream(self) -> Stream:
+        return Stream(self.stream.data_ptr(), self.nibbles.data_ptr(), self.gaps.data_ptr(),
+                      self.blk_off.data_ptr())
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _workspace(count: int, device, workspace=None):
+    import torch
+    need = workspace_bytes(count)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def decode(enc: DeviceEncoded, out=None, workspace=None, stream=None):
+    """Single-tensor GPU decode (ecf8_decode).  Returns the uint8 output tensor."""
+    import torch
+    dev = enc.stream.device
+    if out is None:
+        out = torch.empty(max(enc.n, 1), dtype=torch.uint8, device=dev)[: enc.n]
+    ws = _workspace(1, dev, workspace)
+    s = enc.c_stream()
+    m = enc.meta
+    _check(lib().ecf8_decode(ctypes.byref(s), ctypes.byref(m), ctypes.c_void_p(out.data_ptr()), enc.n,
+                             ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_handle(stream)),
+           "ecf8_decode")
+    return out
+
+
+class DecodePlan:
+    """A prepared batched decode (ecf8_decode_prepare / ecf8_decode_run).
+
+    All tensors decode in one persistent dispatch into `out` (a reused uint8
+    buffer); tensor i lands at out[offsets[i] : offsets[i] + n_i].
+    """
+
+    def __init__(self, encs: Sequence[DeviceEncoded], out=None, offsets: Optional[List[int]] = None,
+                 workspace=None, stream=None):
+        import torch
+        self.encs = list(encs)
+        dev = self.encs[0].stream.device if self.encs else torch.device("cuda")
+        if offsets is None:
+            offsets, off = [], 0
+            for e in self.encs:
+                offsets.append(off)
+                off += (e.n + 255) // 256 * 256
+            total = off
+        else:
+            total = max([o + e.n for o, e in zip(offsets, self.encs)] + [0])
+        self.offsets = list(offsets)
+        self.out = out if out is not None else torch.empty(max(total, 1), dtype=torch.uint8, device=dev)
+        self.workspace = _workspace(len(self.encs), dev, workspace)
+        arr = (TensorDesc * max(1, len(self.encs)))()
+        for i, (e, o) in enumerate(zip(self.encs, self.offsets)):
+            arr[i].s = e.c_stream()
+            arr[i].meta = e.meta
+            arr[i].out_offset = o
+        self._descs = arr
+        self.plan = Plan()
+        _check(lib().ecf8_decode_prepare(arr, len(self.encs), ctypes.c_void_p(self.out.data_ptr()),
+                                         ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
+                                         _stream_handle(stream), ctypes.byref(self.plan)),
+               "ecf8_decode_prepare")
+
+    def run(self, stream=None):
+        _check(lib().ecf8_decode_run(ctypes.byref(self.plan), _stream_handle(stream)), "ecf8_decode_run")
+        return self.out
+
+    def build_tables(self, stream=None):
+        _check(lib().ecf8_build_tables(ctypes.byref(self.plan), _stream_handle(stream)), "ecf8_build_tables")
+
+    def decode_blocks(self, stream=None):
+        _check(lib().ecf8_decode_blocks(ctypes.byref(self.plan), _stream_handle(stream)), "ecf8_decode_blocks")
+        return self.out
+
+    def status(self, stream=None) -> int:
+        """Synchronize and return the number of blocks whose counts disagreed with blk_off."""
+        bad = ctypes.c_uint64(0)
+        rc = lib().ecf8_decode_status(ctypes.c_void_p(self.workspace.data_ptr()), _stream_handle(stream),
+                                      ctypes.byref(bad))
+        if rc not in (0, -5):
+            _check(rc, "ecf8_decode_status")
+        return int(bad.value)
+
+    def view(self, i: int):
+        return self.out[self.offsets[i]: self.offsets[i] + self.encs[i].n]
+
+
+def decode_batched(encs: Sequence[DeviceEncoded], out=None, offsets=None, workspace=None, stream=None):
+    """prepare + run in one call (ecf8_decode_batched semantics)."""
+    p = DecodePlan(encs, out, offsets, workspace, stream)
+    p.run(stream)
+    return p

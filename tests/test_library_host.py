@@ -1,0 +1,177 @@
+"""Host half of libecf8 vs the oracle (CPU only), and the C ABI surface."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import lossless_entropy_coded_ecf8_amd as E
+from lossless_entropy_coded_ecf8_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "ecf8.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w[\w\s\*]*?\b(ecf8_\w+)\s*\(", src, re.M)))
+
+
+def test_every_header_function_is_exported():
+    """libecf8.so loads on a CPU-only host and exports every declared entry point."""
+    names = header_functions()
+    assert len(names) >= 15
+    lib = E.lib()
+    for nm in names:
+        assert hasattr(lib, nm), nm
+    assert set(names) == set(B.EXPORTS)
+    assert lib.ecf8_version() >= 100
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -99):
+        assert lib.ecf8_strerror(code)
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_codebook_matches_oracle_including_ties(seed):
+    rng = np.random.default_rng(seed)
+    k = int(rng.integers(1, 17))
+    freq = np.zeros(16, dtype=np.uint64)
+    syms = rng.choice(16, k, replace=False)
+    if seed % 3 == 0:
+        freq[syms] = rng.integers(1, 4, k)                      # heavy ties
+    elif seed % 3 == 1:
+        freq[syms] = (10 ** rng.uniform(0, 9, k)).astype(np.uint64)  # huge spread, deep trees
+    else:
+        freq[syms] = rng.integers(1, 10 ** 6, k)
+    assert E.codebook_from_freq(freq).tolist() == oracle.huffman_lengths(freq).tolist()
+
+
+def test_fibonacci_depth_15_and_length_limit():
+    freq = [1, 1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144, 233, 377, 610, 987]
+    assert max(E.codebook_from_freq(freq, 15)) == 15
+    with pytest.raises(E.Ecf8Error) as ei:
+        E.codebook_from_freq(freq, 14)
+    assert ei.value.code == -4
+    with pytest.raises(E.Ecf8Error):
+        E.codebook_from_freq(freq, 17)
+
+
+@pytest.mark.parametrize("lengths", [None, [4] * 16, list(range(1, 16)) + [15]])
+def test_canonical_codes_match_oracle(lengths):
+    if lengths is None:
+        lengths = oracle.huffman_lengths(oracle.histogram(synth.small_stable(5000, 1.7, 1)))
+    assert E.canonical_codes(lengths).tolist() == oracle.canonical_codes(lengths).tolist()
+
+
+COMPLETE_CODES = {
+    "uniform4": [4] * 16,
+    "fib15": list(range(1, 16)) + [15],
+    "long12x6": list(range(1, 10)) + [11] + [12] * 6,
+    "two": [1, 1] + [0] * 14,
+}
+
+
+def cases():
+    out = []
+    for n in (0, 1, 2, 3, 7, 63, 64, 65, 1000, 4095, 4096, 4097, 33333):
+        out.append(("stable", n, None))
+    for name in COMPLETE_CODES:
+        out.append((name, 5000, COMPLETE_CODES[name]))
+    out.append(("single", 777, None))
+    out.append(("bytes", 9999, None))
+    return out
+
+
+def make_input(kind, n, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "stable":
+        return synth.small_stable(max(n, 1), 1.75, seed)[:n]
+    if kind == "single":
+        return np.full(n, 0x3B, dtype=np.uint8)
+    if kind == "bytes":
+        return synth.random_bytes(n, seed)
+    L = COMPLETE_CODES[kind]
+    present = [s for s in range(16) if L[s] > 0]
+    e = rng.choice(present, n).astype(np.uint8)
+    return ((rng.integers(0, 2, n, dtype=np.uint8) << 7) | (e << 3) | rng.integers(0, 8, n, dtype=np.uint8)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("C,TB", [(16, 256), (4, 64), (8, 128), (32, 64)])
+@pytest.mark.parametrize("case", cases(), ids=lambda c: "%s-%d" % (c[0], c[1]))
+def test_encode_byte_identical_to_oracle(case, C, TB):
+    kind, n, L = case
+    x = make_input(kind, n, n + C)
+    enc = E.encode(x, lengths=L, chunk_bytes=C, threads_per_block=TB)
+    ref = oracle.encode(x, lengths=L, chunk_bytes=C, tb=TB)
+    m = enc.meta
+    assert m.n == n and m.total_bits == ref["total_bits"]
+    for k in ("n_chunks", "n_blocks", "stream_bytes", "nibble_bytes", "gap_bytes"):
+        assert getattr(m, k) == ref[k], k
+    assert np.array_equal(enc.stream, ref["stream"])
+    assert np.array_equal(enc.nibbles, ref["nibbles"])
+    assert np.array_equal(enc.gaps, ref["gaps"])
+    assert np.array_equal(enc.blk_off, ref["blk_off"])
+    assert B.validate_meta(m) == 0
+    # the oracle decodes the library's stream back to x
+    assert np.array_equal(oracle.decode(enc.stream, enc.nibbles, n, enc.lengths), x)
+
+
+@pytest.mark.parametrize("threads", ["1", "3", "8"])
+def test_multithreaded_encoder_is_deterministic(threads, monkeypatch):
+    x = synth.small_stable(3_000_001, 1.6, 2)
+    monkeypatch.setenv("ECF8_THREADS", threads)
+    enc = E.encode(x)
+    ref = oracle.encode(x)
+    assert np.array_equal(enc.stream, ref["stream"])
+    assert np.array_equal(enc.gaps, ref["gaps"])
+    assert np.array_equal(enc.blk_off, ref["blk_off"])
+    assert np.array_equal(enc.nibbles, ref["nibbles"])
+
+
+def test_validate_meta_rejects_corruption():
+    x = synth.small_stable(50000, 1.8, 3)
+    m = E.encode(x).meta
+
+    def bad(mutate):
+        mm = B.Meta.from_buffer_copy(m)
+        mutate(mm)
+        return B.validate_meta(mm)
+
+    assert B.validate_meta(m) == 0
+    assert bad(lambda mm: setattr(mm, "n_blocks", mm.n_blocks + 1)) == -3
+    assert bad(lambda mm: setattr(mm, "total_bits", mm.total_bits + 4096)) == -3
+    assert bad(lambda mm: setattr(mm, "stream_bytes", mm.stream_bytes - 1)) == -3
+    assert bad(lambda mm: setattr(mm, "max_len", mm.max_len + 1)) == -3
+    assert bad(lambda mm: setattr(mm, "chunk_bytes", 6)) == -3
+
+    def kill_kraft(mm):
+        mm.cb.len[0] = mm.cb.len[0] + 1
+    assert bad(kill_kraft) == -3
+
+    def too_long(mm):
+        mm.cb.len[0] = 17
+    assert bad(too_long) == -3
+
+
+def test_encode_rejects_bad_arguments():
+    x = synth.small_stable(1000, 1.8, 4)
+    with pytest.raises(E.Ecf8Error) as ei:
+        E.encode(x, chunk_bytes=6)
+    assert ei.value.code == -1
+    with pytest.raises(E.Ecf8Error) as ei:
+        E.encode(x, threads_per_block=100)
+    assert ei.value.code == -1
+    L = oracle.huffman_lengths(oracle.histogram(x)).copy()
+    present = int(np.nonzero(L)[0][0])
+    L2 = [4] * 16
+    L2[present] = 0                       # a present symbol without a code
+    with pytest.raises(E.Ecf8Error) as ei:
+        E.encode(x, lengths=L2)
+    assert ei.value.code == -3
+
+
+def test_workspace_size_grows_with_count():
+    a, b = E.workspace_bytes(1), E.workspace_bytes(768)
+    assert 0 < a < b
+    assert b % 256 == 0
