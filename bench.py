@@ -79,13 +79,14 @@ def cpu_baseline(encs_host, seconds: float):
         return hi - lo
 
     oracle.lib()
-    # calibrate on one block per core, then size the sample to ~`seconds` of wall time
+    # calibrate on 32 blocks per core, then size the sample to ~`seconds` of wall time
+    cal = min(int(m.n_blocks) // 2, 32 * cores)
     t0 = time.perf_counter()
     with concurrent.futures.ThreadPoolExecutor(cores) as ex:
-        done = sum(ex.map(one, range(cores)))
+        done = sum(ex.map(one, range(cal)))
     dt = time.perf_counter() - t0
-    nblk = int(max(cores, min(m.n_blocks - cores, cores * int(seconds / max(dt, 1e-6)))))
-    blocks = list(range(cores, cores + nblk))
+    nblk = int(max(cores, min(int(m.n_blocks) - cal, cal * seconds / max(dt, 1e-6))))
+    blocks = list(range(cal, cal + nblk))
     t0 = time.perf_counter()
     with concurrent.futures.ThreadPoolExecutor(cores) as ex:
         done = sum(ex.map(one, blocks))
