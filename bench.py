@@ -60,6 +60,24 @@ def load_traffic(workload: str, kernel_hash: str, launches_bytes: float):
     return rec.get("traffic_bytes_per_launch")
 
 
+def copy_ceiling(torch, d, gib: float = 1.0, reps: int = 5):
+    """Event-timed plain streaming kernel (uint8 bitwise_not: reads and writes `gib` GiB each)."""
+    n = int(gib * (1 << 30))
+    a = torch.empty(n, dtype=torch.uint8, device=d).fill_(0x5A)
+    b = torch.empty_like(a)
+    torch.bitwise_not(a, out=b)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        torch.bitwise_not(a, out=b)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del a, b
+    return 2.0 * n / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(encs_host, seconds: float):
     """Time the C oracle decoding whole blocks of the largest tensor, all host cores."""
     import numpy as np
@@ -163,6 +181,7 @@ def main():
     step_ms = start.elapsed_time(end) / K
     dec_ms = sum(a.elapsed_time(b) for a, b in ev) / K
 
+    copy_gbs = copy_ceiling(torch, d)
     bb = batch_bytes(encs)
     n_total = bb["written"]
     value = n_total / (step_ms * 1e-3) / 1e9
@@ -188,7 +207,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "ecf8_decode_kernel", "kernel_ms": round(dec_ms, 5),
-                     "algorithmic_bytes": bb["total"], "kernel_sha": khash},
+                     "algorithmic_bytes": bb["total"], "kernel_sha": khash,
+                     "copy_ceiling_gbs": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4)},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")

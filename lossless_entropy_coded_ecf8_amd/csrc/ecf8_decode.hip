@@ -49,11 +49,12 @@ namespace {
 constexpr int kWin = 11;                                            // primary window bits
 constexpr int kLongPrefixMax = 8;                                   // prefixes of codes > kWin bits
 constexpr int kTableMax = (1 << kWin) + ((1 << (16 - kWin)) - 1) * kLongPrefixMax;  // 2296
-constexpr uint32_t kTableStrideEntries = 2304;                      // 18432 B per tensor table
+constexpr uint32_t kTabStride = 2304;                               // entries per table array
 constexpr int kChunk = 16;                                          // C
 constexpr int kLanes = 256;                                         // TB
 constexpr uint64_t kStatusBytes = 256;
 constexpr int kTableThreads = 256;
+constexpr int kNibPrefetch = 4;                                     // write-back groups prefetched per lane
 
 // Device descriptor of one tensor (workspace resident).
 struct alignas(16) DevDesc {
@@ -81,12 +82,42 @@ uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
 uint64_t desc_offset() { return kStatusBytes; }
 uint64_t table_offset(int count) { return kStatusBytes + round_up((uint64_t)count * sizeof(DevDesc), 256); }
+constexpr uint64_t kTableBytes = 2ull * kTabStride * sizeof(uint32_t);   // X and Y arrays
+
+// Global-memory accessors: descriptor pointers are generic; casting them to
+// the global address space makes the compiler emit global_* (not flat_*)
+// instructions, which only touch the vector-memory counter.
+#define ECF8_GLOBAL __attribute__((address_space(1)))
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <class T>
+__device__ __forceinline__ T gld(const T* p) { return *(const ECF8_GLOBAL T*)(p); }
+template <class T>
+__device__ __forceinline__ void gst(T* p, const T& v) { *(ECF8_GLOBAL T*)(p) = v; }
+__device__ __forceinline__ uint4 gld4(const void* p)
+{
+    const u32x4 v = *(const ECF8_GLOBAL u32x4*)(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 gld2(const void* p)
+{
+    const u32x2 v = *(const ECF8_GLOBAL u32x2*)(p);
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void gst4(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    u32x4 v;
+    v.x = a; v.y = b; v.z = c; v.w = d;
+    *(ECF8_GLOBAL u32x4*)(p) = v;
+}
 
 // ------------------------------------------------------------ table kernel
-// One workgroup per tensor.  Entry layout: .x = bits consumed | (symbols << 16),
-// .y = symbols as nibbles, first symbol in the low nibble.
+// One workgroup per tensor.  Two arrays per tensor (structure of arrays, so a
+// lane reading only X touches every LDS bank):
+//   X[idx] = bits consumed | (4 * symbols) << 16,
+//   Y[idx] = symbols as nibbles, first symbol in the low nibble.
 __global__ __launch_bounds__(kTableThreads) void ecf8_table_kernel(DevDesc* __restrict__ descs,
-                                                                   uint2* __restrict__ tables)
+                                                                   uint32_t* __restrict__ tables)
 {
     __shared__ uint32_t s_start[16];   // left-justified 16-bit first code of k-th codeword (canonical order)
     __shared__ uint32_t s_len[16];
@@ -134,7 +165,8 @@ __global__ __launch_bounds__(kTableThreads) void ecf8_table_kernel(DevDesc* __re
     __syncthreads();
     const int k = (int)s_info[0];
     const uint32_t p_long = s_info[1], cdelta = s_info[2], entries = s_info[3];
-    uint2* tab = tables + (uint64_t)blockIdx.x * kTableStrideEntries;
+    uint32_t* tx = tables + (uint64_t)blockIdx.x * (2 * kTabStride);
+    uint32_t* ty = tx + kTabStride;
     for (uint32_t idx = threadIdx.x; idx < entries; idx += kTableThreads) {
         uint32_t v, known;
         if (idx < p_long) {
@@ -160,7 +192,8 @@ __global__ __launch_bounds__(kTableThreads) void ecf8_table_kernel(DevDesc* __re
             ns++;
             pos += l;
         }
-        tab[idx] = make_uint2((pos ? pos : 1u) | (ns << 16), sy);
+        tx[idx] = (pos ? pos : 1u) | ((4 * ns) << 16);
+        ty[idx] = sy;
     }
 }
 
@@ -180,110 +213,262 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane)
     return v;
 }
 
+__device__ __forceinline__ uint32_t bitsel(uint32_t mask, uint32_t a, uint32_t b)
+{
+    return (a & mask) | (b & ~mask);   // v_bfi_b32
+}
+
 // 8 exponent nibbles (e) + 8 sign/mantissa nibbles (nm), element i in nibble i,
 // -> 8 FP8 bytes: byte = (s << 7) | (e << 3) | m with nm = (s << 3) | m.
 __device__ __forceinline__ uint2 assemble8(uint32_t e, uint32_t nm)
 {
-    // even elements 0,2,4,6 -> bytes of ev; odd 1,3,5,7 -> bytes of od
-    const uint32_t nev = (nm & 0x0F0F0F0Fu) | ((nm << 4) & 0xF0F0F0F0u);   // nibble copied to both halves
-    const uint32_t nod = ((nm >> 4) & 0x0F0F0F0Fu) | (nm & 0xF0F0F0F0u);
-    const uint32_t ev = ((e << 3) & 0x78787878u) | (nev & 0x87878787u);
-    const uint32_t od = ((e >> 1) & 0x78787878u) | (nod & 0x87878787u);
+    const uint32_t nev = bitsel(0xF0F0F0F0u, nm << 4, nm);   // byte j: nibble 2j in both halves
+    const uint32_t nod = bitsel(0x0F0F0F0Fu, nm >> 4, nm);   // byte j: nibble 2j+1 in both halves
+    const uint32_t ev = bitsel(0x78787878u, e << 3, nev);    // elements 0,2,4,6
+    const uint32_t od = bitsel(0x78787878u, e >> 1, nod);    // elements 1,3,5,7
     uint2 r;
-    r.x = (ev & 0xFFu) | ((od & 0xFFu) << 8) | ((ev & 0xFF00u) << 8) | ((od & 0xFF00u) << 16);
-    r.y = ((ev >> 16) & 0xFFu) | ((od >> 8) & 0xFF00u) | (ev & 0xFF000000u) >> 8 | (od & 0xFF000000u);
+    r.x = __builtin_amdgcn_perm(od, ev, 0x05010400u);         // e0 e1 e2 e3
+    r.y = __builtin_amdgcn_perm(od, ev, 0x07030602u);         // e4 e5 e6 e7
     return r;
+}
+
+// Write back group g (elements 16g .. 16g+15 of the block-relative range):
+// exponent nibbles from the LDS staging, sign/mantissa nibbles nm from HBM.
+__device__ __forceinline__ void group_bytes(const uint32_t* s_out, uint32_t g, uint2 nm, uint32_t w[4])
+{
+    const uint2 ex = reinterpret_cast<const uint2*>(s_out)[g];
+    const uint2 r0 = assemble8(ex.x, nm.x);
+    const uint2 r1 = assemble8(ex.y, nm.y);
+    w[0] = r0.x;
+    w[1] = r0.y;
+    w[2] = r1.x;
+    w[3] = r1.y;
+}
+
+// A group fully inside the block's range: one 16-byte store.
+__device__ __forceinline__ void write_full(const uint32_t* s_out, uint8_t* out_blk, uint32_t g, uint2 nm)
+{
+    uint32_t w[4];
+    group_bytes(s_out, g, nm, w);
+    gst4(out_blk + 16u * g, w[0], w[1], w[2], w[3]);
+}
+
+// One of the (at most two) ragged edge groups of a block: store only the
+// bytes inside [a0, endo).
+__device__ __forceinline__ void write_edge(const uint32_t* s_out, uint8_t* out_blk, uint32_t g, uint2 nm,
+                                           uint32_t a0, uint32_t endo)
+{
+    uint32_t w[4];
+    group_bytes(s_out, g, nm, w);
+    const uint32_t e0 = 16u * g;
+    const uint32_t kb = e0 < a0 ? a0 - e0 : 0u;
+    const uint32_t ke = endo - e0 < 16u ? endo - e0 : 16u;
+    for (uint32_t q = kb; q < ke; ++q) gst(out_blk + e0 + q, (uint8_t)(w[q >> 2] >> (8 * (q & 3))));
 }
 
 // ------------------------------------------------------------ decode kernel
 template <int C, int TB>
 struct DecodeLds {
     static constexpr int kSlot = C / 4 + 1;                                   // dwords per lane slot
-    static constexpr int kStreamDw = 1 + TB * kSlot;
+    static constexpr int kStreamDw = TB * kSlot + 2;
     static constexpr int kOutDw = ((8 * C * TB + 15 + 8 + 16) / 8 + 2 + 3) / 4 * 4;   // nibble staging
 };
+
+// Per-block inputs loaded one block ahead (software pipelining of the
+// persistent loop: HBM latency overlaps the previous block's decode).  The
+// block offsets are loaded lane-parallel (lane 0: blk_off[b], lane 1:
+// blk_off[b+1]) and broadcast with readlane where they are first needed, so
+// that no wait for the prefetch is forced right after it is issued.
+struct BlockIn {
+    uint4 sv;          // the lane's 16 stream bytes
+    uint32_t la;       // first dword of the next lane's chunk (look-ahead)
+    uint32_t gb;       // byte holding the lane's gap
+    uint64_t off;      // lane 0: blk_off[b]; lane 1: blk_off[b + 1]
+};
+
+// Descriptor fields the prefetch needs, cached in registers per tensor.
+struct NextTensor {
+    int t;
+    uint64_t begin, end;
+    const uint8_t* stream;
+    const uint8_t* gaps;
+    const uint64_t* blk_off;
+};
+
+__device__ __forceinline__ void fetch_next_tensor(const DevDesc* descs, int t, NextTensor& nt)
+{
+    const DevDesc* d = descs + t;
+    nt.t = t;
+    nt.begin = d->block_begin;
+    nt.end = d->block_end;
+    nt.stream = d->stream;
+    nt.gaps = d->gaps;
+    nt.blk_off = d->blk_off;
+}
+
+__device__ __forceinline__ void load_block(const NextTensor& nt, uint64_t gblk, int tid, BlockIn& in)
+{
+    const uint64_t b = gblk - nt.begin;
+    const uint64_t chunk = b * kLanes + tid;
+    const uint8_t* sp = nt.stream + chunk * kChunk;
+    in.sv = gld4(sp);
+    in.la = gld(reinterpret_cast<const uint32_t*>(sp + kChunk));
+    in.gb = gld(nt.gaps + (chunk >> 1));
+    in.off = gld(nt.blk_off + b + (tid & 1));
+}
+
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l)
+{
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
 
 template <int C, int TB>
 __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restrict__ descs, int count,
                                                          uint64_t total_blocks,
-                                                         const uint2* __restrict__ tables,
+                                                         const uint32_t* __restrict__ tables,
                                                          unsigned long long* __restrict__ status)
 {
+    static_assert(C == kChunk && TB == kLanes, "one instantiation");
     using L = DecodeLds<C, TB>;
     constexpr int kWaves = TB / 64;
-    __shared__ uint2 s_table[kTableMax];
-    __shared__ uint32_t s_stream[L::kStreamDw];
-    __shared__ __align__(16) uint32_t s_out[L::kOutDw];
-    __shared__ uint32_t s_wsum[kWaves];
+    constexpr int S = L::kSlot;
+    // one LDS arena: table X | table Y (256-byte aligned, so X[i] and Y[i]
+    // are one ds_read2st64) | lane stream slots | nibble staging | wave sums
+    constexpr int kStreamOff = 2 * kTabStride;
+    constexpr int kOutOff = (kStreamOff + L::kStreamDw + 3) / 4 * 4;
+    constexpr int kSumOff = kOutOff + L::kOutDw;
+    __shared__ __align__(256) uint32_t lds[kSumOff + kWaves];
+    uint32_t* const s_tx = lds;
+    uint32_t* const s_ty = lds + kTabStride;
+    uint32_t* const s_stream = lds + kStreamOff;
+    uint32_t* const s_out = lds + kOutOff;
+    uint32_t* const s_wsum = lds + kSumOff;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    uint32_t* const slot_m1 = s_stream + tid * L::kSlot;   // dword before this lane's slot
+    // Lane slot, stored in reverse word order: word k (k = -1..S-1, where
+    // k = S-1 is the look-ahead and k = -1 aliases the next lane's look-ahead)
+    // lives at s_stream[tid*S + S - k].  With r = 192 - bitpos, the window
+    // pair (word ceil(bitpos/32)-1, next word) sits at dwords
+    // tid*S + (r >> 5) and tid*S + (r >> 5) - 1, and the funnel shift is r & 31.
+    uint32_t* const slot = s_stream + tid * S;
+    const uint32_t slot_addr = (uint32_t)(tid * S - 1) * 4u;   // byte address of slot[-1] within s_stream
+    const char* const s_stream_b = reinterpret_cast<const char*>(s_stream);
 
+    uint64_t blk = blockIdx.x;
+    if (blk >= total_blocks) return;
+
+    NextTensor nt;
+    fetch_next_tensor(descs, 0, nt);
+    while (nt.t + 1 < count && blk >= nt.end) fetch_next_tensor(descs, nt.t + 1, nt);
+    BlockIn nx;
+    load_block(nt, blk, tid, nx);
+    int ptens = nt.t;                  // tensor of the prefetched block
+
+    // fields of the tensor being decoded
     int cur = -1;
-    int t = 0;
-    for (uint64_t blk = blockIdx.x; blk < total_blocks; blk += gridDim.x) {
-        while (t + 1 < count && blk >= descs[t].block_end) t++;
-        const DevDesc* d = descs + t;
-        if (t != cur) {
-            __syncthreads();
+    uint64_t c_begin = 0, c_n = 0, c_T = 0, c_lenpack = 0;
+    const uint8_t* c_nib = nullptr;
+    uint8_t* c_out = nullptr;
+    int c_cd = 0;
+    uint32_t c_ok = 0;
+
+    for (; blk < total_blocks; blk += gridDim.x) {
+        const BlockIn in = nx;
+        if (ptens != cur) {
+            const DevDesc* d = descs + ptens;
+            c_begin = d->block_begin;
+            c_n = d->n;
+            c_T = d->total_bits;
+            c_lenpack = d->lenpack;
+            c_nib = d->nibbles;
+            c_out = d->out;
+            c_cd = d->cdelta;
             uint32_t ne = d->entries;
-            if (ne == 0) {               // tables were never built for this plan: flag and skip
-                if (tid == 0) atomicAdd(status, 1ull);
-                continue;
-            }
+            c_ok = ne != 0;                       // 0: tables were never built for this plan
             ne = ne < (uint32_t)kTableMax ? ne : (uint32_t)kTableMax;
-            const uint2* tab = tables + (uint64_t)t * kTableStrideEntries;
-            for (uint32_t i = tid; i < ne; i += TB) s_table[i] = tab[i];
-            cur = t;
+            const uint32_t* tx = tables + (uint64_t)ptens * (2 * kTabStride);
+            __syncthreads();
+            for (uint32_t i = tid; i < ne; i += TB) {
+                s_tx[i] = gld(tx + i);
+                s_ty[i] = gld(tx + kTabStride + i);
+            }
+            cur = ptens;
             __syncthreads();
         }
-        const uint64_t b = blk - d->block_begin;
+        const uint64_t b = blk - c_begin;
         const uint64_t chunk = b * TB + tid;
-        const uint64_t T = d->total_bits;
         const uint64_t cstart = chunk * (8ull * C);
-        const uint32_t E = cstart >= T ? 0u : (uint32_t)((T - cstart) < 8ull * C ? (T - cstart) : 8ull * C);
-        const uint32_t gap = ((uint32_t)d->gaps[chunk >> 1] >> ((chunk & 1) * 4)) & 15u;
-        const uint4 sv = *reinterpret_cast<const uint4*>(d->stream + chunk * C);
-        const uint32_t la = *reinterpret_cast<const uint32_t*>(d->stream + chunk * C + C);
-        slot_m1[1] = __builtin_bswap32(sv.x);
-        slot_m1[2] = __builtin_bswap32(sv.y);
-        slot_m1[3] = __builtin_bswap32(sv.z);
-        slot_m1[4] = __builtin_bswap32(sv.w);
-        slot_m1[5] = __builtin_bswap32(la);
-        const uint64_t lo = d->blk_off[b];
-        const uint64_t hi_raw = d->blk_off[b + 1];
-        const int cd = d->cdelta;
-        const uint64_t lenpack = d->lenpack;
+        uint32_t E = cstart >= c_T ? 0u : (uint32_t)((c_T - cstart) < 8ull * C ? (c_T - cstart) : 8ull * C);
+        E = c_ok ? E : 0u;
+        const uint32_t gap = (in.gb >> ((chunk & 1) * 4)) & 15u;
+
+        // stage the chunk (big-endian words, reversed order) into the lane's slot
+        slot[S] = __builtin_bswap32(in.sv.x);
+        slot[S - 1] = __builtin_bswap32(in.sv.y);
+        slot[S - 2] = __builtin_bswap32(in.sv.z);
+        slot[S - 3] = __builtin_bswap32(in.sv.w);
+        slot[S - 4] = __builtin_bswap32(in.la);
+
+        // block output range and its 16-element groups; prefetch the sign/mantissa plane
+        const uint64_t lo_raw = lane_u64(in.off, 0), hi_raw = lane_u64(in.off, 1);
+        const uint64_t hi = hi_raw < c_n ? hi_raw : c_n;
+        const uint64_t lo = lo_raw < hi ? lo_raw : hi;
+        const uint64_t want = hi - lo;
+        const uint32_t cap = 8u * C * TB;
+        const uint32_t nw = want < cap ? (uint32_t)want : cap;
+        const uint64_t base = lo & ~15ull;
+        const uint32_t a0 = (uint32_t)(lo - base);
+        const uint32_t groups = (a0 + nw + 15) >> 4;
+        const uint8_t* nib_blk = c_nib + (base >> 1);
+        uint2 nv[kNibPrefetch];
+#pragma unroll
+        for (int k = 0; k < kNibPrefetch; ++k) {
+            const uint32_t g = tid + k * TB;
+            nv[k] = g < groups ? gld2(nib_blk + 8ull * g) : make_uint2(0, 0);
+        }
+
+        // prefetch the next block of this workgroup
+        {
+            const uint64_t nb = blk + gridDim.x;
+            if (nb < total_blocks) {
+                while (nt.t + 1 < count && nb >= nt.end) fetch_next_tensor(descs, nt.t + 1, nt);
+                load_block(nt, nb, tid, nx);
+                ptens = nt.t;
+            }
+        }
 
         // ---- phase 2: count the codewords that start inside [gap, E)
-        const uint32_t pend = E + 31;
-        uint32_t p = gap + 31;              // bit position + 31 (see window below)
-        uint32_t cnt = 0, last_p = 0, last_idx = 0;
-        while (p < pend) {
-            // window of 32 stream bits starting at bit p - 31:
-            // dwords (p >> 5) - 1 and (p >> 5) of the slot, shifted by (-(p-31)) & 31
-            const uint32_t w0 = slot_m1[p >> 5];
-            const uint32_t w1 = slot_m1[(p >> 5) + 1];
-            const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, ~p);
-            const int idx = max((int)(win >> (32 - kWin)), (int)(win >> 16) - cd);
-            const uint32_t ex = s_table[idx].x;
-            last_p = p;
-            last_idx = (uint32_t)idx;
-            p += ex & 0xFFFFu;
-            cnt += ex >> 16;
+        const int cd = c_cd;
+        const uint32_t rend = 192u - E;
+        const uint32_t r0 = 192u - gap;
+        uint32_t r = r0;
+        uint32_t cnt4 = 0, idx = 0;
+        while (r > rend) {
+            const uint32_t a = slot_addr + 4u * __builtin_amdgcn_ubfe(r, 5, 3);
+            const uint32_t w1 = *reinterpret_cast<const uint32_t*>(s_stream_b + a);
+            const uint32_t w0 = *reinterpret_cast<const uint32_t*>(s_stream_b + a + 4);
+            const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, r);
+            idx = (uint32_t)max((int)(win >> (32 - kWin)), (int)(win >> 16) - cd);
+            const uint32_t ex = s_tx[idx];
+            r -= ex & 0xFFFFu;
+            cnt4 += ex >> 16;
         }
-        if (last_p) {
-            // the last lookup may have decoded codewords that start at or after E
-            const uint2 e = s_table[last_idx];
-            const uint32_t room = pend - last_p;
-            const uint32_t ns = e.x >> 16;
-            uint32_t sy = e.y, start = 0, keep = 0;
+        uint32_t cnt = cnt4 >> 2;
+        if (r != r0) {
+            // the last lookup (at r + its bit count) may have decoded codewords
+            // that start at or after E: keep those starting before E
+            const uint32_t ex = s_tx[idx];
+            const uint32_t ns = ex >> 18;
+            const uint32_t room = r + (ex & 0xFFFFu) - rend;
+            uint32_t sy = s_ty[idx], start = 0, keep = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 if ((uint32_t)i < ns) {
                     keep += start < room ? 1u : 0u;
-                    start += (uint32_t)((lenpack >> (4 * (sy & 15))) & 15) + 1;
+                    start += (uint32_t)((c_lenpack >> (4 * (sy & 15))) & 15) + 1;
                     sy >>= 4;
                 }
             }
@@ -297,62 +482,62 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
         uint32_t before = 0, total = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const uint32_t s = s_wsum[w];
-            before += (w < wave) ? s : 0u;
-            total += s;
+            const uint32_t sw = s_wsum[w];
+            before += (w < wave) ? sw : 0u;
+            total += sw;
         }
         const uint32_t pos = before + incl - cnt;
         for (int i = tid; i < L::kOutDw / 4; i += TB) reinterpret_cast<uint4*>(s_out)[i] = make_uint4(0, 0, 0, 0);
         __syncthreads();
 
         // ---- phase 4: cooperative decode into the LDS staging (packed nibbles)
-        const uint32_t a0 = (uint32_t)(lo & 15);
-        uint32_t o = a0 + pos;
-        p = gap + 31;
-        while (p < pend) {
-            const uint32_t w0 = slot_m1[p >> 5];
-            const uint32_t w1 = slot_m1[(p >> 5) + 1];
-            const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, ~p);
+        uint32_t ob = (a0 + pos) * 4;      // bit offset of the lane's first nibble in the staging
+        r = r0;
+        while (r > rend) {
+            const uint32_t a = slot_addr + 4u * __builtin_amdgcn_ubfe(r, 5, 3);
+            const uint32_t w1 = *reinterpret_cast<const uint32_t*>(s_stream_b + a);
+            const uint32_t w0 = *reinterpret_cast<const uint32_t*>(s_stream_b + a + 4);
+            const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, r);
             const int idx = max((int)(win >> (32 - kWin)), (int)(win >> 16) - cd);
-            const uint2 e = s_table[idx];
-            const uint64_t v = (uint64_t)e.y << ((o & 7) * 4);
-            const uint32_t wa = o >> 3;
+            const uint32_t ex = s_tx[idx];
+            const uint32_t sy = s_ty[idx];
+            const uint64_t v = (uint64_t)sy << (ob & 31);
+            const uint32_t wa = ob >> 5;
             atomicOr(&s_out[wa], (uint32_t)v);
             atomicOr(&s_out[wa + 1], (uint32_t)(v >> 32));
-            o += e.x >> 16;
-            p += e.x & 0xFFFFu;
+            ob += ex >> 16;
+            r -= ex & 0xFFFFu;
         }
         __syncthreads();
 
-        // ---- phase 5: write back [lo, hi) of this tensor
-        const uint64_t n = d->n;
-        const uint64_t hi = hi_raw < n ? hi_raw : n;
-        const uint64_t lo_c = lo < hi ? lo : hi;
-        const uint64_t want = hi - lo_c;
-        if (tid == 0 && want != total) atomicAdd(status, 1ull);
-        const uint32_t cap = 8u * C * TB;
-        const uint32_t nw = want < cap ? (uint32_t)want : cap;
-        const uint64_t base = lo_c & ~15ull;
-        const uint32_t groups = ((uint32_t)(lo_c - base) + nw + 15) >> 4;
-        const uint64_t end = lo_c + nw;
-        const uint8_t* __restrict__ nib = d->nibbles;
-        uint8_t* __restrict__ out = d->out;
-        for (uint32_t g = tid; g < groups; g += TB) {
-            const uint2 ex = reinterpret_cast<const uint2*>(s_out)[g];
-            const uint64_t e0 = base + 16ull * g;
-            const uint2 nv = *reinterpret_cast<const uint2*>(nib + (e0 >> 1));
-            const uint2 r0 = assemble8(ex.x, nv.x);
-            const uint2 r1 = assemble8(ex.y, nv.y);
-            if (e0 >= lo_c && e0 + 16 <= end) {
-                *reinterpret_cast<uint4*>(out + e0) = make_uint4(r0.x, r0.y, r1.x, r1.y);
-            } else {
-                const uint32_t wv[4] = {r0.x, r0.y, r1.x, r1.y};
+        // ---- phase 5: write back [lo, lo + nw) as 16-element groups
+        if (tid == 0 && (want != total || !c_ok)) atomicAdd(status, 1ull);
+        uint8_t* const out_blk = c_out + base;
+        const uint32_t endo = a0 + nw;                 // one past the last valid element, group-relative
+        const uint32_t first_full = a0 ? 1u : 0u;
+        const uint32_t end_full = endo >> 4;           // groups [first_full, end_full) are whole
+        // assemble every prefetched group first, then issue the stores back to back:
+        // stores share the vector-memory counter with loads, so no wait falls between them
+        uint32_t wb[kNibPrefetch][4];
 #pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    const uint64_t j = e0 + k;
-                    if (j >= lo_c && j < end) out[j] = (uint8_t)(wv[k >> 2] >> (8 * (k & 3)));
-                }
-            }
+        for (int k = 0; k < kNibPrefetch; ++k) group_bytes(s_out, tid + k * TB, nv[k], wb[k]);
+#pragma unroll
+        for (int k = 0; k < kNibPrefetch; ++k) {
+            const uint32_t g = tid + k * TB;
+            if (g >= first_full && g < end_full) gst4(out_blk + 16u * g, wb[k][0], wb[k][1], wb[k][2], wb[k][3]);
+        }
+        for (uint32_t g = tid + kNibPrefetch * TB; g < end_full; g += TB)   // blocks of > 16K elements
+            write_full(s_out, out_blk, g, gld2(nib_blk + 8ull * g));
+        // ragged edges: group 0 when the range starts mid-group, group end_full when it ends mid-group
+        if (a0 && tid == 0) write_edge(s_out, out_blk, 0, nv[0], a0, endo);
+        if (end_full < groups && !(end_full == 0 && a0) && tid == (int)(end_full % TB)) {
+            const uint32_t k = end_full / TB;
+            uint2 nm = nv[0];
+#pragma unroll
+            for (int q = 1; q < kNibPrefetch; ++q)
+                if (k == (uint32_t)q) nm = nv[q];
+            if (k >= (uint32_t)kNibPrefetch) nm = gld2(nib_blk + 8ull * end_full);
+            write_edge(s_out, out_blk, end_full, nm, a0, endo);
         }
     }
 }
@@ -394,7 +579,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 extern "C" uint64_t ecf8_workspace_bytes(int count)
 {
     if (count < 0) return 0;
-    return table_offset(count) + (uint64_t)count * kTableStrideEntries * sizeof(uint2);
+    return table_offset(count) + (uint64_t)count * kTableBytes;
 }
 
 extern "C" int ecf8_decode_prepare(const ecf8_tensor_desc* descs, int count, uint8_t* out_base,
@@ -473,7 +658,7 @@ extern "C" int ecf8_build_tables(const ecf8_plan* plan, void* hip_stream)
     if (rc || plan->count == 0 || plan->total_blocks == 0) return rc;
     unsigned char* ws = static_cast<unsigned char*>(plan->workspace);
     DevDesc* dd = reinterpret_cast<DevDesc*>(ws + desc_offset());
-    uint2* tables = reinterpret_cast<uint2*>(ws + table_offset((int)plan->count));
+    uint32_t* tables = reinterpret_cast<uint32_t*>(ws + table_offset((int)plan->count));
     hipLaunchKernelGGL(ecf8_table_kernel, dim3(plan->count), dim3(kTableThreads), 0,
                        reinterpret_cast<hipStream_t>(hip_stream), dd, tables);
     return hipGetLastError() == hipSuccess ? ECF8_OK : ECF8_ERR_HIP;
@@ -485,7 +670,7 @@ extern "C" int ecf8_decode_blocks(const ecf8_plan* plan, void* hip_stream)
     if (rc || plan->count == 0 || plan->total_blocks == 0) return rc;
     unsigned char* ws = static_cast<unsigned char*>(plan->workspace);
     DevDesc* dd = reinterpret_cast<DevDesc*>(ws + desc_offset());
-    uint2* tables = reinterpret_cast<uint2*>(ws + table_offset((int)plan->count));
+    uint32_t* tables = reinterpret_cast<uint32_t*>(ws + table_offset((int)plan->count));
     auto* status = reinterpret_cast<unsigned long long*>(ws);
     hipLaunchKernelGGL((ecf8_decode_kernel<kChunk, kLanes>), dim3(plan->grid), dim3(kLanes), 0,
                        reinterpret_cast<hipStream_t>(hip_stream), dd, (int)plan->count, plan->total_blocks,
