@@ -12,10 +12,10 @@
 //
 // MI355X-specific design (differs from the pages' CUDA sketch, which targets
 // 32-lane warps, 128-thread blocks and an L1-resident two-level 8-bit table):
-//   * decode table: one LDS table of 8-byte entries indexed by the next 11
-//     stream bits.  Each entry decodes greedily every whole codeword inside the
-//     window (up to 8 symbols), so a lookup yields ~3.5-4.5 symbols for the
-//     weight distributions of interest.  Codes longer than 11 bits (rare) live
+//   * decode table: one LDS table of packed 4-byte entries indexed by the
+//     next 11 stream bits.  Each entry decodes greedily the whole codewords
+//     inside the window (up to 4 symbols), so a lookup yields ~3.7-4 symbols
+//     for the weight distributions of interest.  Codes longer than 11 bits (rare) live
 //     in a second region indexed by the next 16 bits; one branch-free
 //     max(prefix11, prefix16 - c) picks the region (canonical codes put every
 //     long code at the top of the code space).  The table is built per tensor
@@ -54,7 +54,7 @@ constexpr int kChunk = 16;                                          // C
 constexpr int kLanes = 256;                                         // TB
 constexpr uint64_t kStatusBytes = 256;
 constexpr int kTableThreads = 256;
-constexpr int kNibPrefetch = 4;                                     // write-back groups prefetched per lane
+constexpr int kNibPrefetch = 6;                                     // write-back groups prefetched per lane
 
 // Device descriptor of one tensor (workspace resident).
 struct alignas(16) DevDesc {
@@ -82,7 +82,8 @@ uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
 uint64_t desc_offset() { return kStatusBytes; }
 uint64_t table_offset(int count) { return kStatusBytes + round_up((uint64_t)count * sizeof(DevDesc), 256); }
-constexpr uint64_t kTableBytes = 2ull * kTabStride * sizeof(uint32_t);   // X and Y arrays
+constexpr uint64_t kTableBytes = kTabStride * sizeof(uint32_t);        // one packed dword per entry
+constexpr int kMaxSymPerEntry = 4;                                  // symbols decoded per lookup, at most
 
 // Global-memory accessors: descriptor pointers are generic; casting them to
 // the global address space makes the compiler emit global_* (not flat_*)
@@ -112,10 +113,11 @@ __device__ __forceinline__ void gst4(void* p, uint32_t a, uint32_t b, uint32_t c
 }
 
 // ------------------------------------------------------------ table kernel
-// One workgroup per tensor.  Two arrays per tensor (structure of arrays, so a
-// lane reading only X touches every LDS bank):
-//   X[idx] = bits consumed | (4 * symbols) << 16,
-//   Y[idx] = symbols as nibbles, first symbol in the low nibble.
+// One workgroup per tensor.  One dword per entry, so a lookup is a single
+// 4-byte LDS read that spreads over every bank:
+//   bits  7..0   bits consumed (1..16)
+//   bits 15..8   4 * symbols decoded (0..16)
+//   bits 31..16  the symbols as nibbles, first symbol in bits 19..16.
 __global__ __launch_bounds__(kTableThreads) void ecf8_table_kernel(DevDesc* __restrict__ descs,
                                                                    uint32_t* __restrict__ tables)
 {
@@ -165,8 +167,7 @@ __global__ __launch_bounds__(kTableThreads) void ecf8_table_kernel(DevDesc* __re
     __syncthreads();
     const int k = (int)s_info[0];
     const uint32_t p_long = s_info[1], cdelta = s_info[2], entries = s_info[3];
-    uint32_t* tx = tables + (uint64_t)blockIdx.x * (2 * kTabStride);
-    uint32_t* ty = tx + kTabStride;
+    uint32_t* tx = tables + (uint64_t)blockIdx.x * kTabStride;
     for (uint32_t idx = threadIdx.x; idx < entries; idx += kTableThreads) {
         uint32_t v, known;
         if (idx < p_long) {
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(kTableThreads) void ecf8_table_kernel(DevDesc* __re
             known = 16;
         }
         uint32_t pos = 0, ns = 0, sy = 0;
-        while (k > 0 && ns < 8 && pos < known) {
+        while (k > 0 && ns < (uint32_t)kMaxSymPerEntry && pos < known) {
             const uint32_t x = (v << pos) & 0xFFFFu;
             int lo = 0, hi = k;
             while (hi - lo > 1) {
@@ -192,8 +193,7 @@ __global__ __launch_bounds__(kTableThreads) void ecf8_table_kernel(DevDesc* __re
             ns++;
             pos += l;
         }
-        tx[idx] = (pos ? pos : 1u) | ((4 * ns) << 16);
-        ty[idx] = sy;
+        tx[idx] = (pos ? pos : 1u) | ((4 * ns) << 8) | (sy << 16);
     }
 }
 
@@ -263,7 +263,9 @@ __device__ __forceinline__ void write_edge(const uint32_t* s_out, uint8_t* out_b
     const uint32_t e0 = 16u * g;
     const uint32_t kb = e0 < a0 ? a0 - e0 : 0u;
     const uint32_t ke = endo - e0 < 16u ? endo - e0 : 16u;
-    for (uint32_t q = kb; q < ke; ++q) gst(out_blk + e0 + q, (uint8_t)(w[q >> 2] >> (8 * (q & 3))));
+#pragma unroll
+    for (uint32_t q = 0; q < 16; ++q)
+        if (q >= kb && q < ke) gst(out_blk + e0 + q, (uint8_t)(w[q >> 2] >> (8 * (q & 3))));
 }
 
 // ------------------------------------------------------------ decode kernel
@@ -289,10 +291,11 @@ struct BlockIn {
 // Descriptor fields the prefetch needs, cached in registers per tensor.
 struct NextTensor {
     int t;
-    uint64_t begin, end;
+    uint64_t begin, end, n;
     const uint8_t* stream;
     const uint8_t* gaps;
     const uint64_t* blk_off;
+    const uint8_t* nibbles;
 };
 
 __device__ __forceinline__ void fetch_next_tensor(const DevDesc* descs, int t, NextTensor& nt)
@@ -301,9 +304,48 @@ __device__ __forceinline__ void fetch_next_tensor(const DevDesc* descs, int t, N
     nt.t = t;
     nt.begin = d->block_begin;
     nt.end = d->block_end;
+    nt.n = d->n;
     nt.stream = d->stream;
     nt.gaps = d->gaps;
     nt.blk_off = d->blk_off;
+    nt.nibbles = d->nibbles;
+}
+
+// Output range of a block: elements [lo, lo + nw), written as 16-element
+// groups from the aligned base (a0 = lo - base), `groups` groups in all.
+struct BlockGeo {
+    uint64_t lo, base, want;
+    uint32_t nw, a0, groups;
+};
+
+__device__ __forceinline__ BlockGeo block_geo(uint64_t lo_raw, uint64_t hi_raw, uint64_t n, uint32_t cap)
+{
+    BlockGeo g;
+    const uint64_t hi = hi_raw < n ? hi_raw : n;
+    g.lo = lo_raw < hi ? lo_raw : hi;
+    g.want = hi - g.lo;
+    g.nw = g.want < cap ? (uint32_t)g.want : cap;
+    g.base = g.lo & ~15ull;
+    g.a0 = (uint32_t)(g.lo - g.base);
+    g.groups = (g.a0 + g.nw + 15) >> 4;
+    return g;
+}
+
+// Issue the sign/mantissa plane loads of a block's groups (one 8-byte load
+// per group, lane tid takes groups tid + k*TB).  The loads are issued
+// unconditionally (groups past the block re-read the plane's first bytes,
+// which always exist for a tensor with blocks) so that the compiler can count
+// outstanding memory operations exactly and never drains the prefetch early.
+template <int TB>
+__device__ __forceinline__ void load_nibbles(const uint8_t* nibbles, const BlockGeo& g, int tid, uint2 (&nv)[kNibPrefetch])
+{
+    const uint64_t nb = g.base >> 1;
+#pragma unroll
+    for (int k = 0; k < kNibPrefetch; ++k) {
+        const uint32_t q = tid + k * TB;
+        const uint64_t off = q < g.groups ? nb + 8ull * q : 0ull;
+        nv[k] = gld2(nibbles + off);
+    }
 }
 
 __device__ __forceinline__ void load_block(const NextTensor& nt, uint64_t gblk, int tid, BlockIn& in)
@@ -334,14 +376,12 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
     using L = DecodeLds<C, TB>;
     constexpr int kWaves = TB / 64;
     constexpr int S = L::kSlot;
-    // one LDS arena: table X | table Y (256-byte aligned, so X[i] and Y[i]
-    // are one ds_read2st64) | lane stream slots | nibble staging | wave sums
-    constexpr int kStreamOff = 2 * kTabStride;
+    // one LDS arena: decode table | lane stream slots | nibble staging | wave sums
+    constexpr int kStreamOff = kTabStride;
     constexpr int kOutOff = (kStreamOff + L::kStreamDw + 3) / 4 * 4;
     constexpr int kSumOff = kOutOff + L::kOutDw;
     __shared__ __align__(256) uint32_t lds[kSumOff + kWaves];
     uint32_t* const s_tx = lds;
-    uint32_t* const s_ty = lds + kTabStride;
     uint32_t* const s_stream = lds + kStreamOff;
     uint32_t* const s_out = lds + kOutOff;
     uint32_t* const s_wsum = lds + kSumOff;
@@ -366,6 +406,12 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
     BlockIn nx;
     load_block(nt, blk, tid, nx);
     int ptens = nt.t;                  // tensor of the prefetched block
+    const uint32_t cap = 8u * C * TB;  // staging capacity in elements
+    uint2 nv[kNibPrefetch];            // sign/mantissa plane of the block about to be decoded
+    load_nibbles<TB>(nt.nibbles, block_geo(lane_u64(nx.off, 0), lane_u64(nx.off, 1), nt.n, cap), tid, nv);
+    // wait for the first block's loads here, so that at the loop head only the
+    // back edge has loads in flight and the compiler can count them exactly
+    asm volatile("" ::"v"(nx.sv.x), "v"(nx.la), "v"(nx.gb), "v"(nv[kNibPrefetch - 1].x));
 
     // fields of the tensor being decoded
     int cur = -1;
@@ -377,6 +423,13 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
 
     for (; blk < total_blocks; blk += gridDim.x) {
         const BlockIn in = nx;
+        // stage the chunk (big-endian words, reversed order) into the lane's slot;
+        // the slot is lane-private and free since the previous decode pass ended
+        slot[S] = __builtin_bswap32(in.sv.x);
+        slot[S - 1] = __builtin_bswap32(in.sv.y);
+        slot[S - 2] = __builtin_bswap32(in.sv.z);
+        slot[S - 3] = __builtin_bswap32(in.sv.w);
+        slot[S - 4] = __builtin_bswap32(in.la);
         if (ptens != cur) {
             const DevDesc* d = descs + ptens;
             c_begin = d->block_begin;
@@ -389,11 +442,11 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
             uint32_t ne = d->entries;
             c_ok = ne != 0;                       // 0: tables were never built for this plan
             ne = ne < (uint32_t)kTableMax ? ne : (uint32_t)kTableMax;
-            const uint32_t* tx = tables + (uint64_t)ptens * (2 * kTabStride);
-            __syncthreads();
+            const uint32_t* tx = tables + (uint64_t)ptens * kTabStride;
+            // (every lane left the previous decode pass at its closing barrier,
+            // so the old table is no longer read)
             for (uint32_t i = tid; i < ne; i += TB) {
                 s_tx[i] = gld(tx + i);
-                s_ty[i] = gld(tx + kTabStride + i);
             }
             cur = ptens;
             __syncthreads();
@@ -405,40 +458,20 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
         E = c_ok ? E : 0u;
         const uint32_t gap = (in.gb >> ((chunk & 1) * 4)) & 15u;
 
-        // stage the chunk (big-endian words, reversed order) into the lane's slot
-        slot[S] = __builtin_bswap32(in.sv.x);
-        slot[S - 1] = __builtin_bswap32(in.sv.y);
-        slot[S - 2] = __builtin_bswap32(in.sv.z);
-        slot[S - 3] = __builtin_bswap32(in.sv.w);
-        slot[S - 4] = __builtin_bswap32(in.la);
-
-        // block output range and its 16-element groups; prefetch the sign/mantissa plane
-        const uint64_t lo_raw = lane_u64(in.off, 0), hi_raw = lane_u64(in.off, 1);
-        const uint64_t hi = hi_raw < c_n ? hi_raw : c_n;
-        const uint64_t lo = lo_raw < hi ? lo_raw : hi;
-        const uint64_t want = hi - lo;
-        const uint32_t cap = 8u * C * TB;
-        const uint32_t nw = want < cap ? (uint32_t)want : cap;
-        const uint64_t base = lo & ~15ull;
-        const uint32_t a0 = (uint32_t)(lo - base);
-        const uint32_t groups = (a0 + nw + 15) >> 4;
+        // block output range and its 16-element groups (its sign/mantissa plane is already in flight)
+        const BlockGeo geo = block_geo(lane_u64(in.off, 0), lane_u64(in.off, 1), c_n, cap);
+        const uint64_t base = geo.base;
+        const uint32_t a0 = geo.a0, nw = geo.nw, groups = geo.groups;
+        const uint64_t want = geo.want;
         const uint8_t* nib_blk = c_nib + (base >> 1);
-        uint2 nv[kNibPrefetch];
-#pragma unroll
-        for (int k = 0; k < kNibPrefetch; ++k) {
-            const uint32_t g = tid + k * TB;
-            nv[k] = g < groups ? gld2(nib_blk + 8ull * g) : make_uint2(0, 0);
-        }
 
-        // prefetch the next block of this workgroup
-        {
-            const uint64_t nb = blk + gridDim.x;
-            if (nb < total_blocks) {
-                while (nt.t + 1 < count && nb >= nt.end) fetch_next_tensor(descs, nt.t + 1, nt);
-                load_block(nt, nb, tid, nx);
-                ptens = nt.t;
-            }
-        }
+        // prefetch the next block of this workgroup (after the last block, the
+        // current one is re-read: unconditional loads keep the wait counts exact)
+        const uint64_t nb = blk + gridDim.x;
+        const uint64_t nbe = nb < total_blocks ? nb : blk;
+        while (nt.t + 1 < count && nbe >= nt.end) fetch_next_tensor(descs, nt.t + 1, nt);
+        load_block(nt, nbe, tid, nx);
+        ptens = nt.t;
 
         // ---- phase 2: count the codewords that start inside [gap, E)
         const int cd = c_cd;
@@ -453,19 +486,19 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
             const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, r);
             idx = (uint32_t)max((int)(win >> (32 - kWin)), (int)(win >> 16) - cd);
             const uint32_t ex = s_tx[idx];
-            r -= ex & 0xFFFFu;
-            cnt4 += ex >> 16;
+            r -= ex & 0xFFu;
+            cnt4 += (ex >> 8) & 0xFFu;
         }
         uint32_t cnt = cnt4 >> 2;
         if (r != r0) {
             // the last lookup (at r + its bit count) may have decoded codewords
             // that start at or after E: keep those starting before E
             const uint32_t ex = s_tx[idx];
-            const uint32_t ns = ex >> 18;
-            const uint32_t room = r + (ex & 0xFFFFu) - rend;
-            uint32_t sy = s_ty[idx], start = 0, keep = 0;
+            const uint32_t ns = (ex >> 10) & 0x3Fu;
+            const uint32_t room = r + (ex & 0xFFu) - rend;
+            uint32_t sy = ex >> 16, start = 0, keep = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < kMaxSymPerEntry; ++i) {
                 if ((uint32_t)i < ns) {
                     keep += start < room ? 1u : 0u;
                     start += (uint32_t)((c_lenpack >> (4 * (sy & 15))) & 15) + 1;
@@ -500,15 +533,17 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
             const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, r);
             const int idx = max((int)(win >> (32 - kWin)), (int)(win >> 16) - cd);
             const uint32_t ex = s_tx[idx];
-            const uint32_t sy = s_ty[idx];
-            const uint64_t v = (uint64_t)sy << (ob & 31);
+            const uint64_t v = (uint64_t)(ex >> 16) << (ob & 31);
             const uint32_t wa = ob >> 5;
             atomicOr(&s_out[wa], (uint32_t)v);
             atomicOr(&s_out[wa + 1], (uint32_t)(v >> 32));
-            ob += ex >> 16;
-            r -= ex & 0xFFFFu;
+            ob += (ex >> 8) & 0xFFu;
+            r -= ex & 0xFFu;
         }
         __syncthreads();
+
+        // geometry of the next block (its offsets arrived during the decode)
+        const BlockGeo ngeo = block_geo(lane_u64(nx.off, 0), lane_u64(nx.off, 1), nt.n, cap);
 
         // ---- phase 5: write back [lo, lo + nw) as 16-element groups
         if (tid == 0 && (want != total || !c_ok)) atomicAdd(status, 1ull);
@@ -516,15 +551,22 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
         const uint32_t endo = a0 + nw;                 // one past the last valid element, group-relative
         const uint32_t first_full = a0 ? 1u : 0u;
         const uint32_t end_full = endo >> 4;           // groups [first_full, end_full) are whole
-        // assemble every prefetched group first, then issue the stores back to back:
-        // stores share the vector-memory counter with loads, so no wait falls between them
-        uint32_t wb[kNibPrefetch][4];
+        // assemble prefetched groups four at a time, then issue their stores back to
+        // back: stores share the vector-memory counter with loads, so no wait falls
+        // between them
+        static_assert(kNibPrefetch % 2 == 0, "write-back batches of two groups");
 #pragma unroll
-        for (int k = 0; k < kNibPrefetch; ++k) group_bytes(s_out, tid + k * TB, nv[k], wb[k]);
+        for (int k0 = 0; k0 < kNibPrefetch; k0 += 2) {
+            if (tid + k0 * TB >= end_full) break;
+            uint32_t wb[2][4];
 #pragma unroll
-        for (int k = 0; k < kNibPrefetch; ++k) {
-            const uint32_t g = tid + k * TB;
-            if (g >= first_full && g < end_full) gst4(out_blk + 16u * g, wb[k][0], wb[k][1], wb[k][2], wb[k][3]);
+            for (int k = 0; k < 2; ++k) group_bytes(s_out, tid + (k0 + k) * TB, nv[k0 + k], wb[k]);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const uint32_t g = tid + (k0 + k) * TB;
+                if (g >= first_full && g < end_full)
+                    gst4(out_blk + 16u * g, wb[k][0], wb[k][1], wb[k][2], wb[k][3]);
+            }
         }
         for (uint32_t g = tid + kNibPrefetch * TB; g < end_full; g += TB)   // blocks of > 16K elements
             write_full(s_out, out_blk, g, gld2(nib_blk + 8ull * g));
@@ -539,6 +581,8 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
             if (k >= (uint32_t)kNibPrefetch) nm = gld2(nib_blk + 8ull * end_full);
             write_edge(s_out, out_blk, end_full, nm, a0, endo);
         }
+        // the next block's sign/mantissa plane: a whole block of latency to hide
+        load_nibbles<TB>(nt.nibbles, ngeo, tid, nv);
     }
 }
 
