@@ -113,88 +113,101 @@ __device__ __forceinline__ void gst4(void* p, uint32_t a, uint32_t b, uint32_t c
 }
 
 // ------------------------------------------------------------ table kernel
-// One workgroup per tensor.  One dword per entry, so a lookup is a single
-// 4-byte LDS read that spreads over every bank:
+// Grid (tensors, kTableSlices): workgroup (i, j) builds entries
+// [256 j, 256 j + 256) of tensor i's table, one entry per lane.  Canonical
+// codes occupy consecutive ranges of the left-justified 16-bit code space in
+// (length, symbol) order, so symbol s starts at the sum of 2^(16 - len) over
+// the symbols before it; each of 16 lanes computes one symbol's range.
+// Entry layout (one dword, so a lookup is a single 4-byte LDS read):
 //   bits  7..0   bits consumed (1..16)
 //   bits 15..8   4 * symbols decoded (0..16)
 //   bits 31..16  the symbols as nibbles, first symbol in bits 19..16.
+constexpr int kTableSlices = (kTableMax + kTableThreads - 1) / kTableThreads;   // 9
+
 __global__ __launch_bounds__(kTableThreads) void ecf8_table_kernel(DevDesc* __restrict__ descs,
                                                                    uint32_t* __restrict__ tables)
 {
-    __shared__ uint32_t s_start[16];   // left-justified 16-bit first code of k-th codeword (canonical order)
+    __shared__ uint32_t s_start[16];   // canonical order: left-justified start of the k-th codeword range
     __shared__ uint32_t s_len[16];
     __shared__ uint32_t s_sym[16];
-    __shared__ uint32_t s_info[4];     // k, p_long, cdelta, entries
+    __shared__ uint32_t s_k;
     DevDesc* d = descs + blockIdx.x;
-    if (threadIdx.x == 0) {
-        uint32_t len[16];
-        uint64_t lenpack = 0;
-        for (int s = 0; s < 16; ++s) {
-            len[s] = d->len[s];
-            if (len[s]) lenpack |= (uint64_t)((len[s] - 1) & 15) << (4 * s);
-        }
-        int k = 0;
-        for (uint32_t l = 1; l <= 16; ++l)
-            for (int s = 0; s < 16; ++s)
-                if (len[s] == l) {
-                    s_sym[k] = s;
-                    s_len[k] = l;
-                    k++;
-                }
-        uint32_t code = 0;
-        uint32_t p_long = 1u << kWin;
-        bool found = false;
-        for (int i = 0; i < k; ++i) {
-            if (i > 0) code = (code + 1) << (s_len[i] - s_len[i - 1]);
-            s_start[i] = code << (16 - s_len[i]);
-            if (!found && s_len[i] > (uint32_t)kWin) {
-                p_long = s_start[i] >> (16 - kWin);
-                found = true;
+    const int tid = threadIdx.x;
+    if (tid < 16) {
+        const uint32_t l = d->len[tid];
+        uint32_t rank = 0, start = 0, k = 0, plong_units = 0;
+        for (int u = 0; u < 16; ++u) {
+            const uint32_t lu = d->len[u];
+            if (!lu) continue;
+            k++;
+            if (lu <= (uint32_t)kWin) plong_units += 1u << (16 - lu);
+            if (l && (lu < l || (lu == l && u < tid))) {
+                rank++;
+                start += 1u << (16 - lu);
             }
         }
-        uint32_t cdelta = ((1u << (16 - kWin)) - 1) * p_long;
-        uint32_t entries = 65536u - cdelta;      // <= kTableMax for every complete code
-        if (entries > (uint32_t)kTableMax) entries = kTableMax;
-        s_info[0] = k;
-        s_info[1] = p_long;
-        s_info[2] = cdelta;
-        s_info[3] = entries;
-        d->lenpack = lenpack;
-        d->p_long = p_long;
-        d->cdelta = (int32_t)cdelta;
-        d->entries = entries;
+        if (l) {
+            s_start[rank] = start;
+            s_len[rank] = l;
+            s_sym[rank] = tid;
+        }
+        if (tid == 0) {
+            s_k = k;
+            // every code of at most kWin bits precedes the long ones, so the
+            // first long prefix is the total space of the short codes
+            const uint32_t p_long = plong_units >> (16 - kWin);
+            uint32_t cdelta = ((1u << (16 - kWin)) - 1) * p_long;
+            uint32_t entries = 65536u - cdelta;      // <= kTableMax for every complete code
+            if (entries > (uint32_t)kTableMax) entries = kTableMax;
+            if (blockIdx.y == 0) {
+                uint64_t lenpack = 0;
+                for (int u = 0; u < 16; ++u)
+                    if (d->len[u]) lenpack |= (uint64_t)((d->len[u] - 1) & 15) << (4 * u);
+                d->lenpack = lenpack;
+                d->p_long = p_long;
+                d->cdelta = (int32_t)cdelta;
+                d->entries = entries;
+            }
+        }
     }
     __syncthreads();
-    const int k = (int)s_info[0];
-    const uint32_t p_long = s_info[1], cdelta = s_info[2], entries = s_info[3];
-    uint32_t* tx = tables + (uint64_t)blockIdx.x * kTabStride;
-    for (uint32_t idx = threadIdx.x; idx < entries; idx += kTableThreads) {
-        uint32_t v, known;
-        if (idx < p_long) {
-            v = idx << (16 - kWin);
-            known = kWin;
-        } else {
-            v = idx + cdelta;
-            known = 16;
-        }
-        uint32_t pos = 0, ns = 0, sy = 0;
-        while (k > 0 && ns < (uint32_t)kMaxSymPerEntry && pos < known) {
-            const uint32_t x = (v << pos) & 0xFFFFu;
-            int lo = 0, hi = k;
-            while (hi - lo > 1) {
-                int mid = (lo + hi) >> 1;
-                if (s_start[mid] <= x) lo = mid;
-                else hi = mid;
-            }
-            const uint32_t l = s_len[lo];
-            if (x >= s_start[lo] + (1u << (16 - l))) break;   // outside an incomplete code
-            if (pos + l > known) break;                          // codeword not fully visible
-            sy |= s_sym[lo] << (4 * ns);
-            ns++;
-            pos += l;
-        }
-        tx[idx] = (pos ? pos : 1u) | ((4 * ns) << 8) | (sy << 16);
+    const int k = (int)s_k;
+    uint32_t plong_units = 0;
+    for (int u = 0; u < 16; ++u) {
+        const uint32_t lu = d->len[u];
+        if (lu && lu <= (uint32_t)kWin) plong_units += 1u << (16 - lu);
     }
+    const uint32_t p_long = plong_units >> (16 - kWin);
+    const uint32_t cdelta = ((1u << (16 - kWin)) - 1) * p_long;
+    uint32_t entries = 65536u - cdelta;
+    if (entries > (uint32_t)kTableMax) entries = kTableMax;
+    const uint32_t idx = blockIdx.y * kTableThreads + tid;
+    if (idx >= entries) return;
+    uint32_t v, known;
+    if (idx < p_long) {
+        v = idx << (16 - kWin);
+        known = kWin;
+    } else {
+        v = idx + cdelta;
+        known = 16;
+    }
+    uint32_t pos = 0, ns = 0, sy = 0;
+    while (k > 0 && ns < (uint32_t)kMaxSymPerEntry && pos < known) {
+        const uint32_t x = (v << pos) & 0xFFFFu;
+        int lo = 0, hi = k;
+        while (hi - lo > 1) {
+            int mid = (lo + hi) >> 1;
+            if (s_start[mid] <= x) lo = mid;
+            else hi = mid;
+        }
+        const uint32_t l = s_len[lo];
+        if (x >= s_start[lo] + (1u << (16 - l))) break;   // outside an incomplete code
+        if (pos + l > known) break;                          // codeword not fully visible
+        sy |= s_sym[lo] << (4 * ns);
+        ns++;
+        pos += l;
+    }
+    tables[(uint64_t)blockIdx.x * kTabStride + idx] = (pos ? pos : 1u) | ((4 * ns) << 8) | (sy << 16);
 }
 
 // ------------------------------------------------------------ helpers
@@ -703,7 +716,7 @@ extern "C" int ecf8_build_tables(const ecf8_plan* plan, void* hip_stream)
     unsigned char* ws = static_cast<unsigned char*>(plan->workspace);
     DevDesc* dd = reinterpret_cast<DevDesc*>(ws + desc_offset());
     uint32_t* tables = reinterpret_cast<uint32_t*>(ws + table_offset((int)plan->count));
-    hipLaunchKernelGGL(ecf8_table_kernel, dim3(plan->count), dim3(kTableThreads), 0,
+    hipLaunchKernelGGL(ecf8_table_kernel, dim3(plan->count, kTableSlices), dim3(kTableThreads), 0,
                        reinterpret_cast<hipStream_t>(hip_stream), dd, tables);
     return hipGetLastError() == hipSuccess ? ECF8_OK : ECF8_ERR_HIP;
 }
