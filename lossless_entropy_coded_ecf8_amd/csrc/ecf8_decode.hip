@@ -22,9 +22,10 @@
 //     on the GPU from the 16 code lengths by a small kernel and copied to LDS
 //     by each persistent workgroup when its tensor changes.
 //   * chunks: 16 bytes per lane, 256 lanes (4 wave64s) per block; the lane's
-//     chunk plus one look-ahead dword are byte-swapped into a private LDS slot
-//     (5 dwords, odd stride: bank-conflict free), and a 32-bit window at any
-//     bit position is one ds_read2 + one v_alignbit.
+//     chunk plus one look-ahead dword are byte-swapped into LDS in word-major
+//     order (word k of every lane is one contiguous row), so the window reads
+//     of a wave hit 64 distinct banks whatever bit position each lane is at;
+//     a 32-bit window is one ds_read2st64 + one v_alignbit.
 //   * counts -> positions: wave64 inclusive scan with DPP row shifts and
 //     readlane row carries, then a 4-entry cross-wave LDS prefix.
 //   * decode: symbols of each lookup are OR-ed as packed nibbles into a
@@ -281,11 +282,42 @@ __device__ __forceinline__ void write_edge(const uint32_t* s_out, uint8_t* out_b
         if (q >= kb && q < ke) gst(out_blk + e0 + q, (uint8_t)(w[q >> 2] >> (8 * (q & 3))));
 }
 
+// One table lookup at stream position r (r = 192 - bit position within the
+// lane's chunk): 32-bit window from the lane's two LDS rows, then the index
+// max(prefix11, prefix16 - cd) into the packed table.
+__device__ __forceinline__ uint32_t lookup(const char* s_stream_b, const uint32_t* s_tx, uint32_t col_addr,
+                                           uint32_t r, int cd)
+{
+    const uint32_t a = col_addr + (4u * kLanes) * (__builtin_amdgcn_ubfe(r, 5, 3) - 2u);
+    const uint32_t w1 = *reinterpret_cast<const uint32_t*>(s_stream_b + a);
+    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(s_stream_b + a + 4u * kLanes);
+    const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, r);
+    const int idx = max((int)(win >> (32 - kWin)), (int)(win >> 16) - cd);
+    return s_tx[idx];
+}
+
+// OR the symbols of one table entry, as packed nibbles, into the zeroed
+// staging at bit offset ob (two dwords: the entry's 16 symbol bits may
+// straddle a dword boundary).
+__device__ __forceinline__ void emit_symbols(uint32_t* s_out, uint32_t ob, uint32_t ex)
+{
+    const uint64_t v = (uint64_t)(ex >> 16) << (ob & 31);
+    const uint32_t wa = ob >> 5;
+    atomicOr(&s_out[wa], (uint32_t)v);
+    atomicOr(&s_out[wa + 1], (uint32_t)(v >> 32));
+}
+
 // ------------------------------------------------------------ decode kernel
+#ifndef ECF8_RECORDS
+#define ECF8_RECORDS 20
+#endif
+constexpr int kRecords = ECF8_RECORDS;   // table entries recorded per lane by the count pass
+
 template <int C, int TB>
 struct DecodeLds {
     static constexpr int kSlot = C / 4 + 1;                                   // dwords per lane slot
-    static constexpr int kStreamDw = TB * kSlot + 2;
+    static constexpr int kStreamRows = kSlot + 1;                             // + one dummy row
+    static constexpr int kStreamDw = TB * kStreamRows;
     static constexpr int kOutDw = ((8 * C * TB + 15 + 8 + 16) / 8 + 2 + 3) / 4 * 4;   // nibble staging
 };
 
@@ -401,13 +433,14 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    // Lane slot, stored in reverse word order: word k (k = -1..S-1, where
-    // k = S-1 is the look-ahead and k = -1 aliases the next lane's look-ahead)
-    // lives at s_stream[tid*S + S - k].  With r = 192 - bitpos, the window
-    // pair (word ceil(bitpos/32)-1, next word) sits at dwords
-    // tid*S + (r >> 5) and tid*S + (r >> 5) - 1, and the funnel shift is r & 31.
-    uint32_t* const slot = s_stream + tid * S;
-    const uint32_t slot_addr = (uint32_t)(tid * S - 1) * 4u;   // byte address of slot[-1] within s_stream
+    // Lane words in word-major, reversed order: word k of the lane's chunk
+    // (k = 0..S-1, k = S-1 the look-ahead) lives in row S - k, element tid;
+    // row S + 1 is a dummy (only read with a zero funnel shift).  With
+    // r = 192 - bitpos, the window pair (word ceil(bitpos/32)-1, next word) is
+    // rows (r >> 5) and (r >> 5) - 1, and the funnel shift is r & 31.
+    static_assert(S == 5, "r = 192 - bitpos assumes 4 chunk words + look-ahead");
+    uint32_t* const col = s_stream - TB + tid;                 // col[row * TB] = row `row`, rows 1..S+1
+    const uint32_t col_addr = (uint32_t)tid * 4u;              // byte address of row 1, this lane
     const char* const s_stream_b = reinterpret_cast<const char*>(s_stream);
 
     uint64_t blk = blockIdx.x;
@@ -438,11 +471,11 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
         const BlockIn in = nx;
         // stage the chunk (big-endian words, reversed order) into the lane's slot;
         // the slot is lane-private and free since the previous decode pass ended
-        slot[S] = __builtin_bswap32(in.sv.x);
-        slot[S - 1] = __builtin_bswap32(in.sv.y);
-        slot[S - 2] = __builtin_bswap32(in.sv.z);
-        slot[S - 3] = __builtin_bswap32(in.sv.w);
-        slot[S - 4] = __builtin_bswap32(in.la);
+        col[S * TB] = __builtin_bswap32(in.sv.x);
+        col[(S - 1) * TB] = __builtin_bswap32(in.sv.y);
+        col[(S - 2) * TB] = __builtin_bswap32(in.sv.z);
+        col[(S - 3) * TB] = __builtin_bswap32(in.sv.w);
+        col[(S - 4) * TB] = __builtin_bswap32(in.la);
         if (ptens != cur) {
             const DevDesc* d = descs + ptens;
             c_begin = d->block_begin;
@@ -490,15 +523,15 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
         const int cd = c_cd;
         const uint32_t rend = 192u - E;
         const uint32_t r0 = 192u - gap;
+        // The lane's table entries are recorded in registers (the loop index is
+        // the same for every active lane, so the record index is uniform) and
+        // replayed by phase 4 instead of walking the stream a second time.
+        uint32_t rec[kRecords + 1];        // the last slot absorbs lookups past kRecords
         uint32_t r = r0;
-        uint32_t cnt4 = 0, idx = 0;
-        while (r > rend) {
-            const uint32_t a = slot_addr + 4u * __builtin_amdgcn_ubfe(r, 5, 3);
-            const uint32_t w1 = *reinterpret_cast<const uint32_t*>(s_stream_b + a);
-            const uint32_t w0 = *reinterpret_cast<const uint32_t*>(s_stream_b + a + 4);
-            const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, r);
-            idx = (uint32_t)max((int)(win >> (32 - kWin)), (int)(win >> 16) - cd);
-            const uint32_t ex = s_tx[idx];
+        uint32_t cnt4 = 0, ex = 0;
+        for (uint32_t it = 0; r > rend; ++it) {
+            ex = lookup(s_stream_b, s_tx, col_addr, r, cd);
+            rec[it < (uint32_t)kRecords ? it : (uint32_t)kRecords] = ex;
             r -= ex & 0xFFu;
             cnt4 += (ex >> 8) & 0xFFu;
         }
@@ -506,7 +539,6 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
         if (r != r0) {
             // the last lookup (at r + its bit count) may have decoded codewords
             // that start at or after E: keep those starting before E
-            const uint32_t ex = s_tx[idx];
             const uint32_t ns = (ex >> 10) & 0x3Fu;
             const uint32_t room = r + (ex & 0xFFu) - rend;
             uint32_t sy = ex >> 16, start = 0, keep = 0;
@@ -539,17 +571,15 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
         // ---- phase 4: cooperative decode into the LDS staging (packed nibbles)
         uint32_t ob = (a0 + pos) * 4;      // bit offset of the lane's first nibble in the staging
         r = r0;
-        while (r > rend) {
-            const uint32_t a = slot_addr + 4u * __builtin_amdgcn_ubfe(r, 5, 3);
-            const uint32_t w1 = *reinterpret_cast<const uint32_t*>(s_stream_b + a);
-            const uint32_t w0 = *reinterpret_cast<const uint32_t*>(s_stream_b + a + 4);
-            const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, r);
-            const int idx = max((int)(win >> (32 - kWin)), (int)(win >> 16) - cd);
-            const uint32_t ex = s_tx[idx];
-            const uint64_t v = (uint64_t)(ex >> 16) << (ob & 31);
-            const uint32_t wa = ob >> 5;
-            atomicOr(&s_out[wa], (uint32_t)v);
-            atomicOr(&s_out[wa + 1], (uint32_t)(v >> 32));
+        for (uint32_t it = 0; it < (uint32_t)kRecords && r > rend; ++it) {
+            const uint32_t ex = rec[it];
+            emit_symbols(s_out, ob, ex);
+            ob += (ex >> 8) & 0xFFu;
+            r -= ex & 0xFFu;
+        }
+        while (r > rend) {                 // lanes with more than kRecords lookups: walk the rest
+            const uint32_t ex = lookup(s_stream_b, s_tx, col_addr, r, cd);
+            emit_symbols(s_out, ob, ex);
             ob += (ex >> 8) & 0xFFu;
             r -= ex & 0xFFu;
         }
