@@ -55,7 +55,7 @@ constexpr int kChunk = 16;                                          // C
 constexpr int kLanes = 256;                                         // TB
 constexpr uint64_t kStatusBytes = 256;
 constexpr int kTableThreads = 256;
-constexpr int kNibPrefetch = 6;                                     // write-back groups prefetched per lane
+constexpr int kNibPrefetch = 4;                                     // write-back groups prefetched per lane
 
 // Device descriptor of one tensor (workspace resident).
 struct alignas(16) DevDesc {
@@ -288,7 +288,10 @@ __device__ __forceinline__ void write_edge(const uint32_t* s_out, uint8_t* out_b
 __device__ __forceinline__ uint32_t lookup(const char* s_stream_b, const uint32_t* s_tx, uint32_t col_addr,
                                            uint32_t r, int cd)
 {
-    const uint32_t a = col_addr + (4u * kLanes) * (__builtin_amdgcn_ubfe(r, 5, 3) - 2u);
+    // a = col_addr + 4 * kLanes * ((r >> 5) - 2), as one v_and + one v_lshl_add
+    static_assert(4 * kLanes == 32 << 5, "row pitch");
+    uint32_t a;
+    asm("v_lshl_add_u32 %0, %1, 5, %2" : "=v"(a) : "v"(r & 0xE0u), "v"(col_addr - 2u * 4u * kLanes));
     const uint32_t w1 = *reinterpret_cast<const uint32_t*>(s_stream_b + a);
     const uint32_t w0 = *reinterpret_cast<const uint32_t*>(s_stream_b + a + 4u * kLanes);
     const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, r);
@@ -307,11 +310,27 @@ __device__ __forceinline__ void emit_symbols(uint32_t* s_out, uint32_t ob, uint3
     atomicOr(&s_out[wa + 1], (uint32_t)(v >> 32));
 }
 
+// OR the symbols of two consecutive table entries of a lane (an entry of 0
+// contributes nothing) into the staging at bit offset ob: their packets joined
+// into one bit string of at most 32 bits, spread over two dwords.  Returns the
+// bit offset after them.
+__device__ __forceinline__ uint32_t emit_pair(uint32_t* s_out, uint32_t ob, uint32_t e0, uint32_t e1)
+{
+    const uint32_t n0 = (e0 >> 8) & 0xFFu;
+    const uint32_t p01 = ((e1 >> 16) << n0) | (e0 >> 16);
+    const uint64_t v = (uint64_t)p01 << (ob & 31u);
+    const uint32_t wa = ob >> 5;
+    atomicOr(&s_out[wa], (uint32_t)v);
+    atomicOr(&s_out[wa + 1], (uint32_t)(v >> 32));
+    return ob + n0 + ((e1 >> 8) & 0xFFu);
+}
+
 // ------------------------------------------------------------ decode kernel
 #ifndef ECF8_RECORDS
 #define ECF8_RECORDS 20
 #endif
 constexpr int kRecords = ECF8_RECORDS;   // table entries recorded per lane by the count pass
+static_assert(kRecords % 4 == 0, "records are taken four at a time");
 
 template <int C, int TB>
 struct DecodeLds {
@@ -412,7 +431,7 @@ __device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l)
 }
 
 template <int C, int TB>
-__global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restrict__ descs, int count,
+__global__ __launch_bounds__(TB, 5) void ecf8_decode_kernel(const DevDesc* __restrict__ descs, int count,
                                                          uint64_t total_blocks,
                                                          const uint32_t* __restrict__ tables,
                                                          unsigned long long* __restrict__ status)
@@ -520,25 +539,47 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
         ptens = nt.t;
 
         // ---- phase 2: count the codewords that start inside [gap, E)
+        // The walk runs in steps of four lookups with one wave-uniform exit test
+        // per step; a lane that has passed E keeps looking up at its final
+        // position but records 0 (no bits, no symbols).  The recorded entries sit
+        // in statically indexed registers and are replayed by phase 4, so the
+        // stream is walked once (lanes with more than kRecords lookups finish with
+        // a plain walk).
         const int cd = c_cd;
         const uint32_t rend = 192u - E;
         const uint32_t r0 = 192u - gap;
-        // The lane's table entries are recorded in registers (the loop index is
-        // the same for every active lane, so the record index is uniform) and
-        // replayed by phase 4 instead of walking the stream a second time.
-        uint32_t rec[kRecords + 1];        // the last slot absorbs lookups past kRecords
+        uint32_t rec[kRecords];
         uint32_t r = r0;
-        uint32_t cnt4 = 0, ex = 0;
-        for (uint32_t it = 0; r > rend; ++it) {
-            ex = lookup(s_stream_b, s_tx, col_addr, r, cd);
-            rec[it < (uint32_t)kRecords ? it : (uint32_t)kRecords] = ex;
-            r -= ex & 0xFFu;
-            cnt4 += (ex >> 8) & 0xFFu;
+        uint32_t cnt4 = 0, lastex = 0;
+        bool act = r > rend;
+        int nq = 0;                        // four-lookup steps taken (wave-uniform)
+#pragma unroll
+        for (int q = 0; q < kRecords / 4; ++q) {
+            if (__builtin_amdgcn_ballot_w64(act) == 0) break;
+            nq = q + 1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t e = lookup(s_stream_b, s_tx, col_addr, r, cd);
+                const uint32_t em = act ? e : 0u;
+                lastex = act ? e : lastex;
+                rec[4 * q + j] = em;
+                r -= em & 0xFFu;
+                cnt4 += (em >> 8) & 0xFFu;
+                act = r > rend;
+            }
+        }
+        const uint32_t r_rec = r;          // where the recorded lookups end
+        while (r > rend) {
+            const uint32_t e = lookup(s_stream_b, s_tx, col_addr, r, cd);
+            lastex = e;
+            r -= e & 0xFFu;
+            cnt4 += (e >> 8) & 0xFFu;
         }
         uint32_t cnt = cnt4 >> 2;
         if (r != r0) {
             // the last lookup (at r + its bit count) may have decoded codewords
             // that start at or after E: keep those starting before E
+            const uint32_t ex = lastex;
             const uint32_t ns = (ex >> 10) & 0x3Fu;
             const uint32_t room = r + (ex & 0xFFu) - rend;
             uint32_t sy = ex >> 16, start = 0, keep = 0;
@@ -570,13 +611,13 @@ __global__ __launch_bounds__(TB) void ecf8_decode_kernel(const DevDesc* __restri
 
         // ---- phase 4: cooperative decode into the LDS staging (packed nibbles)
         uint32_t ob = (a0 + pos) * 4;      // bit offset of the lane's first nibble in the staging
-        r = r0;
-        for (uint32_t it = 0; it < (uint32_t)kRecords && r > rend; ++it) {
-            const uint32_t ex = rec[it];
-            emit_symbols(s_out, ob, ex);
-            ob += (ex >> 8) & 0xFFu;
-            r -= ex & 0xFFu;
+#pragma unroll
+        for (int q = 0; q < kRecords / 4; ++q) {
+            if (q >= nq) break;
+            ob = emit_pair(s_out, ob, rec[4 * q], rec[4 * q + 1]);
+            ob = emit_pair(s_out, ob, rec[4 * q + 2], rec[4 * q + 3]);
         }
+        r = r_rec;
         while (r > rend) {                 // lanes with more than kRecords lookups: walk the rest
             const uint32_t ex = lookup(s_stream_b, s_tx, col_addr, r, cd);
             emit_symbols(s_out, ob, ex);
