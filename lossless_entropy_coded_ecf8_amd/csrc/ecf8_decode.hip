@@ -106,11 +106,45 @@ __device__ __forceinline__ uint2 gld2(const void* p)
     const u32x2 v = *(const ECF8_GLOBAL u32x2*)(p);
     return make_uint2(v.x, v.y);
 }
-__device__ __forceinline__ void gst4(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+
+// Buffer resources for the streaming loads and stores of the decode kernel: a
+// wave-uniform base and byte size in SGPRs, 32-bit per-lane byte offsets, and
+// the hardware range check (a load past the end reads 0, a store past the end
+// is dropped).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;   // raw, untyped dword access (gfx9 descriptor word 3)
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint64_t bytes)
+{
+    const uint32_t nr = bytes < 0xFFFFFFFFull ? (uint32_t)bytes : 0xFFFFFFFFu;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nr, kRsrcWord3);
+}
+__device__ __forceinline__ uint32_t bld1(Rsrc r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bld(Rsrc r, uint32_t off, uint32_t soff = 0)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+}
+__device__ __forceinline__ uint2 bld2(Rsrc r, uint32_t off, uint32_t soff = 0)
+{
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint4 bld4(Rsrc r, uint32_t off)
+{
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void bst4(Rsrc r, uint32_t off, uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
     u32x4 v;
     v.x = a; v.y = b; v.z = c; v.w = d;
-    *(ECF8_GLOBAL u32x4*)(p) = v;
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void bst1(Rsrc r, uint32_t off, uint8_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b8(v, r, off, 0, 0);
 }
 
 // ------------------------------------------------------------ table kernel
@@ -227,9 +261,13 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane)
     return v;
 }
 
+// (a & mask) | (b & ~mask) as one v_bfi_b32 (the compiler otherwise splits it
+// into and/or sequences)
 __device__ __forceinline__ uint32_t bitsel(uint32_t mask, uint32_t a, uint32_t b)
 {
-    return (a & mask) | (b & ~mask);   // v_bfi_b32
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(mask), "v"(a), "v"(b));
+    return r;
 }
 
 // 8 exponent nibbles (e) + 8 sign/mantissa nibbles (nm), element i in nibble i,
@@ -260,16 +298,16 @@ __device__ __forceinline__ void group_bytes(const uint32_t* s_out, uint32_t g, u
 }
 
 // A group fully inside the block's range: one 16-byte store.
-__device__ __forceinline__ void write_full(const uint32_t* s_out, uint8_t* out_blk, uint32_t g, uint2 nm)
+__device__ __forceinline__ void write_full(const uint32_t* s_out, Rsrc out_blk, uint32_t g, uint2 nm)
 {
     uint32_t w[4];
     group_bytes(s_out, g, nm, w);
-    gst4(out_blk + 16u * g, w[0], w[1], w[2], w[3]);
+    bst4(out_blk, 16u * g, w[0], w[1], w[2], w[3]);
 }
 
 // One of the (at most two) ragged edge groups of a block: store only the
 // bytes inside [a0, endo).
-__device__ __forceinline__ void write_edge(const uint32_t* s_out, uint8_t* out_blk, uint32_t g, uint2 nm,
+__device__ __forceinline__ void write_edge(const uint32_t* s_out, Rsrc out_blk, uint32_t g, uint2 nm,
                                            uint32_t a0, uint32_t endo)
 {
     uint32_t w[4];
@@ -279,7 +317,7 @@ __device__ __forceinline__ void write_edge(const uint32_t* s_out, uint8_t* out_b
     const uint32_t ke = endo - e0 < 16u ? endo - e0 : 16u;
 #pragma unroll
     for (uint32_t q = 0; q < 16; ++q)
-        if (q >= kb && q < ke) gst(out_blk + e0 + q, (uint8_t)(w[q >> 2] >> (8 * (q & 3))));
+        if (q >= kb && q < ke) bst1(out_blk, e0 + q, (uint8_t)(w[q >> 2] >> (8 * (q & 3))));
 }
 
 // One table lookup at stream position r (r = 192 - bit position within the
@@ -316,13 +354,23 @@ __device__ __forceinline__ void emit_symbols(uint32_t* s_out, uint32_t ob, uint3
 // bit offset after them.
 __device__ __forceinline__ uint32_t emit_pair(uint32_t* s_out, uint32_t ob, uint32_t e0, uint32_t e1)
 {
-    const uint32_t n0 = (e0 >> 8) & 0xFFu;
-    const uint32_t p01 = ((e1 >> 16) << n0) | (e0 >> 16);
+    // p01 = ((e1 >> 16) << n0) | (e0 >> 16), n0 = 4 * symbols of e0 (<= 16, the low
+    // five bits of e0 >> 8), with word selects instead of shifts
+    const uint32_t n0s = e0 >> 8;
+    uint32_t p01;
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1\n\t"
+        "v_or_b32_sdwa %0, %0, %3 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
+        : "=&v"(p01) : "v"(n0s), "v"(e1), "v"(e0));
     const uint64_t v = (uint64_t)p01 << (ob & 31u);
     const uint32_t wa = ob >> 5;
     atomicOr(&s_out[wa], (uint32_t)v);
     atomicOr(&s_out[wa + 1], (uint32_t)(v >> 32));
-    return ob + n0 + ((e1 >> 8) & 0xFFu);
+    // ob + (4 * symbols of e0) + (4 * symbols of e1), with byte selects
+    uint32_t nob;
+    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD\n\t"
+        "v_add_u32_sdwa %0, %3, %0 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD"
+        : "=&v"(nob) : "v"(e0), "v"(ob), "v"(e1));
+    return nob;
 }
 
 // ------------------------------------------------------------ decode kernel
@@ -334,11 +382,24 @@ static_assert(kRecords % 4 == 0, "records are taken four at a time");
 
 template <int C, int TB>
 struct DecodeLds {
-    static constexpr int kSlot = C / 4 + 1;                                   // dwords per lane slot
-    static constexpr int kStreamRows = kSlot + 1;                             // + one dummy row
-    static constexpr int kStreamDw = TB * kStreamRows;
+    static constexpr int kSlot = C / 4 + 1;                                   // dwords per lane: chunk + look-ahead
+    static constexpr int kStreamDw = TB * (kSlot + 1);                        // rows, + one row only read at shift 0
     static constexpr int kOutDw = ((8 * C * TB + 15 + 8 + 16) / 8 + 2 + 3) / 4 * 4;   // nibble staging
+    static constexpr int kUnionDw = kOutDw > kStreamDw ? kOutDw : kStreamDw;
+    static_assert(kUnionDw % 4 == 0, "cleared as 16-byte words");
 };
+
+// Window at bit position p (p < 128 + 16) of a lane's chunk held in registers
+// (w[0..3] the chunk as big-endian words, w[4] the look-ahead word).
+__device__ __forceinline__ uint32_t reg_window(const uint32_t (&w)[5], uint32_t p)
+{
+    const uint32_t k = p >> 5;
+    uint32_t hi = w[0], lo = w[1];
+    if (k == 1) { hi = w[1]; lo = w[2]; }
+    if (k == 2) { hi = w[2]; lo = w[3]; }
+    if (k >= 3) { hi = w[3]; lo = w[4]; }
+    return (uint32_t)(((((uint64_t)hi << 32) | lo) << (p & 31)) >> 32);
+}
 
 // Per-block inputs loaded one block ahead (software pipelining of the
 // persistent loop: HBM latency overlaps the previous block's decode).  The
@@ -395,32 +456,37 @@ __device__ __forceinline__ BlockGeo block_geo(uint64_t lo_raw, uint64_t hi_raw, 
     return g;
 }
 
+// The sign/mantissa plane of a block, from its first group on (8 bytes per
+// 16-element group; the plane of n elements has ceil(n / 16) * 8 bytes).
+__device__ __forceinline__ Rsrc nibble_rsrc(const uint8_t* nibbles, uint64_t n, uint64_t base)
+{
+    return make_rsrc(nibbles + (base >> 1), (((n + 15) >> 4) << 3) - (base >> 1));
+}
+
 // Issue the sign/mantissa plane loads of a block's groups (one 8-byte load
 // per group, lane tid takes groups tid + k*TB).  The loads are issued
-// unconditionally (groups past the block re-read the plane's first bytes,
-// which always exist for a tensor with blocks) so that the compiler can count
-// outstanding memory operations exactly and never drains the prefetch early.
+// unconditionally (past the block they read the next block's plane, past the
+// tensor they read 0) so that the compiler can count outstanding memory
+// operations exactly and never drains the prefetch early.
 template <int TB>
-__device__ __forceinline__ void load_nibbles(const uint8_t* nibbles, const BlockGeo& g, int tid, uint2 (&nv)[kNibPrefetch])
+__device__ __forceinline__ void load_nibbles(Rsrc rn, int tid, uint2 (&nv)[kNibPrefetch])
 {
-    const uint64_t nb = g.base >> 1;
 #pragma unroll
-    for (int k = 0; k < kNibPrefetch; ++k) {
-        const uint32_t q = tid + k * TB;
-        const uint64_t off = q < g.groups ? nb + 8ull * q : 0ull;
-        nv[k] = gld2(nibbles + off);
-    }
+    for (int k = 0; k < kNibPrefetch; ++k) nv[k] = bld2(rn, 8u * tid, 8u * k * TB);
 }
 
 __device__ __forceinline__ void load_block(const NextTensor& nt, uint64_t gblk, int tid, BlockIn& in)
 {
     const uint64_t b = gblk - nt.begin;
-    const uint64_t chunk = b * kLanes + tid;
-    const uint8_t* sp = nt.stream + chunk * kChunk;
-    in.sv = gld4(sp);
-    in.la = gld(reinterpret_cast<const uint32_t*>(sp + kChunk));
-    in.gb = gld(nt.gaps + (chunk >> 1));
-    in.off = gld(nt.blk_off + b + (tid & 1));
+    // block offsets first: they are the first of these loads to be needed
+    const uint2 o = bld2(make_rsrc(nt.blk_off + b, 16), (tid & 1) * 8u);
+    in.off = ((uint64_t)o.y << 32) | o.x;
+    // the block's chunks and the look-ahead word of its last lane (the stream
+    // has 16 bytes past its last block)
+    const Rsrc rs = make_rsrc(nt.stream + b * (kLanes * kChunk), kLanes * kChunk + 16);
+    in.sv = bld4(rs, tid * kChunk);
+    in.la = bld(rs, tid * kChunk + kChunk);
+    in.gb = bld1(make_rsrc(nt.gaps + b * (kLanes / 2), kLanes / 2), tid >> 1);
 }
 
 __device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l)
@@ -430,8 +496,12 @@ __device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l)
     return ((uint64_t)hi << 32) | lo;
 }
 
+#ifndef ECF8_MIN_WAVES
+#define ECF8_MIN_WAVES 6
+#endif
+
 template <int C, int TB>
-__global__ __launch_bounds__(TB, 5) void ecf8_decode_kernel(const DevDesc* __restrict__ descs, int count,
+__global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAVES))) void ecf8_decode_kernel(const DevDesc* __restrict__ descs, int count,
                                                          uint64_t total_blocks,
                                                          const uint32_t* __restrict__ tables,
                                                          unsigned long long* __restrict__ status)
@@ -440,21 +510,27 @@ __global__ __launch_bounds__(TB, 5) void ecf8_decode_kernel(const DevDesc* __res
     using L = DecodeLds<C, TB>;
     constexpr int kWaves = TB / 64;
     constexpr int S = L::kSlot;
-    // one LDS arena: decode table | lane stream slots | nibble staging | wave sums
-    constexpr int kStreamOff = kTabStride;
-    constexpr int kOutOff = (kStreamOff + L::kStreamDw + 3) / 4 * 4;
-    constexpr int kSumOff = kOutOff + L::kOutDw;
+    // One LDS arena: decode table | nibble staging, whose first S * TB dwords
+    // double as the stream rows | wave sums.  The stream rows are read only by
+    // the count pass and the staging is written only after the block-wide
+    // scan, so the two share memory: a lane clears its own rows once it has
+    // counted, the write-back clears what the decode wrote, and a barrier at
+    // the top of each block orders the previous block's write-back before the
+    // new rows are written.
+    constexpr int kUnionOff = (int)kTabStride;
+    constexpr int kSumOff = kUnionOff + L::kUnionDw;
     __shared__ __align__(256) uint32_t lds[kSumOff + kWaves];
     uint32_t* const s_tx = lds;
-    uint32_t* const s_stream = lds + kStreamOff;
-    uint32_t* const s_out = lds + kOutOff;
+    uint32_t* const s_out = lds + kUnionOff;
+    uint32_t* const s_stream = lds + kUnionOff;
     uint32_t* const s_wsum = lds + kSumOff;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     // Lane words in word-major, reversed order: word k of the lane's chunk
     // (k = 0..S-1, k = S-1 the look-ahead) lives in row S - k, element tid;
-    // row S + 1 is a dummy (only read with a zero funnel shift).  With
+    // row S + 1 (staging memory) is only read with a zero funnel shift, and a
+    // finished lane may read row 0 (the last table dwords) for a window it drops.  With
     // r = 192 - bitpos, the window pair (word ceil(bitpos/32)-1, next word) is
     // rows (r >> 5) and (r >> 5) - 1, and the funnel shift is r & 31.
     static_assert(S == 5, "r = 192 - bitpos assumes 4 chunk words + look-ahead");
@@ -464,6 +540,7 @@ __global__ __launch_bounds__(TB, 5) void ecf8_decode_kernel(const DevDesc* __res
 
     uint64_t blk = blockIdx.x;
     if (blk >= total_blocks) return;
+    for (int i = tid; i < L::kUnionDw / 4; i += TB) reinterpret_cast<uint4*>(s_out)[i] = make_uint4(0, 0, 0, 0);
 
     NextTensor nt;
     fetch_next_tensor(descs, 0, nt);
@@ -473,7 +550,8 @@ __global__ __launch_bounds__(TB, 5) void ecf8_decode_kernel(const DevDesc* __res
     int ptens = nt.t;                  // tensor of the prefetched block
     const uint32_t cap = 8u * C * TB;  // staging capacity in elements
     uint2 nv[kNibPrefetch];            // sign/mantissa plane of the block about to be decoded
-    load_nibbles<TB>(nt.nibbles, block_geo(lane_u64(nx.off, 0), lane_u64(nx.off, 1), nt.n, cap), tid, nv);
+    load_nibbles<TB>(nibble_rsrc(nt.nibbles, nt.n, block_geo(lane_u64(nx.off, 0), lane_u64(nx.off, 1), nt.n, cap).base),
+                     tid, nv);
     // wait for the first block's loads here, so that at the loop head only the
     // back edge has loads in flight and the compiler can count them exactly
     asm volatile("" ::"v"(nx.sv.x), "v"(nx.la), "v"(nx.gb), "v"(nv[kNibPrefetch - 1].x));
@@ -482,19 +560,13 @@ __global__ __launch_bounds__(TB, 5) void ecf8_decode_kernel(const DevDesc* __res
     int cur = -1;
     uint64_t c_begin = 0, c_n = 0, c_T = 0, c_lenpack = 0;
     const uint8_t* c_nib = nullptr;
+    const uint8_t* c_stream = nullptr;
     uint8_t* c_out = nullptr;
     int c_cd = 0;
     uint32_t c_ok = 0;
 
     for (; blk < total_blocks; blk += gridDim.x) {
         const BlockIn in = nx;
-        // stage the chunk (big-endian words, reversed order) into the lane's slot;
-        // the slot is lane-private and free since the previous decode pass ended
-        col[S * TB] = __builtin_bswap32(in.sv.x);
-        col[(S - 1) * TB] = __builtin_bswap32(in.sv.y);
-        col[(S - 2) * TB] = __builtin_bswap32(in.sv.z);
-        col[(S - 3) * TB] = __builtin_bswap32(in.sv.w);
-        col[(S - 4) * TB] = __builtin_bswap32(in.la);
         if (ptens != cur) {
             const DevDesc* d = descs + ptens;
             c_begin = d->block_begin;
@@ -502,6 +574,7 @@ __global__ __launch_bounds__(TB, 5) void ecf8_decode_kernel(const DevDesc* __res
             c_T = d->total_bits;
             c_lenpack = d->lenpack;
             c_nib = d->nibbles;
+            c_stream = d->stream;
             c_out = d->out;
             c_cd = d->cdelta;
             uint32_t ne = d->entries;
@@ -514,21 +587,32 @@ __global__ __launch_bounds__(TB, 5) void ecf8_decode_kernel(const DevDesc* __res
                 s_tx[i] = gld(tx + i);
             }
             cur = ptens;
-            __syncthreads();
         }
+        // the table is in place and every lane has finished the previous block's
+        // write-back, whose staging memory the stream rows reuse
+        __syncthreads();
+        // stage the chunk (big-endian words, reversed order) into the lane's rows
+        col[S * TB] = __builtin_bswap32(in.sv.x);
+        col[(S - 1) * TB] = __builtin_bswap32(in.sv.y);
+        col[(S - 2) * TB] = __builtin_bswap32(in.sv.z);
+        col[(S - 3) * TB] = __builtin_bswap32(in.sv.w);
+        col[(S - 4) * TB] = __builtin_bswap32(in.la);
         const uint64_t b = blk - c_begin;
-        const uint64_t chunk = b * TB + tid;
-        const uint64_t cstart = chunk * (8ull * C);
-        uint32_t E = cstart >= c_T ? 0u : (uint32_t)((c_T - cstart) < 8ull * C ? (c_T - cstart) : 8ull * C);
-        E = c_ok ? E : 0u;
-        const uint32_t gap = (in.gb >> ((chunk & 1) * 4)) & 15u;
+        // stream bits of the tensor from this block's start (uniform), then the
+        // lane's own: E = bits of its chunk before the end of the stream
+        const uint64_t bbits = b * (8ull * C * TB);
+        const uint64_t left = (c_T > bbits && c_ok) ? c_T - bbits : 0ull;
+        const uint32_t leftc = left < 8ull * C * TB ? (uint32_t)left : 8u * C * TB;
+        const uint32_t lstart = (uint32_t)tid * (8u * C);
+        const uint32_t E = leftc > lstart ? min(leftc - lstart, 8u * C) : 0u;
+        const uint32_t gap = (in.gb >> ((tid & 1) * 4)) & 15u;
 
         // block output range and its 16-element groups (its sign/mantissa plane is already in flight)
         const BlockGeo geo = block_geo(lane_u64(in.off, 0), lane_u64(in.off, 1), c_n, cap);
         const uint64_t base = geo.base;
         const uint32_t a0 = geo.a0, nw = geo.nw, groups = geo.groups;
         const uint64_t want = geo.want;
-        const uint8_t* nib_blk = c_nib + (base >> 1);
+        const Rsrc nib_blk = nibble_rsrc(c_nib, c_n, base);
 
         // prefetch the next block of this workgroup (after the last block, the
         // current one is re-read: unconditional loads keep the wait counts exact)
@@ -538,6 +622,7 @@ __global__ __launch_bounds__(TB, 5) void ecf8_decode_kernel(const DevDesc* __res
         load_block(nt, nbe, tid, nx);
         ptens = nt.t;
 
+        __builtin_amdgcn_s_setprio(3);
         // ---- phase 2: count the codewords that start inside [gap, E)
         // The walk runs in steps of four lookups with one wave-uniform exit test
         // per step; a lane that has passed E keeps looking up at its final
@@ -575,6 +660,10 @@ __global__ __launch_bounds__(TB, 5) void ecf8_decode_kernel(const DevDesc* __res
             r -= e & 0xFFu;
             cnt4 += (e >> 8) & 0xFFu;
         }
+        __builtin_amdgcn_s_setprio(0);
+        // the lane's rows are staging memory from here on: leave them cleared
+#pragma unroll
+        for (int k = 0; k < S; ++k) col[(S - k) * TB] = 0u;
         uint32_t cnt = cnt4 >> 2;
         if (r != r0) {
             // the last lookup (at r + its bit count) may have decoded codewords
@@ -606,8 +695,6 @@ __global__ __launch_bounds__(TB, 5) void ecf8_decode_kernel(const DevDesc* __res
             total += sw;
         }
         const uint32_t pos = before + incl - cnt;
-        for (int i = tid; i < L::kOutDw / 4; i += TB) reinterpret_cast<uint4*>(s_out)[i] = make_uint4(0, 0, 0, 0);
-        __syncthreads();
 
         // ---- phase 4: cooperative decode into the LDS staging (packed nibbles)
         uint32_t ob = (a0 + pos) * 4;      // bit offset of the lane's first nibble in the staging
@@ -617,21 +704,28 @@ __global__ __launch_bounds__(TB, 5) void ecf8_decode_kernel(const DevDesc* __res
             ob = emit_pair(s_out, ob, rec[4 * q], rec[4 * q + 1]);
             ob = emit_pair(s_out, ob, rec[4 * q + 2], rec[4 * q + 3]);
         }
-        r = r_rec;
-        while (r > rend) {                 // lanes with more than kRecords lookups: walk the rest
-            const uint32_t ex = lookup(s_stream_b, s_tx, col_addr, r, cd);
-            emit_symbols(s_out, ob, ex);
-            ob += (ex >> 8) & 0xFFu;
-            r -= ex & 0xFFu;
+        if (r_rec > rend) {
+            // lanes with more than kRecords lookups walk the rest from registers
+            // (their rows are staging memory now): reload the chunk (L2-resident)
+            const uint8_t* sp = c_stream + (b * TB + tid) * kChunk;
+            const uint4 cv = gld4(sp);
+            const uint32_t w[5] = {__builtin_bswap32(cv.x), __builtin_bswap32(cv.y), __builtin_bswap32(cv.z),
+                                   __builtin_bswap32(cv.w), __builtin_bswap32(gld(reinterpret_cast<const uint32_t*>(sp + kChunk)))};
+            r = r_rec;
+            while (r > rend) {
+                const uint32_t win = reg_window(w, 192u - r);
+                const int idx = max((int)(win >> (32 - kWin)), (int)(win >> 16) - cd);
+                const uint32_t ex = s_tx[idx];
+                emit_symbols(s_out, ob, ex);
+                ob += (ex >> 8) & 0xFFu;
+                r -= ex & 0xFFu;
+            }
         }
         __syncthreads();
 
-        // geometry of the next block (its offsets arrived during the decode)
-        const BlockGeo ngeo = block_geo(lane_u64(nx.off, 0), lane_u64(nx.off, 1), nt.n, cap);
-
         // ---- phase 5: write back [lo, lo + nw) as 16-element groups
         if (tid == 0 && (want != total || !c_ok)) atomicAdd(status, 1ull);
-        uint8_t* const out_blk = c_out + base;
+        const Rsrc out_blk = make_rsrc(c_out + base, c_n - base);
         const uint32_t endo = a0 + nw;                 // one past the last valid element, group-relative
         const uint32_t first_full = a0 ? 1u : 0u;
         const uint32_t end_full = endo >> 4;           // groups [first_full, end_full) are whole
@@ -649,11 +743,11 @@ __global__ __launch_bounds__(TB, 5) void ecf8_decode_kernel(const DevDesc* __res
             for (int k = 0; k < 2; ++k) {
                 const uint32_t g = tid + (k0 + k) * TB;
                 if (g >= first_full && g < end_full)
-                    gst4(out_blk + 16u * g, wb[k][0], wb[k][1], wb[k][2], wb[k][3]);
+                    bst4(out_blk, 16u * g, wb[k][0], wb[k][1], wb[k][2], wb[k][3]);
             }
         }
         for (uint32_t g = tid + kNibPrefetch * TB; g < end_full; g += TB)   // blocks of > 16K elements
-            write_full(s_out, out_blk, g, gld2(nib_blk + 8ull * g));
+            write_full(s_out, out_blk, g, bld2(nib_blk, 8u * g));
         // ragged edges: group 0 when the range starts mid-group, group end_full when it ends mid-group
         if (a0 && tid == 0) write_edge(s_out, out_blk, 0, nv[0], a0, endo);
         if (end_full < groups && !(end_full == 0 && a0) && tid == (int)(end_full % TB)) {
@@ -662,11 +756,21 @@ __global__ __launch_bounds__(TB, 5) void ecf8_decode_kernel(const DevDesc* __res
 #pragma unroll
             for (int q = 1; q < kNibPrefetch; ++q)
                 if (k == (uint32_t)q) nm = nv[q];
-            if (k >= (uint32_t)kNibPrefetch) nm = gld2(nib_blk + 8ull * end_full);
+            if (k >= (uint32_t)kNibPrefetch) nm = bld2(nib_blk, 8u * end_full);
             write_edge(s_out, out_blk, end_full, nm, a0, endo);
         }
-        // the next block's sign/mantissa plane: a whole block of latency to hide
-        load_nibbles<TB>(nt.nibbles, ngeo, tid, nv);
+        // clear the staging the decode wrote: groups [0, zend) cover every
+        // nibble OR-ed in, the codewords a last lane decodes past the end included
+        // (each group is cleared by the lane that read it above)
+        {
+            const uint32_t zend0 = (a0 + total + 3u + 15u) >> 4;
+            const uint32_t zend = zend0 < (uint32_t)(L::kOutDw / 2) ? zend0 : (uint32_t)(L::kOutDw / 2);
+            for (uint32_t g = tid; g < zend; g += TB) reinterpret_cast<uint2*>(s_out)[g] = make_uint2(0u, 0u);
+        }
+        // the next block's sign/mantissa plane (its offsets arrived during the
+        // decode): a whole block of latency to hide
+        const BlockGeo ngeo = block_geo(lane_u64(nx.off, 0), lane_u64(nx.off, 1), nt.n, cap);
+        load_nibbles<TB>(nibble_rsrc(nt.nibbles, nt.n, ngeo.base), tid, nv);
     }
 }
 
