@@ -113,6 +113,11 @@ __device__ __forceinline__ uint2 gld2(const void* p)
 // is dropped).
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;   // raw, untyped dword access (gfx9 descriptor word 3)
+// The decoded output is written once and not read back by this kernel: its
+// 16-byte stores carry the non-temporal hint (cache-policy bit 1), which
+// measured faster than the default; the loads keep the default policy (their
+// neighbouring lines are reused from L2).
+constexpr int kNonTemporal = 2;
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint64_t bytes)
 {
     const uint32_t nr = bytes < 0xFFFFFFFFull ? (uint32_t)bytes : 0xFFFFFFFFu;
@@ -140,7 +145,7 @@ __device__ __forceinline__ void bst4(Rsrc r, uint32_t off, uint32_t a, uint32_t 
 {
     u32x4 v;
     v.x = a; v.y = b; v.z = c; v.w = d;
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kNonTemporal);
 }
 __device__ __forceinline__ void bst1(Rsrc r, uint32_t off, uint8_t v)
 {
@@ -456,18 +461,18 @@ __device__ __forceinline__ BlockGeo block_geo(uint64_t lo_raw, uint64_t hi_raw, 
     return g;
 }
 
-// The sign/mantissa plane of a block, from its first group on (8 bytes per
-// 16-element group; the plane of n elements has ceil(n / 16) * 8 bytes).
-__device__ __forceinline__ Rsrc nibble_rsrc(const uint8_t* nibbles, uint64_t n, uint64_t base)
+// The sign/mantissa plane of a block's groups (8 bytes per 16-element group):
+// the range ends with the block, so that loads for groups past it read 0
+// without touching memory.
+__device__ __forceinline__ Rsrc nibble_rsrc(const uint8_t* nibbles, const BlockGeo& g)
 {
-    return make_rsrc(nibbles + (base >> 1), (((n + 15) >> 4) << 3) - (base >> 1));
+    return make_rsrc(nibbles + (g.base >> 1), 8ull * g.groups);
 }
 
 // Issue the sign/mantissa plane loads of a block's groups (one 8-byte load
 // per group, lane tid takes groups tid + k*TB).  The loads are issued
-// unconditionally (past the block they read the next block's plane, past the
-// tensor they read 0) so that the compiler can count outstanding memory
-// operations exactly and never drains the prefetch early.
+// unconditionally (past the block they read 0) so that the compiler can count
+// outstanding memory operations exactly and never drains the prefetch early.
 template <int TB>
 __device__ __forceinline__ void load_nibbles(Rsrc rn, int tid, uint2 (&nv)[kNibPrefetch])
 {
@@ -550,8 +555,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
     int ptens = nt.t;                  // tensor of the prefetched block
     const uint32_t cap = 8u * C * TB;  // staging capacity in elements
     uint2 nv[kNibPrefetch];            // sign/mantissa plane of the block about to be decoded
-    load_nibbles<TB>(nibble_rsrc(nt.nibbles, nt.n, block_geo(lane_u64(nx.off, 0), lane_u64(nx.off, 1), nt.n, cap).base),
-                     tid, nv);
+    load_nibbles<TB>(nibble_rsrc(nt.nibbles, block_geo(lane_u64(nx.off, 0), lane_u64(nx.off, 1), nt.n, cap)), tid, nv);
     // wait for the first block's loads here, so that at the loop head only the
     // back edge has loads in flight and the compiler can count them exactly
     asm volatile("" ::"v"(nx.sv.x), "v"(nx.la), "v"(nx.gb), "v"(nv[kNibPrefetch - 1].x));
@@ -612,7 +616,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
         const uint64_t base = geo.base;
         const uint32_t a0 = geo.a0, nw = geo.nw, groups = geo.groups;
         const uint64_t want = geo.want;
-        const Rsrc nib_blk = nibble_rsrc(c_nib, c_n, base);
+        const Rsrc nib_blk = nibble_rsrc(c_nib, geo);
 
         // prefetch the next block of this workgroup (after the last block, the
         // current one is re-read: unconditional loads keep the wait counts exact)
@@ -770,7 +774,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
         // the next block's sign/mantissa plane (its offsets arrived during the
         // decode): a whole block of latency to hide
         const BlockGeo ngeo = block_geo(lane_u64(nx.off, 0), lane_u64(nx.off, 1), nt.n, cap);
-        load_nibbles<TB>(nibble_rsrc(nt.nibbles, nt.n, ngeo.base), tid, nv);
+        load_nibbles<TB>(nibble_rsrc(nt.nibbles, ngeo), tid, nv);
     }
 }
 
