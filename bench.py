@@ -42,8 +42,12 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the decode kernel source with comments and blank lines removed."""
+    import re
     p = os.path.join(ROOT, "lossless_entropy_coded_ecf8_amd", "csrc", "ecf8_decode.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    text = re.sub(r"//[^\n]*", "", open(p).read())
+    code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def load_traffic(workload: str, kernel_hash: str, launches_bytes: float):

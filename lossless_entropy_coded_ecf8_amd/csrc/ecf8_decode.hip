@@ -14,8 +14,8 @@
 // 32-lane warps, 128-thread blocks and an L1-resident two-level 8-bit table):
 //   * decode table: one LDS table of packed 4-byte entries indexed by the
 //     next 11 stream bits.  Each entry decodes greedily the whole codewords
-//     inside the window (up to 4 symbols), so a lookup yields ~3.7-4 symbols
-//     for the weight distributions of interest.  Codes longer than 11 bits (rare) live
+//     inside the window (up to 4 symbols), ~3.7 symbols per lookup for the
+//     weight distributions of interest.  Codes longer than 11 bits (rare) live
 //     in a second region indexed by the next 16 bits; one branch-free
 //     max(prefix11, prefix16 - c) picks the region (canonical codes put every
 //     long code at the top of the code space).  The table is built per tensor
@@ -26,16 +26,23 @@
 //     order (word k of every lane is one contiguous row), so the window reads
 //     of a wave hit 64 distinct banks whatever bit position each lane is at;
 //     a 32-bit window is one ds_read2st64 + one v_alignbit.
+//   * one walk: the count pass records each lookup's table entry in registers
+//     (four lookups per wave-uniform step, so the record index is static) and
+//     the decode pass replays them; only lanes with more lookups walk again.
 //   * counts -> positions: wave64 inclusive scan with DPP row shifts and
 //     readlane row carries, then a 4-entry cross-wave LDS prefix.
-//   * decode: symbols of each lookup are OR-ed as packed nibbles into a
-//     zeroed LDS staging area at the scanned nibble positions.  A lane's last
-//     lookup may decode a few codewords that belong to the next lane; they are
-//     the same symbols at the same positions, so OR-ing them twice is exact.
+//   * decode: the recorded entries are OR-ed two at a time as packed nibbles
+//     into the cleared LDS staging area at the scanned nibble positions.  A
+//     lane's last lookup may decode a few codewords that belong to the next
+//     lane; they are the same symbols at the same positions, so OR-ing them
+//     twice is exact.  The stream rows share memory with the staging.
 //   * write back: 16 elements per lane-step: 8 bytes of exponent nibbles from
-//     LDS, 8 bytes of the sign/mantissa plane from HBM, SWAR byte assembly,
-//     one 16-byte store; byte stores only at the two ragged block edges.
-//   * one persistent dispatch walks all blocks of all tensors of a batch.
+//     LDS, 8 bytes of the sign/mantissa plane from HBM (prefetched a block
+//     ahead), SWAR byte assembly, one non-temporal 16-byte store; byte stores
+//     only at the two ragged block edges.
+//   * streaming loads and stores are buffer instructions (SGPR descriptors,
+//     32-bit offsets, hardware range checks); one persistent dispatch walks
+//     all blocks of all tensors of a batch at 6 workgroups per CU.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
