@@ -118,6 +118,79 @@ def cpu_baseline(encs_host, seconds: float):
                       "one thread per core, %.1f s" % (len(blocks), done, dt)}
 
 
+def pipeline_bench(args):
+    """Decode-on-use (ECF8 blog §3.2.2/§3.3): forward time of the block's linear layers with weights
+    decoded ahead of use into a 3-slot pool, against the same FP8 GEMMs on resident FP8 weights."""
+    import torch
+    import synth
+    import lossless_entropy_coded_ecf8_amd as E
+    from lossless_entropy_coded_ecf8_amd import pipeline as P
+
+    d = torch.device("cuda:0")
+    names, ws, layers = [], [], []
+    for name, x in synth.workload_tensors(args.workload, device=d):
+        o, k = x.shape[-2], x.shape[-1]
+        names.append(name)
+        ws.append(x.reshape(o, k))
+        layers.append(E.ECF8Linear(x.reshape(o, k), scale=1.0 / 64, device=d))
+        log("compressed %-10s %d x %d" % (name, o, k))
+    ws, layers = ws * args.repeats, layers * args.repeats
+    resident = sum(w.numel() for w in ws)
+    compressed = sum(l.compressed_bytes() for l in layers[: len(layers) // args.repeats]) * args.repeats
+    configs = [("serial", 3, 0, None), ("ahead2", 3, 2, None), ("ahead2_wg256", 3, 2, 256)]
+    chosen = args.pipe_configs.split(",")
+    pipes = {nm: P.DecodePipeline(layers, slots=s, ahead=a, workgroups=wg) for nm, s, a, wg in configs
+             if nm in chosen}
+    results = []
+    for T in [int(t) for t in args.tokens.split(",")]:
+        g = torch.Generator(device=d).manual_seed(T)
+        xs = [(torch.randn(T, l.in_features, device=d, generator=g) * 4).clamp(-448, 448)
+              .to(torch.float8_e4m3fn) for l in layers]
+        scs = [torch.tensor(0.25, dtype=torch.float32, device=d) for _ in layers]
+        ref = [P.linear_fp8(x, s, w, l.w_scale) for x, s, w, l in zip(xs, scs, ws, layers)]
+        for nm, pipe in pipes.items():                      # bit-exact against resident weights
+            outs = pipe.run(xs, scs)
+            torch.cuda.synchronize()
+            if not all(torch.equal(o, r) for o, r in zip(outs, ref)):
+                log("MISMATCH in pipeline", nm, "T", T)
+                sys.exit(1)
+        del ref
+
+        def timed(fn, reps):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps
+
+        reps = max(3, min(20, args.steps))
+        row = {"tokens": T, "resident_ms": round(timed(
+            lambda: [P.linear_fp8(x, s, w, l.w_scale) for x, s, w, l in zip(xs, scs, ws, layers)], reps), 4)}
+        for nm, pipe in pipes.items():
+            row[nm + "_ms"] = round(timed(lambda: pipe.run(xs, scs), reps), 4)
+            row[nm + "_vs_resident"] = round(row[nm + "_ms"] / row["resident_ms"], 4)
+        log(json.dumps(row))
+        results.append(row)
+        del xs
+    main_cfg = "ahead2" if "ahead2" in pipes else next(iter(pipes))
+    pool = pipes[main_cfg].pool_bytes()
+    res = {"metric": "ECF8 decode-on-use forward time / resident-FP8 forward time (FP8 GEMMs of the block's "
+                     "linear layers, decode 2 layers ahead on a side stream into a 3-slot pool)",
+           "value": results[-1][main_cfg + "_vs_resident"], "unit": "ratio", "n_gpus": 1,
+           "higher_is_better": False, "dtype": "fp8 e4m3 GEMM, u8 decode", "data": "synthetic",
+           "config": {"workload": WORKLOAD_TEXT[args.workload], "layers": len(layers), "repeats": args.repeats,
+                      "gemm": "torch._scaled_mm" if P._scaled_mm_ok(d) else "bf16 matmul"},
+           "memory": {"resident_fp8_bytes": resident, "compressed_bytes": compressed, "pool_bytes": pool,
+                      "ecf8_total_bytes": compressed + pool},
+           "results": results}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,11 +199,21 @@ def main():
     ap.add_argument("--workload", default="llama70b", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", default="decode", choices=["decode", "pipeline"],
+                    help="decode: the batched decode step (default); pipeline: decode-on-use of the "
+                         "block's layers beside FP8 GEMMs, against resident FP8 weights")
+    ap.add_argument("--tokens", default="128,1024,4096", help="pipeline mode: GEMM rows (comma list)")
+    ap.add_argument("--repeats", type=int, default=2, help="pipeline mode: copies of the block's 7 layers")
+    ap.add_argument("--pipe-configs", default="serial,ahead2,ahead2_wg256",
+                    help="pipeline mode: which decode schedules to run (comma list)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: ECF8 decode is GPU-local (each GPU decodes its own "
               "shard); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.mode == "pipeline":
+        pipeline_bench(args)
+        return
 
     import torch
     import synth

@@ -127,7 +127,11 @@ typedef struct {
     uint32_t count;
     uint32_t chunk_bytes;
     uint32_t threads_per_block;
-    uint32_t grid;           /* workgroups of the persistent decode kernel */
+    uint32_t grid;           /* workgroups of the persistent decode kernel; the caller
+                                may lower it (to any value >= 1) before a run to leave
+                                compute units to kernels on other streams: every
+                                workgroup walks blocks grid apart, so all blocks are
+                                decoded whatever the value */
 } ecf8_plan;
 
 /* ---------------------------- host side ------------------------------- */

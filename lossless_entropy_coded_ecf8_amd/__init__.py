@@ -10,6 +10,8 @@ from .binding import (DecodePlan, DeviceEncoded, Ecf8Error, Encoded, build_codeb
                       codebook_from_freq, decode, decode_batched, encode, histogram, lib, validate_meta,
                       workspace_bytes)
 
-__all__ = ["DecodePlan", "DeviceEncoded", "Ecf8Error", "Encoded", "build_codebook", "canonical_codes",
+from .pipeline import DecodePipeline, ECF8Linear, fp8_e4m3_bytes, linear_fp8
+
+__all__ = ["DecodePipeline", "ECF8Linear", "fp8_e4m3_bytes", "linear_fp8", "DecodePlan", "DeviceEncoded", "Ecf8Error", "Encoded", "build_codebook", "canonical_codes",
            "codebook_from_freq", "decode", "decode_batched", "encode", "histogram", "lib", "validate_meta",
            "workspace_bytes"]

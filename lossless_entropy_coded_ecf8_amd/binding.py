@@ -298,7 +298,10 @@ class DecodePlan:
     """
 
     def __init__(self, encs: Sequence[DeviceEncoded], out=None, offsets: Optional[List[int]] = None,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, workgroups: Optional[int] = None):
+        """workgroups: upper bound on the persistent decode's workgroups (default:
+        every compute unit at full occupancy); a smaller grid leaves compute units
+        to kernels running concurrently on other streams."""
         import torch
         self.encs = list(encs)
         dev = self.encs[0].stream.device if self.encs else torch.device("cuda")
@@ -324,6 +327,8 @@ class DecodePlan:
                                          ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
                                          _stream_handle(stream), ctypes.byref(self.plan)),
                "ecf8_decode_prepare")
+        if workgroups is not None:
+            self.plan.grid = max(1, min(int(self.plan.grid), int(workgroups)))
 
     def run(self, stream=None):
         _check(lib().ecf8_decode_run(ctypes.byref(self.plan), _stream_handle(stream)), "ecf8_decode_run")

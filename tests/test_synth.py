@@ -71,3 +71,32 @@ def test_dit_tile_scaling_hits_448_per_tile():
     mags = (x & 0x7F)
     t = mags.reshape(2, 128, 3, 128).amax(dim=(1, 3))
     assert bool((t == 0x7E).all())
+
+
+def test_fp8_weight_quantizer_scale_and_saturation():
+    """Per-tensor max-abs scaling puts max|w| at 448 exactly; the cast is round-to-nearest-even."""
+    import torch
+    from lossless_entropy_coded_ecf8_amd.pipeline import fp8_e4m3_bytes
+    w = torch.tensor([[0.0, -3.5, 7.0, 1.0], [2.0, -7.0, 0.125, 6.9]])
+    q, scale = fp8_e4m3_bytes(w)
+    assert q.dtype == torch.uint8 and q.shape == w.shape
+    assert scale == 7.0 / 448.0
+    f = q.view(torch.float8_e4m3fn).float()
+    assert f.abs().max().item() == 448.0
+    assert q[0, 2].item() == 0x7E and q[1, 1].item() == 0xFE          # +-448
+    assert q[0, 0].item() == 0x00
+    # 1.0 / scale = 64 exactly representable
+    assert f[0, 3].item() == 64.0
+    z, s0 = fp8_e4m3_bytes(torch.zeros(3, 3))
+    assert s0 == 1.0 and int(z.sum()) == 0
+
+
+def test_pipeline_argument_checks():
+    import pytest as _pt
+    from lossless_entropy_coded_ecf8_amd.pipeline import DecodePipeline
+    with _pt.raises(ValueError):
+        DecodePipeline([])
+    with _pt.raises(ValueError):
+        DecodePipeline([object()], slots=2, ahead=2)
+    with _pt.raises(ValueError):
+        DecodePipeline([object()], slots=0, ahead=0)
