@@ -118,6 +118,39 @@ def cpu_baseline(encs_host, seconds: float):
                       "one thread per core, %.1f s" % (len(blocks), done, dt)}
 
 
+def alpha_report(n: int = 1 << 24):
+    """Tail index vs exponent entropy (ECF8 blog §2.2 bound, §6 estimator) on seeded CMS samples."""
+    import math
+    import numpy as np
+    import torch
+    import synth
+    import lossless_entropy_coded_ecf8_amd as E
+
+    d = torch.device("cuda:0") if torch.cuda.is_available() else torch.device("cpu")
+    rows = []
+    for alpha in (1.5, 1.6, 1.7, 1.8, 1.9, 2.0):
+        g = torch.Generator(device=d).manual_seed(synth.seed_of("alpha-report", alpha))
+        x = synth.alpha_stable(alpha, n, g, d, synth.GAMMA)
+        ah = E.alpha_hat(x.float().cpu().numpy(), synth.GAMMA)
+        # the pages' E = floor(log2 |x|) of the raw weight, and the E4M3 exponent field after scaling
+        e_raw = torch.floor(torch.log2(x.abs().clamp_min(1e-300))).to(torch.int64).cpu().numpy()
+        _, c = np.unique(e_raw, return_counts=True)
+        p = c / c.sum()
+        h_raw = float(-(p * np.log2(p)).sum())
+        q = synth.to_e4m3_bytes(synth.maxabs_scale(x)).cpu().numpy()
+        f = E.histogram(q).astype(np.float64)
+        pf = f[f > 0] / f.sum()
+        h_fp8 = float(-(pf * np.log2(pf)).sum())
+        enc = E.encode(q)
+        rows.append({"alpha": alpha, "n": n, "alpha_hat": round(ah, 4), "H_floor_log2": round(h_raw, 4),
+                     "H_e4m3_exponent": round(h_fp8, 4), "huffman_bits": round(enc.meta.total_bits / n, 4),
+                     "bound": round(E.exponent_entropy_bound(alpha), 4)})
+        log(json.dumps(rows[-1]))
+    print(json.dumps({"report": "alpha-stable tail index vs exponent entropy", "gamma": synth.GAMMA,
+                      "estimator": "alpha_hat = log n / log(max|w| / gamma)",
+                      "bound": "alpha / (1 - 2^-alpha)", "rows": rows}), flush=True)
+
+
 def pipeline_bench(args):
     """Decode-on-use (ECF8 blog §3.2.2/§3.3): forward time of the block's linear layers with weights
     decoded ahead of use into a 3-slot pool, against the same FP8 GEMMs on resident FP8 weights."""
@@ -199,7 +232,7 @@ def main():
     ap.add_argument("--workload", default="llama70b", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="decode", choices=["decode", "pipeline"],
+    ap.add_argument("--mode", default="decode", choices=["decode", "pipeline", "alpha"],
                     help="decode: the batched decode step (default); pipeline: decode-on-use of the "
                          "block's layers beside FP8 GEMMs, against resident FP8 weights")
     ap.add_argument("--tokens", default="128,1024,4096", help="pipeline mode: GEMM rows (comma list)")
@@ -213,6 +246,9 @@ def main():
         sys.exit(2)
     if args.mode == "pipeline":
         pipeline_bench(args)
+        return
+    if args.mode == "alpha":
+        alpha_report()
         return
 
     import torch

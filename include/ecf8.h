@@ -224,6 +224,22 @@ int ecf8_decode(const ecf8_stream* s, const ecf8_meta* meta, uint8_t* out_fp8, u
  * prepare) into *bad_blocks and returns ECF8_ERR_CORRUPT if it is non-zero. */
 int ecf8_decode_status(const void* workspace, void* hip_stream, uint64_t* bad_blocks);
 
+/* ------------------------- weight statistics --------------------------- */
+
+/* ECF8 blog §6 (adaptive α estimation): the tail-index estimate
+ *     α̂ = log n / log(max_i |w_i| / γ)
+ * of n weights w (host, float32, before FP8 quantization) of an α-stable law
+ * with scale γ.  NaN weights are skipped.  *alpha_hat receives α̂ (natural
+ * logs; the ratio makes the base irrelevant).
+ * Errors: ECF8_ERR_ARG if w is NULL with n > 0, alpha_hat is NULL, n < 2,
+ * γ <= 0 (or NaN), or max |w| <= γ (the estimate is then undefined). */
+int ecf8_alpha_hat(const float* w, uint64_t n, double gamma, double* alpha_hat);
+
+/* ECF8 blog §2.2: the upper bound α / (1 - 2^-α) on the entropy, in bits, of
+ * the floating-point exponent of an α-stable weight (8/3 at α = 2).  NaN for
+ * α <= 0. */
+double ecf8_exponent_entropy_bound(double alpha);
+
 /* Human-readable name of an error code (static string). */
 const char* ecf8_strerror(int code);
 

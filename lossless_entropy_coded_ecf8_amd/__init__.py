@@ -6,12 +6,12 @@ sign and mantissa stay raw as packed nibbles (ECF8 technical blog,
 codearts.csdn.net, §3.1.1).  Decode runs in hand-written HIP kernels behind a
 C ABI (include/ecf8.h); this package is a thin ctypes binding over it.
 """
-from .binding import (DecodePlan, DeviceEncoded, Ecf8Error, Encoded, build_codebook, canonical_codes,
+from .binding import (DecodePlan, alpha_hat, exponent_entropy_bound, DeviceEncoded, Ecf8Error, Encoded, build_codebook, canonical_codes,
                       codebook_from_freq, decode, decode_batched, encode, histogram, lib, validate_meta,
                       workspace_bytes)
 
 from .pipeline import DecodePipeline, ECF8Linear, fp8_e4m3_bytes, linear_fp8
 
-__all__ = ["DecodePipeline", "ECF8Linear", "fp8_e4m3_bytes", "linear_fp8", "DecodePlan", "DeviceEncoded", "Ecf8Error", "Encoded", "build_codebook", "canonical_codes",
+__all__ = ["alpha_hat", "exponent_entropy_bound", "DecodePipeline", "ECF8Linear", "fp8_e4m3_bytes", "linear_fp8", "DecodePlan", "DeviceEncoded", "Ecf8Error", "Encoded", "build_codebook", "canonical_codes",
            "codebook_from_freq", "decode", "decode_batched", "encode", "histogram", "lib", "validate_meta",
            "workspace_bytes"]

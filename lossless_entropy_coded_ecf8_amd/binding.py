@@ -68,7 +68,8 @@ EXPORTS = ["ecf8_histogram", "ecf8_codebook_from_freq", "ecf8_build_codebook", "
            "ecf8_encode_sizes", "ecf8_encode", "ecf8_validate_meta", "ecf8_workspace_bytes",
            "ecf8_decode_prepare", "ecf8_decode_run", "ecf8_build_tables", "ecf8_decode_blocks",
            "ecf8_decode_batched", "ecf8_decode",
-           "ecf8_decode_status", "ecf8_strerror", "ecf8_version"]
+           "ecf8_decode_status", "ecf8_alpha_hat", "ecf8_exponent_entropy_bound", "ecf8_strerror",
+           "ecf8_version"]
 
 _lib = None
 
@@ -105,6 +106,8 @@ def lib() -> ctypes.CDLL:
         "ecf8_decode": (i, [ctypes.POINTER(Stream), ctypes.POINTER(Meta), vp, ctypes.c_uint64, vp,
                             ctypes.c_uint64, vp]),
         "ecf8_decode_status": (i, [vp, vp, u64p]),
+        "ecf8_alpha_hat": (i, [vp, ctypes.c_uint64, ctypes.c_double, ctypes.POINTER(ctypes.c_double)]),
+        "ecf8_exponent_entropy_bound": (ctypes.c_double, [ctypes.c_double]),
         "ecf8_strerror": (ctypes.c_char_p, [i]),
         "ecf8_version": (i, []),
     }
@@ -226,6 +229,22 @@ def encode(x, lengths=None, chunk_bytes: int = DEFAULT_CHUNK_BYTES,
                              _ptr(nib), nib.size, _ptr(gaps), gaps.size, _ptr(blk), blk.size,
                              ctypes.byref(m2)), "ecf8_encode")
     return Encoded(m2, stream, nib, gaps, blk, shape)
+
+
+def alpha_hat(w, gamma: float) -> float:
+    """Tail-index estimate log n / log(max|w| / gamma) of float32 weights (ecf8_alpha_hat)."""
+    if hasattr(w, "detach"):
+        w = w.detach().float().cpu().numpy()
+    a = np.ascontiguousarray(np.asarray(w, dtype=np.float32).ravel())
+    out = ctypes.c_double(0.0)
+    _check(lib().ecf8_alpha_hat(a.ctypes.data_as(ctypes.c_void_p), a.size, float(gamma), ctypes.byref(out)),
+           "ecf8_alpha_hat")
+    return float(out.value)
+
+
+def exponent_entropy_bound(alpha: float) -> float:
+    """alpha / (1 - 2^-alpha), the pages' bound on the exponent entropy in bits."""
+    return float(lib().ecf8_exponent_entropy_bound(float(alpha)))
 
 
 def validate_meta(m: Meta) -> int:

@@ -12,6 +12,7 @@
 #include "ecf8.h"
 
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <thread>
@@ -134,6 +135,25 @@ void histogram_mt(const uint8_t* x, uint64_t n, uint64_t freq[kNsym])
 }
 
 }  // namespace
+
+extern "C" int ecf8_alpha_hat(const float* w, uint64_t n, double gamma, double* alpha_hat)
+{
+    if ((!w && n) || !alpha_hat || n < 2 || !(gamma > 0.0)) return ECF8_ERR_ARG;
+    double m = 0.0;
+    for (uint64_t i = 0; i < n; ++i) {
+        const double a = std::fabs((double)w[i]);
+        if (a > m) m = a;                     // NaN compares false and is skipped
+    }
+    if (!(m > gamma)) return ECF8_ERR_ARG;
+    *alpha_hat = std::log((double)n) / std::log(m / gamma);
+    return ECF8_OK;
+}
+
+extern "C" double ecf8_exponent_entropy_bound(double alpha)
+{
+    if (!(alpha > 0.0)) return std::nan("");
+    return alpha / (1.0 - std::exp2(-alpha));
+}
 
 extern "C" int ecf8_version(void) { return 100; }
 

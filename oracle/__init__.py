@@ -198,3 +198,17 @@ def average_length(freq, lengths) -> float:
 def kraft_sum(lengths) -> float:
     L = [int(l) for l in lengths if int(l) > 0]
     return float(sum(2.0 ** -l for l in L))
+
+
+# ---------------------------------------------------------------- alpha statistics
+
+def alpha_hat(w, gamma: float) -> float:
+    """ECF8 blog §6: alpha_hat = log N / log(max |w_i| / gamma), fp64 (NaN weights skipped)."""
+    a = np.abs(np.asarray(w, dtype=np.float64).ravel())
+    a = a[~np.isnan(a)]
+    return float(np.log(np.float64(np.asarray(w).size)) / np.log(a.max() / gamma))
+
+
+def entropy_bound(alpha: float) -> float:
+    """ECF8 blog §2.2: H(E) <= alpha / (1 - 2^-alpha) bits for an alpha-stable weight."""
+    return float(alpha / (1.0 - 2.0 ** (-alpha)))

@@ -175,3 +175,31 @@ def test_workspace_size_grows_with_count():
     a, b = E.workspace_bytes(1), E.workspace_bytes(768)
     assert 0 < a < b
     assert b % 256 == 0
+
+
+# ---------------------------------------------------------------- alpha statistics
+
+def test_alpha_hat_matches_oracle():
+    rng = np.random.default_rng(11)
+    for n in (2, 17, 1000, 100003):
+        w = (rng.standard_cauchy(n) * 0.01).astype(np.float32)
+        w[rng.integers(0, n)] = np.nan
+        gamma = 0.001
+        got = E.alpha_hat(w, gamma)
+        ref = oracle.alpha_hat(w.astype(np.float64), gamma)
+        assert abs(got - ref) <= 1e-12 * abs(ref), (n, got, ref)
+
+
+def test_alpha_hat_rejects_undefined_cases():
+    with pytest.raises(E.Ecf8Error):
+        E.alpha_hat(np.ones(1, dtype=np.float32), 0.5)          # n < 2
+    with pytest.raises(E.Ecf8Error):
+        E.alpha_hat(np.ones(8, dtype=np.float32), 0.0)          # gamma <= 0
+    with pytest.raises(E.Ecf8Error):
+        E.alpha_hat(np.full(8, 0.5, dtype=np.float32), 0.5)     # max|w| <= gamma
+
+
+def test_entropy_bound_matches_oracle():
+    for a in (0.5, 1.0, 1.5, 1.9, 2.0):
+        assert abs(E.exponent_entropy_bound(a) - oracle.entropy_bound(a)) < 1e-15
+    assert np.isnan(E.exponent_entropy_bound(0.0))

@@ -322,3 +322,31 @@ def test_gaussian_exponent_entropy_and_short_codes():
     avg = oracle.average_length(f, L)
     assert H <= avg < H + 1
     assert max(L) <= 16
+
+
+# ---------------------------------------------------------------- alpha statistics (ECF8 blog §2.2, §6)
+
+def test_alpha_hat_closed_form():
+    """If max|w| = gamma * N^(1/alpha) exactly, the estimate returns alpha."""
+    for alpha in (1.5, 1.8, 2.0):
+        for n in (10, 1000, 123457):
+            gamma = 0.01
+            w = np.full(n, gamma * 0.5)
+            w[n // 3] = -gamma * n ** (1.0 / alpha)
+            assert abs(oracle.alpha_hat(w, gamma) - alpha) < 1e-12
+
+
+def test_alpha_hat_ignores_nan_and_sign():
+    w = np.array([0.5, -3.0, np.nan, 1.0])
+    assert oracle.alpha_hat(w, 1.0) == np.log(4.0) / np.log(3.0)
+
+
+def test_entropy_bound_values():
+    """alpha / (1 - 2^-alpha): 8/3 at alpha = 2 (the page's 2.67 bits), 2 at alpha = 1,
+    1/ln 2 in the limit alpha -> 0, increasing in alpha."""
+    assert abs(oracle.entropy_bound(2.0) - 8.0 / 3.0) < 1e-15
+    assert abs(round(oracle.entropy_bound(2.0), 2) - 2.67) < 1e-12
+    assert oracle.entropy_bound(1.0) == 2.0
+    assert abs(oracle.entropy_bound(1e-9) - 1.0 / np.log(2.0)) < 1e-6
+    v = [oracle.entropy_bound(a) for a in np.linspace(0.1, 2.0, 20)]
+    assert all(b > a for a, b in zip(v, v[1:]))
