@@ -224,6 +224,67 @@ def pipeline_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def encode_bench(args):
+    """GPU encode (ECF8 blog §3.1.1 / §3.2.1 on the device) of every tensor of the workload: histogram,
+    then tile sums, scans and the encode kernel; output checked byte-identical to the host encoder."""
+    import numpy as np
+    import torch
+    import synth
+    import lossless_entropy_coded_ecf8_amd as E
+    from lossless_entropy_coded_ecf8_amd import binding as B
+
+    d = torch.device("cuda:0")
+    names, xs = [], []
+    for name, x in synth.workload_tensors(args.workload, device=d):
+        names.append(name)
+        xs.append(x.reshape(-1))
+    encs = [E.encode_device(x) for x in xs]
+    torch.cuda.synchronize()
+    for nm, x, e in zip(names, xs, encs):                  # byte-identical to the host encoder
+        h = E.encode(x.cpu())
+        same = (B.meta_dict(h.meta) == B.meta_dict(e.meta) and np.array_equal(h.stream, e.stream.cpu().numpy())
+                and np.array_equal(h.nibbles, e.nibbles.cpu().numpy()) and np.array_equal(h.gaps, e.gaps.cpu().numpy())
+                and np.array_equal(h.blk_off.view(np.int64), e.blk_off.cpu().numpy()))
+        if not same:
+            log("MISMATCH device encode vs host encoder:", nm)
+            sys.exit(1)
+    log("device encode byte-identical to the host encoder on %d tensors" % len(xs))
+    ws = torch.empty(max(E.encode_workspace_bytes(x.numel()) for x in xs), dtype=torch.uint8, device=d)
+    freqs = [torch.empty(16, dtype=torch.int64, device=d) for _ in xs]
+
+    def timed(fn, reps):
+        for _ in range(max(2, args.warmup // 10)):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    reps = max(3, args.steps // 5)
+    hist_ms = timed(lambda: [B.histogram_device(x, f) for x, f in zip(xs, freqs)], reps)
+    enc_ms = timed(lambda: [B.encode_into(x, e, ws) for x, e in zip(xs, encs)], reps)
+    e2e_ms = timed(lambda: [E.encode_device(x) for x in xs], reps)
+    n = sum(x.numel() for x in xs)
+    comp = sum(E.binding.compressed_bytes(e.meta) for e in encs)
+    res = {"metric": "ECF8 GPU encode, FP8 GB/s encoded on 1 MI355X (histogram + encode kernels)",
+           "value": round(n / ((hist_ms + enc_ms) * 1e-3) / 1e9, 3), "unit": "GB/s", "n_gpus": 1,
+           "higher_is_better": True, "dtype": "u8", "data": "synthetic",
+           "config": {"workload": WORKLOAD_TEXT[args.workload], "tensors": len(xs), "elements": n,
+                      "compressed_bytes": comp},
+           "histogram_ms": round(hist_ms, 4), "encode_ms": round(enc_ms, 4),
+           "end_to_end_ms": round(e2e_ms, 4),
+           "end_to_end_note": "encode_device per tensor: histogram, 128 B copy to the host and one "
+                              "synchronisation, codebook and sizes on the host, buffer allocation, encode",
+           "encode_pass_hbm_gbs": round((2 * n + comp) / (enc_ms * 1e-3) / 1e9, 2),
+           "encode_pass_note": "the encode pass reads the input twice (tile sums, encode) and writes the "
+                               "compressed form; the histogram pass reads it once more"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,7 +293,7 @@ def main():
     ap.add_argument("--workload", default="llama70b", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="decode", choices=["decode", "pipeline", "alpha"],
+    ap.add_argument("--mode", default="decode", choices=["decode", "pipeline", "alpha", "encode"],
                     help="decode: the batched decode step (default); pipeline: decode-on-use of the "
                          "block's layers beside FP8 GEMMs, against resident FP8 weights")
     ap.add_argument("--tokens", default="128,1024,4096", help="pipeline mode: GEMM rows (comma list)")
@@ -249,6 +310,9 @@ def main():
         return
     if args.mode == "alpha":
         alpha_report()
+        return
+    if args.mode == "encode":
+        encode_bench(args)
         return
 
     import torch

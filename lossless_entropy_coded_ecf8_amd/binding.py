@@ -68,7 +68,8 @@ EXPORTS = ["ecf8_histogram", "ecf8_codebook_from_freq", "ecf8_build_codebook", "
            "ecf8_encode_sizes", "ecf8_encode", "ecf8_validate_meta", "ecf8_workspace_bytes",
            "ecf8_decode_prepare", "ecf8_decode_run", "ecf8_build_tables", "ecf8_decode_blocks",
            "ecf8_decode_batched", "ecf8_decode",
-           "ecf8_decode_status", "ecf8_alpha_hat", "ecf8_exponent_entropy_bound", "ecf8_strerror",
+           "ecf8_decode_status", "ecf8_histogram_device", "ecf8_meta_from_freq", "ecf8_encode_workspace_bytes",
+           "ecf8_encode_device", "ecf8_alpha_hat", "ecf8_exponent_entropy_bound", "ecf8_strerror",
            "ecf8_version"]
 
 _lib = None
@@ -106,6 +107,11 @@ def lib() -> ctypes.CDLL:
         "ecf8_decode": (i, [ctypes.POINTER(Stream), ctypes.POINTER(Meta), vp, ctypes.c_uint64, vp,
                             ctypes.c_uint64, vp]),
         "ecf8_decode_status": (i, [vp, vp, u64p]),
+        "ecf8_histogram_device": (i, [vp, ctypes.c_uint64, vp, vp]),
+        "ecf8_meta_from_freq": (i, [u64p, ctypes.c_uint64, ctypes.POINTER(Codebook), ctypes.POINTER(Params),
+                                    ctypes.POINTER(Meta)]),
+        "ecf8_encode_workspace_bytes": (ctypes.c_uint64, [ctypes.c_uint64]),
+        "ecf8_encode_device": (i, [vp, ctypes.POINTER(Meta), vp, vp, vp, vp, vp, ctypes.c_uint64, vp]),
         "ecf8_alpha_hat": (i, [vp, ctypes.c_uint64, ctypes.c_double, ctypes.POINTER(ctypes.c_double)]),
         "ecf8_exponent_entropy_bound": (ctypes.c_double, [ctypes.c_double]),
         "ecf8_strerror": (ctypes.c_char_p, [i]),
@@ -247,6 +253,22 @@ def exponent_entropy_bound(alpha: float) -> float:
     return float(lib().ecf8_exponent_entropy_bound(float(alpha)))
 
 
+def meta_from_freq(freq, n: int, lengths, chunk_bytes: int = DEFAULT_CHUNK_BYTES,
+                   threads_per_block: int = DEFAULT_THREADS_PER_BLOCK) -> Meta:
+    """Metadata for n elements with exponent histogram freq under code lengths (ecf8_meta_from_freq)."""
+    f = (ctypes.c_uint64 * NSYM)(*[int(v) for v in freq])
+    cb = _codebook(lengths)
+    p = Params(chunk_bytes, threads_per_block)
+    m = Meta()
+    _check(lib().ecf8_meta_from_freq(f, int(n), ctypes.byref(cb), ctypes.byref(p), ctypes.byref(m)),
+           "ecf8_meta_from_freq")
+    return m
+
+
+def encode_workspace_bytes(n: int) -> int:
+    return int(lib().ecf8_encode_workspace_bytes(int(n)))
+
+
 def validate_meta(m: Meta) -> int:
     return int(lib().ecf8_validate_meta(ctypes.byref(m)))
 
@@ -292,6 +314,64 @@ def _workspace(count: int, device, workspace=None):
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
     return workspace
+
+
+def histogram_device(x, freq=None, stream=None):
+    """Exponent histogram of a device uint8 tensor (ecf8_histogram_device); returns 16 int64 counts on the device."""
+    import torch
+    x = x.contiguous().view(-1)
+    if freq is None:
+        freq = torch.empty(NSYM, dtype=torch.int64, device=x.device)
+    _check(lib().ecf8_histogram_device(ctypes.c_void_p(x.data_ptr()), x.numel(), ctypes.c_void_p(freq.data_ptr()),
+                                       _stream_handle(stream)), "ecf8_histogram_device")
+    return freq
+
+
+def alloc_device(meta: Meta, device, shape=()) -> DeviceEncoded:
+    """Uninitialised device buffers of meta's sizes (stream, nibbles, gaps, blk_off)."""
+    import torch
+    e = lambda k, dt=torch.uint8: torch.empty(max(int(k), 1), dtype=dt, device=device)
+    return DeviceEncoded(meta, e(meta.stream_bytes), e(meta.nibble_bytes), e(meta.gap_bytes),
+                         e(meta.n_blocks + 1, torch.int64), shape)
+
+
+def encode_into(x, enc: DeviceEncoded, workspace=None, stream=None) -> DeviceEncoded:
+    """Encode device bytes x into enc's buffers under enc.meta (ecf8_encode_device)."""
+    import torch
+    x = x.contiguous().view(-1)
+    need = encode_workspace_bytes(x.numel())
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    m = enc.meta
+    _check(lib().ecf8_encode_device(ctypes.c_void_p(x.data_ptr()), ctypes.byref(m),
+                                    ctypes.c_void_p(enc.stream.data_ptr()), ctypes.c_void_p(enc.nibbles.data_ptr()),
+                                    ctypes.c_void_p(enc.gaps.data_ptr()), ctypes.c_void_p(enc.blk_off.data_ptr()),
+                                    ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                    _stream_handle(stream)), "ecf8_encode_device")
+    return enc
+
+
+def encode_device(x, lengths=None, chunk_bytes: int = DEFAULT_CHUNK_BYTES,
+                  threads_per_block: int = DEFAULT_THREADS_PER_BLOCK, max_len: int = 16,
+                  stream=None) -> DeviceEncoded:
+    """GPU encode of a device uint8 (FP8 E4M3 bytes) tensor.
+
+    Histogram on the GPU; the 16 counts come to the host (one synchronisation)
+    for the code lengths and buffer sizes; the encode itself runs on the GPU.
+    The buffers equal those of encode() on the same bytes.
+    """
+    import torch
+    shape = tuple(x.shape)
+    x = x.contiguous().view(-1)
+    if x.dtype != torch.uint8:
+        x = x.view(torch.uint8)
+    n = x.numel()
+    freq = histogram_device(x, stream=stream).cpu().numpy().astype(np.uint64)
+    if lengths is None:
+        lengths = codebook_from_freq(freq, max_len) if n else [0] * NSYM
+    m = meta_from_freq(freq, n, lengths, chunk_bytes, threads_per_block)
+    enc = alloc_device(m, x.device, shape)
+    return encode_into(x, enc, stream=stream)
 
 
 def decode(enc: DeviceEncoded, out=None, workspace=None, stream=None):

@@ -23,7 +23,7 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
 
 
 def sources():
-    return [os.path.join(CSRC, f) for f in ("ecf8_host.cpp", "ecf8_decode.hip")]
+    return [os.path.join(CSRC, f) for f in ("ecf8_host.cpp", "ecf8_decode.hip", "ecf8_encode.hip")]
 
 
 def build(verbose: bool = False, extra=None) -> str:

@@ -278,6 +278,16 @@ static int sizes_from_freq(const uint64_t freq[kNsym], uint64_t n, const ecf8_co
     return ECF8_OK;
 }
 
+extern "C" int ecf8_meta_from_freq(const uint64_t freq[kNsym], uint64_t n, const ecf8_codebook* cb,
+                                   const ecf8_params* params, ecf8_meta* out)
+{
+    if (!freq || !cb || !out || !params_ok(params)) return ECF8_ERR_ARG;
+    uint64_t total = 0;
+    for (int s = 0; s < kNsym; ++s) total += freq[s];
+    if (total != n) return ECF8_ERR_SIZE;
+    return sizes_from_freq(freq, n, cb, params, out);
+}
+
 extern "C" int ecf8_encode_sizes(const uint8_t* fp8, uint64_t n, const ecf8_codebook* cb,
                                  const ecf8_params* params, ecf8_meta* out)
 {

@@ -177,6 +177,73 @@ def test_workspace_size_grows_with_count():
     assert b % 256 == 0
 
 
+# ---------------------------------------------------------------- device encode (host-side logic)
+
+@pytest.mark.parametrize("C,TB", [(16, 256), (4, 64), (12, 192), (64, 1024)])
+def test_meta_from_freq_equals_encode_sizes_and_oracle(C, TB):
+    for n in (1, 17, 4097, 100_003):
+        x = synth.small_stable(n, 1.8, n)
+        L = oracle.huffman_lengths(oracle.histogram(x))
+        m = E.meta_from_freq(oracle.histogram(x).astype(np.uint64), n, L, C, TB)
+        host = E.encode(x, lengths=L, chunk_bytes=C, threads_per_block=TB).meta
+        assert B.meta_dict(m) == B.meta_dict(host)
+        ref = oracle.encode(x, lengths=L, chunk_bytes=C, tb=TB)
+        assert int(m.total_bits) == ref["total_bits"]
+        for k in ("n_chunks", "n_blocks", "stream_bytes", "nibble_bytes", "gap_bytes"):
+            assert int(getattr(m, k)) == ref[k], k
+        assert B.validate_meta(m) == 0
+
+
+def test_meta_from_freq_rejects_inconsistent_counts():
+    x = synth.small_stable(1000, 1.8, 2)
+    f = oracle.histogram(x).astype(np.uint64)
+    L = oracle.huffman_lengths(f)
+    with pytest.raises(E.Ecf8Error) as ei:
+        E.meta_from_freq(f, 999, L)                   # counts do not sum to n
+    assert ei.value.code == -2
+    L2 = list(L)
+    L2[int(np.nonzero(f)[0][0])] = 0                 # a counted symbol without a code
+    with pytest.raises(E.Ecf8Error):
+        E.meta_from_freq(f, 1000, L2)
+    with pytest.raises(E.Ecf8Error) as ei:
+        E.meta_from_freq(f, 1000, L, chunk_bytes=6)
+    assert ei.value.code == -1
+
+
+def test_encode_workspace_bytes():
+    assert E.encode_workspace_bytes(0) >= 256
+    sizes = [E.encode_workspace_bytes(n) for n in (1, 4096, 4097, 10 ** 9, 11_300_000_000)]
+    assert sizes == sorted(sizes) and all(v % 256 == 0 for v in sizes)
+    # tile sums (4 B) and tile offsets (8 B) per 4096-element tile, at least
+    assert sizes[-2] >= 12 * (10 ** 9 // 4096)
+
+
+def test_encode_device_argument_checks_need_no_gpu():
+    """Every rejection happens on the host before any launch (fake device pointers)."""
+    x = synth.small_stable(10_000, 1.8, 3)
+    m = E.encode(x).meta
+    L = E.lib()
+    ws_need = E.encode_workspace_bytes(m.n)
+    P = lambda v: ctypes.c_void_p(v)
+    good = dict(fp8=0x100000, stream=0x200000, nib=0x300000, gaps=0x400000, blk=0x500000, ws=0x600000)
+
+    def call(meta=m, ws_bytes=ws_need, **kw):
+        a = dict(good, **kw)
+        return L.ecf8_encode_device(P(a["fp8"]), ctypes.byref(meta) if meta is not None else None,
+                                    P(a["stream"]), P(a["nib"]), P(a["gaps"]), P(a["blk"]), P(a["ws"]),
+                                    ws_bytes, None)
+    assert call(meta=None) == -1
+    assert call(stream=0) == -1 and call(stream=0x200002) == -1
+    assert call(blk=0x500004) == -1 and call(nib=0x300004) == -1 and call(gaps=0x400002) == -1
+    assert call(fp8=0) == -1
+    assert call(ws=0x600010) == -7 and call(ws_bytes=ws_need - 1) == -7
+    bad = B.Meta.from_buffer_copy(m)
+    bad.total_bits += 1 << 20
+    assert call(meta=bad) == -3
+    assert L.ecf8_histogram_device(P(0), 5, P(0x100000), None) == -1
+    assert L.ecf8_histogram_device(P(0x100000), 5, P(0x100004), None) == -1
+
+
 # ---------------------------------------------------------------- alpha statistics
 
 def test_alpha_hat_matches_oracle():
