@@ -228,9 +228,13 @@ int ecf8_decode_status(const void* workspace, void* hip_stream, uint64_t* bad_bl
 
 /* ECF8 blog §3.1.1 step 1 on the GPU: histogram of the exponent field of n
  * FP8 E4M3 bytes.  fp8: device; freq: device, 16 uint64 counters (8-byte
- * aligned), overwritten.  Asynchronous on hip_stream.
- * Errors: ECF8_ERR_ARG (NULL or misaligned), ECF8_ERR_HIP. */
-int ecf8_histogram_device(const uint8_t* fp8, uint64_t n, uint64_t* freq, void* hip_stream);
+ * aligned), overwritten.  workspace: NULL, or device memory of at least
+ * ecf8_encode_workspace_bytes(n) bytes (256-byte aligned, caller-owned) that
+ * receives the per-tile symbol counts ecf8_encode_device needs for the same
+ * data.  Asynchronous on hip_stream.
+ * Errors: ECF8_ERR_ARG (NULL or misaligned), ECF8_ERR_WORKSPACE, ECF8_ERR_HIP. */
+int ecf8_histogram_device(const uint8_t* fp8, uint64_t n, uint64_t* freq, void* workspace,
+                          uint64_t workspace_bytes, void* hip_stream);
 
 /* Host: metadata (T = sum of freq[s] * len[s], chunk and block counts, the
  * four buffer sizes) for n elements with exponent histogram freq, codebook cb
@@ -239,22 +243,26 @@ int ecf8_histogram_device(const uint8_t* fp8, uint64_t n, uint64_t* freq, void* 
 int ecf8_meta_from_freq(const uint64_t freq[ECF8_NSYM], uint64_t n, const ecf8_codebook* cb,
                         const ecf8_params* params, ecf8_meta* out);
 
-/* Device workspace bytes ecf8_encode_device needs for n elements (256-byte
- * aligned device memory, owned by the caller). */
+/* Device workspace bytes ecf8_histogram_device and ecf8_encode_device need
+ * for n elements (256-byte aligned device memory, owned by the caller):
+ * 32 B per 4096 elements of per-tile counts, 8 B per 4096 of tile offsets. */
 uint64_t ecf8_encode_workspace_bytes(uint64_t n);
 
 /* ECF8 blog §3.1.1 / §3.2.1 on the GPU: encode n = meta->n FP8 bytes (fp8,
  * device) into the four device buffers, of at least meta's sizes: the same
  * bytes as ecf8_encode writes (canonical codes MSB-first, nibble plane, gaps,
- * block offsets, padding zeroed).  meta comes from ecf8_meta_from_freq (or
- * ecf8_encode_sizes) for this data and is validated; with a meta whose T does
- * not match the data no write leaves the buffers, and the stream fails
- * decode's block check.  n = 0 writes the 16 zero bytes of the stream and
+ * block offsets, padding zeroed).  workspace: the one ecf8_histogram_device
+ * filled for this same data (it holds the per-tile symbol counts, which fix
+ * every tile's bit offset; the counts are kept, so one histogram serves
+ * several encodes of the data under different codes or parameters).  meta
+ * comes from ecf8_meta_from_freq (or ecf8_encode_sizes) for this data and is
+ * validated.  Counts or a meta that do not match the data give a wrong
+ * stream, which fails decode's block check, but no write leaves the four
+ * buffers or the workspace.  n = 0 writes the 16 zero bytes of the stream and
  * blk_off[0] = 0 only (fp8, nibbles, gaps and workspace may be NULL).
- * Alignment: stream and gaps 4 B, nibbles and blk_off 8 B, workspace 256 B
- * (ecf8_encode_workspace_bytes(n) bytes, caller-owned).
- * Asynchronous on hip_stream: zero-fill, tile sums, three scan launches,
- * encode.  Errors: ECF8_ERR_ARG (NULL or misaligned), ECF8_ERR_META,
+ * Alignment: stream and gaps 4 B, nibbles and blk_off 8 B, workspace 256 B.
+ * Asynchronous on hip_stream: gap clear, three scan launches, encode.
+ * Errors: ECF8_ERR_ARG (NULL or misaligned), ECF8_ERR_META,
  * ECF8_ERR_WORKSPACE, ECF8_ERR_SIZE (n >= 2^44), ECF8_ERR_HIP. */
 int ecf8_encode_device(const uint8_t* fp8, const ecf8_meta* meta, uint8_t* stream, uint8_t* nibbles,
                        uint8_t* gaps, uint64_t* blk_off, void* workspace, uint64_t workspace_bytes,

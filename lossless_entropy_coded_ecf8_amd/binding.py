@@ -107,7 +107,7 @@ def lib() -> ctypes.CDLL:
         "ecf8_decode": (i, [ctypes.POINTER(Stream), ctypes.POINTER(Meta), vp, ctypes.c_uint64, vp,
                             ctypes.c_uint64, vp]),
         "ecf8_decode_status": (i, [vp, vp, u64p]),
-        "ecf8_histogram_device": (i, [vp, ctypes.c_uint64, vp, vp]),
+        "ecf8_histogram_device": (i, [vp, ctypes.c_uint64, vp, vp, ctypes.c_uint64, vp]),
         "ecf8_meta_from_freq": (i, [u64p, ctypes.c_uint64, ctypes.POINTER(Codebook), ctypes.POINTER(Params),
                                     ctypes.POINTER(Meta)]),
         "ecf8_encode_workspace_bytes": (ctypes.c_uint64, [ctypes.c_uint64]),
@@ -316,14 +316,23 @@ def _workspace(count: int, device, workspace=None):
     return workspace
 
 
-def histogram_device(x, freq=None, stream=None):
-    """Exponent histogram of a device uint8 tensor (ecf8_histogram_device); returns 16 int64 counts on the device."""
+def encode_workspace(n: int, device):
+    """Device workspace for histogram_device / encode_into of n elements."""
+    import torch
+    return torch.empty(encode_workspace_bytes(n), dtype=torch.uint8, device=device)
+
+
+def histogram_device(x, freq=None, workspace=None, stream=None):
+    """Exponent histogram of a device uint8 tensor (ecf8_histogram_device); returns 16 int64 counts on the
+    device.  With `workspace` (encode_workspace) the per-tile counts an encode_into of x needs are kept there."""
     import torch
     x = x.contiguous().view(-1)
     if freq is None:
         freq = torch.empty(NSYM, dtype=torch.int64, device=x.device)
+    ws_ptr, ws_n = (ctypes.c_void_p(workspace.data_ptr()), workspace.numel()) if workspace is not None \
+        else (ctypes.c_void_p(0), 0)
     _check(lib().ecf8_histogram_device(ctypes.c_void_p(x.data_ptr()), x.numel(), ctypes.c_void_p(freq.data_ptr()),
-                                       _stream_handle(stream)), "ecf8_histogram_device")
+                                       ws_ptr, ws_n, _stream_handle(stream)), "ecf8_histogram_device")
     return freq
 
 
@@ -335,13 +344,10 @@ def alloc_device(meta: Meta, device, shape=()) -> DeviceEncoded:
                          e(meta.n_blocks + 1, torch.int64), shape)
 
 
-def encode_into(x, enc: DeviceEncoded, workspace=None, stream=None) -> DeviceEncoded:
-    """Encode device bytes x into enc's buffers under enc.meta (ecf8_encode_device)."""
-    import torch
+def encode_into(x, enc: DeviceEncoded, workspace, stream=None) -> DeviceEncoded:
+    """Encode device bytes x into enc's buffers under enc.meta (ecf8_encode_device); `workspace` is the one a
+    histogram_device of the same x filled."""
     x = x.contiguous().view(-1)
-    need = encode_workspace_bytes(x.numel())
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     m = enc.meta
     _check(lib().ecf8_encode_device(ctypes.c_void_p(x.data_ptr()), ctypes.byref(m),
                                     ctypes.c_void_p(enc.stream.data_ptr()), ctypes.c_void_p(enc.nibbles.data_ptr()),
@@ -353,12 +359,12 @@ def encode_into(x, enc: DeviceEncoded, workspace=None, stream=None) -> DeviceEnc
 
 def encode_device(x, lengths=None, chunk_bytes: int = DEFAULT_CHUNK_BYTES,
                   threads_per_block: int = DEFAULT_THREADS_PER_BLOCK, max_len: int = 16,
-                  stream=None) -> DeviceEncoded:
+                  stream=None, workspace=None) -> DeviceEncoded:
     """GPU encode of a device uint8 (FP8 E4M3 bytes) tensor.
 
-    Histogram on the GPU; the 16 counts come to the host (one synchronisation)
-    for the code lengths and buffer sizes; the encode itself runs on the GPU.
-    The buffers equal those of encode() on the same bytes.
+    Histogram pass on the GPU; the 16 counts come to the host (one
+    synchronisation) for the code lengths and buffer sizes; the encode pass
+    runs on the GPU.  The buffers equal those of encode() on the same bytes.
     """
     import torch
     shape = tuple(x.shape)
@@ -366,12 +372,17 @@ def encode_device(x, lengths=None, chunk_bytes: int = DEFAULT_CHUNK_BYTES,
     if x.dtype != torch.uint8:
         x = x.view(torch.uint8)
     n = x.numel()
-    freq = histogram_device(x, stream=stream).cpu().numpy().astype(np.uint64)
+    if workspace is None or workspace.numel() < encode_workspace_bytes(n):
+        workspace = encode_workspace(n, x.device)
+    freq = histogram_device(x, workspace=workspace, stream=stream)
+    if stream is not None:
+        stream.synchronize()
+    freq = freq.cpu().numpy().astype(np.uint64)
     if lengths is None:
         lengths = codebook_from_freq(freq, max_len) if n else [0] * NSYM
     m = meta_from_freq(freq, n, lengths, chunk_bytes, threads_per_block)
     enc = alloc_device(m, x.device, shape)
-    return encode_into(x, enc, stream=stream)
+    return encode_into(x, enc, workspace, stream=stream)
 
 
 def decode(enc: DeviceEncoded, out=None, workspace=None, stream=None):

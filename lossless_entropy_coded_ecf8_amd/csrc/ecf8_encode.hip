@@ -9,21 +9,26 @@
 // codes MSB-first, nibble plane (s << 3) | m with the even element low, 4-bit
 // gaps with T counted as a codeword start, uint64 block offsets.
 //
-// Structure (n elements, tiles of 4096 = 256 lanes x 16 elements):
-//   1. tile sums of code lengths;
-//   2. three small launches scan the tile sums into 64-bit tile bit offsets
-//      (group totals over 4096 tiles, one workgroup scanning the group totals,
-//      each group rescanning its tiles);
-//   3. per tile: lane and workgroup scans give each element's bit position
-//      p; codewords are OR-ed into an LDS image of the tile's bit range and
-//      written out as 32-bit words (the first and last word of a tile, which
-//      neighbouring tiles share, with global atomic ORs on the zeroed
-//      stream); each element whose bit interval (p, p + len] holds a chunk
-//      start sets that chunk's gap (p + len - start), and likewise a block
-//      start sets the block offset; the nibble plane is written per lane.
-//      Chunks are at least 32 bits and codewords at most 16, so an interval
-//      holds at most one chunk start; a lane finds them by carrying its
-//      offset inside the current chunk.
+// Two passes over the input, in tiles of 4096 elements (256 lanes x 16):
+//   1. histogram: per tile, the count of each of the 16 exponent symbols
+//      (kept in the workspace as 16-bit fields) and the tensor's totals;
+//   -- the host turns the totals into code lengths and sizes --
+//   2. three small launches turn the per-tile counts and the code lengths
+//      into 64-bit tile bit offsets (tile bits = sum of count x length;
+//      group totals over 1024 tiles, one workgroup scanning the group
+//      totals, each group rescanning its tiles), clear the stream words that
+//      two tiles share, and write a 256-entry table of codeword pairs;
+//   3. encode, one workgroup per tile: a lane looks up its 8 element pairs
+//      in the pair table, lane and workgroup scans give the bit positions,
+//      each pair is OR-ed into an LDS image of the tile's bit range, and the
+//      image goes out as 32-bit words (the first and last word of the tile,
+//      when shared with a neighbouring tile, with a global atomic OR on the
+//      cleared word); each chunk start inside a lane's bit range gives that
+//      chunk's gap (next codeword start - chunk start) into an LDS gap image,
+//      written out as whole words, and a block start the block offset; the
+//      nibble plane is written per lane.  Chunks are at least 32 bits and
+//      codewords at most 16, so an element's bit interval holds at most one
+//      chunk start.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -35,49 +40,78 @@ namespace {
 
 constexpr int kEncLanes = 256;
 constexpr int kEncPerLane = 16;
-constexpr uint64_t kTile = (uint64_t)kEncLanes * kEncPerLane;   // 4096 elements
-constexpr int kTileWords = (int)(kTile * ECF8_MAX_CODE_LEN / 32) + 2;   // LDS bit image
-constexpr int kScanLanes = 1024;
-constexpr uint64_t kGroupTiles = 4ull * kScanLanes;                  // tiles per scan group
+constexpr uint64_t kTile = (uint64_t)kEncLanes * kEncPerLane;          // 4096 elements
+constexpr int kTileWords = (int)(kTile * ECF8_MAX_CODE_LEN / 32) + 2;  // LDS bit image
+// LDS gap image: a tile's bits span at most kTileWords * 32 bits, so (chunks
+// being >= 32 bits) at most kTileWords + 1 chunk starts, 8 gaps per word.
+constexpr int kGapWords = (kTileWords + 1) / 8 + 3;
+constexpr int kScanLanes = 256;                                        // lanes of the per-group scans
+constexpr int kTopLanes = 1024;                                        // lanes of the group-total scan
+constexpr uint64_t kGroupTiles = 4ull * kScanLanes;                    // tiles per scan group
+constexpr int kCountWords = 8;                                         // per-tile counts: 16 x 16 bits
+constexpr uint32_t kHistGrid = 2048;
+constexpr int kHistTiles = 4;                                          // tiles per histogram step
 
-// Code table for the kernels: length and MSB-first code per symbol.
+// Symbol counted by 16-bit field f (0 = low half) of per-tile count word d.
+__host__ __device__ constexpr int count_symbol(int d, int f) { return (d >> 1) + 4 * (2 * (d & 1) + f); }
+
+// Code table for the encode kernel: length and MSB-first code per symbol.
 struct EncTable {
     uint32_t code[ECF8_NSYM];
     uint32_t len[ECF8_NSYM];
 };
 
+// Code length of the symbol of each count field: v[2d + f] for word d, half f.
+struct CountLens {
+    uint32_t v[2 * kCountWords];
+};
+
 struct EncArgs {
     const uint8_t* fp8;
     uint64_t n;
+    uint64_t tiles;
     uint64_t n_blocks;
     uint32_t chunk_bits;       // 8 * C
     uint32_t tb;               // chunks per block
     uint64_t gap_count;        // chunks with a gap entry (n_blocks * TB)
+    uint64_t gap_words;        // gap_bytes / 4
     uint64_t stream_words;     // stream_bytes / 4
-    uint8_t* stream;
+    uint32_t* stream;
     uint8_t* nibbles;
     uint32_t* gaps;            // 4-byte words of the gap array
     uint64_t* blk_off;
-    const uint32_t* tile_sum;
-    const uint64_t* tile_off;
+    const uint64_t* tile_off;  // tiles + 1 entries; tile_off[tiles] = T
+    const uint64_t* tile_chunk;   // per tile and for T: chunk holding bit tile_off & ~31, and its block
+    const uint2* pairs;        // codeword-pair table, 256 entries
+    uint64_t m_chunk;          // ceil(2^40 / chunk_bits)
+    uint64_t m_tb;             // ceil(2^40 / tb)
 };
 
-__device__ __forceinline__ uint32_t load_byte(const uint8_t* p, uint64_t i, uint64_t n)
-{
-    return i < n ? (uint32_t)p[i] : 0u;
-}
+// x / d for x < 2^20 and d <= 1024 through m = ceil(2^40 / d): the product's
+// error is below x / 2^40 < 1 / d, so the quotient is exact.
+__device__ __forceinline__ uint32_t div_small(uint32_t x, uint64_t m) { return (uint32_t)(((uint64_t)x * m) >> 40); }
 
-// Load the lane's 16 bytes (elements e0 .. e0 + 15), zero past n.
-__device__ __forceinline__ void load16(const uint8_t* p, uint64_t e0, uint64_t n, uint32_t (&b)[kEncPerLane])
+// The lane's 16 bytes (elements e0 .. e0 + 15) as 4 little-endian words, zero past n.
+__device__ __forceinline__ void load16(const uint8_t* p, uint64_t e0, uint64_t n, uint32_t (&w)[4])
 {
     if (e0 + kEncPerLane <= n && ((uintptr_t)(p + e0) & 15) == 0) {
         const uint4 v = *reinterpret_cast<const uint4*>(p + e0);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        w[0] = v.x;
+        w[1] = v.y;
+        w[2] = v.z;
+        w[3] = v.w;
+    } else {            // ragged tail or unaligned input: byte loads at clamped addresses (n >= 1)
 #pragma unroll
-        for (int i = 0; i < kEncPerLane; ++i) b[i] = (w[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-    } else {
+        for (int q = 0; q < 4; ++q) {
+            uint32_t x = 0;
 #pragma unroll
-        for (int i = 0; i < kEncPerLane; ++i) b[i] = load_byte(p, e0 + i, n);
+            for (int k = 0; k < 4; ++k) {
+                const uint64_t i = e0 + 4 * q + k;
+                const uint32_t v = p[i < n ? i : n - 1];
+                x |= (i < n ? v : 0u) << (8 * k);
+            }
+            w[q] = x;
+        }
     }
 }
 
@@ -88,70 +122,147 @@ __global__ __launch_bounds__(256) void ecf8_zero_kernel(uint32_t* p, uint64_t wo
         p[i] = 0u;
 }
 
-// Exponent histogram.  Every lane counts into its own 16 LDS bins (bin s of
-// lane j at s * 256 + j: the lanes of a wave hit 64 distinct banks), then
-// each bin is summed over the 256 lanes and added once to the global count.
-__global__ __launch_bounds__(256) void ecf8_hist_kernel(const uint8_t* __restrict__ fp8, uint64_t n,
-                                                        unsigned long long* __restrict__ freq)
+// Symbol counts of one lane's 16 bytes as 16-bit fields of 8 words (field
+// (d, f) counts symbol count_symbol(d, f)).  Each element adds 1 << (4 s) to
+// a 64-bit register of 4-bit fields (elements 0..7 and 8..15 in two
+// registers, so no field passes 8); the fields are then widened.  `pad`
+// zero bytes past n were counted as symbol 0 and are taken off.
+__device__ __forceinline__ void lane_counts(const uint32_t (&w)[4], uint32_t pad, uint32_t (&c)[kCountWords])
 {
-    __shared__ uint32_t bins[ECF8_NSYM * kEncLanes];
-    const int tid = threadIdx.x;
+    uint64_t A = 0, B = 0;
 #pragma unroll
-    for (int s = 0; s < ECF8_NSYM; ++s) bins[s * kEncLanes + tid] = 0u;
-    const uint64_t stride = (uint64_t)gridDim.x * kTile;
-    for (uint64_t e0 = (uint64_t)blockIdx.x * kTile + (uint64_t)tid * kEncPerLane; e0 < n; e0 += stride) {
-        uint32_t b[kEncPerLane];
-        load16(fp8, e0, n, b);
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t e = w[q] & 0x78787878u;                 // exponent fields in place
 #pragma unroll
-        for (int i = 0; i < kEncPerLane; ++i)
-            if (e0 + i < n) bins[((b[i] >> 3) & 15u) * kEncLanes + tid] += 1u;
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t sh = (e >> (8 * k + 1)) & 63u;      // 4 x symbol
+            if (q < 2)
+                A += 1ull << sh;
+            else
+                B += 1ull << sh;
+        }
+    }
+    const uint64_t m8 = 0x0F0F0F0F0F0F0F0Full, m16 = 0x00FF00FF00FF00FFull;
+    const uint64_t even = (A & m8) + (B & m8);                 // byte j: symbol 2j
+    const uint64_t odd = ((A >> 4) & m8) + ((B >> 4) & m8);    // byte j: symbol 2j + 1
+    const uint64_t r[4] = {(even & m16) - pad, odd & m16, (even >> 8) & m16, (odd >> 8) & m16};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        c[2 * q] = (uint32_t)r[q];
+        c[2 * q + 1] = (uint32_t)(r[q] >> 32);
+    }
+}
+
+// Sum of v over the 64 lanes of the wave (uniform): DPP row shifts leave each
+// 16-lane row's total in its last lane; the four row totals are read out.
+__device__ __forceinline__ uint32_t wave_total(uint32_t v)
+{
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+    return __builtin_amdgcn_readlane(v, 15) + __builtin_amdgcn_readlane(v, 31) + __builtin_amdgcn_readlane(v, 47) +
+           __builtin_amdgcn_readlane(v, 63);
+}
+
+// Pass 1: exponent histogram.  A workgroup takes kHistTiles consecutive
+// tiles per step (all their loads issued first).  Per tile, each wave's 16
+// counts (a DPP reduction of the lanes' packed counts) meet in LDS, and 32
+// lanes sum the four waves and store the tiles' count words to tile_counts
+// (if given).  Those lanes also keep the workgroup's running totals, which
+// are added to the global counts once at the end.
+__global__ __launch_bounds__(256) void ecf8_hist_kernel(const uint8_t* __restrict__ fp8, uint64_t n, uint64_t tiles,
+                                                        unsigned long long* __restrict__ freq,
+                                                        uint32_t* __restrict__ tile_counts)
+{
+    __shared__ uint32_t part[2][kHistTiles][4][kCountWords];
+    __shared__ uint64_t fold[kHistTiles * kCountWords][2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint64_t tot_lo = 0, tot_hi = 0;
+    const uint64_t steps = (tiles + kHistTiles - 1) / kHistTiles;
+    int buf = 0;
+    for (uint64_t g = blockIdx.x; g < steps; g += gridDim.x, buf ^= 1) {
+        uint32_t w[kHistTiles][4];
+#pragma unroll
+        for (int k = 0; k < kHistTiles; ++k) {
+            const uint64_t tile = g * kHistTiles + k;
+            if (tile < tiles) {
+                load16(fp8, tile * kTile + (uint64_t)tid * kEncPerLane, n, w[k]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) w[k][q] = 0u;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kHistTiles; ++k) {
+            const uint64_t e0 = (g * kHistTiles + k) * kTile + (uint64_t)tid * kEncPerLane;
+            const uint32_t pad =
+                e0 >= n ? kEncPerLane : (e0 + kEncPerLane > n ? (uint32_t)(e0 + kEncPerLane - n) : 0u);
+            uint32_t c[kCountWords];
+            lane_counts(w[k], pad, c);
+#pragma unroll
+            for (int d = 0; d < kCountWords; ++d) c[d] = wave_total(c[d]);
+            if (lane == 0) {
+#pragma unroll
+                for (int d = 0; d < kCountWords; ++d) part[buf][k][wave][d] = c[d];
+            }
+        }
+        __syncthreads();    // part[buf] complete; part[buf ^ 1] was read before this barrier
+        if (tid < kHistTiles * kCountWords) {
+            const int k = tid / kCountWords, d = tid % kCountWords;
+            const uint64_t tile = g * kHistTiles + k;
+            const uint32_t v = part[buf][k][0][d] + part[buf][k][1][d] + part[buf][k][2][d] + part[buf][k][3][d];
+            if (tile < tiles) {
+                if (tile_counts) tile_counts[tile * kCountWords + d] = v;
+                tot_lo += v & 0xFFFFu;
+                tot_hi += v >> 16;
+            }
+        }
+    }
+    if (tid < kHistTiles * kCountWords) {
+        fold[tid][0] = tot_lo;
+        fold[tid][1] = tot_hi;
     }
     __syncthreads();
-    // 16 lanes per bin, each summing 16 entries, then a 16-lane reduction
-    const int bin = tid >> 4, part = tid & 15;
-    uint32_t s = 0;
+    if (tid < kCountWords) {
+        uint64_t lo = 0, hi = 0;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) s += bins[bin * kEncLanes + part * 16 + k];
-    for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off, 16);
-    if (part == 0 && s) atomicAdd(&freq[bin], (unsigned long long)s);
+        for (int k = 0; k < kHistTiles; ++k) {
+            lo += fold[k * kCountWords + tid][0];
+            hi += fold[k * kCountWords + tid][1];
+        }
+        if (lo) atomicAdd(&freq[count_symbol(tid, 0)], (unsigned long long)lo);
+        if (hi) atomicAdd(&freq[count_symbol(tid, 1)], (unsigned long long)hi);
+    }
 }
 
-// Step 1: code-length sum of each tile.
-__global__ __launch_bounds__(256) void ecf8_tile_sum_kernel(EncArgs a, EncTable tab, uint32_t* __restrict__ tile_sum)
+// Code bits of one tile from its counts.
+__device__ __forceinline__ uint32_t tile_bits(const uint32_t* __restrict__ counts, uint64_t tile, const CountLens& L)
 {
-    __shared__ uint32_t part[4];
-    __shared__ uint32_t s_len[ECF8_NSYM];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid < ECF8_NSYM) s_len[tid] = tab.len[tid];
-    __syncthreads();
-    const uint64_t tile = blockIdx.x;
-    const uint64_t e0 = tile * kTile + (uint64_t)tid * kEncPerLane;
-    uint32_t b[kEncPerLane];
-    load16(a.fp8, e0, a.n, b);
+    const uint4 a = reinterpret_cast<const uint4*>(counts)[2 * tile];
+    const uint4 b = reinterpret_cast<const uint4*>(counts)[2 * tile + 1];
+    const uint32_t c[kCountWords] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     uint32_t s = 0;
 #pragma unroll
-    for (int i = 0; i < kEncPerLane; ++i)
-        if (e0 + i < a.n) s += s_len[(b[i] >> 3) & 15u];
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) part[wave] = s;
-    __syncthreads();
-    if (tid == 0) tile_sum[tile] = part[0] + part[1] + part[2] + part[3];
+    for (int d = 0; d < kCountWords; ++d) s += (c[d] & 0xFFFFu) * L.v[2 * d] + (c[d] >> 16) * L.v[2 * d + 1];
+    return s;
 }
 
-// Sum of the four tile sums a scan lane owns (zero past the last tile).
-__device__ __forceinline__ uint32_t lane_tiles(const uint32_t* __restrict__ tile_sum, uint64_t tiles, uint64_t t0,
-                                               uint32_t (&v)[4])
+// Bits of the four tiles a scan lane owns (zero past the last tile).
+__device__ __forceinline__ uint32_t lane_tiles(const uint32_t* __restrict__ counts, const CountLens& L, uint64_t tiles,
+                                               uint64_t t0, uint32_t (&v)[4])
 {
     uint32_t s = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        v[k] = t0 + k < tiles ? tile_sum[t0 + k] : 0u;
+        v[k] = t0 + k < tiles ? tile_bits(counts, t0 + k, L) : 0u;
         s += v[k];
     }
     return s;
 }
 
-// Inclusive scan over a 1024-lane workgroup (64-bit), `wsum` 16 entries of LDS.
+// Inclusive scan over a workgroup of kLanes lanes (64-bit), `wsum` kLanes / 64 entries of LDS.
+template <int kLanes>
 __device__ __forceinline__ uint64_t block_incl_scan(uint64_t v, uint64_t* wsum)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -162,31 +273,47 @@ __device__ __forceinline__ uint64_t block_incl_scan(uint64_t v, uint64_t* wsum)
     if (lane == 63) wsum[wave] = v;
     __syncthreads();
     uint64_t before = 0;
-    for (int w = 0; w < kScanLanes / 64; ++w) before += w < wave ? wsum[w] : 0ull;
+    for (int w = 0; w < kLanes / 64; ++w) before += w < wave ? wsum[w] : 0ull;
     return v + before;
 }
 
-// Step 2a: total of each group of 4096 tiles.
-__global__ __launch_bounds__(kScanLanes) void ecf8_group_sum_kernel(const uint32_t* __restrict__ tile_sum,
+// x / d for x < 2^53 and 0 < d < 2^32: the rounded double quotient, corrected to the floor.
+__device__ __forceinline__ uint64_t div_u64(uint64_t x, uint32_t d)
+{
+    uint64_t q = (uint64_t)((double)x / (double)d);
+    if (q * d > x) --q;
+    else if ((q + 1) * d <= x) ++q;
+    return q;
+}
+
+// Pass 2a: total bits of each group of 1024 tiles.
+__global__ __launch_bounds__(kScanLanes) void ecf8_group_sum_kernel(const uint32_t* __restrict__ counts, CountLens L,
                                                                     uint64_t tiles, uint64_t* __restrict__ gsum)
 {
     __shared__ uint64_t wsum[kScanLanes / 64];
     uint32_t v[4];
-    const uint64_t s = lane_tiles(tile_sum, tiles, blockIdx.x * kGroupTiles + 4ull * threadIdx.x, v);
-    const uint64_t incl = block_incl_scan(s, wsum);
+    const uint64_t s = lane_tiles(counts, L, tiles, blockIdx.x * kGroupTiles + 4ull * threadIdx.x, v);
+    const uint64_t incl = block_incl_scan<kScanLanes>(s, wsum);
     if (threadIdx.x == kScanLanes - 1) gsum[blockIdx.x] = incl;
 }
 
-// Step 2b: exclusive scan of the group totals in place (one workgroup; each
-// lane owns a contiguous run of groups).
-__global__ __launch_bounds__(kScanLanes) void ecf8_group_scan_kernel(uint64_t* __restrict__ g, uint64_t groups)
+// Pass 2b: exclusive scan of the group totals in place (one workgroup; each
+// lane owns a contiguous run of groups); the same launch writes the 256-entry
+// codeword-pair table the encode kernel looks up.
+__global__ __launch_bounds__(kTopLanes) void ecf8_group_scan_kernel(uint64_t* __restrict__ g, uint64_t groups,
+                                                                    EncTable tab, uint2* __restrict__ pairs)
 {
-    __shared__ uint64_t wsum[kScanLanes / 64];
-    const uint64_t per = (groups + kScanLanes - 1) / kScanLanes;
+    __shared__ uint64_t wsum[kTopLanes / 64];
+    if (threadIdx.x < 256) {                              // the codeword-pair table (see lane_pairs)
+        const uint32_t sa = threadIdx.x & 15u, sb = threadIdx.x >> 4;
+        const uint32_t la = tab.len[sa], lb = tab.len[sb];
+        pairs[threadIdx.x] = make_uint2((tab.code[sa] << lb) | tab.code[sb], la | ((la + lb) << 8));
+    }
+    const uint64_t per = (groups + kTopLanes - 1) / kTopLanes;
     const uint64_t lo = (uint64_t)threadIdx.x * per, hi = lo + per < groups ? lo + per : groups;
     uint64_t s = 0;
     for (uint64_t i = lo; i < hi; ++i) s += g[i];
-    uint64_t run = block_incl_scan(s, wsum) - s;
+    uint64_t run = block_incl_scan<kTopLanes>(s, wsum) - s;
     for (uint64_t i = lo; i < hi; ++i) {
         const uint64_t x = g[i];
         g[i] = run;
@@ -194,137 +321,262 @@ __global__ __launch_bounds__(kScanLanes) void ecf8_group_scan_kernel(uint64_t* _
     }
 }
 
-// Step 2c: tile bit offsets = group offset + exclusive scan inside the group.
-__global__ __launch_bounds__(kScanLanes) void ecf8_tile_off_kernel(const uint32_t* __restrict__ tile_sum,
+// Pass 2c: tile bit offsets = group offset + exclusive scan inside the group
+// (tile_off[tiles] = T), with the chunk and block holding each tile's first
+// stream word; the stream word holding a tile start that is not word aligned
+// is shared by two tiles and is cleared for their atomic ORs.
+__global__ __launch_bounds__(kScanLanes) void ecf8_tile_off_kernel(const uint32_t* __restrict__ counts, CountLens L,
                                                                    uint64_t tiles, const uint64_t* __restrict__ goff,
-                                                                   uint64_t* __restrict__ tile_off)
+                                                                   uint64_t* __restrict__ tile_off,
+                                                                   uint64_t* __restrict__ tile_chunk, uint32_t chunk_bits,
+                                                                   uint32_t tb, uint32_t* __restrict__ stream,
+                                                                   uint64_t stream_words)
 {
     __shared__ uint64_t wsum[kScanLanes / 64];
     uint32_t v[4];
     const uint64_t t0 = blockIdx.x * kGroupTiles + 4ull * threadIdx.x;
-    const uint64_t s = lane_tiles(tile_sum, tiles, t0, v);
-    uint64_t run = goff[blockIdx.x] + block_incl_scan(s, wsum) - s;
+    const uint64_t s = lane_tiles(counts, L, tiles, t0, v);
+    uint64_t run = goff[blockIdx.x] + block_incl_scan<kScanLanes>(s, wsum) - s;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        if (t0 + k < tiles) tile_off[t0 + k] = run;
+        if (t0 + k < tiles) {
+            tile_off[t0 + k] = run;
+            const uint64_t c = div_u64(run & ~31ull, chunk_bits);
+            tile_chunk[2 * (t0 + k)] = c;
+            tile_chunk[2 * (t0 + k) + 1] = div_u64(c, tb);
+            if ((run & 31) && (run >> 5) < stream_words) stream[run >> 5] = 0u;
+        }
         run += v[k];
+        if (t0 + k + 1 == tiles) {
+            tile_off[tiles] = run;
+            const uint64_t c = div_u64(run & ~31ull, chunk_bits);
+            tile_chunk[2 * tiles] = c;
+            tile_chunk[2 * tiles + 1] = div_u64(c, tb);
+        }
     }
 }
 
+// Inclusive scan over the 64 lanes of the wave: DPP row shifts inside each
+// 16-lane row, then the earlier rows' totals through readlane.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane)
 {
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t t = __shfl_up(v, off);
-        if (lane >= off) v += t;
-    }
-    return v;
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 15);
+    const uint32_t r1 = __builtin_amdgcn_readlane(v, 31);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = lane >> 4;
+    return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
 
-// Step 3: encode one tile.
-__global__ __launch_bounds__(256) void ecf8_encode_kernel(EncArgs a, EncTable tab)
+// A tile's metadata, one 64-bit word per lane: lane 0 tile_off[tile], 1
+// tile_off[tile + 1], 2..4 its chunk C0, block B0 and the next tile's chunk C1.
+__device__ __forceinline__ uint64_t tile_meta(const EncArgs& a, uint64_t tile, int lane)
 {
-    __shared__ uint32_t img[kTileWords];
-    __shared__ uint32_t wsum[4];
-    __shared__ uint32_t s_len[ECF8_NSYM], s_code[ECF8_NSYM];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid < ECF8_NSYM) {
-        s_len[tid] = tab.len[tid];
-        s_code[tid] = tab.code[tid];
+    if (lane >= 5) return 0;
+    const uint64_t* p = lane < 2 ? a.tile_off + tile + lane : a.tile_chunk + 2 * tile + (lane - 2);
+    return *p;
+}
+
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l)
+{
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Nibble plane of one lane's 16 bytes: (s << 3) | m of each byte, element 0
+// in the low nibble (SWAR: each byte's nibble, then two halvings).
+__device__ __forceinline__ uint2 nibbles16(const uint32_t (&w)[4])
+{
+    uint32_t h[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t x = ((w[q] >> 4) & 0x08080808u) | (w[q] & 0x07070707u);   // nibble in the low half of each byte
+        x = (x | (x >> 4)) & 0x00FF00FFu;                                  // bytes 0 and 2: two nibbles each
+        h[q] = (x | (x >> 8)) & 0xFFFFu;                                   // four nibbles, element 4q lowest
     }
-    __syncthreads();
-    const uint64_t tile = blockIdx.x;
-    const uint64_t e0 = tile * kTile + (uint64_t)tid * kEncPerLane;
-    const uint64_t P0 = a.tile_off[tile];              // first bit of the tile
-    const uint32_t S = a.tile_sum[tile];               // bits of the tile
-    const uint64_t W0 = P0 >> 5;                       // first stream word of the tile
-    const uint32_t nwords = (uint32_t)(((P0 + S + 31) >> 5) - W0);
+    return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+}
 
-    for (uint32_t i = tid; i < nwords; i += kEncLanes) img[i] = 0u;
-
-    uint32_t b[kEncPerLane];
-    load16(a.fp8, e0, a.n, b);
-    uint32_t len[kEncPerLane], acc = 0;
+// Codeword pairs of one lane's 16 elements from the pair table `tbl`: entry
+// s_a + 16 s_b holds pc = code(s_a) followed by code(s_b) (at most 32 bits)
+// and pl = len(s_a) | (len(s_a) + len(s_b)) << 8.  The entry's byte offset
+// 8 s_a + 128 s_b comes straight from the exponent bits (byte & 0x78 = 8 s).
+// Elements at or past `valid` (ragged tail) get length 0.
+template <bool kFull>
+__device__ __forceinline__ void lane_pairs(const uint32_t (&w)[4], uint32_t valid, const uint2* tbl,
+                                           uint32_t (&pc)[8], uint32_t (&pl)[8])
+{
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(tbl);
 #pragma unroll
-    for (int i = 0; i < kEncPerLane; ++i) {
-        len[i] = e0 + i < a.n ? s_len[(b[i] >> 3) & 15u] : 0u;
-        acc += len[i];
-    }
-    const uint32_t incl = wave_incl_scan(acc, lane);
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    uint32_t before = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) before += w < wave ? wsum[w] : 0u;
-    uint32_t rel = (uint32_t)(P0 & 31) + before + incl - acc;   // bit offset inside the tile image
-
-    // nibble plane: (s << 3) | m, even element in the low nibble
-    if (e0 < a.n) {
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            lo |= ((((b[i] >> 4) & 8u) | (b[i] & 7u)) << (4 * i));
-            hi |= ((((b[8 + i] >> 4) & 8u) | (b[8 + i] & 7u)) << (4 * i));
-        }
-        *reinterpret_cast<uint2*>(a.nibbles + (e0 >> 1)) = make_uint2(lo, hi);
-    }
-
-    // codewords into the LDS image (big-endian bit numbering inside each
-    // word); gaps and block offsets from the chunk starts in (p, p + len]
-    const uint64_t p_lane = (P0 & ~31ull) + rel;       // absolute start bit of the lane's first codeword
-    uint64_t t = p_lane / a.chunk_bits;                // chunk holding it
-    uint32_t r = (uint32_t)(p_lane - t * a.chunk_bits);   // offset inside chunk t
-    uint64_t blk = t / a.tb;                           // block of chunk t ...
-    uint32_t tb = (uint32_t)(t - blk * a.tb);          // ... and its place in the block
-#pragma unroll
-    for (int i = 0; i < kEncPerLane; ++i) {
-        const uint32_t l = len[i];
-        if (l) {
-            const uint32_t code = s_code[(b[i] >> 3) & 15u];
-            const uint64_t v = (uint64_t)code << (64 - l - (rel & 31));
-            const uint32_t wi = rel >> 5;
-            atomicOr(&img[wi], (uint32_t)(v >> 32));
-            if ((uint32_t)v) atomicOr(&img[wi + 1], (uint32_t)v);
-            rel += l;
-            r += l;
-            if (r >= a.chunk_bits) {                   // chunk t + 1 starts in (p, p + l]
-                r -= a.chunk_bits;                     // its gap: next codeword start - chunk start
-                ++t;
-                if (++tb == a.tb) {
-                    tb = 0;
-                    ++blk;
-                    if (blk <= a.n_blocks) a.blk_off[blk] = e0 + i + 1;
-                }
-                if (r && t < a.gap_count) atomicOr(&a.gaps[t >> 3], r << (4 * (uint32_t)(t & 7)));
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t m = w[j >> 1] & 0x78787878u;
+        const uint32_t ia = (m >> (16 * (j & 1))) & 0x78u, ib = (m >> (16 * (j & 1) + 8)) & 0x78u;
+        const uint2 e = *reinterpret_cast<const uint2*>(base + ia + (ib << 4));
+        pc[j] = e.x;
+        pl[j] = e.y;
+        if (!kFull) {
+            if ((uint32_t)(2 * j) >= valid) {
+                pc[j] = 0u;
+                pl[j] = 0u;
+            } else if ((uint32_t)(2 * j + 1) >= valid) {  // first codeword only
+                pc[j] = e.x >> ((e.y >> 8) - (e.y & 255u));
+                pl[j] = (e.y & 255u) * 257u;
             }
         }
     }
-    __syncthreads();
+}
 
-    // tile image -> stream (bytes MSB-first: store each big-endian word
-    // byte-swapped); words past the stream (a meta that undercounts T) are
+// Pass 3: encode, one workgroup per tile.
+//   * The workgroup copies the pair table into LDS (one entry per lane).
+//   * The tile's image words and gap words are cleared before the scan
+//     barrier.
+//   * A lane's 8 pairs are OR-ed into the LDS image at their bit positions,
+//     each as a 64-bit window over two words.
+//   * The chunk starts inside a lane's bit range (p, p + acc] are visited
+//     one by one (most lanes have none): the pair holding one is found from
+//     the cumulative pair ends E, its gap is the next codeword start after
+//     it (the end of the pair's first codeword, or of the pair) minus the
+//     chunk start, OR-ed into an LDS gap image (gap words from C0 / 8 on),
+//     and a block start also stores the block offset.
+//   * Chunk, block and position bookkeeping is 32-bit, relative to the
+//     tile's chunk C0 and block B0.
+__global__ __launch_bounds__(256) void ecf8_encode_kernel(EncArgs a)
+{
+    __shared__ uint32_t img[kTileWords];
+    __shared__ uint32_t gimg[kGapWords];                  // gap words from word C0 / 8 on
+    __shared__ uint32_t wsum[4];
+    __shared__ uint2 s_pair[256];                         // the pair table
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint64_t tile = blockIdx.x;
+    const uint64_t e0 = tile * kTile + (uint64_t)tid * kEncPerLane;
+    uint32_t w[4];
+    load16(a.fp8, e0, a.n, w);
+    const uint64_t tm = tile_meta(a, tile, lane);
+    s_pair[tid] = a.pairs[tid];
+    const uint64_t P0 = lane_u64(tm, 0), P1 = lane_u64(tm, 1), C0 = lane_u64(tm, 2), B0 = lane_u64(tm, 3),
+                   C1 = lane_u64(tm, 4);
+    const uint64_t W0 = P0 >> 5;                          // first stream word of the tile
+    const uint64_t nw = P1 > P0 ? ((P1 + 31) >> 5) - W0 : 0;
+    const uint32_t nwords = (uint32_t)(nw < (uint64_t)kTileWords - 1 ? nw : (uint64_t)kTileWords - 1);
+    const uint32_t g_lo = (uint32_t)(((C0 + 1) >> 3) - (C0 >> 3));
+    const uint64_t g_hi64 = C1 > C0 ? (C1 >> 3) - (C0 >> 3) + 1 : 0;
+    const uint32_t g_hi = (uint32_t)(g_hi64 < (uint64_t)kGapWords ? g_hi64 : (uint64_t)kGapWords);
+    for (uint32_t i = tid; i < nwords + 1; i += kEncLanes) img[i] = 0u;   // + 1: the last window's spill word
+    for (uint32_t i = tid; i < g_hi; i += kEncLanes) gimg[i] = 0u;
+    __syncthreads();                                      // pair table
+
+    const uint32_t valid = e0 >= a.n ? 0u : (a.n - e0 >= (uint64_t)kEncPerLane ? 16u : (uint32_t)(a.n - e0));
+    uint32_t pc[8], pl[8], E[8];
+    if ((tile + 1) * kTile <= a.n)
+        lane_pairs<true>(w, 16u, s_pair, pc, pl);
+    else
+        lane_pairs<false>(w, valid, s_pair, pc, pl);
+    uint32_t acc = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        acc += pl[j] >> 8;
+        E[j] = acc;                                       // end of pair j, from the lane's first bit
+    }
+    if (valid) *reinterpret_cast<uint2*>(a.nibbles + (e0 >> 1)) = nibbles16(w);
+
+    const uint32_t incl = wave_incl_scan(acc, lane);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();                                      // wsum; images cleared
+    uint32_t before = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) before += v < wave ? wsum[v] : 0u;
+    const uint32_t rel = (uint32_t)(P0 & 31) + before + incl - acc;   // bit offset inside the tile image
+
+    // codeword pairs into the image: the pair's bits left-aligned in a 64-bit
+    // window starting at its word (offset + length <= 63)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t pos = rel + (j ? E[j - 1] : 0u), L = pl[j] >> 8;
+        const uint64_t v = (uint64_t)pc[j] << ((64u - (pos & 31u) - L) & 63u);
+        atomicOr(&img[pos >> 5], (uint32_t)(v >> 32));
+        atomicOr(&img[(pos >> 5) + 1], (uint32_t)v);
+    }
+
+    // chunk starts in (p, p + acc]: d = their offsets from the lane's first bit
+    const uint32_t x = (uint32_t)((P0 & ~31ull) - C0 * a.chunk_bits) + rel;
+    const uint32_t dt = div_small(x, a.m_chunk);
+    uint32_t u = (uint32_t)(C0 & 7) + dt;                 // chunk of the lane's first bit - 8 * (C0 / 8)
+    const uint32_t tbx = (uint32_t)(C0 - B0 * a.tb) + dt;
+    uint32_t bk = div_small(tbx, a.m_tb);                 // its block - B0
+    uint32_t tbp = tbx - bk * a.tb;                       // its place in the block
+    for (uint32_t d = a.chunk_bits - (x - dt * a.chunk_bits); d <= acc; d += a.chunk_bits) {
+        uint32_t st = 0, en = E[0], la = pl[0] & 255u, jj = 0;   // pair jj: E[jj - 1] < d <= E[jj]
+#pragma unroll
+        for (int k = 0; k < 7; ++k) {
+            const bool past = E[k] < d;
+            st = past ? E[k] : st;
+            en = past ? E[k + 1] : en;
+            la = past ? (pl[k + 1] & 255u) : la;
+            jj += past ? 1u : 0u;
+        }
+        const uint32_t mid = st + la;                     // end of the pair's first codeword
+        const bool in_a = d <= mid;
+        const uint32_t gap = (in_a ? mid : en) - d;
+        ++u;
+        if (++tbp == a.tb) {
+            tbp = 0;
+            ++bk;
+            const uint64_t blk = B0 + bk;
+            if (blk <= a.n_blocks) a.blk_off[blk] = e0 + 2 * jj + (in_a ? 1 : 2);
+        }
+        if (gap && (u >> 3) < g_hi) atomicOr(&gimg[u >> 3], gap << (4 * (u & 7)));
+    }
+    __syncthreads();                                      // images complete
+
+    // tile image -> stream (bytes MSB-first: each big-endian word
+    // byte-swapped); words past the stream (metadata that undercounts T) are
     // dropped
-    uint32_t* const out = reinterpret_cast<uint32_t*>(a.stream);
-    for (uint32_t i = tid; i < nwords; i += kEncLanes) {
-        if (W0 + i >= a.stream_words) break;
-        const uint32_t w = __builtin_bswap32(img[i]);
-        if (i == 0 || i == nwords - 1) {
-            if (w) atomicOr(&out[W0 + i], w);
+    const bool last_tile = tile + 1 == a.tiles;
+    const bool first_shared = (P0 & 31) != 0;
+    const bool last_shared = (P1 & 31) != 0 && !last_tile;
+    const uint32_t nout = W0 >= a.stream_words ? 0u
+                          : (a.stream_words - W0 < (uint64_t)nwords ? (uint32_t)(a.stream_words - W0) : nwords);
+    for (uint32_t i = tid; i < nout; i += kEncLanes) {
+        const uint32_t v = __builtin_bswap32(img[i]);
+        if ((i == 0 && first_shared) || (i == nwords - 1 && last_shared)) {
+            if (v) atomicOr(&a.stream[W0 + i], v);
         } else {
-            out[W0 + i] = w;
+            a.stream[W0 + i] = v;
         }
     }
-    if (tile == 0 && tid == 0) {
-        a.blk_off[0] = 0;
-        a.blk_off[a.n_blocks] = a.n;
+    // gap image -> gaps: the words of chunks C0 + 1 .. C1 (those starting in
+    // (P0, P1]); the first and last may hold other tiles' chunks and are
+    // OR-ed into the cleared gap array
+    for (uint32_t j = g_lo + tid; j < g_hi; j += kEncLanes) {
+        const uint64_t g = (C0 >> 3) + j;
+        if (g >= a.gap_words) break;
+        const uint32_t v = gimg[j];
+        if (j == g_lo || j + 1 == g_hi) {
+            if (v) atomicOr(&a.gaps[g], v);
+        } else {
+            a.gaps[g] = v;
+        }
+    }
+    if (last_tile) {                                      // zero padding after T
+        for (uint64_t g = W0 + nwords + tid; g < a.stream_words; g += kEncLanes) a.stream[g] = 0u;
+        if (tid == 0) {
+            a.blk_off[0] = 0;
+            a.blk_off[a.n_blocks] = a.n;
+        }
     }
 }
 
 int check(hipError_t e) { return e == hipSuccess ? ECF8_OK : ECF8_ERR_HIP; }
 
-// Workspace: tile sums (u32) | tile offsets (u64) | group totals/offsets (u64),
-// each part 256-byte aligned.
+// Workspace: per-tile counts (32 B per tile) | tile bit offsets (tiles + 1,
+// u64) | per-tile chunk and block (2 x u64) | group totals/offsets (u64) |
+// codeword-pair table (2 KB), each part 256-byte aligned.
 struct EncWorkspace {
-    uint64_t tiles, groups, sum_off, off_off, group_off, bytes;
+    uint64_t tiles, groups, off_off, chunk_off, group_off, pair_off, bytes;
 };
 
 EncWorkspace enc_workspace(uint64_t n)
@@ -333,33 +585,37 @@ EncWorkspace enc_workspace(uint64_t n)
     EncWorkspace w;
     w.tiles = (n + kTile - 1) / kTile;
     w.groups = (w.tiles + kGroupTiles - 1) / kGroupTiles;
-    w.sum_off = 0;
-    w.off_off = round(w.tiles * 4);
-    w.group_off = w.off_off + round(w.tiles * 8);
-    w.bytes = w.group_off + round(w.groups * 8) + 256;
+    w.off_off = round(w.tiles * 4 * kCountWords);
+    w.chunk_off = w.off_off + round((w.tiles + 1) * 8);
+    w.group_off = w.chunk_off + round((w.tiles + 1) * 16);
+    w.pair_off = w.group_off + round(w.groups * 8);
+    w.bytes = w.pair_off + 256 * 8 + 256;
     return w;
 }
 
 }  // namespace
 
-extern "C" int ecf8_histogram_device(const uint8_t* fp8, uint64_t n, uint64_t* freq, void* hip_stream)
+extern "C" uint64_t ecf8_encode_workspace_bytes(uint64_t n)
+{
+    return enc_workspace(n).bytes;
+}
+
+extern "C" int ecf8_histogram_device(const uint8_t* fp8, uint64_t n, uint64_t* freq, void* workspace,
+                                     uint64_t workspace_bytes, void* hip_stream)
 {
     if ((!fp8 && n) || !freq || ((uintptr_t)freq & 7)) return ECF8_ERR_ARG;
+    const EncWorkspace W = enc_workspace(n);
+    if (workspace && (workspace_bytes < W.bytes || ((uintptr_t)workspace & 255))) return ECF8_ERR_WORKSPACE;
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     hipLaunchKernelGGL(ecf8_zero_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<uint32_t*>(freq),
                        (uint64_t)2 * ECF8_NSYM);
     if (n) {
-        const uint64_t tiles = (n + kTile - 1) / kTile;
-        const uint64_t grid = tiles < 2048 ? tiles : 2048;
-        hipLaunchKernelGGL(ecf8_hist_kernel, dim3((uint32_t)grid), dim3(256), 0, st, fp8, n,
-                           reinterpret_cast<unsigned long long*>(freq));
+        const uint64_t steps = (W.tiles + kHistTiles - 1) / kHistTiles;
+        const uint64_t grid = steps < kHistGrid ? steps : kHistGrid;
+        hipLaunchKernelGGL(ecf8_hist_kernel, dim3((uint32_t)grid), dim3(256), 0, st, fp8, n, W.tiles,
+                           reinterpret_cast<unsigned long long*>(freq), reinterpret_cast<uint32_t*>(workspace));
     }
     return check(hipGetLastError());
-}
-
-extern "C" uint64_t ecf8_encode_workspace_bytes(uint64_t n)
-{
-    return enc_workspace(n).bytes;
 }
 
 extern "C" int ecf8_encode_device(const uint8_t* fp8, const ecf8_meta* meta, uint8_t* stream, uint8_t* nibbles,
@@ -383,7 +639,7 @@ extern "C" int ecf8_encode_device(const uint8_t* fp8, const ecf8_meta* meta, uin
         return ECF8_ERR_ARG;
     const EncWorkspace W = enc_workspace(n);
     if (workspace_bytes < W.bytes || ((uintptr_t)workspace & 255)) return ECF8_ERR_WORKSPACE;
-    if (W.tiles > 0xFFFFFFFFull || W.groups > 0xFFFFFFFFull) return ECF8_ERR_SIZE;
+    if (W.tiles > 0xFFFFFFFFull) return ECF8_ERR_SIZE;
 
     ecf8_codebook cb = meta->cb;
     uint32_t code[ECF8_NSYM];
@@ -394,39 +650,44 @@ extern "C" int ecf8_encode_device(const uint8_t* fp8, const ecf8_meta* meta, uin
         tab.code[s] = code[s];
         tab.len[s] = cb.len[s];
     }
+    CountLens L;
+    for (int d = 0; d < kCountWords; ++d)
+        for (int f = 0; f < 2; ++f) L.v[2 * d + f] = cb.len[count_symbol(d, f)];
     uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
-    uint32_t* tile_sum = reinterpret_cast<uint32_t*>(ws + W.sum_off);
+    const uint32_t* counts = reinterpret_cast<const uint32_t*>(ws);
     uint64_t* tile_off = reinterpret_cast<uint64_t*>(ws + W.off_off);
+    uint64_t* tile_chunk = reinterpret_cast<uint64_t*>(ws + W.chunk_off);
     uint64_t* group = reinterpret_cast<uint64_t*>(ws + W.group_off);
+    uint2* pairs = reinterpret_cast<uint2*>(ws + W.pair_off);
     EncArgs a;
     a.fp8 = fp8;
     a.n = n;
+    a.tiles = W.tiles;
     a.n_blocks = meta->n_blocks;
     a.chunk_bits = 8u * meta->chunk_bytes;
     a.tb = meta->threads_per_block;
     a.gap_count = meta->n_blocks * meta->threads_per_block;
-    a.stream_words = meta->stream_bytes / 4;
-    a.stream = stream;
+    a.gap_words = meta->gap_bytes / 4;
+    a.stream_words = meta->stream_bytes / 4;   // C and TB are multiples of 4 and 64: a whole number of words
+    a.stream = reinterpret_cast<uint32_t*>(stream);
     a.nibbles = nibbles;
     a.gaps = reinterpret_cast<uint32_t*>(gaps);
     a.blk_off = blk_off;
-    a.tile_sum = tile_sum;
     a.tile_off = tile_off;
+    a.tile_chunk = tile_chunk;
+    a.pairs = pairs;
+    a.m_chunk = ((1ull << 40) + a.chunk_bits - 1) / a.chunk_bits;
+    a.m_tb = ((1ull << 40) + a.tb - 1) / a.tb;
 
-    // zero the stream (shared boundary words and padding are OR-ed) and the
-    // gaps (OR-ed nibbles; zero gaps are not written).  stream_bytes and
-    // gap_bytes are multiples of 4 (C and TB are multiples of 4 and 64); the
-    // kernel writes the whole nibble plane itself.
-    hipLaunchKernelGGL(ecf8_zero_kernel, dim3(1024), dim3(256), 0, st, reinterpret_cast<uint32_t*>(stream),
-                       meta->stream_bytes / 4);
+    // gaps are OR-ed nibbles (zero gaps are not written): clear them; every
+    // other output word is written by the kernels
     hipLaunchKernelGGL(ecf8_zero_kernel, dim3(256), dim3(256), 0, st, reinterpret_cast<uint32_t*>(gaps),
                        meta->gap_bytes / 4);
-    hipLaunchKernelGGL(ecf8_tile_sum_kernel, dim3((uint32_t)W.tiles), dim3(kEncLanes), 0, st, a, tab, tile_sum);
-    hipLaunchKernelGGL(ecf8_group_sum_kernel, dim3((uint32_t)W.groups), dim3(kScanLanes), 0, st, tile_sum,
-                       W.tiles, group);
-    hipLaunchKernelGGL(ecf8_group_scan_kernel, dim3(1), dim3(kScanLanes), 0, st, group, W.groups);
-    hipLaunchKernelGGL(ecf8_tile_off_kernel, dim3((uint32_t)W.groups), dim3(kScanLanes), 0, st, tile_sum, W.tiles,
-                       group, tile_off);
-    hipLaunchKernelGGL(ecf8_encode_kernel, dim3((uint32_t)W.tiles), dim3(kEncLanes), 0, st, a, tab);
+    hipLaunchKernelGGL(ecf8_group_sum_kernel, dim3((uint32_t)W.groups), dim3(kScanLanes), 0, st, counts, L, W.tiles,
+                       group);
+    hipLaunchKernelGGL(ecf8_group_scan_kernel, dim3(1), dim3(kTopLanes), 0, st, group, W.groups, tab, pairs);
+    hipLaunchKernelGGL(ecf8_tile_off_kernel, dim3((uint32_t)W.groups), dim3(kScanLanes), 0, st, counts, L, W.tiles,
+                       group, tile_off, tile_chunk, a.chunk_bits, a.tb, a.stream, a.stream_words);
+    hipLaunchKernelGGL(ecf8_encode_kernel, dim3((uint32_t)W.tiles), dim3(kEncLanes), 0, st, a);
     return check(hipGetLastError());
 }

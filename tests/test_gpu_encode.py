@@ -66,12 +66,13 @@ def encode_on_device(x_np, lengths, C, TB, d, offset=0):
     up = torch.zeros(n + offset + 16, dtype=torch.uint8, device=d)
     up[offset:offset + n] = torch.from_numpy(np.ascontiguousarray(x_np)).to(d)
     x = up[offset:offset + n]
-    freq = B.histogram_device(x).cpu().numpy()
+    ws = B.encode_workspace(n, d)
+    freq = B.histogram_device(x, workspace=ws).cpu().numpy()
     if lengths is None:
         lengths = B.codebook_from_freq(freq.astype(np.uint64)) if n else [0] * 16
     m = B.meta_from_freq(freq.astype(np.uint64), n, lengths, C, TB)
     enc, wholes = canary_buffers(m, d)
-    B.encode_into(x, enc)
+    B.encode_into(x, enc, ws)
     torch.cuda.synchronize()
     return enc, wholes, freq
 
@@ -153,23 +154,46 @@ def test_encode_device_matches_host_encoder_and_round_trips():
     assert torch.equal(out, xd)
 
 
-def test_encode_device_undercounted_meta_stays_in_bounds():
-    """A meta whose T is smaller than the data's: nothing is written past meta's sizes."""
+@pytest.mark.parametrize("counts_from", ["data", "other"])
+def test_encode_device_mismatched_meta_or_counts_stays_in_bounds(counts_from):
+    """Metadata (and, for "other", per-tile counts) of other data with fewer bits: the stream comes
+    out wrong, but nothing is written past the buffers' sizes."""
     d = dev()
     x, _ = make_input("stable", 50_000, 9)
     L = list(oracle.huffman_lengths(oracle.histogram(x)))
     longest = int(max(L))
-    # data made only of the longest symbol: more bits than the meta of x allows for
     s_long = int(np.argmax(L))
-    y = ((x & 0x87) | (s_long << 3)).astype(np.uint8)
-    freq = oracle.histogram(x).astype(np.uint64)
-    m = B.meta_from_freq(freq, x.size, L, 16, 256)
+    y = ((x & 0x87) | (s_long << 3)).astype(np.uint8)     # every element the longest code
+    m = B.meta_from_freq(oracle.histogram(x).astype(np.uint64), x.size, L, 16, 256)
     assert int(m.total_bits) < longest * x.size
+    yd = torch.from_numpy(y).to(d)
+    ws_whole = torch.full((E.encode_workspace_bytes(x.size) + PAD,), CANARY, dtype=torch.uint8, device=d)
+    ws = ws_whole[:E.encode_workspace_bytes(x.size)]
+    B.histogram_device(yd if counts_from == "data" else torch.from_numpy(x).to(d), workspace=ws)
     enc, wholes = canary_buffers(m, d)
-    B.encode_into(torch.from_numpy(y).to(d), enc)
+    B.encode_into(yd, enc, ws)
     torch.cuda.synchronize()
-    for whole, size in zip(wholes, [m.stream_bytes, m.nibble_bytes, m.gap_bytes, 8 * (m.n_blocks + 1)]):
+    for whole, size in zip(wholes + [ws_whole], [m.stream_bytes, m.nibble_bytes, m.gap_bytes, 8 * (m.n_blocks + 1),
+                                                 ws.numel()]):
         assert (whole.cpu().numpy()[int(size):] == CANARY).all()
+
+
+def test_one_histogram_serves_several_encodes():
+    """The per-tile counts survive an encode: the same workspace encodes under other codes and params."""
+    d = dev()
+    x, _ = make_input("stable", 300_001, 4)
+    xd = torch.from_numpy(x).to(d)
+    ws = B.encode_workspace(x.size, d)
+    freq = B.histogram_device(xd, workspace=ws).cpu().numpy().astype(np.uint64)
+    for L, C, TB in [(None, 16, 256), ([4] * 16, 4, 64), (None, 12, 192)]:
+        L = B.codebook_from_freq(freq) if L is None else L
+        m = B.meta_from_freq(freq, x.size, L, C, TB)
+        enc = B.encode_into(xd, B.alloc_device(m, d), ws)
+        torch.cuda.synchronize()
+        ref = oracle.encode(x, lengths=L, chunk_bytes=C, tb=TB)
+        assert np.array_equal(enc.stream.cpu().numpy(), ref["stream"])
+        assert np.array_equal(enc.gaps.cpu().numpy(), ref["gaps"])
+        assert np.array_equal(enc.blk_off.cpu().numpy().view(np.uint64), ref["blk_off"])
 
 
 def test_encode_device_rejects_bad_arguments():
@@ -179,6 +203,10 @@ def test_encode_device_rejects_bad_arguments():
     ws = torch.empty(E.encode_workspace_bytes(x.numel()) + 512, dtype=torch.uint8, device=d)
     with pytest.raises(E.Ecf8Error, match="WORKSPACE"):
         B.encode_into(x, enc, workspace=ws[1:])
+    with pytest.raises(E.Ecf8Error, match="WORKSPACE"):
+        B.encode_into(x, enc, workspace=ws[:E.encode_workspace_bytes(x.numel()) - 1])
+    with pytest.raises(E.Ecf8Error, match="WORKSPACE"):
+        B.histogram_device(x, workspace=ws[:64])
     bad = B.Meta.from_buffer_copy(enc.meta)
     bad.n_blocks += 1
     enc2 = B.DeviceEncoded(bad, enc.stream, enc.nibbles, enc.gaps, enc.blk_off)

@@ -214,8 +214,8 @@ def test_encode_workspace_bytes():
     assert E.encode_workspace_bytes(0) >= 256
     sizes = [E.encode_workspace_bytes(n) for n in (1, 4096, 4097, 10 ** 9, 11_300_000_000)]
     assert sizes == sorted(sizes) and all(v % 256 == 0 for v in sizes)
-    # tile sums (4 B) and tile offsets (8 B) per 4096-element tile, at least
-    assert sizes[-2] >= 12 * (10 ** 9 // 4096)
+    # per-tile counts (32 B) and tile offsets (8 B) per 4096-element tile, at least
+    assert sizes[-2] >= 40 * (10 ** 9 // 4096)
 
 
 def test_encode_device_argument_checks_need_no_gpu():
@@ -240,8 +240,10 @@ def test_encode_device_argument_checks_need_no_gpu():
     bad = B.Meta.from_buffer_copy(m)
     bad.total_bits += 1 << 20
     assert call(meta=bad) == -3
-    assert L.ecf8_histogram_device(P(0), 5, P(0x100000), None) == -1
-    assert L.ecf8_histogram_device(P(0x100000), 5, P(0x100004), None) == -1
+    assert L.ecf8_histogram_device(P(0), 5, P(0x100000), P(0), 0, None) == -1
+    assert L.ecf8_histogram_device(P(0x100000), 5, P(0x100004), P(0), 0, None) == -1
+    assert L.ecf8_histogram_device(P(0x100000), 5, P(0x100000), P(0x600010), 1 << 20, None) == -7
+    assert L.ecf8_histogram_device(P(0x100000), 5, P(0x100000), P(0x600000), 255, None) == -7
 
 
 # ---------------------------------------------------------------- alpha statistics
