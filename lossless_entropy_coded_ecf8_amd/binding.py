@@ -64,6 +64,33 @@ class Plan(ctypes.Structure):
                 ("grid", ctypes.c_uint32)]
 
 
+MAXSYM_V = 256
+FORMAT_V = {"bf16": 1, "e5m2": 2}
+
+
+class MetaV(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_uint64), ("total_bits", ctypes.c_uint64), ("n_chunks", ctypes.c_uint64),
+                ("n_blocks", ctypes.c_uint64), ("stream_bytes", ctypes.c_uint64), ("raw_bytes", ctypes.c_uint64),
+                ("gap_bytes", ctypes.c_uint64), ("chunk_bytes", ctypes.c_uint32),
+                ("threads_per_block", ctypes.c_uint32), ("format", ctypes.c_uint32), ("max_len", ctypes.c_uint32),
+                ("len", ctypes.c_uint8 * MAXSYM_V)]
+
+
+class TensorDescV(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("raw", ctypes.c_void_p), ("gaps", ctypes.c_void_p),
+                ("blk_off", ctypes.c_void_p), ("meta", MetaV), ("out_offset", ctypes.c_uint64)]
+
+
+class PlanV(ctypes.Structure):
+    _fields_ = [("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
+                ("total_blocks", ctypes.c_uint64), ("count", ctypes.c_uint32), ("format", ctypes.c_uint32),
+                ("threads_per_block", ctypes.c_uint32), ("grid", ctypes.c_uint32)]
+
+
+EXPORTS_V = ["ecf8v_nsym", "ecf8v_histogram", "ecf8v_code_lengths", "ecf8v_canonical_codes", "ecf8v_encode_sizes",
+             "ecf8v_encode", "ecf8v_validate_meta", "ecf8v_workspace_bytes", "ecf8v_decode_prepare",
+             "ecf8v_decode_run", "ecf8v_decode_status"]
+
 EXPORTS = ["ecf8_histogram", "ecf8_codebook_from_freq", "ecf8_build_codebook", "ecf8_canonical_codes",
            "ecf8_encode_sizes", "ecf8_encode", "ecf8_validate_meta", "ecf8_workspace_bytes",
            "ecf8_decode_prepare", "ecf8_decode_run", "ecf8_build_tables", "ecf8_decode_blocks",
@@ -117,6 +144,22 @@ def lib() -> ctypes.CDLL:
         "ecf8_strerror": (ctypes.c_char_p, [i]),
         "ecf8_version": (i, []),
     }
+    sig.update({
+        "ecf8v_nsym": (i, [ctypes.c_uint32]),
+        "ecf8v_histogram": (i, [ctypes.c_uint32, vp, ctypes.c_uint64, u64p]),
+        "ecf8v_code_lengths": (i, [u64p, ctypes.c_uint32, ctypes.c_uint32, u8p]),
+        "ecf8v_canonical_codes": (i, [u8p, ctypes.c_uint32, u32p]),
+        "ecf8v_encode_sizes": (i, [ctypes.c_uint32, vp, ctypes.c_uint64, u8p, ctypes.POINTER(Params),
+                                   ctypes.POINTER(MetaV)]),
+        "ecf8v_encode": (i, [ctypes.c_uint32, vp, ctypes.c_uint64, u8p, ctypes.POINTER(Params), vp, ctypes.c_uint64,
+                             vp, ctypes.c_uint64, vp, ctypes.c_uint64, vp, ctypes.c_uint64, ctypes.POINTER(MetaV)]),
+        "ecf8v_validate_meta": (i, [ctypes.POINTER(MetaV)]),
+        "ecf8v_workspace_bytes": (ctypes.c_uint64, [i]),
+        "ecf8v_decode_prepare": (i, [ctypes.POINTER(TensorDescV), i, vp, vp, ctypes.c_uint64, vp,
+                                     ctypes.POINTER(PlanV)]),
+        "ecf8v_decode_run": (i, [ctypes.POINTER(PlanV), vp]),
+        "ecf8v_decode_status": (i, [vp, vp, u64p]),
+    })
     for name, (res, args) in sig.items():
         f = getattr(L, name)
         f.restype = res
@@ -469,3 +512,209 @@ def decode_batched(encs: Sequence[DeviceEncoded], out=None, offsets=None, worksp
     p = DecodePlan(encs, out, offsets, workspace, stream)
     p.run(stream)
     return p
+
+
+# ------------------------------------------------------------------ format variants (include/ecf8v.h)
+
+def _fmt_v(fmt) -> int:
+    return FORMAT_V[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def _elems_v(fmt, x) -> np.ndarray:
+    """Host elements of the format: uint16 BF16 bit patterns, or E5M2 bytes."""
+    if hasattr(x, "detach"):
+        import torch
+        t = x.detach().cpu().contiguous().view(-1)
+        if t.dtype == torch.bfloat16:
+            t = t.view(torch.int16)
+        elif t.dtype == torch.float8_e5m2:
+            t = t.view(torch.uint8)
+        x = t.numpy()
+    a = np.ascontiguousarray(np.asarray(x).reshape(-1))
+    if _fmt_v(fmt) == 1:
+        return np.ascontiguousarray(a.view(np.uint16) if a.dtype.itemsize == 2 else a.astype(np.uint16))
+    return np.ascontiguousarray(a.view(np.uint8) if a.dtype.itemsize == 1 else a.astype(np.uint8))
+
+
+def v_nsym(fmt) -> int:
+    r = int(lib().ecf8v_nsym(_fmt_v(fmt)))
+    _check(min(r, 0), "ecf8v_nsym")
+    return r
+
+
+def v_histogram(fmt, x) -> np.ndarray:
+    a = _elems_v(fmt, x)
+    f = np.zeros(v_nsym(fmt), dtype=np.uint64)
+    _check(lib().ecf8v_histogram(_fmt_v(fmt), _ptr(a), a.size, f.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))),
+           "ecf8v_histogram")
+    return f
+
+
+def v_code_lengths(freq, max_len: int = 16) -> np.ndarray:
+    """Optimal prefix-code lengths no longer than max_len (ecf8v_code_lengths, package-merge)."""
+    f = np.ascontiguousarray(np.asarray(freq, dtype=np.uint64))
+    L = np.zeros(f.size, dtype=np.uint8)
+    _check(lib().ecf8v_code_lengths(f.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), f.size, int(max_len),
+                                    L.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))), "ecf8v_code_lengths")
+    return L.astype(np.int64)
+
+
+def v_canonical_codes(lengths) -> np.ndarray:
+    L = np.ascontiguousarray(np.asarray(lengths, dtype=np.uint8))
+    c = np.zeros(L.size, dtype=np.uint32)
+    _check(lib().ecf8v_canonical_codes(L.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), L.size,
+                                       c.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))), "ecf8v_canonical_codes")
+    return c.astype(np.int64)
+
+
+def meta_v_dict(m: MetaV) -> dict:
+    d = {k: getattr(m, k) for k, _ in MetaV._fields_ if k != "len"}
+    d["lengths"] = list(m.len)
+    return d
+
+
+def compressed_bytes_v(m: MetaV) -> int:
+    """Bytes one decode reads: stream payload, raw plane, gaps, block offsets."""
+    raw = m.n if m.format == 1 else (m.n + 1) // 2
+    return int((m.total_bits + 7) // 8 + raw + (m.n_chunks + 1) // 2 + 8 * (m.n_blocks + 1))
+
+
+@dataclasses.dataclass
+class EncodedV:
+    """Host-side encoded tensor of a format variant."""
+    meta: MetaV
+    stream: np.ndarray
+    raw: np.ndarray
+    gaps: np.ndarray
+    blk_off: np.ndarray
+    shape: tuple = ()
+
+    @property
+    def n(self) -> int:
+        return int(self.meta.n)
+
+    @property
+    def lengths(self) -> np.ndarray:
+        return np.array(list(self.meta.len)[: v_nsym(self.meta.format)], dtype=np.int64)
+
+    def compressed_bytes(self) -> int:
+        return compressed_bytes_v(self.meta)
+
+    def to(self, device) -> "DeviceEncodedV":
+        import torch
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        return DeviceEncodedV(self.meta, t(self.stream), t(self.raw if self.raw.size else np.zeros(1, np.uint8)),
+                              t(self.gaps if self.gaps.size else np.zeros(1, np.uint8)),
+                              t(self.blk_off.view(np.int64)), self.shape)
+
+
+def v_encode(fmt, x, lengths=None, chunk_bytes: int = DEFAULT_CHUNK_BYTES,
+             threads_per_block: int = DEFAULT_THREADS_PER_BLOCK, max_len: int = 16) -> EncodedV:
+    """Histogram -> package-merge lengths (unless given) -> encode, all in libecf8."""
+    f = _fmt_v(fmt)
+    shape = tuple(x.shape) if hasattr(x, "shape") else ()
+    a = _elems_v(f, x)
+    ns = v_nsym(f)
+    if lengths is None:
+        lengths = v_code_lengths(v_histogram(f, a), max_len)
+    L = np.zeros(MAXSYM_V, dtype=np.uint8)
+    L[:ns] = np.asarray(lengths, dtype=np.uint8)[:ns]
+    Lp = L.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+    p = Params(chunk_bytes, threads_per_block)
+    m = MetaV()
+    _check(lib().ecf8v_encode_sizes(f, _ptr(a), a.size, Lp, ctypes.byref(p), ctypes.byref(m)), "ecf8v_encode_sizes")
+    stream = np.empty(m.stream_bytes, dtype=np.uint8)
+    raw = np.empty(m.raw_bytes, dtype=np.uint8)
+    gaps = np.empty(m.gap_bytes, dtype=np.uint8)
+    blk = np.empty(m.n_blocks + 1, dtype=np.uint64)
+    m2 = MetaV()
+    _check(lib().ecf8v_encode(f, _ptr(a), a.size, Lp, ctypes.byref(p), _ptr(stream), stream.size, _ptr(raw),
+                              raw.size, _ptr(gaps), gaps.size, _ptr(blk), blk.size, ctypes.byref(m2)), "ecf8v_encode")
+    return EncodedV(m2, stream, raw, gaps, blk, shape)
+
+
+def v_validate_meta(m: MetaV) -> int:
+    return int(lib().ecf8v_validate_meta(ctypes.byref(m)))
+
+
+@dataclasses.dataclass
+class DeviceEncodedV:
+    """Device-resident encoded tensor of a format variant."""
+    meta: MetaV
+    stream: "object"
+    raw: "object"
+    gaps: "object"
+    blk_off: "object"
+    shape: tuple = ()
+
+    @property
+    def n(self) -> int:
+        return int(self.meta.n)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.meta.format == 1 else 1
+
+    def compressed_bytes(self) -> int:
+        return compressed_bytes_v(self.meta)
+
+
+class DecodePlanV:
+    """A prepared batched decode of variant tensors (ecf8v_decode_prepare / ecf8v_decode_run).
+
+    All tensors decode in one persistent dispatch into `out` (uint8 bytes);
+    tensor i lands at byte offset offsets[i] (n_i elements of the format).
+    """
+
+    def __init__(self, encs, out=None, offsets=None, workspace=None, stream=None, workgroups=None):
+        import torch
+        self.encs = list(encs)
+        dev = self.encs[0].stream.device if self.encs else torch.device("cuda")
+        if offsets is None:
+            offsets, off = [], 0
+            for e in self.encs:
+                offsets.append(off)
+                off += (e.n * e.elem_bytes + 255) // 256 * 256
+            total = off
+        else:
+            total = max([o + e.n * e.elem_bytes for o, e in zip(offsets, self.encs)] + [0])
+        self.offsets = list(offsets)
+        self.out = out if out is not None else torch.empty(max(total, 1), dtype=torch.uint8, device=dev)
+        need = int(lib().ecf8v_workspace_bytes(len(self.encs)))
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+        arr = (TensorDescV * max(1, len(self.encs)))()
+        for i, (e, o) in enumerate(zip(self.encs, self.offsets)):
+            arr[i].stream = e.stream.data_ptr()
+            arr[i].raw = e.raw.data_ptr()
+            arr[i].gaps = e.gaps.data_ptr()
+            arr[i].blk_off = e.blk_off.data_ptr()
+            arr[i].meta = e.meta
+            arr[i].out_offset = o
+        self._descs = arr
+        self.plan = PlanV()
+        _check(lib().ecf8v_decode_prepare(arr, len(self.encs), ctypes.c_void_p(self.out.data_ptr()),
+                                          ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
+                                          _stream_handle(stream), ctypes.byref(self.plan)), "ecf8v_decode_prepare")
+        if workgroups is not None:
+            self.plan.grid = max(1, min(int(self.plan.grid), int(workgroups)))
+
+    def run(self, stream=None):
+        _check(lib().ecf8v_decode_run(ctypes.byref(self.plan), _stream_handle(stream)), "ecf8v_decode_run")
+        return self.out
+
+    def status(self, stream=None) -> int:
+        bad = ctypes.c_uint64(0)
+        rc = lib().ecf8v_decode_status(ctypes.c_void_p(self.workspace.data_ptr()), _stream_handle(stream),
+                                       ctypes.byref(bad))
+        if rc not in (0, -5):
+            _check(rc, "ecf8v_decode_status")
+        return int(bad.value)
+
+    def view(self, i: int):
+        """Tensor i's decoded elements (uint16 bit patterns for BF16, bytes for E5M2)."""
+        import torch
+        e = self.encs[i]
+        b = self.out[self.offsets[i]: self.offsets[i] + e.n * e.elem_bytes]
+        return b.view(torch.int16) if e.elem_bytes == 2 else b

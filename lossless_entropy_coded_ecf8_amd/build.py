@@ -23,7 +23,8 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
 
 
 def sources():
-    return [os.path.join(CSRC, f) for f in ("ecf8_host.cpp", "ecf8_decode.hip", "ecf8_encode.hip")]
+    return [os.path.join(CSRC, f) for f in ("ecf8_host.cpp", "ecf8_decode.hip", "ecf8_encode.hip", "ecf8v_host.cpp",
+                                                "ecf8v_decode.hip")]
 
 
 def build(verbose: bool = False, extra=None) -> str:

@@ -10,6 +10,7 @@
 // chunk of the bitstream plus a stored gap (offset of its first codeword), so
 // the encoder records those gaps and the per-block output offsets.
 #include "ecf8.h"
+#include "host_threads.h"
 
 #include <algorithm>
 #include <cmath>
@@ -22,32 +23,8 @@ namespace {
 
 constexpr int kNsym = ECF8_NSYM;
 
-int worker_count(uint64_t items, uint64_t min_per_worker)
-{
-    unsigned hw = std::thread::hardware_concurrency();
-    if (hw == 0) hw = 1;
-    if (const char* env = std::getenv("ECF8_THREADS")) {
-        int v = std::atoi(env);
-        if (v > 0) hw = (unsigned)v;
-    }
-    hw = std::min(hw, 64u);
-    uint64_t by_work = std::max<uint64_t>(1, items / std::max<uint64_t>(1, min_per_worker));
-    return (int)std::min<uint64_t>(hw, by_work);
-}
-
-template <class F>
-void run_parallel(int workers, F&& fn)
-{
-    if (workers <= 1) {
-        fn(0);
-        return;
-    }
-    std::vector<std::thread> pool;
-    pool.reserve(workers - 1);
-    for (int w = 1; w < workers; ++w) pool.emplace_back([&, w] { fn(w); });
-    fn(0);
-    for (auto& t : pool) t.join();
-}
+using ecf8_host::run_parallel;
+using ecf8_host::worker_count;
 
 inline int expo(uint8_t b) { return (b >> 3) & 15; }
 

@@ -162,6 +162,46 @@ def make_tensor(workload: str, name: str, shape, kind: str, params: dict, device
     raise KeyError(kind)
 
 
+def float_weights(workload: str, name: str, shape, kind: str, params: dict, device="cpu",
+                  base_seed: int = 0) -> torch.Tensor:
+    """The same tensor as make_tensor before any scaling or rounding (float64, `shape`)."""
+    seed = seed_of(workload, name, base_seed)
+    g = _gen(seed, device)
+    n = int(np.prod(shape))
+    if kind == "gauss":
+        x = torch.randn(n, generator=g, device=device, dtype=torch.float64) * params["std"]
+    elif kind == "stable":
+        x = alpha_stable(params["alpha"], n, g, device, GAMMA)
+    elif kind == "dit":
+        x = alpha_stable(1.5, n, g, device, GAMMA)
+        mask = torch.rand(n, generator=g, device=device, dtype=torch.float64) < 0.02
+        out = torch.randn(n, generator=g, device=device, dtype=torch.float64) * 0.2
+        x = torch.where(mask, out, x)
+    else:
+        raise KeyError(kind)
+    return x.reshape(shape)
+
+
+E5M2_MAX = 57344.0
+
+
+def workload_tensors_as(workload: str, fmt: str, device="cpu", experts=None, base_seed: int = 0):
+    """Yield (name, tensor) for every tensor of a workload in another float format:
+    "bf16" -> torch.bfloat16 (round to nearest even, no scaling), "e5m2" -> uint8 bytes of
+    torch.float8_e5m2 after per-tensor max-abs scaling to 57344."""
+    for name, shape, kind, params in tensor_specs(workload, experts):
+        x = float_weights(workload, name, shape, kind, params, device, base_seed)
+        if fmt == "bf16":
+            yield name, x.to(torch.bfloat16)
+        elif fmt == "e5m2":
+            amax = x.abs().max()
+            s = torch.where(amax > 0, E5M2_MAX / amax, torch.ones_like(amax))
+            yield name, (x * s).clamp(-E5M2_MAX, E5M2_MAX).to(torch.float8_e5m2).view(torch.uint8)
+        else:
+            raise KeyError(fmt)
+        del x
+
+
 def workload_tensors(workload: str, device="cpu", experts=None, base_seed: int = 0):
     """Yield (name, uint8 tensor) for every tensor of a workload, one at a time."""
     for name, shape, kind, params in tensor_specs(workload, experts):

@@ -100,3 +100,20 @@ def test_pipeline_argument_checks():
         DecodePipeline([object()], slots=2, ahead=2)
     with _pt.raises(ValueError):
         DecodePipeline([object()], slots=0, ahead=0)
+
+
+def test_float_weights_are_the_e4m3_tensors_before_rounding():
+    for wl in ("gauss1m", "llama8b"):
+        name, shape, kind, params = synth.tensor_specs(wl)[0]
+        if wl == "llama8b":
+            shape = (64, 128)                     # a small tensor of the same kind and seed
+        x = synth.float_weights(wl, name, shape, kind, params)
+        ref = synth.make_tensor(wl, name, shape, kind, params)
+        assert torch.equal(synth.to_e4m3_bytes(synth.maxabs_scale(x.reshape(-1))).reshape(shape), ref)
+
+
+def test_workload_as_bf16_and_e5m2():
+    (n1, b), = list(synth.workload_tensors_as("gauss1m", "bf16"))
+    (n2, e), = list(synth.workload_tensors_as("gauss1m", "e5m2"))
+    assert b.dtype == torch.bfloat16 and e.dtype == torch.uint8 and b.shape == e.shape == (1024, 1024)
+    assert float(e.view(torch.float8_e5m2).float().abs().max()) == 57344.0
