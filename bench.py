@@ -291,6 +291,61 @@ def encode_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def variant_bench(args):
+    """Batched GPU decode of a format variant (BF16 in the DFloat11 layout, or FP8 E5M2) on the workload:
+    host encode, upload, one decode plan; output checked bit-exact against the input before timing."""
+    import torch
+    import synth
+    from lossless_entropy_coded_ecf8_amd import binding as B
+
+    d = torch.device("cuda:0")
+    fmt = args.format
+    names, xs, hs = [], [], []
+    for name, x in synth.workload_tensors_as(args.workload, fmt, device=d):
+        names.append(name)
+        xs.append(x.reshape(-1).view(torch.int16) if fmt == "bf16" else x.reshape(-1))
+        hs.append(B.v_encode(fmt, x.cpu()))
+        log("encoded %-12s n=%d  %.3f code bits/element, max_len %d" % (name, hs[-1].n,
+                                                                        hs[-1].meta.total_bits / hs[-1].n,
+                                                                        hs[-1].meta.max_len))
+    plan = B.DecodePlanV([h.to(d) for h in hs])
+    plan.run()
+    torch.cuda.synchronize()
+    if plan.status() or not all(torch.equal(plan.view(i), x) for i, x in enumerate(xs)):
+        log("MISMATCH in the variant decode")
+        sys.exit(1)
+    log("bit-exact check passed on %d tensors" % len(xs))
+    for _ in range(args.warmup):
+        plan.run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        plan.run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    eb = 2 if fmt == "bf16" else 1
+    n = sum(h.n for h in hs)
+    read = sum(h.compressed_bytes() for h in hs)
+    written = n * eb
+    res = {"metric": "ECF8 variant decoded GB/s on 1 MI355X (%s, %s)" %
+                     (fmt, "DFloat11 layout" if fmt == "bf16" else "5-bit exponent coded"),
+           "value": round(written / (ms * 1e-3) / 1e9, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "dtype": "u8",
+           "data": "synthetic",
+           "config": {"workload": WORKLOAD_TEXT[args.workload] + ", cast to " + fmt, "format": fmt,
+                      "tensors": len(hs), "elements": n, "compressed_bytes": read,
+                      "compressed_ratio": round(read / written, 4), "chunk_bytes": 16, "lanes_per_block": 256,
+                      "grid": int(plan.plan.grid)},
+           "roofline": {"bound": "hbm", "achieved": round((read + written) / (ms * 1e-3) / 1e9, 2),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round((read + written) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "traffic": None, "kernel": "ecf8v_decode_kernel (+ table kernel, one run)",
+                        "algorithmic_bytes": read + written}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -299,9 +354,10 @@ def main():
     ap.add_argument("--workload", default="llama70b", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="decode", choices=["decode", "pipeline", "alpha", "encode"],
+    ap.add_argument("--mode", default="decode", choices=["decode", "pipeline", "alpha", "encode", "variant"],
                     help="decode: the batched decode step (default); pipeline: decode-on-use of the "
                          "block's layers beside FP8 GEMMs, against resident FP8 weights")
+    ap.add_argument("--format", default="bf16", choices=["bf16", "e5m2"], help="variant mode: the float format")
     ap.add_argument("--tokens", default="128,1024,4096", help="pipeline mode: GEMM rows (comma list)")
     ap.add_argument("--repeats", type=int, default=2, help="pipeline mode: copies of the block's 7 layers")
     ap.add_argument("--pipe-configs", default="serial,ahead2,ahead2_wg256",
@@ -319,6 +375,9 @@ def main():
         return
     if args.mode == "encode":
         encode_bench(args)
+        return
+    if args.mode == "variant":
+        variant_bench(args)
         return
 
     import torch

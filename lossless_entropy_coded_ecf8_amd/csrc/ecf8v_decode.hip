@@ -27,9 +27,10 @@
 // 4 bytes of look-ahead, walks it from its gap counting codewords that start
 // inside the chunk, the workgroup scans the counts (checked against the
 // block offsets), and in rounds of at most 16384 symbols the lanes walk
-// again writing each symbol byte into LDS at its scanned position; the
-// workgroup then assembles the output elements from the symbol and the raw
-// plane and stores them.
+// again writing each symbol byte into LDS at its scanned position (the stage
+// aligned to 16 output elements); the workgroup then assembles whole groups
+// of 16 elements from 16 symbol bytes and the raw plane with 16-byte loads
+// and stores (byte permutes and masks), the ragged ends one element a lane.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -104,11 +105,11 @@ __global__ __launch_bounds__(256) void ecf8v_table_kernel(const DescV* __restric
     const DescV& d = descs[blockIdx.x];
     uint32_t* tab = tables + (uint64_t)blockIdx.x * kTabEntries;
     L[tid] = d.len[tid];
+    if (tid < 18) cnt[tid] = 0;
+    __syncthreads();
+    if (L[tid]) atomicAdd(&cnt[L[tid]], 1u);
     __syncthreads();
     if (tid == 0) {
-        for (int l = 0; l < 18; ++l) cnt[l] = 0;
-        for (int s = 0; s < ECF8V_MAX_SYM; ++s) cnt[L[s]]++;
-        cnt[0] = 0;
         uint32_t c = 0, o = 0;
         for (int l = 1; l <= 16; ++l) {
             c = (c + cnt[l - 1]) << 1;
@@ -136,16 +137,35 @@ __global__ __launch_bounds__(256) void ecf8v_table_kernel(const DescV* __restric
     __syncthreads();
     if (ls > kPrimBits) atomicMax(&dmax32[code >> (ls - kPrimBits)], (uint32_t)ls);
     __syncthreads();
-    if (tid == 0) {
-        uint32_t next = 1 << kPrimBits;
-        for (int i = 0; i < (1 << kPrimBits); ++i) {
-            const uint32_t dm = dmax32[i];
-            dmax[i] = (uint8_t)(dm ? dm - kPrimBits : 0);
-            sub_base[i] = (uint16_t)(next < 65535 ? next : 65535);
-            if (dm) next += 1u << (dm - kPrimBits);
+    {
+        // subtable bases: an exclusive scan of the subtable sizes, 4 prefixes a lane
+        uint32_t sz[4], mine = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t dm = dmax32[4 * tid + q];
+            dmax[4 * tid + q] = (uint8_t)(dm ? dm - kPrimBits : 0);
+            sz[q] = dm ? 1u << (dm - kPrimBits) : 0u;
+            mine += sz[q];
         }
-        used = next;
-        if (next > (uint32_t)kTabEntries) atomicAdd(status + 1, 1ull);
+        __shared__ uint32_t part[256];
+        part[tid] = mine;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {         // Hillis-Steele inclusive scan
+            const uint32_t v = tid >= off ? part[tid - off] : 0u;
+            __syncthreads();
+            part[tid] += v;
+            __syncthreads();
+        }
+        uint32_t next = (1u << kPrimBits) + part[tid] - mine;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            sub_base[4 * tid + q] = (uint16_t)(next < 65535 ? next : 65535);
+            next += sz[q];
+        }
+        if (tid == 255) {
+            used = next;
+            if (next > (uint32_t)kTabEntries) atomicAdd(status + 1, 1ull);
+        }
     }
     __syncthreads();
     const bool fits = used <= (uint32_t)kTabEntries;
@@ -219,26 +239,6 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
     return before + x - v;
 }
 
-// A lane's chunk: 20 big-endian bytes as five words, shifted out as the walk
-// advances (w[0] holds the word at the current position).
-struct Chunk {
-    uint32_t w[5];
-};
-
-__device__ __forceinline__ uint32_t window(const Chunk& c, uint32_t o)
-{
-    return (uint32_t)(((((uint64_t)c.w[0] << 32) | c.w[1]) << o) >> 32);
-}
-
-__device__ __forceinline__ void advance(Chunk& c, bool adv)
-{
-    c.w[0] = adv ? c.w[1] : c.w[0];
-    c.w[1] = adv ? c.w[2] : c.w[1];
-    c.w[2] = adv ? c.w[3] : c.w[2];
-    c.w[3] = adv ? c.w[4] : c.w[3];
-    c.w[4] = adv ? 0u : c.w[4];
-}
-
 // Table lookup at the window; returns the symbols entry (0 = no codeword).
 __device__ __forceinline__ uint32_t lookup(const uint32_t* tab, uint32_t win)
 {
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256) void ecf8v_decode_kernel(const DescV* __restri
                                                            unsigned long long* __restrict__ status)
 {
     __shared__ uint32_t tab[kTabEntries];
-    __shared__ uint8_t stage[kStageSyms];
+    __shared__ __align__(16) uint8_t stage[kStageSyms + 32];   // element j at j - (first element & ~15)
     __shared__ uint32_t wsum[kTB / 64];
     const int tid = threadIdx.x;
     int t = -1;
@@ -279,12 +279,8 @@ __global__ __launch_bounds__(256) void ecf8v_decode_kernel(const DescV* __restri
         const uint64_t blk0 = d.blk_off[lb], blk1 = d.blk_off[lb + 1];
         const uint64_t c = lb * kTB + tid;                // chunk of this lane
         const uint4 v = *reinterpret_cast<const uint4*>(d.stream + c * kChunk);
-        Chunk ch0;
-        ch0.w[0] = bswap(v.x);
-        ch0.w[1] = bswap(v.y);
-        ch0.w[2] = bswap(v.z);
-        ch0.w[3] = bswap(v.w);
-        ch0.w[4] = bswap(ld_u32(d.stream + (c + 1) * kChunk));
+        const uint32_t W[5] = {bswap(v.x), bswap(v.y), bswap(v.z), bswap(v.w),
+                               bswap(ld_u32(d.stream + (c + 1) * kChunk))};
         const uint32_t gap = (d.gaps[c >> 1] >> (4 * (uint32_t)(c & 1))) & 15u;
         // codewords start before the chunk end and before T
         const uint64_t cstart = c * (uint64_t)kChunkBits;
@@ -292,21 +288,22 @@ __global__ __launch_bounds__(256) void ecf8v_decode_kernel(const DescV* __restri
                              : (d.total_bits - cstart < (uint64_t)kChunkBits ? (uint32_t)(d.total_bits - cstart)
                                                                             : (uint32_t)kChunkBits);
 
-        // count the codewords that start inside the chunk
-        Chunk ch = ch0;
+        // count the codewords that start inside the chunk.  Four phases, one
+        // per 32-bit word: a codeword starting in word q lies inside words q
+        // and q + 1 (at most 16 bits), so each phase windows a fixed pair.
         uint32_t pos = gap, n_here = 0;
         bool bad = false;
-        while (pos < end) {
-            const uint32_t e = lookup(tab, window(ch, pos & 31));
-            if (!e) {
-                bad = true;
-                break;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t lim = end < 32u * (q + 1) ? end : 32u * (q + 1);
+            const uint64_t pair = ((uint64_t)W[q] << 32) | W[q + 1];
+            while (pos < lim) {
+                const uint32_t e = lookup(tab, (uint32_t)((pair << (pos - 32u * q)) >> 32));
+                const uint32_t nb = e & 31u, l1 = (e >> 7) & 31u;
+                bad |= e == 0u;
+                n_here += 1u + ((((e >> 5) & 3u) == 2u && pos + l1 < end) ? 1u : 0u);
+                pos += e ? nb : 128u;
             }
-            const uint32_t nb = e & 31u, l1 = (e >> 7) & 31u, ns = (e >> 5) & 3u;
-            n_here += 1u + ((ns == 2u && pos + l1 < end) ? 1u : 0u);
-            const uint32_t np = pos + nb;
-            advance(ch, (np >> 5) != (pos >> 5));
-            pos = np;
         }
         uint32_t total;
         const uint32_t off = block_excl_scan<kTB>(n_here, wsum, &total);
@@ -318,40 +315,78 @@ __global__ __launch_bounds__(256) void ecf8v_decode_kernel(const DescV* __restri
         }
         for (uint32_t base = 0; base < total; base += kStageSyms) {
             const uint32_t lim = total - base < (uint32_t)kStageSyms ? total - base : (uint32_t)kStageSyms;
+            const uint64_t j_start = blk0 + base, j_end = j_start + lim;
+            const uint32_t shift = (uint32_t)(j_start & 15);          // stage aligned to 16 elements
             // emit this round's symbols into the stage
             if (off < base + lim && off + n_here > base) {
-                ch = ch0;
-                pos = gap;
-                uint32_t k = off;                         // output index of the next symbol
-                while (pos < end && k < base + lim) {
-                    const uint32_t e = lookup(tab, window(ch, pos & 31));
-                    const uint32_t nb = e & 31u, l1 = (e >> 7) & 31u, ns = (e >> 5) & 3u;
-                    if (k >= base) stage[k - base] = (uint8_t)(e >> 12);
-                    ++k;
-                    if (ns == 2u && pos + l1 < end) {
-                        if (k >= base && k < base + lim) stage[k - base] = (uint8_t)(e >> 20);
+                uint32_t p = gap, k = off;                // k: output index of the next symbol
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t plim = end < 32u * (q + 1) ? end : 32u * (q + 1);
+                    const uint64_t pair = ((uint64_t)W[q] << 32) | W[q + 1];
+                    while (p < plim && k < base + lim) {
+                        const uint32_t e = lookup(tab, (uint32_t)((pair << (p - 32u * q)) >> 32));
+                        const uint32_t nb = e & 31u, l1 = (e >> 7) & 31u;
+                        if (k >= base) stage[k - base + shift] = (uint8_t)(e >> 12);
                         ++k;
+                        if (((e >> 5) & 3u) == 2u && p + l1 < end) {
+                            if (k >= base && k < base + lim) stage[k - base + shift] = (uint8_t)(e >> 20);
+                            ++k;
+                        }
+                        p += nb;
                     }
-                    const uint32_t np = pos + nb;
-                    advance(ch, (np >> 5) != (pos >> 5));
-                    pos = np;
                 }
             }
             __syncthreads();
-            // write back: element j = blk0 + base + i
-            const uint64_t j0 = blk0 + base;
-            if (kFmt == ECF8V_BF16) {
-                uint16_t* out = reinterpret_cast<uint16_t*>(d.out);
-                for (uint32_t i = tid; i < lim; i += kTB) {
-                    const uint64_t j = j0 + i;
-                    const uint32_t r = d.raw[j], s = stage[i];
-                    out[j] = (uint16_t)(((r >> 7) << 15) | (s << 7) | (r & 127u));
+            // write back: whole aligned groups of 16 elements with 16-byte
+            // accesses, the ragged head and tail one element per lane
+            const uint64_t g_lo = (j_start + 15) >> 4, g_hi = j_end >> 4;
+            const uint64_t head_end = g_lo <= g_hi ? 16 * g_lo : j_end;
+            const uint64_t tail_start = g_lo <= g_hi ? 16 * g_hi : j_end;
+            const uint32_t n_head = (uint32_t)(head_end - j_start), n_tail = (uint32_t)(j_end - tail_start);
+            const uint64_t sbase = j_start & ~15ull;      // element at stage[0]
+            if ((uint32_t)tid < n_head + n_tail) {
+                const uint64_t j = (uint32_t)tid < n_head ? j_start + tid : tail_start + (tid - n_head);
+                const uint32_t sy = stage[j - sbase];
+                if (kFmt == ECF8V_BF16) {
+                    const uint32_t r = d.raw[j];
+                    reinterpret_cast<uint16_t*>(d.out)[j] = (uint16_t)(((r >> 7) << 15) | (sy << 7) | (r & 127u));
+                } else {
+                    const uint32_t r = (d.raw[j >> 1] >> (4 * (uint32_t)(j & 1))) & 15u;
+                    d.out[j] = (uint8_t)(((r >> 2) << 7) | (sy << 2) | (r & 3u));
                 }
-            } else {
-                for (uint32_t i = tid; i < lim; i += kTB) {
-                    const uint64_t j = j0 + i;
-                    const uint32_t r = (d.raw[j >> 1] >> (4 * (uint32_t)(j & 1))) & 15u, s = stage[i];
-                    d.out[j] = (uint8_t)(((r >> 2) << 7) | (s << 2) | (r & 3u));
+            }
+            for (uint64_t g = g_lo + tid; g < g_hi; g += kTB) {
+                const uint4 sv = *reinterpret_cast<const uint4*>(stage + (16 * g - sbase));
+                const uint32_t S[4] = {sv.x, sv.y, sv.z, sv.w};
+                if (kFmt == ECF8V_BF16) {
+                    const uint4 rv = *reinterpret_cast<const uint4*>(d.raw + 16 * g);
+                    const uint32_t R[4] = {rv.x, rv.y, rv.z, rv.w};
+                    uint32_t o[8];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {     // elements 4q + 2h, 4q + 2h + 1 into one word
+                            const uint32_t sel = h ? 0x0c030c02u : 0x0c010c00u;
+                            const uint32_t rr = __builtin_amdgcn_perm(0u, R[q], sel);
+                            const uint32_t ss = __builtin_amdgcn_perm(0u, S[q], sel);
+                            o[2 * q + h] = ((rr & 0x00800080u) << 8) | (ss << 7) | (rr & 0x007F007Fu);
+                        }
+                    }
+                    uint4* dst = reinterpret_cast<uint4*>(d.out + 32 * g);
+                    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+                    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+                } else {
+                    const uint2 rv = *reinterpret_cast<const uint2*>(d.raw + 8 * g);
+                    uint32_t o[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        uint32_t t = ((q < 2 ? rv.x : rv.y) >> (16 * (q & 1))) & 0xFFFFu;   // 4 nibbles
+                        t = (t | (t << 8)) & 0x00FF00FFu;
+                        t = (t | (t << 4)) & 0x0F0F0F0Fu;                               // one per byte
+                        o[q] = ((t & 0x04040404u) << 5) | ((S[q] & 0x1F1F1F1Fu) << 2) | (t & 0x03030303u);
+                    }
+                    *reinterpret_cast<uint4*>(d.out + 16 * g) = make_uint4(o[0], o[1], o[2], o[3]);
                 }
             }
             __syncthreads();
@@ -429,7 +464,9 @@ extern "C" int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, u
         if (t.meta.format != fmt || t.meta.threads_per_block != tb) return ECF8_ERR_ARG;
         if (t.meta.chunk_bytes != (uint32_t)kChunk || !pick_kernel(fmt, tb)) return ECF8_ERR_UNSUPPORTED;
         if (t.meta.n && (!t.stream || !t.raw || !t.gaps || !t.blk_off)) return ECF8_ERR_ARG;
-        if (!aligned(t.stream, 16) || !aligned(t.blk_off, 8) || (t.out_offset & 15)) return ECF8_ERR_ARG;
+        if (!aligned(t.stream, 16) || !aligned(t.blk_off, 8) || (t.out_offset & 15) ||
+            !aligned(t.raw, fmt == ECF8V_BF16 ? 16 : 8))
+            return ECF8_ERR_ARG;
         DescV& d = dv[i];
         std::memset(&d, 0, sizeof(d));
         d.stream = t.stream;
