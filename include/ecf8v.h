@@ -124,6 +124,8 @@ typedef struct {
     uint32_t format;
     uint32_t threads_per_block;
     uint32_t grid;            /* persistent workgroups; may be lowered (>= 1) */
+    uint32_t table_entries;   /* LDS decode-table entries: the plan's largest table */
+    uint32_t reserved;
 } ecf8v_plan;
 
 /* Device workspace bytes for a batched decode of `count` tensors (256-byte
@@ -133,7 +135,9 @@ uint64_t ecf8v_workspace_bytes(int count);
 /* Validate `count` descriptors of one format and upload them to the
  * workspace (synchronous copy).  Decode kernels exist for chunk_bytes = 16
  * and threads_per_block in {64, 128, 256}; other params give
- * ECF8_ERR_UNSUPPORTED.  Output of tensor i: out_base + out_offset_i, n_i
+ * ECF8_ERR_UNSUPPORTED, and so does a code whose decode table (1024 primary
+ * entries plus subtables for codewords longer than 10 bits) would pass 4096
+ * entries (complete codes never do).  Output of tensor i: out_base + out_offset_i, n_i
  * elements of the format.  Errors: ECF8_ERR_ARG, ECF8_ERR_META,
  * ECF8_ERR_UNSUPPORTED, ECF8_ERR_WORKSPACE, ECF8_ERR_HIP. */
 int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, uint8_t* out_base, void* workspace,

@@ -84,7 +84,8 @@ class TensorDescV(ctypes.Structure):
 class PlanV(ctypes.Structure):
     _fields_ = [("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
                 ("total_blocks", ctypes.c_uint64), ("count", ctypes.c_uint32), ("format", ctypes.c_uint32),
-                ("threads_per_block", ctypes.c_uint32), ("grid", ctypes.c_uint32)]
+                ("threads_per_block", ctypes.c_uint32), ("grid", ctypes.c_uint32),
+                ("table_entries", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
 
 EXPORTS_V = ["ecf8v_nsym", "ecf8v_histogram", "ecf8v_code_lengths", "ecf8v_canonical_codes", "ecf8v_encode_sizes",

@@ -35,7 +35,9 @@
 
 #include <cstdint>
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <tuple>
 #include <vector>
 
 #include "ecf8v.h"
@@ -240,12 +242,13 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
 }
 
 // Table lookup at the window; returns the symbols entry (0 = no codeword).
-__device__ __forceinline__ uint32_t lookup(const uint32_t* tab, uint32_t win)
+__device__ __forceinline__ uint32_t lookup(const uint32_t* tab, uint32_t tab_n, uint32_t win)
 {
     uint32_t e = tab[win >> (32 - kPrimBits)];
     if (e & 0x80000000u) {
         const uint32_t k = (e >> 16) & 15u;
-        e = tab[((e & 0xFFFFu) + ((win << kPrimBits) >> (32 - k))) & (kTabEntries - 1)];
+        const uint32_t i = (e & 0xFFFFu) + ((win << kPrimBits) >> (32 - k));
+        e = tab[i < tab_n ? i : 0u];
         if (e & 0x80000000u) e = 0;
     }
     return (e & 31u) ? e : 0u;
@@ -254,10 +257,13 @@ __device__ __forceinline__ uint32_t lookup(const uint32_t* tab, uint32_t win)
 template <int kFmt, int kTB>
 __global__ __launch_bounds__(256) void ecf8v_decode_kernel(const DescV* __restrict__ descs, int count,
                                                            const uint32_t* __restrict__ tables, uint64_t total_blocks,
-                                                           unsigned long long* __restrict__ status)
+                                                           unsigned long long* __restrict__ status, uint32_t tab_n)
 {
-    __shared__ uint32_t tab[kTabEntries];
-    __shared__ __align__(16) uint8_t stage[kStageSyms + 32];   // element j at j - (first element & ~15)
+    // dynamic LDS: the stage (element j at j - (first element & ~15)), then
+    // tab_n table entries (the largest table of the plan, a multiple of 4)
+    extern __shared__ __align__(16) uint8_t dyn[];
+    uint8_t* const stage = dyn;
+    uint32_t* const tab = reinterpret_cast<uint32_t*>(dyn + kStageSyms + 32);
     __shared__ uint32_t wsum[kTB / 64];
     const int tid = threadIdx.x;
     int t = -1;
@@ -271,7 +277,7 @@ __global__ __launch_bounds__(256) void ecf8v_decode_kernel(const DescV* __restri
             } while (gb >= t_end && t + 1 < count);
             __syncthreads();                              // the previous table is no longer read
             const uint4* src = reinterpret_cast<const uint4*>(tables + (uint64_t)t * kTabEntries);
-            for (int i = tid; i < kTabEntries / 4; i += kTB) reinterpret_cast<uint4*>(tab)[i] = src[i];
+            for (uint32_t i = tid; i < tab_n / 4; i += kTB) reinterpret_cast<uint4*>(tab)[i] = src[i];
             __syncthreads();
         }
         const DescV& d = descs[t];
@@ -298,7 +304,7 @@ __global__ __launch_bounds__(256) void ecf8v_decode_kernel(const DescV* __restri
             const uint32_t lim = end < 32u * (q + 1) ? end : 32u * (q + 1);
             const uint64_t pair = ((uint64_t)W[q] << 32) | W[q + 1];
             while (pos < lim) {
-                const uint32_t e = lookup(tab, (uint32_t)((pair << (pos - 32u * q)) >> 32));
+                const uint32_t e = lookup(tab, tab_n, (uint32_t)((pair << (pos - 32u * q)) >> 32));
                 const uint32_t nb = e & 31u, l1 = (e >> 7) & 31u;
                 bad |= e == 0u;
                 n_here += 1u + ((((e >> 5) & 3u) == 2u && pos + l1 < end) ? 1u : 0u);
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(256) void ecf8v_decode_kernel(const DescV* __restri
                     const uint32_t plim = end < 32u * (q + 1) ? end : 32u * (q + 1);
                     const uint64_t pair = ((uint64_t)W[q] << 32) | W[q + 1];
                     while (p < plim && k < base + lim) {
-                        const uint32_t e = lookup(tab, (uint32_t)((pair << (p - 32u * q)) >> 32));
+                        const uint32_t e = lookup(tab, tab_n, (uint32_t)((pair << (p - 32u * q)) >> 32));
                         const uint32_t nb = e & 31u, l1 = (e >> 7) & 31u;
                         if (k >= base) stage[k - base + shift] = (uint8_t)(e >> 12);
                         ++k;
@@ -417,25 +423,47 @@ const void* pick_kernel(uint32_t fmt, uint32_t tb)
 }
 
 std::mutex g_mu;
-std::vector<std::vector<uint32_t>> g_slots;     // [device][kernel index]: resident workgroups
+std::map<std::tuple<int, uint32_t, uint32_t, uint32_t>, uint32_t> g_slots;   // (device, fmt, tb, lds): workgroups
 
-int kernel_slots(uint32_t fmt, uint32_t tb, uint32_t* out)
+// Resident decode workgroups of the current device for a kernel and its dynamic LDS.
+int kernel_slots(uint32_t fmt, uint32_t tb, uint32_t lds, uint32_t* out)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return ECF8_ERR_HIP;
-    const int idx = (fmt == ECF8V_BF16 ? 0 : 3) + (tb == 64 ? 0 : tb == 128 ? 1 : 2);
     std::lock_guard<std::mutex> lk(g_mu);
-    if ((int)g_slots.size() <= dev) g_slots.resize(dev + 1, std::vector<uint32_t>(6, 0u));
-    if (g_slots[dev][idx] == 0) {
+    const auto key = std::make_tuple(dev, fmt, tb, lds);
+    auto it = g_slots.find(key);
+    if (it == g_slots.end()) {
         int cus = 0, occ = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return ECF8_ERR_HIP;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, pick_kernel(fmt, tb), (int)tb, 0) != hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, pick_kernel(fmt, tb), (int)tb, lds) != hipSuccess)
             return ECF8_ERR_HIP;
-        g_slots[dev][idx] = (uint32_t)((cus > 0 ? cus : 1) * (occ > 0 ? occ : 1));
+        it = g_slots.emplace(key, (uint32_t)((cus > 0 ? cus : 1) * (occ > 0 ? occ : 1))).first;
     }
-    *out = g_slots[dev][idx];
+    *out = it->second;
     return ECF8_OK;
 }
+
+// Entries of a tensor's decode table (the layout the table kernel builds:
+// 1024 primary entries plus one subtable per prefix of codewords longer than
+// 10 bits, sized by the longest of them), rounded up to 4.
+uint32_t table_entries(const uint8_t* len)
+{
+    uint32_t code[ECF8V_MAX_SYM];
+    if (ecf8v_canonical_codes(len, ECF8V_MAX_SYM, code) != ECF8_OK) return 0;
+    uint8_t dmax[1 << kPrimBits] = {0};
+    for (int s = 0; s < ECF8V_MAX_SYM; ++s)
+        if (len[s] > kPrimBits) {
+            const uint32_t pre = code[s] >> (len[s] - kPrimBits);
+            if (len[s] > dmax[pre]) dmax[pre] = len[s];
+        }
+    uint32_t used = 1u << kPrimBits;
+    for (int i = 0; i < (1 << kPrimBits); ++i)
+        if (dmax[i]) used += 1u << (dmax[i] - kPrimBits);
+    return (used + 3) & ~3u;
+}
+
+uint32_t decode_lds_bytes(uint32_t tab_n) { return (uint32_t)(kStageSyms + 32) + 4 * tab_n; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -456,6 +484,7 @@ extern "C" int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, u
     std::memset(plan, 0, sizeof(*plan));
     std::vector<DescV> dv(count);
     uint64_t blocks = 0;
+    uint32_t tab_n = 4;
     uint32_t fmt = count ? descs[0].meta.format : ECF8V_BF16, tb = count ? descs[0].meta.threads_per_block : 256;
     for (int i = 0; i < count; ++i) {
         const ecf8v_tensor_desc& t = descs[i];
@@ -480,6 +509,11 @@ extern "C" int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, u
         d.total_bits = t.meta.total_bits;
         std::memcpy(d.len, t.meta.len, sizeof(d.len));
         blocks += d.n_blocks;
+        if (d.n_blocks) {
+            const uint32_t te = table_entries(t.meta.len);
+            if (te == 0 || te > (uint32_t)kTabEntries) return ECF8_ERR_UNSUPPORTED;
+            if (te > tab_n) tab_n = te;
+        }
     }
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     if (count && hipMemcpy(ws + desc_offset(), dv.data(), sizeof(DescV) * count, hipMemcpyHostToDevice) != hipSuccess)
@@ -490,9 +524,10 @@ extern "C" int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, u
     plan->count = (uint32_t)count;
     plan->format = fmt;
     plan->threads_per_block = tb;
+    plan->table_entries = tab_n;
     uint32_t slots = 1;
     if (blocks) {
-        int rc = kernel_slots(fmt, tb, &slots);
+        int rc = kernel_slots(fmt, tb, decode_lds_bytes(tab_n), &slots);
         if (rc) return rc;
     }
     plan->grid = (uint32_t)(blocks < slots ? (blocks ? blocks : 1) : slots);
@@ -516,8 +551,11 @@ extern "C" int ecf8v_decode_run(const ecf8v_plan* plan, void* hip_stream)
     if (!k) return ECF8_ERR_UNSUPPORTED;
     int count = (int)plan->count;
     uint64_t total = plan->total_blocks;
-    void* args[] = {(void*)&descs, (void*)&count, (void*)&tables, (void*)&total, (void*)&status};
-    if (hipLaunchKernel(k, dim3(plan->grid), dim3(tb), args, 0, st) != hipSuccess) return ECF8_ERR_HIP;
+    uint32_t tab_n = plan->table_entries;
+    if (tab_n < 4 || tab_n > (uint32_t)kTabEntries || (tab_n & 3)) return ECF8_ERR_ARG;
+    void* args[] = {(void*)&descs, (void*)&count, (void*)&tables, (void*)&total, (void*)&status, (void*)&tab_n};
+    if (hipLaunchKernel(k, dim3(plan->grid), dim3(tb), args, decode_lds_bytes(tab_n), st) != hipSuccess)
+        return ECF8_ERR_HIP;
     return check(hipGetLastError());
 }
 
