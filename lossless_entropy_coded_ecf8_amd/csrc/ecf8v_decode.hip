@@ -251,7 +251,7 @@ __device__ __forceinline__ uint32_t lookup(const uint32_t* tab, uint32_t tab_n, 
         e = tab[i < tab_n ? i : 0u];
         if (e & 0x80000000u) e = 0;
     }
-    return (e & 31u) ? e : 0u;
+    return e;      // total bits 0: no codeword
 }
 
 template <int kFmt, int kTB>
@@ -297,20 +297,26 @@ __global__ __launch_bounds__(256) void ecf8v_decode_kernel(const DescV* __restri
         // count the codewords that start inside the chunk.  Four phases, one
         // per 32-bit word: a codeword starting in word q lies inside words q
         // and q + 1 (at most 16 bits), so each phase windows a fixed pair.
-        uint32_t pos = gap, n_here = 0;
-        bool bad = false;
+        // Every symbol of an entry is counted; only the last lookup can hold
+        // a second codeword starting at or past the end, taken off after the
+        // walk.  A lookup with no codeword moves the position by 256, which
+        // ends the walk and marks the chunk bad.
+        uint32_t pos = gap, n_here = 0, p_last = 0, e_last = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const uint32_t lim = end < 32u * (q + 1) ? end : 32u * (q + 1);
             const uint64_t pair = ((uint64_t)W[q] << 32) | W[q + 1];
             while (pos < lim) {
                 const uint32_t e = lookup(tab, tab_n, (uint32_t)((pair << (pos - 32u * q)) >> 32));
-                const uint32_t nb = e & 31u, l1 = (e >> 7) & 31u;
-                bad |= e == 0u;
-                n_here += 1u + ((((e >> 5) & 3u) == 2u && pos + l1 < end) ? 1u : 0u);
-                pos += e ? nb : 128u;
+                const uint32_t nb = e & 31u;
+                n_here += (e >> 5) & 3u;
+                p_last = pos;
+                e_last = e;
+                pos += nb ? nb : 256u;
             }
         }
+        const bool bad = pos >= 256u;
+        if (((e_last >> 5) & 3u) == 2u && p_last + ((e_last >> 7) & 31u) >= end) n_here -= 1;
         uint32_t total;
         const uint32_t off = block_excl_scan<kTB>(n_here, wsum, &total);
         const bool ok = __syncthreads_count(bad) == 0 && blk0 <= blk1 && blk1 <= d.n && total == blk1 - blk0;
@@ -324,7 +330,23 @@ __global__ __launch_bounds__(256) void ecf8v_decode_kernel(const DescV* __restri
             const uint64_t j_start = blk0 + base, j_end = j_start + lim;
             const uint32_t shift = (uint32_t)(j_start & 15);          // stage aligned to 16 elements
             // emit this round's symbols into the stage
-            if (off < base + lim && off + n_here > base) {
+            if (total <= (uint32_t)kStageSyms) {          // one round: every symbol has its slot
+                uint32_t p = gap, k = off + shift;
+                const uint32_t dummy = kStageSyms + 31;   // slot for an uncounted second codeword
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t plim = end < 32u * (q + 1) ? end : 32u * (q + 1);
+                    const uint64_t pair = ((uint64_t)W[q] << 32) | W[q + 1];
+                    while (p < plim) {
+                        const uint32_t e = lookup(tab, tab_n, (uint32_t)((pair << (p - 32u * q)) >> 32));
+                        const bool two = ((e >> 5) & 3u) == 2u && p + ((e >> 7) & 31u) < end;
+                        stage[k] = (uint8_t)(e >> 12);
+                        stage[two ? k + 1 : dummy] = (uint8_t)(e >> 20);
+                        k += two ? 2u : 1u;
+                        p += e & 31u;
+                    }
+                }
+            } else if (off < base + lim && off + n_here > base) {
                 uint32_t p = gap, k = off;                // k: output index of the next symbol
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
