@@ -132,8 +132,9 @@ typedef struct {
  * aligned device memory, owned by the caller). */
 uint64_t ecf8v_workspace_bytes(int count);
 
-/* Validate `count` descriptors of one format and upload them to the
- * workspace (synchronous copy).  Decode kernels exist for chunk_bytes = 16
+/* Validate `count` descriptors of one format, upload them to the workspace
+ * and build every tensor's decode table there (one workgroup per tensor on
+ * hip_stream, waited for: the tables depend on the code lengths only).  Decode kernels exist for chunk_bytes = 16
  * and threads_per_block in {64, 128, 256}; other params give
  * ECF8_ERR_UNSUPPORTED, and so does a code whose decode table (1024 primary
  * entries plus subtables for codewords longer than 10 bits) would pass 4096
@@ -144,13 +145,14 @@ int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, uint8_t* out
                          uint64_t workspace_bytes, void* hip_stream, ecf8v_plan* plan);
 
 /* DFloat11 article §3.2 / ECF8 blog §3.2.1: the decode of a prepared plan,
- * asynchronous on hip_stream: per-tensor decode tables (one workgroup per
- * tensor), then one persistent dispatch over all tensors' blocks. */
+ * asynchronous on hip_stream: one persistent dispatch over all tensors'
+ * blocks (the workspace must still hold what prepare put there). */
 int ecf8v_decode_run(const ecf8v_plan* plan, void* hip_stream);
 
 /* Synchronize hip_stream and report the blocks whose decoded symbol count
- * disagreed with blk_off (those blocks are not written) in *bad_blocks;
- * returns ECF8_ERR_CORRUPT if non-zero.  The counter is cleared by each run. */
+ * disagreed with blk_off (those blocks are not written), plus 1 if a decode
+ * table overflowed at prepare, in *bad_blocks; returns ECF8_ERR_CORRUPT if
+ * non-zero.  The block counter is cleared by each run. */
 int ecf8v_decode_status(const void* workspace, void* hip_stream, uint64_t* bad_blocks);
 
 #ifdef __cplusplus

@@ -8,7 +8,8 @@
 // at its stored gap, counts its codewords, a block-wide scan places them, the
 // lanes decode into shared memory, the block writes back).
 //
-// Decode table (one per tensor, built on the GPU from the code lengths):
+// Decode table (one per tensor, built on the GPU from the code lengths when
+// the plan is prepared):
 //   * primary: 1024 entries indexed by the next 10 stream bits.  An entry
 //     holds the one or two whole codewords those bits start with (symbols,
 //     total bits, length of the first), or, for a prefix of codewords longer
@@ -208,9 +209,9 @@ __global__ __launch_bounds__(256) void ecf8v_table_kernel(const DescV* __restric
     }
 }
 
-__global__ __launch_bounds__(64) void ecf8v_clear_kernel(unsigned long long* status)
+__global__ __launch_bounds__(64) void ecf8v_clear_kernel(unsigned long long* status, uint32_t words)
 {
-    if (threadIdx.x < 2) status[threadIdx.x] = 0ull;
+    if (threadIdx.x < words) status[threadIdx.x] = 0ull;
 }
 
 __device__ __forceinline__ uint32_t bswap(uint32_t x) { return __builtin_bswap32(x); }
@@ -540,6 +541,15 @@ extern "C" int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, u
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     if (count && hipMemcpy(ws + desc_offset(), dv.data(), sizeof(DescV) * count, hipMemcpyHostToDevice) != hipSuccess)
         return ECF8_ERR_HIP;
+    // the decode tables depend on the code lengths only: built once here
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    auto* status = reinterpret_cast<unsigned long long*>(ws);
+    hipLaunchKernelGGL(ecf8v_clear_kernel, dim3(1), dim3(64), 0, st, status, 2u);
+    if (count)
+        hipLaunchKernelGGL(ecf8v_table_kernel, dim3((uint32_t)count), dim3(256), 0, st,
+                           reinterpret_cast<const DescV*>(ws + desc_offset()),
+                           reinterpret_cast<uint32_t*>(ws + table_offset(count)), status);
+    if (hipGetLastError() != hipSuccess || hipStreamSynchronize(st) != hipSuccess) return ECF8_ERR_HIP;
     plan->workspace = workspace;
     plan->workspace_bytes = workspace_bytes;
     plan->total_blocks = blocks;
@@ -553,7 +563,6 @@ extern "C" int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, u
         if (rc) return rc;
     }
     plan->grid = (uint32_t)(blocks < slots ? (blocks ? blocks : 1) : slots);
-    (void)hip_stream;
     return ECF8_OK;
 }
 
@@ -565,9 +574,8 @@ extern "C" int ecf8v_decode_run(const ecf8v_plan* plan, void* hip_stream)
     auto* status = reinterpret_cast<unsigned long long*>(ws);
     const DescV* descs = reinterpret_cast<const DescV*>(ws + desc_offset());
     uint32_t* tables = reinterpret_cast<uint32_t*>(ws + table_offset((int)plan->count));
-    hipLaunchKernelGGL(ecf8v_clear_kernel, dim3(1), dim3(64), 0, st, status);
+    hipLaunchKernelGGL(ecf8v_clear_kernel, dim3(1), dim3(64), 0, st, status, 1u);
     if (plan->count == 0 || plan->total_blocks == 0) return check(hipGetLastError());
-    hipLaunchKernelGGL(ecf8v_table_kernel, dim3(plan->count), dim3(256), 0, st, descs, tables, status);
     const uint32_t tb = plan->threads_per_block;
     const void* k = pick_kernel(plan->format, tb);
     if (!k) return ECF8_ERR_UNSUPPORTED;
