@@ -133,14 +133,15 @@ typedef struct {
 uint64_t ecf8v_workspace_bytes(int count);
 
 /* Validate `count` descriptors of one format, upload them to the workspace
- * and build every tensor's decode table there (one workgroup per tensor on
- * hip_stream, waited for: the tables depend on the code lengths only).  Decode kernels exist for chunk_bytes = 16
- * and threads_per_block in {64, 128, 256}; other params give
- * ECF8_ERR_UNSUPPORTED, and so does a code whose decode table (1024 primary
- * entries plus subtables for codewords longer than 10 bits) would pass 4096
- * entries (complete codes never do).  Output of tensor i: out_base + out_offset_i, n_i
- * elements of the format.  Errors: ECF8_ERR_ARG, ECF8_ERR_META,
- * ECF8_ERR_UNSUPPORTED, ECF8_ERR_WORKSPACE, ECF8_ERR_HIP. */
+ * and build every tensor's decode table there (on hip_stream, waited for: the
+ * tables depend on the code lengths only).  A table has one entry per 10-bit
+ * prefix covered by codewords of at most 10 bits and one per 16-bit value of
+ * the space the longer codewords take (at most 9089 entries for any valid
+ * code); each entry decodes up to three whole codewords.  Decode kernels
+ * exist for chunk_bytes = 16 and threads_per_block in {64, 128, 256}; other
+ * params give ECF8_ERR_UNSUPPORTED.  Output of tensor i: out_base +
+ * out_offset_i, n_i elements of the format.  Errors: ECF8_ERR_ARG,
+ * ECF8_ERR_META, ECF8_ERR_UNSUPPORTED, ECF8_ERR_WORKSPACE, ECF8_ERR_HIP. */
 int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, uint8_t* out_base, void* workspace,
                          uint64_t workspace_bytes, void* hip_stream, ecf8v_plan* plan);
 
@@ -150,9 +151,9 @@ int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, uint8_t* out
 int ecf8v_decode_run(const ecf8v_plan* plan, void* hip_stream);
 
 /* Synchronize hip_stream and report the blocks whose decoded symbol count
- * disagreed with blk_off (those blocks are not written), plus 1 if a decode
- * table overflowed at prepare, in *bad_blocks; returns ECF8_ERR_CORRUPT if
- * non-zero.  The block counter is cleared by each run. */
+ * disagreed with blk_off, or whose stream held a window that is no codeword
+ * (those blocks are not written), in *bad_blocks; returns ECF8_ERR_CORRUPT
+ * if non-zero.  The counter is cleared by each run. */
 int ecf8v_decode_status(const void* workspace, void* hip_stream, uint64_t* bad_blocks);
 
 #ifdef __cplusplus

@@ -9,29 +9,49 @@
 // lanes decode into shared memory, the block writes back).
 //
 // Decode table (one per tensor, built on the GPU from the code lengths when
-// the plan is prepared):
-//   * primary: 1024 entries indexed by the next 10 stream bits.  An entry
-//     holds the one or two whole codewords those bits start with (symbols,
-//     total bits, length of the first), or, for a prefix of codewords longer
-//     than 10 bits, a pointer to a subtable;
-//   * subtables: one per such prefix, indexed by the next k bits, k being the
-//     longest codeword below the prefix minus 10 (1..6).  A complete code
-//     of at most 256 symbols needs at most about 2340 subtable entries (a
-//     subtree of depth k holds at least k + 1 codewords), so every table
-//     fits in 4096 entries (16 KB of LDS).
-// Entry bits: 31 pointer flag; pointer: 15..0 subtable base, 19..16 k;
-// symbols: 4..0 total bits, 6..5 count (0 = no codeword), 11..7 length of
-// the first, 19..12 first symbol, 27..20 second symbol.
+// the plan is prepared).  Canonical codes fill the 16-bit code space from 0
+// in (length, symbol) order, so every codeword of at most 10 bits lies below
+// every longer one:
+//   * region 1: one entry per 10-bit prefix covered by codewords of at most
+//     10 bits (p_long of them);
+//   * region 2: one entry per 16-bit value of the space the longer codewords
+//     take, then entries that decode nothing (unused code space, and padding
+//     to at least 1025 entries and a multiple of 4).
+// The index of a 32-bit window w is min(max(w >> 22, (w >> 16) - cdelta),
+// last) with cdelta = 63 * p_long: one branch-free expression picks the
+// region, and the clamp sends any window past the codes to an entry that
+// decodes nothing.  Codewords longer than 10 bits cover at most 1/8 of the
+// space when there are at most 256 symbols, so a table has at most 9089
+// entries.
+// Entry bits: 4..0 bits consumed (1 for no codeword), 6..5 whole codewords
+// decoded (0..3), 7 set for no codeword, 31..8 the symbols as bytes, first
+// symbol lowest, bytes past the count zero.
 //
 // Decode kernel: persistent workgroups of TB lanes walk the global block
-// index over all tensors.  Per block each lane loads its 16-byte chunk plus
-// 4 bytes of look-ahead, walks it from its gap counting codewords that start
-// inside the chunk, the workgroup scans the counts (checked against the
-// block offsets), and in rounds of at most 16384 symbols the lanes walk
-// again writing each symbol byte into LDS at its scanned position (the stage
-// aligned to 16 output elements); the workgroup then assembles whole groups
-// of 16 elements from 16 symbol bytes and the raw plane with 16-byte loads
-// and stores (byte permutes and masks), the ragged ends one element a lane.
+// index over all tensors; each block's stream chunks, gaps and offsets are
+// loaded one block ahead.  Per block:
+//   * the lanes' 16-byte chunks plus a look-ahead word go to LDS in
+//     word-major rows, so a 32-bit window at any bit position is two LDS
+//     reads and a funnel shift;
+//   * counting walk: lookups in wave-uniform steps of four, each entry
+//     recorded in statically indexed registers (lanes past their chunk end
+//     record 0); a lane's last lookup may decode codewords starting past its
+//     chunk, which are taken off its count;
+//   * block scan of the counts (checked against the block offsets);
+//   * replay: each recorded entry's symbol bytes are OR-ed into the cleared
+//     LDS stage at the scanned position (two dword ORs).  Codewords a lane
+//     decodes past its chunk end are the next lane's first ones, at the same
+//     positions, so OR-ing them twice is exact.  Lanes with more lookups than
+//     records walk the rest from registers;
+//   * write back: per 16-element group the 16 staged symbols and the raw
+//     plane make 16 elements with byte permutes and masks, stored with 16-byte
+//     non-temporal buffer stores; the ragged ends element by element from the
+//     same assembled words.  Every raw group a lane writes is loaded during
+//     the replay, and the next block's inputs are taken before the stores are
+//     issued, so no load waits behind the stores.  The lane that reads a
+//     group clears it for the next block.
+// Blocks of more than 16384 symbols (codes averaging under 2 bits) take a
+// slower path: rounds of 16384 symbols, each lane walking its chunk again.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -45,11 +65,19 @@
 
 namespace {
 
-constexpr int kChunk = 16;                 // bytes per lane
+constexpr int kChunk = 16;                  // bytes per lane
 constexpr int kChunkBits = 8 * kChunk;
-constexpr int kPrimBits = 10;
-constexpr int kTabEntries = 4096;
-constexpr int kStageSyms = 16384;           // symbols staged per round
+constexpr int kWin = 10;                    // region-1 window bits
+constexpr int kLongShift = 16 - kWin;
+constexpr int kTabMax = 9092;               // entries per table (at most 9089 used), a multiple of 4
+constexpr int kTabMin = 1028;               // 1025 rounded up to a multiple of 4
+constexpr int kStageSyms = 16384;           // symbols staged per block on the fast path
+constexpr int kStageBytes = kStageSyms + 64;   // + alignment shift, symbols OR-ed past the end
+constexpr int kRecords = 20;                // table entries recorded per lane by the counting walk
+constexpr int kRawGroups = 4;               // raw groups per lane loaded after the block scan (with 256
+                                            // lanes: every whole group of a fast-path block)
+constexpr int kTableSlices = (kTabMax + 255) / 256;
+static_assert(kRecords % 4 == 0, "records are taken four at a time");
 
 // Per-tensor descriptor in the workspace.
 struct DescV {
@@ -59,154 +87,168 @@ struct DescV {
     const uint64_t* blk_off;
     uint8_t* out;
     uint64_t n;
-    uint64_t n_blocks;
     uint64_t first_block;      // global index of the tensor's first block
+    uint64_t end_block;        // one past its last
     uint64_t total_bits;       // T: codewords start only before it
+    int32_t cdelta;            // 63 * p_long
+    uint32_t p_long;           // 10-bit prefixes covered by codewords of at most 10 bits
+    uint32_t long_units;       // 16-bit code values taken by the longer codewords
+    uint32_t entries;          // table entries (the last decodes nothing), a multiple of 4
     uint8_t len[ECF8V_MAX_SYM];
 };
 
-// Workspace: status (bad-block counter, table-overflow counter) | descriptors
-// | one table per tensor, each part 256-byte aligned.
+// Workspace: status (bad-block counter) | descriptors | one table per tensor,
+// each part 256-byte aligned.
 constexpr uint64_t kStatusBytes = 256;
 uint64_t desc_offset() { return kStatusBytes; }
 uint64_t table_offset(int count) { return desc_offset() + ((uint64_t)count * sizeof(DescV) + 255) / 256 * 256; }
 
-__device__ __forceinline__ uint32_t ld_u32(const uint8_t* p)
-{
-    return *reinterpret_cast<const uint32_t*>(p);
-}
+// Table geometry of a code (host): region sizes and the entry count.
+struct TabGeo {
+    uint32_t p_long, long_units, entries;
+    int32_t cdelta;
+};
 
-// Canonical decode of the top bits of a `width`-bit value v, trying lengths
-// lo..hi: the first length l whose prefix falls inside that length's code
-// range.  Returns the symbol and sets *len, or -1.
-__device__ __forceinline__ int canon_find(uint32_t v, int width, int lo, int hi, const uint32_t* first,
-                                          const uint32_t* cnt, const uint16_t* offs, const uint8_t* sorted, int* len)
+TabGeo table_geometry(const uint8_t* len)
 {
-    for (int l = lo; l <= hi; ++l) {
-        const uint32_t c = v >> (width - l);
-        if (c - first[l] < cnt[l]) {
-            *len = l;
-            return sorted[offs[l] + (c - first[l])];
-        }
+    uint32_t short_units = 0, all_units = 0;
+    for (int s = 0; s < ECF8V_MAX_SYM; ++s) {
+        if (!len[s]) continue;
+        const uint32_t u = 1u << (16 - len[s]);
+        all_units += u;
+        if (len[s] <= kWin) short_units += u;
     }
-    return -1;
+    TabGeo g;
+    g.p_long = short_units >> kLongShift;
+    g.long_units = all_units - short_units;
+    g.cdelta = (int32_t)(g.p_long * ((1u << kLongShift) - 1));
+    uint32_t e = g.p_long + g.long_units + 1;
+    if (e < (uint32_t)kTabMin) e = kTabMin;
+    g.entries = (e + 3) & ~3u;
+    return g;
 }
 
-// One workgroup (256 lanes) per tensor: canonical codes from the lengths,
-// then the primary table and the subtables.
-__global__ __launch_bounds__(256) void ecf8v_table_kernel(const DescV* __restrict__ descs, uint32_t* __restrict__ tables,
-                                                          unsigned long long* __restrict__ status)
+// ------------------------------------------------------------ memory helpers
+
+// Global memory through an address-space-1 pointer (the descriptor pointers
+// are generic; generic accesses also count against the LDS/scalar wait counter).
+#define ECF8V_GLOBAL __attribute__((address_space(1)))
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 gld16(const void* p)
 {
-    __shared__ uint8_t L[ECF8V_MAX_SYM];
-    __shared__ uint8_t sorted[ECF8V_MAX_SYM];
-    __shared__ uint32_t first[18], cnt[18];
-    __shared__ uint16_t offs[18];
-    __shared__ uint8_t dmax[1 << kPrimBits];
-    __shared__ uint16_t sub_base[1 << kPrimBits];
-    __shared__ uint32_t used;
-    const int tid = threadIdx.x;
+    const ECF8V_GLOBAL u32x4* q = (const ECF8V_GLOBAL u32x4*)p;
+    const u32x4 v = *q;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Buffer resources for the streaming loads and stores: wave-uniform base and
+// byte size, 32-bit lane offsets, hardware range checks (loads past the end
+// read 0, stores past the end are dropped).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;      // raw, untyped dword access
+constexpr int kNonTemporal = 2;             // cache-policy bit for the output stores
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint64_t bytes)
+{
+    const uint32_t nr = bytes < 0xFFFFFFFFull ? (uint32_t)bytes : 0xFFFFFFFFu;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nr, kRsrcWord3);
+}
+__device__ __forceinline__ uint32_t bld1(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0); }
+__device__ __forceinline__ uint32_t bld(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+__device__ __forceinline__ uint2 bld2(Rsrc r, uint32_t off, uint32_t soff = 0)
+{
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint4 bld4(Rsrc r, uint32_t off, uint32_t soff = 0)
+{
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void bst4(Rsrc r, uint32_t off, uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    u32x4 v;
+    v.x = a;
+    v.y = b;
+    v.z = c;
+    v.w = d;
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kNonTemporal);
+}
+__device__ __forceinline__ void bst2(Rsrc r, uint32_t off, uint16_t v) { __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0); }
+__device__ __forceinline__ void bst1(Rsrc r, uint32_t off, uint8_t v) { __builtin_amdgcn_raw_buffer_store_b8(v, r, off, 0, 0); }
+
+__device__ __forceinline__ uint32_t bswap(uint32_t x) { return __builtin_bswap32(x); }
+
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l)
+{
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// ------------------------------------------------------------ table kernel
+// Grid (tensors, kTableSlices) of 256 lanes: workgroup (i, j) builds entries
+// [256 j, 256 j + 256) of tensor i's table, one entry per lane.  Lane s first
+// places symbol s in canonical order (its rank and the left-justified start
+// of its code range); an entry is then decoded greedily from its known bits
+// (10 in region 1, 16 in region 2) by binary search over the code starts.
+__global__ __launch_bounds__(256) void ecf8v_table_kernel(const DescV* __restrict__ descs, uint32_t* __restrict__ tables)
+{
+    __shared__ uint32_t s_start[ECF8V_MAX_SYM];
+    __shared__ uint8_t s_len[ECF8V_MAX_SYM];
+    __shared__ uint8_t s_sym[ECF8V_MAX_SYM];
+    __shared__ uint32_t s_k;
     const DescV& d = descs[blockIdx.x];
-    uint32_t* tab = tables + (uint64_t)blockIdx.x * kTabEntries;
-    L[tid] = d.len[tid];
-    if (tid < 18) cnt[tid] = 0;
+    const int tid = threadIdx.x;
+    const uint32_t entries = d.entries;
+    if (blockIdx.y * 256u >= entries) return;                 // uniform per workgroup
+    if (tid == 0) s_k = 0;
     __syncthreads();
-    if (L[tid]) atomicAdd(&cnt[L[tid]], 1u);
-    __syncthreads();
-    if (tid == 0) {
-        uint32_t c = 0, o = 0;
-        for (int l = 1; l <= 16; ++l) {
-            c = (c + cnt[l - 1]) << 1;
-            first[l] = c;
-            offs[l] = (uint16_t)o;
-            o += cnt[l];
-        }
-        first[17] = 0;
-        cnt[17] = 0;
-        offs[17] = (uint16_t)o;
-    }
-    __syncthreads();
-    const int ls = L[tid];
-    uint32_t code = 0;
-    if (ls) {
-        uint32_t rank = 0;
-        for (int s = 0; s < tid; ++s) rank += L[s] == ls;
-        code = first[ls] + rank;
-        sorted[offs[ls] + rank] = (uint8_t)tid;
-    }
-    __syncthreads();
-    // longest codeword below each long prefix
-    __shared__ uint32_t dmax32[1 << kPrimBits];
-    for (int i = tid; i < (1 << kPrimBits); i += 256) dmax32[i] = 0;
-    __syncthreads();
-    if (ls > kPrimBits) atomicMax(&dmax32[code >> (ls - kPrimBits)], (uint32_t)ls);
-    __syncthreads();
-    {
-        // subtable bases: an exclusive scan of the subtable sizes, 4 prefixes a lane
-        uint32_t sz[4], mine = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t dm = dmax32[4 * tid + q];
-            dmax[4 * tid + q] = (uint8_t)(dm ? dm - kPrimBits : 0);
-            sz[q] = dm ? 1u << (dm - kPrimBits) : 0u;
-            mine += sz[q];
-        }
-        __shared__ uint32_t part[256];
-        part[tid] = mine;
-        __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {         // Hillis-Steele inclusive scan
-            const uint32_t v = tid >= off ? part[tid - off] : 0u;
-            __syncthreads();
-            part[tid] += v;
-            __syncthreads();
-        }
-        uint32_t next = (1u << kPrimBits) + part[tid] - mine;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            sub_base[4 * tid + q] = (uint16_t)(next < 65535 ? next : 65535);
-            next += sz[q];
-        }
-        if (tid == 255) {
-            used = next;
-            if (next > (uint32_t)kTabEntries) atomicAdd(status + 1, 1ull);
-        }
-    }
-    __syncthreads();
-    const bool fits = used <= (uint32_t)kTabEntries;
-    // primary entries
-    for (int i = tid; i < (1 << kPrimBits); i += 256) {
-        uint32_t e = 0;
-        if (dmax[i] && fits) {
-            e = 0x80000000u | ((uint32_t)dmax[i] << 16) | sub_base[i];
-        } else {
-            int l1 = 0;
-            const int s1 = canon_find((uint32_t)i, kPrimBits, 1, kPrimBits, first, cnt, offs, sorted, &l1);
-            if (s1 >= 0) {
-                e = (uint32_t)l1 | (1u << 5) | ((uint32_t)l1 << 7) | ((uint32_t)s1 << 12);
-                const int w2 = kPrimBits - l1;
-                if (w2 > 0) {
-                    int l2 = 0;
-                    const uint32_t rem = (uint32_t)i & ((1u << w2) - 1u);
-                    const int s2 = canon_find(rem, w2, 1, w2, first, cnt, offs, sorted, &l2);
-                    if (s2 >= 0) e = (uint32_t)(l1 + l2) | (2u << 5) | ((uint32_t)l1 << 7) | ((uint32_t)s1 << 12) |
-                                     ((uint32_t)s2 << 20);
-                }
+    const uint32_t l = d.len[tid];
+    if (l) {
+        uint32_t rank = 0, start = 0;
+        for (int u = 0; u < ECF8V_MAX_SYM; ++u) {
+            const uint32_t lu = d.len[u];
+            if (lu && (lu < l || (lu == l && u < tid))) {
+                ++rank;
+                start += 1u << (16 - lu);
             }
         }
-        tab[i] = e;
+        s_start[rank] = start;
+        s_len[rank] = (uint8_t)l;
+        s_sym[rank] = (uint8_t)tid;
+        atomicAdd(&s_k, 1u);
     }
-    // subtables
-    if (fits) {
-        for (int i = tid; i < (1 << kPrimBits); i += 256) {
-            const int k = dmax[i];
-            if (!k) continue;
-            for (int j = 0; j < (1 << k); ++j) {
-                const uint32_t v = ((uint32_t)i << k) | (uint32_t)j;
-                int l = 0;
-                const int s = canon_find(v, kPrimBits + k, kPrimBits + 1, kPrimBits + k, first, cnt, offs, sorted, &l);
-                tab[sub_base[i] + j] = s >= 0 ? ((uint32_t)l | (1u << 5) | ((uint32_t)l << 7) | ((uint32_t)s << 12)) : 0u;
-            }
+    __syncthreads();
+    const int k = (int)s_k;
+    const uint32_t idx = blockIdx.y * 256u + tid;
+    if (idx >= entries) return;
+    uint32_t v = 0, known = 0;
+    if (idx < d.p_long) {
+        v = idx << kLongShift;
+        known = kWin;
+    } else if (idx < d.p_long + d.long_units) {
+        v = idx + (uint32_t)d.cdelta;
+        known = 16;
+    }
+    uint32_t pos = 0, ns = 0, sy = 0;
+    while (k > 0 && ns < 3 && pos < known) {
+        const uint32_t x = (v << pos) & 0xFFFFu;
+        int lo = 0, hi = k;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_start[mid] <= x) lo = mid;
+            else hi = mid;
         }
+        const uint32_t ll = s_len[lo];
+        if (x < s_start[lo] || x - s_start[lo] >= (1u << (16 - ll))) break;   // unused code space
+        if (pos + ll > known) break;                                         // codeword not fully known
+        sy |= (uint32_t)s_sym[lo] << (8 * ns);
+        ++ns;
+        pos += ll;
     }
+    tables[(uint64_t)blockIdx.x * kTabMax + idx] = ns ? (pos | (ns << 5) | (sy << 8)) : 0x81u;
 }
 
 __global__ __launch_bounds__(64) void ecf8v_clear_kernel(unsigned long long* status, uint32_t words)
@@ -214,211 +256,512 @@ __global__ __launch_bounds__(64) void ecf8v_clear_kernel(unsigned long long* sta
     if (threadIdx.x < words) status[threadIdx.x] = 0ull;
 }
 
-__device__ __forceinline__ uint32_t bswap(uint32_t x) { return __builtin_bswap32(x); }
+// ------------------------------------------------------------ decode helpers
 
-// Block scan over kTB lanes; returns the exclusive prefix, *total the sum.
+// Block inputs loaded one block ahead: the lane's chunk, the look-ahead word,
+// the byte holding its gap, and (lanes 0 and 1) the block's two offsets.
+struct BlockIn {
+    uint4 sv;
+    uint32_t la;
+    uint32_t gb;
+    uint64_t off;
+};
+
+// Descriptor fields the prefetch needs, cached per tensor.
+struct NextTensor {
+    int t;
+    uint64_t begin, end, n;
+    const uint8_t* stream;
+    const uint8_t* gaps;
+    const uint64_t* blk_off;
+};
+
+__device__ __forceinline__ void fetch_tensor(const DescV* descs, int t, NextTensor& nt)
+{
+    const DescV* d = descs + t;
+    nt.t = t;
+    nt.begin = d->first_block;
+    nt.end = d->end_block;
+    nt.n = d->n;
+    nt.stream = d->stream;
+    nt.gaps = d->gaps;
+    nt.blk_off = d->blk_off;
+}
+
 template <int kTB>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total)
+__device__ __forceinline__ void load_block(const NextTensor& nt, uint64_t gblk, int tid, BlockIn& in)
 {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t x = v;
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true);
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true);
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, true);
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true);
-    const uint32_t r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
-                   r2 = __builtin_amdgcn_readlane(x, 47), r3 = __builtin_amdgcn_readlane(x, 63);
-    const int row = lane >> 4;
-    x += (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
-    if (lane == 0) wsum[wave] = r0 + r1 + r2 + r3;
-    __syncthreads();
-    uint32_t before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < kTB / 64; ++w) {
-        before += w < wave ? wsum[w] : 0u;
-        all += wsum[w];
-    }
-    *total = all;
-    return before + x - v;
+    const uint64_t b = gblk - nt.begin;
+    const uint2 o = bld2(make_rsrc(nt.blk_off + b, 16), (tid & 1) * 8u);
+    in.off = ((uint64_t)o.y << 32) | o.x;
+    // the stream has 16 bytes past its last block for the last look-ahead
+    const Rsrc rs = make_rsrc(nt.stream + b * (kTB * kChunk), kTB * kChunk + 16);
+    in.sv = bld4(rs, tid * kChunk);
+    in.la = bld(rs, tid * kChunk + kChunk);
+    in.gb = bld1(make_rsrc(nt.gaps + b * (kTB / 2), kTB / 2), tid >> 1);
 }
 
-// Table lookup at the window; returns the symbols entry (0 = no codeword).
-__device__ __forceinline__ uint32_t lookup(const uint32_t* tab, uint32_t tab_n, uint32_t win)
+// Output range of a block (or round): elements [lo, lo + nw), 16-element
+// groups counted from base = lo & ~15 (a0 = lo - base).
+struct BlockGeo {
+    uint64_t lo, base, want;
+    uint32_t nw, a0, groups;
+    bool sane;          // lo <= hi <= n
+};
+
+__device__ __forceinline__ BlockGeo block_geo(uint64_t lo_raw, uint64_t hi_raw, uint64_t n)
 {
-    uint32_t e = tab[win >> (32 - kPrimBits)];
-    if (e & 0x80000000u) {
-        const uint32_t k = (e >> 16) & 15u;
-        const uint32_t i = (e & 0xFFFFu) + ((win << kPrimBits) >> (32 - k));
-        e = tab[i < tab_n ? i : 0u];
-        if (e & 0x80000000u) e = 0;
-    }
-    return e;      // total bits 0: no codeword
+    BlockGeo g;
+    g.sane = lo_raw <= hi_raw && hi_raw <= n;
+    const uint64_t hi = hi_raw < n ? hi_raw : n;
+    g.lo = lo_raw < hi ? lo_raw : hi;
+    g.want = hi - g.lo;
+    g.nw = g.want < (uint64_t)kStageSyms ? (uint32_t)g.want : (uint32_t)kStageSyms;
+    g.base = g.lo & ~15ull;
+    g.a0 = (uint32_t)(g.lo - g.base);
+    g.groups = (g.a0 + g.nw + 15) >> 4;
+    return g;
 }
 
-template <int kFmt, int kTB>
-__global__ __launch_bounds__(256) void ecf8v_decode_kernel(const DescV* __restrict__ descs, int count,
-                                                           const uint32_t* __restrict__ tables, uint64_t total_blocks,
-                                                           unsigned long long* __restrict__ status, uint32_t tab_n)
-{
-    // dynamic LDS: the stage (element j at j - (first element & ~15)), then
-    // tab_n table entries (the largest table of the plan, a multiple of 4)
-    extern __shared__ __align__(16) uint8_t dyn[];
-    uint8_t* const stage = dyn;
-    uint32_t* const tab = reinterpret_cast<uint32_t*>(dyn + kStageSyms + 32);
-    __shared__ uint32_t wsum[kTB / 64];
-    const int tid = threadIdx.x;
-    int t = -1;
-    uint64_t t_first = 0, t_end = 0;
-    for (uint64_t gb = blockIdx.x; gb < total_blocks; gb += gridDim.x) {
-        if (gb >= t_end) {                                // next tensor(s): blocks come in increasing order
-            do {
-                ++t;
-                t_first = descs[t].first_block;
-                t_end = t_first + descs[t].n_blocks;
-            } while (gb >= t_end && t + 1 < count);
-            __syncthreads();                              // the previous table is no longer read
-            const uint4* src = reinterpret_cast<const uint4*>(tables + (uint64_t)t * kTabEntries);
-            for (uint32_t i = tid; i < tab_n / 4; i += kTB) reinterpret_cast<uint4*>(tab)[i] = src[i];
-            __syncthreads();
-        }
-        const DescV& d = descs[t];
-        const uint64_t lb = gb - t_first;
-        const uint64_t blk0 = d.blk_off[lb], blk1 = d.blk_off[lb + 1];
-        const uint64_t c = lb * kTB + tid;                // chunk of this lane
-        const uint4 v = *reinterpret_cast<const uint4*>(d.stream + c * kChunk);
-        const uint32_t W[5] = {bswap(v.x), bswap(v.y), bswap(v.z), bswap(v.w),
-                               bswap(ld_u32(d.stream + (c + 1) * kChunk))};
-        const uint32_t gap = (d.gaps[c >> 1] >> (4 * (uint32_t)(c & 1))) & 15u;
-        // codewords start before the chunk end and before T
-        const uint64_t cstart = c * (uint64_t)kChunkBits;
-        const uint32_t end = d.total_bits <= cstart ? 0u
-                             : (d.total_bits - cstart < (uint64_t)kChunkBits ? (uint32_t)(d.total_bits - cstart)
-                                                                            : (uint32_t)kChunkBits);
+// Raw plane of a group of 16 elements: 16 bytes (BF16) or 8 (E5M2).
+template <int kFmt>
+struct RawOf {
+    using T = uint4;
+    static constexpr uint32_t kGroupBytes = 16;
+};
+template <>
+struct RawOf<ECF8V_E5M2> {
+    using T = uint2;
+    static constexpr uint32_t kGroupBytes = 8;
+};
 
-        // count the codewords that start inside the chunk.  Four phases, one
-        // per 32-bit word: a codeword starting in word q lies inside words q
-        // and q + 1 (at most 16 bits), so each phase windows a fixed pair.
-        // Every symbol of an entry is counted; only the last lookup can hold
-        // a second codeword starting at or past the end, taken off after the
-        // walk.  A lookup with no codeword moves the position by 256, which
-        // ends the walk and marks the chunk bad.
-        uint32_t pos = gap, n_here = 0, p_last = 0, e_last = 0;
+// The raw plane of the groups of a range (the resource ends with the range,
+// so loads past it read 0 without touching memory).
+template <int kFmt>
+__device__ __forceinline__ Rsrc raw_rsrc(const uint8_t* raw, const BlockGeo& g)
+{
+    return make_rsrc(raw + (kFmt == ECF8V_BF16 ? g.base : g.base >> 1), (uint64_t)RawOf<kFmt>::kGroupBytes * g.groups);
+}
+
+// Output elements from base on, to the end of the tensor.
+template <int kFmt>
+__device__ __forceinline__ Rsrc out_rsrc(uint8_t* out, uint64_t base, uint64_t n)
+{
+    const uint64_t eb = kFmt == ECF8V_BF16 ? 2 : 1;
+    return make_rsrc(out + eb * base, eb * (n - base));
+}
+
+template <int kFmt>
+__device__ __forceinline__ typename RawOf<kFmt>::T load_raw_group(Rsrc rr, uint32_t g)
+{
+    if constexpr (kFmt == ECF8V_BF16)
+        return bld4(rr, 16u * g);
+    else
+        return bld2(rr, 8u * g);
+}
+
+// The 16 elements of a group from its 16 staged symbol bytes and its raw
+// plane (byte permutes and masks): 8 words (BF16, two elements a word) or 4
+// (E5M2, four a word).
+template <int kFmt>
+struct GroupWords {
+    static constexpr int kWords = kFmt == ECF8V_BF16 ? 8 : 4;
+};
+
+template <int kFmt>
+__device__ __forceinline__ void assemble_group(uint4 sv, typename RawOf<kFmt>::T rv, uint32_t (&o)[GroupWords<kFmt>::kWords])
+{
+    const uint32_t S[4] = {sv.x, sv.y, sv.z, sv.w};
+    if constexpr (kFmt == ECF8V_BF16) {
+        const uint32_t R[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const uint32_t lim = end < 32u * (q + 1) ? end : 32u * (q + 1);
-            const uint64_t pair = ((uint64_t)W[q] << 32) | W[q + 1];
-            while (pos < lim) {
-                const uint32_t e = lookup(tab, tab_n, (uint32_t)((pair << (pos - 32u * q)) >> 32));
-                const uint32_t nb = e & 31u;
-                n_here += (e >> 5) & 3u;
-                p_last = pos;
-                e_last = e;
-                pos += nb ? nb : 256u;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {     // elements 4q + 2h, 4q + 2h + 1 into one word
+                const uint32_t sel = h ? 0x0c030c02u : 0x0c010c00u;
+                const uint32_t rr = __builtin_amdgcn_perm(0u, R[q], sel);
+                const uint32_t ss = __builtin_amdgcn_perm(0u, S[q], sel);
+                o[2 * q + h] = ((rr & 0x00800080u) << 8) | (ss << 7) | (rr & 0x007F007Fu);
             }
         }
-        const bool bad = pos >= 256u;
-        if (((e_last >> 5) & 3u) == 2u && p_last + ((e_last >> 7) & 31u) >= end) n_here -= 1;
-        uint32_t total;
-        const uint32_t off = block_excl_scan<kTB>(n_here, wsum, &total);
-        const bool ok = __syncthreads_count(bad) == 0 && blk0 <= blk1 && blk1 <= d.n && total == blk1 - blk0;
-        if (!ok) {
-            if (tid == 0) atomicAdd(status, 1ull);
-            __syncthreads();                              // wsum reused by the next block
-            continue;
-        }
-        for (uint32_t base = 0; base < total; base += kStageSyms) {
-            const uint32_t lim = total - base < (uint32_t)kStageSyms ? total - base : (uint32_t)kStageSyms;
-            const uint64_t j_start = blk0 + base, j_end = j_start + lim;
-            const uint32_t shift = (uint32_t)(j_start & 15);          // stage aligned to 16 elements
-            // emit this round's symbols into the stage
-            if (total <= (uint32_t)kStageSyms) {          // one round: every symbol has its slot
-                uint32_t p = gap, k = off + shift;
-                const uint32_t dummy = kStageSyms + 31;   // slot for an uncounted second codeword
+    } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t plim = end < 32u * (q + 1) ? end : 32u * (q + 1);
-                    const uint64_t pair = ((uint64_t)W[q] << 32) | W[q + 1];
-                    while (p < plim) {
-                        const uint32_t e = lookup(tab, tab_n, (uint32_t)((pair << (p - 32u * q)) >> 32));
-                        const bool two = ((e >> 5) & 3u) == 2u && p + ((e >> 7) & 31u) < end;
-                        stage[k] = (uint8_t)(e >> 12);
-                        stage[two ? k + 1 : dummy] = (uint8_t)(e >> 20);
-                        k += two ? 2u : 1u;
+        for (int q = 0; q < 4; ++q) {
+            uint32_t t = ((q < 2 ? rv.x : rv.y) >> (16 * (q & 1))) & 0xFFFFu;   // 4 nibbles
+            t = (t | (t << 8)) & 0x00FF00FFu;
+            t = (t | (t << 4)) & 0x0F0F0F0Fu;                               // one per byte
+            o[q] = ((t & 0x04040404u) << 5) | ((S[q] & 0x1F1F1F1Fu) << 2) | (t & 0x03030303u);
+        }
+    }
+}
+
+// A whole group: one (E5M2) or two (BF16) 16-byte stores.
+template <int kFmt>
+__device__ __forceinline__ void write_group(Rsrc ro, uint32_t g, uint4 sv, typename RawOf<kFmt>::T rv)
+{
+    uint32_t o[GroupWords<kFmt>::kWords];
+    assemble_group<kFmt>(sv, rv, o);
+    if constexpr (kFmt == ECF8V_BF16) {
+        bst4(ro, 32u * g, o[0], o[1], o[2], o[3]);
+        bst4(ro, 32u * g + 16u, o[4], o[5], o[6], o[7]);
+    } else {
+        bst4(ro, 16u * g, o[0], o[1], o[2], o[3]);
+    }
+}
+
+// A ragged group ge of a range (range-relative elements [a0, endo)): the
+// group is assembled whole, its elements inside the range stored one by one.
+template <int kFmt>
+__device__ __forceinline__ void write_edge(Rsrc ro, uint32_t ge, uint4 sv, typename RawOf<kFmt>::T rv, uint32_t a0,
+                                           uint32_t endo)
+{
+    uint32_t o[GroupWords<kFmt>::kWords];
+    assemble_group<kFmt>(sv, rv, o);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const uint32_t i = 16u * ge + e;
+        if (i >= a0 && i < endo) {
+            if constexpr (kFmt == ECF8V_BF16)
+                bst2(ro, 2u * i, (uint16_t)(o[e >> 1] >> (16 * (e & 1))));
+            else
+                bst1(ro, i, (uint8_t)(o[e >> 2] >> (8 * (e & 3))));
+        }
+    }
+}
+
+// Write back a range: range-relative elements [a0, endo), element i staged
+// at stage[i].  Lane tid writes the whole groups g = tid + k * kTB with
+// 16-byte stores, the first kPre of them with the raw plane already in rv;
+// lane 0 writes a ragged first group (its raw plane rv[0] when kPre > 0) and
+// lane end_full % kTB a ragged last group (its raw plane tail_raw when
+// kPre > 0) element-wise.  The lane that reads a group from the stage clears it.
+template <int kFmt, int kTB, int kPre>
+__device__ __forceinline__ void write_back(uint8_t* stage, Rsrc rr, Rsrc ro, uint32_t a0, uint32_t endo, int tid,
+                                           const typename RawOf<kFmt>::T (&rv)[kRawGroups],
+                                           typename RawOf<kFmt>::T tail_raw)
+{
+    const uint32_t first_full = a0 ? 1u : 0u;
+    const uint32_t end_full = endo >> 4;                 // groups [first_full, end_full) are whole
+    const uint32_t groups = (endo + 15) >> 4;
+    uint4* const st16 = reinterpret_cast<uint4*>(stage);
+    uint32_t g = (uint32_t)tid;
+#pragma unroll
+    for (int k = 0; k < kPre; ++k, g += kTB) {
+        if (g >= first_full && g < end_full) {
+            const uint4 sv = st16[g];
+            st16[g] = make_uint4(0u, 0u, 0u, 0u);
+            write_group<kFmt>(ro, g, sv, rv[k]);
+        }
+    }
+    for (; g < end_full; g += kTB) {
+        if (g >= first_full) {
+            const uint4 sv = st16[g];
+            st16[g] = make_uint4(0u, 0u, 0u, 0u);
+            write_group<kFmt>(ro, g, sv, load_raw_group<kFmt>(rr, g));
+        }
+    }
+    if (a0 && tid == 0) {                                // group 0 (which may also be the last)
+        const uint4 sv = st16[0];
+        st16[0] = make_uint4(0u, 0u, 0u, 0u);
+        write_edge<kFmt>(ro, 0u, sv, kPre > 0 ? rv[0] : load_raw_group<kFmt>(rr, 0u), a0, endo);
+    }
+    if (end_full < groups && end_full >= first_full && (uint32_t)tid == end_full % kTB) {
+        const uint4 sv = st16[end_full];
+        st16[end_full] = make_uint4(0u, 0u, 0u, 0u);
+        write_edge<kFmt>(ro, end_full, sv, kPre > 0 ? tail_raw : load_raw_group<kFmt>(rr, end_full), a0, endo);
+    }
+}
+
+// OR the symbol bytes of an entry into the stage at byte position ob (its
+// 24 bits straddle at most two dwords).
+__device__ __forceinline__ void emit_entry(uint32_t* stage32, uint32_t ob, uint32_t e)
+{
+    const uint64_t v = (uint64_t)(e >> 8) << (8 * (ob & 3));
+    uint32_t* w = stage32 + (ob >> 2);
+    atomicOr(w, (uint32_t)v);
+    atomicOr(w + 1, (uint32_t)(v >> 32));
+}
+
+// Window at chunk bit p from the lane's words in registers (w[4] the look-ahead).
+__device__ __forceinline__ uint32_t reg_window(const uint32_t (&w)[5], uint32_t p)
+{
+    const uint32_t k = p >> 5;
+    uint32_t hi = w[0], lo = w[1];
+    if (k == 1) { hi = w[1]; lo = w[2]; }
+    if (k == 2) { hi = w[2]; lo = w[3]; }
+    if (k >= 3) { hi = w[3]; lo = w[4]; }
+    return (uint32_t)(((((uint64_t)hi << 32) | lo) << (p & 31)) >> 32);
+}
+
+__device__ __forceinline__ uint32_t tab_index(uint32_t win, int cd, int last)
+{
+    const int a = (int)(win >> (32 - kWin));
+    const int b = (int)(win >> 16) - cd;
+    const int m = a > b ? a : b;
+    return (uint32_t)(m < last ? m : last);
+}
+
+// Waves per SIMD the register allocation must allow (measured best: BF16
+// keeps its 16 raw-plane registers per lane unspilled at 5, E5M2 fits 6).
+template <int kFmt>
+constexpr int kMinWaves = kFmt == ECF8V_BF16 ? 5 : 6;
+
+// Dynamic LDS: the stage (the stream rows live inside it) | code lengths
+// (256 bytes) | table (tab_n entries).
+template <int kFmt, int kTB>
+__global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<kFmt>))) void ecf8v_decode_kernel(
+    const DescV* __restrict__ descs, int count, const uint32_t* __restrict__ tables, uint64_t total_blocks,
+    unsigned long long* __restrict__ status, uint32_t tab_n)
+{
+    constexpr int kWaves = kTB / 64;
+    constexpr uint32_t kPitch = 4u * kTB;                      // bytes per row
+    constexpr int kPitchShift = kTB == 256 ? 5 : (kTB == 128 ? 4 : 3);   // (r & 0xE0) << s == (r >> 5) * kPitch
+    static_assert(7 * kPitch <= (uint32_t)kStageBytes, "rows inside the stage");
+    using RawT = typename RawOf<kFmt>::T;
+    extern __shared__ __align__(16) uint8_t dyn[];
+    uint8_t* const stage = dyn;
+    uint32_t* const stage32 = reinterpret_cast<uint32_t*>(dyn);
+    uint8_t* const s_len = dyn + kStageBytes;
+    uint32_t* const s_tab = reinterpret_cast<uint32_t*>(dyn + kStageBytes + ECF8V_MAX_SYM);
+    __shared__ uint32_t s_wsum[kWaves];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    // Row rho (0..5) sits at stage + kPitch * (rho + 1), lane tid's dword at
+    // + 4 tid; word w of the lane's chunk (w = 4: look-ahead) in row 4 - w,
+    // row 5 only feeds a window's discarded half.  With r = 160 - p for chunk
+    // bit p, the window at p is alignbit(row (r >> 5), row (r >> 5) - 1, r);
+    // a lane past its end may read row -1 (stage bytes [0, kPitch)).
+    uint32_t* const col = reinterpret_cast<uint32_t*>(stage + kPitch) + tid;
+    const uint32_t col_lo = (uint32_t)tid * 4u;
+
+    uint64_t blk = blockIdx.x;
+    if (blk >= total_blocks) return;
+    for (int i = tid; i < kStageBytes / 16; i += kTB) reinterpret_cast<uint4*>(stage)[i] = make_uint4(0u, 0u, 0u, 0u);
+
+    NextTensor nt;
+    fetch_tensor(descs, 0, nt);
+    while (nt.t + 1 < count && blk >= nt.end) fetch_tensor(descs, nt.t + 1, nt);
+    BlockIn nx;
+    load_block<kTB>(nt, blk, tid, nx);
+    int ptens = nt.t;
+    // the first block's inputs are taken here, so that at the loop head only
+    // the back edge has loads in flight (whose order the compiler then knows)
+    asm volatile("" ::"v"(nx.sv.x), "v"(nx.la), "v"(nx.gb), "v"((uint32_t)nx.off));
+
+    int cur = -1;
+    uint64_t c_begin = 0, c_n = 0, c_T = 0;
+    const uint8_t* c_raw = nullptr;
+    const uint8_t* c_stream = nullptr;
+    uint8_t* c_out = nullptr;
+    int c_cd = 0, c_last = 0;
+
+    for (; blk < total_blocks; blk += gridDim.x) {
+        const BlockIn in = nx;
+        RawT rc[kRawGroups];
+        if (ptens != cur) {
+            // every lane is past the previous block's last table read
+            const DescV* d = descs + ptens;
+            c_begin = d->first_block;
+            c_n = d->n;
+            c_T = d->total_bits;
+            c_raw = d->raw;
+            c_stream = d->stream;
+            c_out = d->out;
+            c_cd = d->cdelta;
+            const uint32_t ne = d->entries <= tab_n ? d->entries : tab_n;
+            c_last = (int)ne - 1;
+            const uint32_t* tx = tables + (uint64_t)ptens * kTabMax;
+            for (uint32_t i = tid; i < ne / 4; i += kTB) reinterpret_cast<uint4*>(s_tab)[i] = gld16(tx + 4 * i);
+            for (int i = tid; i < ECF8V_MAX_SYM; i += kTB) s_len[i] = d->len[i];
+            cur = ptens;
+        }
+        // the table is in place and the previous block's write-back (which
+        // clears the stage memory the rows reuse) is done
+        __syncthreads();
+        col[4 * kTB] = bswap(in.sv.x);
+        col[3 * kTB] = bswap(in.sv.y);
+        col[2 * kTB] = bswap(in.sv.z);
+        col[1 * kTB] = bswap(in.sv.w);
+        col[0] = bswap(in.la);
+        const uint64_t b = blk - c_begin;
+        const uint64_t cstart = (b * kTB + tid) * (uint64_t)kChunkBits;
+        const uint32_t E = c_T > cstart ? (c_T - cstart < (uint64_t)kChunkBits ? (uint32_t)(c_T - cstart) : (uint32_t)kChunkBits) : 0u;
+        const uint32_t gap = (in.gb >> ((tid & 1) * 4)) & 15u;
+        const BlockGeo geo = block_geo(lane_u64(in.off, 0), lane_u64(in.off, 1), c_n);
+
+        // prefetch the next block of this workgroup (after the last block the
+        // current one is loaded again: unconditional loads keep the wait counts exact)
+        const uint64_t nb = blk + gridDim.x;
+        const uint64_t nbe = nb < total_blocks ? nb : blk;
+        while (nt.t + 1 < count && nbe >= nt.end) fetch_tensor(descs, nt.t + 1, nt);
+        load_block<kTB>(nt, nbe, tid, nx);
+        ptens = nt.t;
+
+        // ---- counting walk, recording each lookup's entry
+        const int cd = c_cd, last = c_last;
+        const uint32_t rend = 160u - E;
+        const uint32_t r0 = 160u - gap;
+        uint32_t rec[kRecords];
+        uint32_t r = r0, cnt = 0, inv = 0, lastex = 0;
+        bool act = r > rend;
+        int nq = 0;                           // four-lookup steps taken (wave-uniform)
+#pragma unroll
+        for (int q = 0; q < kRecords / 4; ++q) {
+            if (__builtin_amdgcn_ballot_w64(act) == 0) break;
+            nq = q + 1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t a = col_lo + ((r & 0xE0u) << kPitchShift);
+                const uint32_t wlo = *reinterpret_cast<const uint32_t*>(stage + a);
+                const uint32_t whi = *reinterpret_cast<const uint32_t*>(stage + a + kPitch);
+                const uint32_t e = s_tab[tab_index(__builtin_amdgcn_alignbit(whi, wlo, r), cd, last)];
+                const uint32_t em = act ? e : 0u;
+                rec[4 * q + j] = em;
+                lastex = act ? e : lastex;
+                r -= em & 31u;
+                cnt += (em >> 5) & 3u;
+                inv |= em;
+                act = r > rend;
+            }
+        }
+        const uint32_t r_rec = r;            // where the recorded lookups end
+        while (r > rend) {
+            const uint32_t a = col_lo + ((r & 0xE0u) << kPitchShift);
+            const uint32_t wlo = *reinterpret_cast<const uint32_t*>(stage + a);
+            const uint32_t whi = *reinterpret_cast<const uint32_t*>(stage + a + kPitch);
+            const uint32_t e = s_tab[tab_index(__builtin_amdgcn_alignbit(whi, wlo, r), cd, last)];
+            lastex = e;
+            r -= e & 31u;
+            cnt += (e >> 5) & 3u;
+            inv |= e;
+        }
+        // the lane's rows are stage memory from here on: leave them cleared
+#pragma unroll
+        for (int k = 0; k < 5; ++k) col[k * kTB] = 0u;
+        if (r != r0) {
+            // the last lookup started `room` bits before the chunk end: keep
+            // its codewords that start before it
+            const uint32_t ns = (lastex >> 5) & 3u;
+            const uint32_t room = r + (lastex & 31u) - rend;
+            const uint32_t l1 = s_len[(lastex >> 8) & 255u], l2 = s_len[(lastex >> 16) & 255u];
+            const uint32_t keep = 1u + (ns >= 2 && l1 < room ? 1u : 0u) + (ns >= 3 && l1 + l2 < room ? 1u : 0u);
+            cnt -= ns - keep;
+        }
+        // a window with no codeword spoils the block's total
+        if (inv & 0x80u) cnt += 1u << 22;
+
+        // ---- block scan of the counts
+        uint32_t x = cnt;
+        x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true);
+        x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true);
+        x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, true);
+        x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true);
+        const uint32_t q0 = __builtin_amdgcn_readlane(x, 15), q1 = __builtin_amdgcn_readlane(x, 31),
+                       q2 = __builtin_amdgcn_readlane(x, 47), q3 = __builtin_amdgcn_readlane(x, 63);
+        const int row = lane >> 4;
+        x += (row >= 1 ? q0 : 0u) + (row >= 2 ? q1 : 0u) + (row >= 3 ? q2 : 0u);
+        if (lane == 0) s_wsum[wave] = q0 + q1 + q2 + q3;
+        __syncthreads();
+        uint32_t before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const uint32_t sw = s_wsum[w];
+            before += w < wave ? sw : 0u;
+            total += sw;
+        }
+        const uint32_t pos = before + x - cnt;
+        const bool ok = geo.sane && total == geo.want;
+
+        // the next block's inputs have been in flight during the walk: take
+        // them into registers now, before this block's stores are issued (a
+        // later wait for them would also wait for those stores)
+        asm volatile("" ::"v"(nx.sv.x), "v"(nx.sv.y), "v"(nx.sv.z), "v"(nx.sv.w), "v"(nx.la), "v"(nx.gb),
+                     "v"((uint32_t)nx.off), "v"((uint32_t)(nx.off >> 32)));
+        if (ok && total <= (uint32_t)kStageSyms) {
+            // the block's raw plane, in flight during the replay (loaded a
+            // block ahead instead, it measured slower: more registers live
+            // across the walk, and the loads queued behind the stores)
+            const Rsrc rr = raw_rsrc<kFmt>(c_raw, geo);
+#pragma unroll
+            for (int k = 0; k < kRawGroups; ++k) {
+                if constexpr (kFmt == ECF8V_BF16)
+                    rc[k] = bld4(rr, 16u * tid, 16u * k * kTB);
+                else
+                    rc[k] = bld2(rr, 8u * tid, 8u * k * kTB);
+            }
+            // and the ragged last group's, for the lane that writes it (other
+            // lanes load past the range: no memory access)
+            const uint32_t endo = geo.a0 + geo.nw, end_full = endo >> 4;
+            const bool tail_lane = (endo & 15) && end_full >= (geo.a0 ? 1u : 0u) && (uint32_t)tid == end_full % kTB;
+            const RawT tail_raw = load_raw_group<kFmt>(rr, tail_lane ? end_full : 0x0FFFFFFFu);
+            // ---- replay into the stage
+            uint32_t ob = geo.a0 + pos;
+#pragma unroll
+            for (int q = 0; q < kRecords / 4; ++q) {
+                if (q >= nq) break;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t e = rec[4 * q + j];
+                    emit_entry(stage32, ob, e);
+                    ob += (e >> 5) & 3u;
+                }
+            }
+            if (r_rec > rend) {
+                // lanes with more lookups than records: the rest from registers
+                // (the rows are stage memory now; the chunk is L2-resident)
+                const Rsrc rs = make_rsrc(c_stream + b * (kTB * kChunk), kTB * kChunk + 16);
+                const uint4 cv = bld4(rs, tid * kChunk);
+                const uint32_t w[5] = {bswap(cv.x), bswap(cv.y), bswap(cv.z), bswap(cv.w),
+                                       bswap(bld(rs, tid * kChunk + kChunk))};
+                uint32_t r2 = r_rec;
+                while (r2 > rend) {
+                    const uint32_t e = s_tab[tab_index(reg_window(w, 160u - r2), cd, last)];
+                    emit_entry(stage32, ob, e);
+                    ob += (e >> 5) & 3u;
+                    r2 -= e & 31u;
+                }
+            }
+            __syncthreads();
+            // ---- write back; every group read is cleared
+            write_back<kFmt, kTB, kRawGroups>(stage, rr, out_rsrc<kFmt>(c_out, geo.base, c_n), geo.a0, endo, tid, rc,
+                                              tail_raw);
+            // symbols OR-ed past the block's end (by the last lane, or decoded
+            // from the padding after T) lie in the groups up to zend
+            const uint32_t zend0 = (geo.a0 + total + 2u + 16u) >> 4;
+            const uint32_t zend = zend0 < (uint32_t)(kStageBytes / 16) ? zend0 : (uint32_t)(kStageBytes / 16);
+            for (uint32_t g = geo.groups + tid; g < zend; g += kTB)
+                reinterpret_cast<uint4*>(stage)[g] = make_uint4(0u, 0u, 0u, 0u);
+        } else if (ok) {
+            // ---- more than kStageSyms symbols: rounds, each lane walking its
+            // chunk again and writing its symbols of the round
+            const Rsrc rs = make_rsrc(c_stream + b * (kTB * kChunk), kTB * kChunk + 16);
+            const uint4 cv = bld4(rs, tid * kChunk);
+            const uint32_t w[5] = {bswap(cv.x), bswap(cv.y), bswap(cv.z), bswap(cv.w),
+                                   bswap(bld(rs, tid * kChunk + kChunk))};
+            for (uint32_t base = 0; base < total; base += kStageSyms) {
+                const uint32_t lim = total - base < (uint32_t)kStageSyms ? total - base : (uint32_t)kStageSyms;
+                const uint64_t j_start = geo.lo + base;
+                const uint32_t shift = (uint32_t)(j_start & 15);
+                if (pos < base + lim && pos + cnt > base) {
+                    uint32_t p = gap, k = pos;
+                    while (p < E && k < base + lim) {
+                        const uint32_t e = s_tab[tab_index(reg_window(w, p), cd, last)];
+                        const uint32_t ns = (e >> 5) & 3u;
+                        for (uint32_t i = 0; i < ns; ++i, ++k)
+                            if (k >= base && k < base + lim && k < pos + cnt)
+                                stage[k - base + shift] = (uint8_t)(e >> (8 + 8 * i));
                         p += e & 31u;
                     }
                 }
-            } else if (off < base + lim && off + n_here > base) {
-                uint32_t p = gap, k = off;                // k: output index of the next symbol
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t plim = end < 32u * (q + 1) ? end : 32u * (q + 1);
-                    const uint64_t pair = ((uint64_t)W[q] << 32) | W[q + 1];
-                    while (p < plim && k < base + lim) {
-                        const uint32_t e = lookup(tab, tab_n, (uint32_t)((pair << (p - 32u * q)) >> 32));
-                        const uint32_t nb = e & 31u, l1 = (e >> 7) & 31u;
-                        if (k >= base) stage[k - base + shift] = (uint8_t)(e >> 12);
-                        ++k;
-                        if (((e >> 5) & 3u) == 2u && p + l1 < end) {
-                            if (k >= base && k < base + lim) stage[k - base + shift] = (uint8_t)(e >> 20);
-                            ++k;
-                        }
-                        p += nb;
-                    }
-                }
+                __syncthreads();
+                const BlockGeo rg = block_geo(j_start, j_start + lim, c_n);
+                write_back<kFmt, kTB, 0>(stage, raw_rsrc<kFmt>(c_raw, rg), out_rsrc<kFmt>(c_out, rg.base, c_n), rg.a0,
+                                         rg.a0 + rg.nw, tid, rc, rc[0]);
+                __syncthreads();
             }
-            __syncthreads();
-            // write back: whole aligned groups of 16 elements with 16-byte
-            // accesses, the ragged head and tail one element per lane
-            const uint64_t g_lo = (j_start + 15) >> 4, g_hi = j_end >> 4;
-            const uint64_t head_end = g_lo <= g_hi ? 16 * g_lo : j_end;
-            const uint64_t tail_start = g_lo <= g_hi ? 16 * g_hi : j_end;
-            const uint32_t n_head = (uint32_t)(head_end - j_start), n_tail = (uint32_t)(j_end - tail_start);
-            const uint64_t sbase = j_start & ~15ull;      // element at stage[0]
-            if ((uint32_t)tid < n_head + n_tail) {
-                const uint64_t j = (uint32_t)tid < n_head ? j_start + tid : tail_start + (tid - n_head);
-                const uint32_t sy = stage[j - sbase];
-                if (kFmt == ECF8V_BF16) {
-                    const uint32_t r = d.raw[j];
-                    reinterpret_cast<uint16_t*>(d.out)[j] = (uint16_t)(((r >> 7) << 15) | (sy << 7) | (r & 127u));
-                } else {
-                    const uint32_t r = (d.raw[j >> 1] >> (4 * (uint32_t)(j & 1))) & 15u;
-                    d.out[j] = (uint8_t)(((r >> 2) << 7) | (sy << 2) | (r & 3u));
-                }
-            }
-            for (uint64_t g = g_lo + tid; g < g_hi; g += kTB) {
-                const uint4 sv = *reinterpret_cast<const uint4*>(stage + (16 * g - sbase));
-                const uint32_t S[4] = {sv.x, sv.y, sv.z, sv.w};
-                if (kFmt == ECF8V_BF16) {
-                    const uint4 rv = *reinterpret_cast<const uint4*>(d.raw + 16 * g);
-                    const uint32_t R[4] = {rv.x, rv.y, rv.z, rv.w};
-                    uint32_t o[8];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                        for (int h = 0; h < 2; ++h) {     // elements 4q + 2h, 4q + 2h + 1 into one word
-                            const uint32_t sel = h ? 0x0c030c02u : 0x0c010c00u;
-                            const uint32_t rr = __builtin_amdgcn_perm(0u, R[q], sel);
-                            const uint32_t ss = __builtin_amdgcn_perm(0u, S[q], sel);
-                            o[2 * q + h] = ((rr & 0x00800080u) << 8) | (ss << 7) | (rr & 0x007F007Fu);
-                        }
-                    }
-                    uint4* dst = reinterpret_cast<uint4*>(d.out + 32 * g);
-                    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-                    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-                } else {
-                    const uint2 rv = *reinterpret_cast<const uint2*>(d.raw + 8 * g);
-                    uint32_t o[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        uint32_t t = ((q < 2 ? rv.x : rv.y) >> (16 * (q & 1))) & 0xFFFFu;   // 4 nibbles
-                        t = (t | (t << 8)) & 0x00FF00FFu;
-                        t = (t | (t << 4)) & 0x0F0F0F0Fu;                               // one per byte
-                        o[q] = ((t & 0x04040404u) << 5) | ((S[q] & 0x1F1F1F1Fu) << 2) | (t & 0x03030303u);
-                    }
-                    *reinterpret_cast<uint4*>(d.out + 16 * g) = make_uint4(o[0], o[1], o[2], o[3]);
-                }
-            }
-            __syncthreads();
+        } else if (tid == 0) {
+            atomicAdd(status, 1ull);
         }
     }
 }
@@ -467,26 +810,7 @@ int kernel_slots(uint32_t fmt, uint32_t tb, uint32_t lds, uint32_t* out)
     return ECF8_OK;
 }
 
-// Entries of a tensor's decode table (the layout the table kernel builds:
-// 1024 primary entries plus one subtable per prefix of codewords longer than
-// 10 bits, sized by the longest of them), rounded up to 4.
-uint32_t table_entries(const uint8_t* len)
-{
-    uint32_t code[ECF8V_MAX_SYM];
-    if (ecf8v_canonical_codes(len, ECF8V_MAX_SYM, code) != ECF8_OK) return 0;
-    uint8_t dmax[1 << kPrimBits] = {0};
-    for (int s = 0; s < ECF8V_MAX_SYM; ++s)
-        if (len[s] > kPrimBits) {
-            const uint32_t pre = code[s] >> (len[s] - kPrimBits);
-            if (len[s] > dmax[pre]) dmax[pre] = len[s];
-        }
-    uint32_t used = 1u << kPrimBits;
-    for (int i = 0; i < (1 << kPrimBits); ++i)
-        if (dmax[i]) used += 1u << (dmax[i] - kPrimBits);
-    return (used + 3) & ~3u;
-}
-
-uint32_t decode_lds_bytes(uint32_t tab_n) { return (uint32_t)(kStageSyms + 32) + 4 * tab_n; }
+uint32_t decode_lds_bytes(uint32_t tab_n) { return (uint32_t)(kStageBytes + ECF8V_MAX_SYM) + 4 * tab_n; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -495,7 +819,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 extern "C" uint64_t ecf8v_workspace_bytes(int count)
 {
     if (count < 0) return 0;
-    return table_offset(count) + (uint64_t)count * kTabEntries * 4;
+    return table_offset(count) + (uint64_t)count * kTabMax * 4;
 }
 
 extern "C" int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, uint8_t* out_base, void* workspace,
@@ -507,7 +831,7 @@ extern "C" int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, u
     std::memset(plan, 0, sizeof(*plan));
     std::vector<DescV> dv(count);
     uint64_t blocks = 0;
-    uint32_t tab_n = 4;
+    uint32_t tab_n = kTabMin;
     uint32_t fmt = count ? descs[0].meta.format : ECF8V_BF16, tb = count ? descs[0].meta.threads_per_block : 256;
     for (int i = 0; i < count; ++i) {
         const ecf8v_tensor_desc& t = descs[i];
@@ -519,6 +843,8 @@ extern "C" int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, u
         if (!aligned(t.stream, 16) || !aligned(t.blk_off, 8) || (t.out_offset & 15) ||
             !aligned(t.raw, fmt == ECF8V_BF16 ? 16 : 8))
             return ECF8_ERR_ARG;
+        const TabGeo g = table_geometry(t.meta.len);
+        if (g.entries > (uint32_t)kTabMax) return ECF8_ERR_UNSUPPORTED;   // never for valid lengths
         DescV& d = dv[i];
         std::memset(&d, 0, sizeof(d));
         d.stream = t.stream;
@@ -527,16 +853,16 @@ extern "C" int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, u
         d.blk_off = t.blk_off;
         d.out = out_base + t.out_offset;
         d.n = t.meta.n;
-        d.n_blocks = t.meta.n ? t.meta.n_blocks : 0;
         d.first_block = blocks;
+        if (t.meta.n) blocks += t.meta.n_blocks;
+        d.end_block = blocks;
         d.total_bits = t.meta.total_bits;
+        d.cdelta = g.cdelta;
+        d.p_long = g.p_long;
+        d.long_units = g.long_units;
+        d.entries = g.entries;
         std::memcpy(d.len, t.meta.len, sizeof(d.len));
-        blocks += d.n_blocks;
-        if (d.n_blocks) {
-            const uint32_t te = table_entries(t.meta.len);
-            if (te == 0 || te > (uint32_t)kTabEntries) return ECF8_ERR_UNSUPPORTED;
-            if (te > tab_n) tab_n = te;
-        }
+        if (t.meta.n && g.entries > tab_n) tab_n = g.entries;
     }
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     if (count && hipMemcpy(ws + desc_offset(), dv.data(), sizeof(DescV) * count, hipMemcpyHostToDevice) != hipSuccess)
@@ -546,9 +872,9 @@ extern "C" int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, u
     auto* status = reinterpret_cast<unsigned long long*>(ws);
     hipLaunchKernelGGL(ecf8v_clear_kernel, dim3(1), dim3(64), 0, st, status, 2u);
     if (count)
-        hipLaunchKernelGGL(ecf8v_table_kernel, dim3((uint32_t)count), dim3(256), 0, st,
+        hipLaunchKernelGGL(ecf8v_table_kernel, dim3((uint32_t)count, (uint32_t)kTableSlices), dim3(256), 0, st,
                            reinterpret_cast<const DescV*>(ws + desc_offset()),
-                           reinterpret_cast<uint32_t*>(ws + table_offset(count)), status);
+                           reinterpret_cast<uint32_t*>(ws + table_offset(count)));
     if (hipGetLastError() != hipSuccess || hipStreamSynchronize(st) != hipSuccess) return ECF8_ERR_HIP;
     plan->workspace = workspace;
     plan->workspace_bytes = workspace_bytes;
@@ -582,7 +908,7 @@ extern "C" int ecf8v_decode_run(const ecf8v_plan* plan, void* hip_stream)
     int count = (int)plan->count;
     uint64_t total = plan->total_blocks;
     uint32_t tab_n = plan->table_entries;
-    if (tab_n < 4 || tab_n > (uint32_t)kTabEntries || (tab_n & 3)) return ECF8_ERR_ARG;
+    if (tab_n < (uint32_t)kTabMin || tab_n > (uint32_t)kTabMax || (tab_n & 3)) return ECF8_ERR_ARG;
     void* args[] = {(void*)&descs, (void*)&count, (void*)&tables, (void*)&total, (void*)&status, (void*)&tab_n};
     if (hipLaunchKernel(k, dim3(plan->grid), dim3(tb), args, decode_lds_bytes(tab_n), st) != hipSuccess)
         return ECF8_ERR_HIP;

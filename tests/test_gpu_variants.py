@@ -85,8 +85,8 @@ def test_small_and_edge_cases_bit_exact(fmt, n, kind, tb):
 
 
 @pytest.mark.parametrize("max_len", [16, 11, 9])
-def test_length_limits_and_subtables(max_len):
-    """Heavy-tailed BF16 at several length limits: codes longer than the 10-bit primary index use subtables."""
+def test_length_limits_and_long_codes(max_len):
+    """Heavy-tailed BF16 at several length limits: codes longer than the 10-bit window use the 16-bit region."""
     d = dev()
     x = make("bf16", 400_000, max_len, "heavy")
     h = B.v_encode("bf16", x, max_len=max_len)
@@ -131,6 +131,27 @@ def test_corrupt_block_offset_is_flagged_and_contained():
     got = b[256:256 + 2 * x.size].view("<u2")
     lo = int(h.blk_off[3])
     assert np.array_equal(got[lo:], x[lo:])      # later blocks unaffected
+
+
+def test_window_with_no_codeword_is_flagged_and_contained():
+    """A single-symbol code leaves half the code space unused: stream bits that start no codeword
+    mark their block bad (not written); the other blocks decode exactly."""
+    d = dev()
+    x = make("bf16", 70_000, 5, "single")
+    h = B.v_encode("bf16", x)
+    assert int(np.count_nonzero(h.lengths)) == 1 and h.meta.n_blocks == 3
+    h.stream[100] = 0xFF                         # inside block 0
+    buf = torch.full((2 * x.size + 512,), CANARY, dtype=torch.uint8, device=d)
+    plan = B.DecodePlanV([h.to(d)], out=buf, offsets=[256])
+    plan.run()
+    torch.cuda.synchronize()
+    assert plan.status() == 1
+    b = buf.cpu().numpy()
+    assert (b[:256] == CANARY).all() and (b[256 + 2 * x.size:] == CANARY).all()
+    got = b[256:256 + 2 * x.size].view("<u2")
+    lo = int(h.blk_off[1])
+    assert (b[256:256 + 2 * lo] == CANARY).all()    # the bad block is not written
+    assert np.array_equal(got[lo:], x[lo:])
 
 
 def test_empty_and_zero_tensor_plans():
