@@ -33,6 +33,8 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "ecf8.h"
 
@@ -49,8 +51,8 @@ constexpr int kScanLanes = 256;                                        // lanes 
 constexpr int kTopLanes = 1024;                                        // lanes of the group-total scan
 constexpr uint64_t kGroupTiles = 4ull * kScanLanes;                    // tiles per scan group
 constexpr int kCountWords = 8;                                         // per-tile counts: 16 x 16 bits
-constexpr uint32_t kHistGrid = 2048;
-constexpr int kHistTiles = 4;                                          // tiles per histogram step
+constexpr int kHistWaves = 4;                                          // histogram: one tile per wave at a time
+constexpr int kHistLoads = (int)(kTile / 64 / 16);                     // 16-byte loads per lane per tile
 
 // Symbol counted by 16-bit field f (0 = low half) of per-tile count word d.
 __host__ __device__ constexpr int count_symbol(int d, int f) { return (d >> 1) + 4 * (2 * (d & 1) + f); }
@@ -165,74 +167,119 @@ __device__ __forceinline__ uint32_t wave_total(uint32_t v)
            __builtin_amdgcn_readlane(v, 63);
 }
 
-// Pass 1: exponent histogram.  A workgroup takes kHistTiles consecutive
-// tiles per step (all their loads issued first).  Per tile, each wave's 16
-// counts (a DPP reduction of the lanes' packed counts) meet in LDS, and 32
-// lanes sum the four waves and store the tiles' count words to tile_counts
-// (if given).  Those lanes also keep the workgroup's running totals, which
-// are added to the global counts once at the end.
+// One tile's histogram by one wave: lane `lane` holds elements
+// k * 1024 + 16 lane + i (k < 4, i < 16) of the tile in w; `pad` of them are
+// zero bytes past n, counted as symbol 0 and taken off.  Per lane the counts
+// go to 4-bit fields (16 elements), then 8-bit fields (64 elements); the
+// tile's 8 count words (16-bit fields, count_symbol order) come from one DPP
+// reduction each and are wave-uniform.
+__device__ __forceinline__ void tile_hist(const uint32_t (&w)[kHistLoads][4], uint32_t pad, uint32_t (&c)[kCountWords])
+{
+    const uint64_t m8 = 0x0F0F0F0F0F0F0F0Full, m16 = 0x00FF00FF00FF00FFull;
+    uint64_t even = 0, odd = 0;                           // byte j: count of symbol 2j / 2j + 1
+#pragma unroll
+    for (int k = 0; k < kHistLoads; ++k) {
+        uint64_t A = 0, B = 0;                            // 4-bit fields, elements 0..7 and 8..15
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t e = w[k][q] & 0x78787878u;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t sh = (e >> (8 * b + 1)) & 63u;   // 4 x symbol
+                if (q < 2)
+                    A += 1ull << sh;
+                else
+                    B += 1ull << sh;
+            }
+        }
+        even += (A & m8) + (B & m8);
+        odd += ((A >> 4) & m8) + ((B >> 4) & m8);
+    }
+    const uint64_t r[4] = {(even & m16) - pad, odd & m16, (even >> 8) & m16, (odd >> 8) & m16};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        c[2 * q] = wave_total((uint32_t)r[q]);
+        c[2 * q + 1] = wave_total((uint32_t)(r[q] >> 32));
+    }
+}
+
+// Pass 1: exponent histogram.  Each wave takes whole tiles (grid-stride), 64
+// elements per lane in four coalesced 16-byte loads, the next tile's loads
+// issued before the current one is counted; the tile's counts are stored (if
+// tile_counts is given) and added to the wave's uniform running totals.  A
+// ragged last tile, or every tile of an input that is not 16-byte aligned,
+// takes a second loop with bounds-checked loads.  No barrier until the end,
+// where the four waves' totals meet in LDS and go to the global counts.
 __global__ __launch_bounds__(256) void ecf8_hist_kernel(const uint8_t* __restrict__ fp8, uint64_t n, uint64_t tiles,
                                                         unsigned long long* __restrict__ freq,
                                                         uint32_t* __restrict__ tile_counts)
 {
-    __shared__ uint32_t part[2][kHistTiles][4][kCountWords];
-    __shared__ uint64_t fold[kHistTiles * kCountWords][2];
+    __shared__ uint64_t fold[kHistWaves][ECF8_NSYM];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint64_t tot_lo = 0, tot_hi = 0;
-    const uint64_t steps = (tiles + kHistTiles - 1) / kHistTiles;
-    int buf = 0;
-    for (uint64_t g = blockIdx.x; g < steps; g += gridDim.x, buf ^= 1) {
-        uint32_t w[kHistTiles][4];
+    uint64_t tot[ECF8_NSYM];                              // wave-uniform running totals, count-field order
 #pragma unroll
-        for (int k = 0; k < kHistTiles; ++k) {
-            const uint64_t tile = g * kHistTiles + k;
-            if (tile < tiles) {
-                load16(fp8, tile * kTile + (uint64_t)tid * kEncPerLane, n, w[k]);
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) w[k][q] = 0u;
-            }
+    for (int i = 0; i < ECF8_NSYM; ++i) tot[i] = 0;
+    auto account = [&](uint64_t t, const uint32_t (&c)[kCountWords]) {
+        if (tile_counts && lane == 0) {
+            uint4* dst = reinterpret_cast<uint4*>(tile_counts + t * kCountWords);
+            dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
+            dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
         }
 #pragma unroll
-        for (int k = 0; k < kHistTiles; ++k) {
-            const uint64_t e0 = (g * kHistTiles + k) * kTile + (uint64_t)tid * kEncPerLane;
-            const uint32_t pad =
-                e0 >= n ? kEncPerLane : (e0 + kEncPerLane > n ? (uint32_t)(e0 + kEncPerLane - n) : 0u);
-            uint32_t c[kCountWords];
-            lane_counts(w[k], pad, c);
-#pragma unroll
-            for (int d = 0; d < kCountWords; ++d) c[d] = wave_total(c[d]);
-            if (lane == 0) {
-#pragma unroll
-                for (int d = 0; d < kCountWords; ++d) part[buf][k][wave][d] = c[d];
-            }
+        for (int d = 0; d < kCountWords; ++d) {
+            tot[2 * d] += c[d] & 0xFFFFu;
+            tot[2 * d + 1] += c[d] >> 16;
         }
-        __syncthreads();    // part[buf] complete; part[buf ^ 1] was read before this barrier
-        if (tid < kHistTiles * kCountWords) {
-            const int k = tid / kCountWords, d = tid % kCountWords;
-            const uint64_t tile = g * kHistTiles + k;
-            const uint32_t v = part[buf][k][0][d] + part[buf][k][1][d] + part[buf][k][2][d] + part[buf][k][3][d];
-            if (tile < tiles) {
-                if (tile_counts) tile_counts[tile * kCountWords + d] = v;
-                tot_lo += v & 0xFFFFu;
-                tot_hi += v >> 16;
-            }
+    };
+    const uint64_t stride = (uint64_t)gridDim.x * kHistWaves;
+    const uint64_t first = (uint64_t)blockIdx.x * kHistWaves + wave;
+    const uint64_t full = ((uintptr_t)fp8 & 15) == 0 ? n / kTile : 0;   // tiles read with plain vector loads
+    const uint32_t lane_off = (uint32_t)lane * kEncPerLane;
+    uint64_t t = first;
+    uint4 nx[kHistLoads];
+    auto load_full = [&](uint64_t tt) {
+        const uint64_t s = tt < full ? tt : 0;            // past the last full tile: tile 0 again (discarded)
+#pragma unroll
+        for (int k = 0; k < kHistLoads; ++k)
+            nx[k] = *reinterpret_cast<const uint4*>(fp8 + s * kTile + k * (64 * kEncPerLane) + lane_off);
+    };
+    if (t < full) load_full(t);
+    for (; t < full; t += stride) {
+        uint32_t w[kHistLoads][4];
+#pragma unroll
+        for (int k = 0; k < kHistLoads; ++k) {
+            w[k][0] = nx[k].x;
+            w[k][1] = nx[k].y;
+            w[k][2] = nx[k].z;
+            w[k][3] = nx[k].w;
         }
+        if (t + stride < full) load_full(t + stride);
+        uint32_t c[kCountWords];
+        tile_hist(w, 0u, c);
+        account(t, c);
     }
-    if (tid < kHistTiles * kCountWords) {
-        fold[tid][0] = tot_lo;
-        fold[tid][1] = tot_hi;
+    // the rest (a ragged last tile; all tiles of an unaligned input)
+    for (t = full + ((first + stride - full % stride) % stride); t < tiles; t += stride) {
+        uint32_t w[kHistLoads][4];
+        uint32_t pad = 0;
+#pragma unroll
+        for (int k = 0; k < kHistLoads; ++k) {
+            const uint64_t e0 = t * kTile + (uint64_t)k * (64 * kEncPerLane) + lane_off;
+            load16(fp8, e0, n, w[k]);
+            pad += e0 >= n ? kEncPerLane : (e0 + kEncPerLane > n ? (uint32_t)(e0 + kEncPerLane - n) : 0u);
+        }
+        uint32_t c[kCountWords];
+        tile_hist(w, pad, c);
+        account(t, c);
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < ECF8_NSYM; ++i) fold[wave][i] = tot[i];
     }
     __syncthreads();
-    if (tid < kCountWords) {
-        uint64_t lo = 0, hi = 0;
-#pragma unroll
-        for (int k = 0; k < kHistTiles; ++k) {
-            lo += fold[k * kCountWords + tid][0];
-            hi += fold[k * kCountWords + tid][1];
-        }
-        if (lo) atomicAdd(&freq[count_symbol(tid, 0)], (unsigned long long)lo);
-        if (hi) atomicAdd(&freq[count_symbol(tid, 1)], (unsigned long long)hi);
+    if (tid < ECF8_NSYM) {
+        const uint64_t v = fold[0][tid] + fold[1][tid] + fold[2][tid] + fold[3][tid];
+        if (v) atomicAdd(&freq[count_symbol(tid >> 1, tid & 1)], (unsigned long long)v);
     }
 }
 
@@ -572,6 +619,28 @@ __global__ __launch_bounds__(256) void ecf8_encode_kernel(EncArgs a)
 
 int check(hipError_t e) { return e == hipSuccess ? ECF8_OK : ECF8_ERR_HIP; }
 
+// Workgroups of a 256-lane kernel resident on the current device at once
+// (the grid of the persistent histogram kernel), per device and kernel.
+std::mutex g_slots_mu;
+std::vector<uint32_t> g_slots;
+
+int resident_slots(int which, const void* kernel, uint32_t* out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return ECF8_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_slots_mu);
+    const size_t i = 2 * (size_t)dev + (size_t)which;
+    if (g_slots.size() <= i) g_slots.resize(i + 1, 0u);
+    if (!g_slots[i]) {
+        int cus = 0, occ = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return ECF8_ERR_HIP;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 256, 0) != hipSuccess) return ECF8_ERR_HIP;
+        g_slots[i] = (uint32_t)((cus > 0 ? cus : 1) * (occ > 0 ? occ : 1));
+    }
+    *out = g_slots[i];
+    return ECF8_OK;
+}
+
 // Workspace: per-tile counts (32 B per tile) | tile bit offsets (tiles + 1,
 // u64) | per-tile chunk and block (2 x u64) | group totals/offsets (u64) |
 // codeword-pair table (2 KB), each part 256-byte aligned.
@@ -610,8 +679,11 @@ extern "C" int ecf8_histogram_device(const uint8_t* fp8, uint64_t n, uint64_t* f
     hipLaunchKernelGGL(ecf8_zero_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<uint32_t*>(freq),
                        (uint64_t)2 * ECF8_NSYM);
     if (n) {
-        const uint64_t steps = (W.tiles + kHistTiles - 1) / kHistTiles;
-        const uint64_t grid = steps < kHistGrid ? steps : kHistGrid;
+        uint32_t slots = 0;
+        const int rc = resident_slots(0, reinterpret_cast<const void*>(ecf8_hist_kernel), &slots);
+        if (rc) return rc;
+        const uint64_t steps = (W.tiles + kHistWaves - 1) / kHistWaves;
+        const uint64_t grid = steps < slots ? steps : slots;
         hipLaunchKernelGGL(ecf8_hist_kernel, dim3((uint32_t)grid), dim3(256), 0, st, fp8, n, W.tiles,
                            reinterpret_cast<unsigned long long*>(freq), reinterpret_cast<uint32_t*>(workspace));
     }
