@@ -37,9 +37,11 @@
 //     lane; they are the same symbols at the same positions, so OR-ing them
 //     twice is exact.  The stream rows share memory with the staging.
 //   * write back: 16 elements per lane-step: 8 bytes of exponent nibbles from
-//     LDS, 8 bytes of the sign/mantissa plane from HBM (prefetched a block
-//     ahead), SWAR byte assembly, one non-temporal 16-byte store; byte stores
-//     only at the two ragged block edges.
+//     LDS, 8 bytes of the sign/mantissa plane from HBM (non-temporal loads
+//     issued after the count, in flight during the scan and decode), SWAR
+//     byte assembly, one non-temporal 16-byte store; byte stores only at the
+//     two ragged block edges.  The next block's inputs are taken into
+//     registers before the stores are issued.
 //   * streaming loads and stores are buffer instructions (SGPR descriptors,
 //     32-bit offsets, hardware range checks); one persistent dispatch walks
 //     all blocks of all tensors of a batch at 6 workgroups per CU.
@@ -122,8 +124,9 @@ typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;   // raw, untyped dword access (gfx9 descriptor word 3)
 // The decoded output is written once and not read back by this kernel: its
 // 16-byte stores carry the non-temporal hint (cache-policy bit 1), which
-// measured faster than the default; the loads keep the default policy (their
-// neighbouring lines are reused from L2).
+// measured faster than the default, and so do the sign/mantissa plane loads
+// (read once); the stream loads keep the default policy (their neighbouring
+// lines are reused from L2 by the look-ahead reads).
 constexpr int kNonTemporal = 2;
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint64_t bytes)
 {
@@ -432,7 +435,6 @@ struct NextTensor {
     const uint8_t* stream;
     const uint8_t* gaps;
     const uint64_t* blk_off;
-    const uint8_t* nibbles;
 };
 
 __device__ __forceinline__ void fetch_next_tensor(const DevDesc* descs, int t, NextTensor& nt)
@@ -445,7 +447,6 @@ __device__ __forceinline__ void fetch_next_tensor(const DevDesc* descs, int t, N
     nt.stream = d->stream;
     nt.gaps = d->gaps;
     nt.blk_off = d->blk_off;
-    nt.nibbles = d->nibbles;
 }
 
 // Output range of a block: elements [lo, lo + nw), written as 16-element
@@ -476,15 +477,18 @@ __device__ __forceinline__ Rsrc nibble_rsrc(const uint8_t* nibbles, const BlockG
     return make_rsrc(nibbles + (g.base >> 1), 8ull * g.groups);
 }
 
-// Issue the sign/mantissa plane loads of a block's groups (one 8-byte load
-// per group, lane tid takes groups tid + k*TB).  The loads are issued
-// unconditionally (past the block they read 0) so that the compiler can count
-// outstanding memory operations exactly and never drains the prefetch early.
+// Issue the sign/mantissa plane loads of a block's groups (one 8-byte
+// non-temporal load per group, lane tid takes groups tid + k*TB).  The loads
+// are issued unconditionally (past the block they read 0) so that the
+// compiler can count outstanding memory operations exactly.
 template <int TB>
 __device__ __forceinline__ void load_nibbles(Rsrc rn, int tid, uint2 (&nv)[kNibPrefetch])
 {
 #pragma unroll
-    for (int k = 0; k < kNibPrefetch; ++k) nv[k] = bld2(rn, 8u * tid, 8u * k * TB);
+    for (int k = 0; k < kNibPrefetch; ++k) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rn, 8u * tid, 8u * k * TB, kNonTemporal);
+        nv[k] = make_uint2(v.x, v.y);
+    }
 }
 
 __device__ __forceinline__ void load_block(const NextTensor& nt, uint64_t gblk, int tid, BlockIn& in)
@@ -561,11 +565,9 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
     load_block(nt, blk, tid, nx);
     int ptens = nt.t;                  // tensor of the prefetched block
     const uint32_t cap = 8u * C * TB;  // staging capacity in elements
-    uint2 nv[kNibPrefetch];            // sign/mantissa plane of the block about to be decoded
-    load_nibbles<TB>(nibble_rsrc(nt.nibbles, block_geo(lane_u64(nx.off, 0), lane_u64(nx.off, 1), nt.n, cap)), tid, nv);
     // wait for the first block's loads here, so that at the loop head only the
     // back edge has loads in flight and the compiler can count them exactly
-    asm volatile("" ::"v"(nx.sv.x), "v"(nx.la), "v"(nx.gb), "v"(nv[kNibPrefetch - 1].x));
+    asm volatile("" ::"v"(nx.sv.x), "v"(nx.la), "v"(nx.gb), "v"((uint32_t)nx.off));
 
     // fields of the tensor being decoded
     int cur = -1;
@@ -618,7 +620,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
         const uint32_t E = leftc > lstart ? min(leftc - lstart, 8u * C) : 0u;
         const uint32_t gap = (in.gb >> ((tid & 1) * 4)) & 15u;
 
-        // block output range and its 16-element groups (its sign/mantissa plane is already in flight)
+        // block output range and its 16-element groups
         const BlockGeo geo = block_geo(lane_u64(in.off, 0), lane_u64(in.off, 1), c_n, cap);
         const uint64_t base = geo.base;
         const uint32_t a0 = geo.a0, nw = geo.nw, groups = geo.groups;
@@ -693,6 +695,15 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
             }
             cnt -= ns - keep;
         }
+
+        // the block's sign/mantissa plane, in flight during the scan and the
+        // decode (loaded a block ahead instead, it measured slower: more
+        // registers live across the count, and loads queued behind stores);
+        // the next block's inputs, issued at the top, are taken now, before
+        // this block's stores
+        uint2 nv[kNibPrefetch];
+        load_nibbles<TB>(nib_blk, tid, nv);
+        asm volatile("" ::"v"(nx.sv.x), "v"(nx.la), "v"(nx.gb), "v"((uint32_t)nx.off));
 
         // ---- phase 3: block-wide exclusive scan of the counts
         const uint32_t incl = wave_inclusive_scan(cnt, lane);
@@ -778,10 +789,6 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
             const uint32_t zend = zend0 < (uint32_t)(L::kOutDw / 2) ? zend0 : (uint32_t)(L::kOutDw / 2);
             for (uint32_t g = tid; g < zend; g += TB) reinterpret_cast<uint2*>(s_out)[g] = make_uint2(0u, 0u);
         }
-        // the next block's sign/mantissa plane (its offsets arrived during the
-        // decode): a whole block of latency to hide
-        const BlockGeo ngeo = block_geo(lane_u64(nx.off, 0), lane_u64(nx.off, 1), nt.n, cap);
-        load_nibbles<TB>(nibble_rsrc(nt.nibbles, ngeo), tid, nv);
     }
 }
 

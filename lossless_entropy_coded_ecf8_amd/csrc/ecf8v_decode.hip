@@ -148,7 +148,7 @@ __device__ __forceinline__ uint4 gld16(const void* p)
 // read 0, stores past the end are dropped).
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;      // raw, untyped dword access
-constexpr int kNonTemporal = 2;             // cache-policy bit for the output stores
+constexpr int kNonTemporal = 2;             // cache-policy bit: output stores and raw-plane loads (used once)
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint64_t bytes)
 {
     const uint32_t nr = bytes < 0xFFFFFFFFull ? (uint32_t)bytes : 0xFFFFFFFFu;
@@ -156,16 +156,20 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint64_t bytes)
 }
 __device__ __forceinline__ uint32_t bld1(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0); }
 __device__ __forceinline__ uint32_t bld(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
-__device__ __forceinline__ uint2 bld2(Rsrc r, uint32_t off, uint32_t soff = 0)
+template <int kPolicy = 0>
+__device__ __forceinline__ uint2 bld2_p(Rsrc r, uint32_t off, uint32_t soff)
 {
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, kPolicy);
     return make_uint2(v.x, v.y);
 }
-__device__ __forceinline__ uint4 bld4(Rsrc r, uint32_t off, uint32_t soff = 0)
+template <int kPolicy = 0>
+__device__ __forceinline__ uint4 bld4_p(Rsrc r, uint32_t off, uint32_t soff)
 {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kPolicy);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ uint2 bld2(Rsrc r, uint32_t off, uint32_t soff = 0) { return bld2_p<0>(r, off, soff); }
+__device__ __forceinline__ uint4 bld4(Rsrc r, uint32_t off, uint32_t soff = 0) { return bld4_p<0>(r, off, soff); }
 __device__ __forceinline__ void bst4(Rsrc r, uint32_t off, uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
     u32x4 v;
@@ -684,11 +688,11 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
             // across the walk, and the loads queued behind the stores)
             const Rsrc rr = raw_rsrc<kFmt>(c_raw, geo);
 #pragma unroll
-            for (int k = 0; k < kRawGroups; ++k) {
+            for (int k = 0; k < kRawGroups; ++k) {       // read once: non-temporal
                 if constexpr (kFmt == ECF8V_BF16)
-                    rc[k] = bld4(rr, 16u * tid, 16u * k * kTB);
+                    rc[k] = bld4_p<kNonTemporal>(rr, 16u * tid, 16u * k * kTB);
                 else
-                    rc[k] = bld2(rr, 8u * tid, 8u * k * kTB);
+                    rc[k] = bld2_p<kNonTemporal>(rr, 8u * tid, 8u * k * kTB);
             }
             // and the ragged last group's, for the lane that writes it (other
             // lanes load past the range: no memory access)
