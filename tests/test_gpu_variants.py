@@ -133,6 +133,41 @@ def test_corrupt_block_offset_is_flagged_and_contained():
     assert np.array_equal(got[lo:], x[lo:])      # later blocks unaffected
 
 
+def dense_sparse_runs(fmt, n, dense_run, sparse_run, seed):
+    """Runs of one exponent (a 1-bit code: 128 codewords per 16-byte chunk) between runs of ~100
+    exponents (long codes), so that blocks stay under 16384 symbols while some chunks need more
+    than 20 table lookups."""
+    rng = np.random.default_rng(seed)
+    bit = lambda k: rng.integers(0, 1 << k, size=n)
+    if fmt == "bf16":
+        sparse = (bit(1) << 15) | (rng.integers(60, 160, size=n) << 7) | bit(7)
+        dense = (bit(1) << 15) | (127 << 7) | bit(7)
+        dt = np.uint16
+    else:
+        sparse = (bit(1) << 7) | (rng.integers(2, 30, size=n) << 2) | bit(2)
+        dense = (bit(1) << 7) | (15 << 2) | bit(2)
+        dt = np.uint8
+    return np.where(np.arange(n) % (dense_run + sparse_run) < dense_run, dense, sparse).astype(dt)
+
+
+@pytest.mark.parametrize("fmt,sparse_run", [("bf16", 3300), ("e5m2", 5000)])
+def test_lanes_past_the_recorded_lookups(fmt, sparse_run):
+    """Chunks of 128 one-bit codewords take more lookups than a lane records; their lanes finish the
+    replay from registers (blocks still fit the stage, so the round path is not taken)."""
+    d = dev()
+    x = dense_sparse_runs(fmt, 300_000, 8192, sparse_run, 7)
+    h = B.v_encode(fmt, x)
+    L = np.asarray(h.lengths, dtype=np.int64)
+    sym = (x.astype(np.int64) >> 7) & 255 if fmt == "bf16" else (x.astype(np.int64) >> 2) & 31
+    starts = np.concatenate([[0], np.cumsum(L[sym])])[:-1]
+    per_chunk = np.bincount(starts // (8 * h.meta.chunk_bytes))
+    assert per_chunk.max() > 3 * 20                                    # more than 20 three-symbol lookups
+    assert np.diff(np.asarray(h.blk_off, dtype=np.int64)).max() <= 16384
+    (got,), _ = decode_checked([h], d)
+    assert np.array_equal(as_elems(fmt, got), x)
+    assert np.array_equal(oracle.v_decode(fmt, h.stream, h.raw, h.n, h.lengths), x)
+
+
 def test_window_with_no_codeword_is_flagged_and_contained():
     """A single-symbol code leaves half the code space unused: stream bits that start no codeword
     mark their block bad (not written); the other blocks decode exactly."""
