@@ -43,10 +43,11 @@
 //     decodes past its chunk end are the next lane's first ones, at the same
 //     positions, so OR-ing them twice is exact.  Lanes with more lookups than
 //     records walk the rest from registers;
-//   * write back: per 16-element group the 16 staged symbols and the raw
-//     plane make 16 elements with byte permutes and masks, stored with 16-byte
-//     non-temporal buffer stores; the ragged ends element by element from the
-//     same assembled words.  Every raw group a lane writes is loaded during
+//   * write back in units of 16 output bytes (8 BF16 or 16 E5M2 elements):
+//     the unit's staged symbols and its 8 raw-plane bytes make its elements
+//     with byte permutes and masks, one non-temporal 16-byte buffer store per
+//     unit, so a wave's store covers 1 KB of contiguous output; the ragged
+//     ends element by element from the same assembled words.  Every raw group a lane writes is loaded during
 //     the replay, and the next block's inputs are taken before the stores are
 //     issued, so no load waits behind the stores.  The lane that reads a
 //     group clears it for the next block.
@@ -74,10 +75,19 @@ constexpr int kTabMin = 1028;               // 1025 rounded up to a multiple of 
 constexpr int kStageSyms = 16384;           // symbols staged per block on the fast path
 constexpr int kStageBytes = kStageSyms + 64;   // + alignment shift, symbols OR-ed past the end
 constexpr int kRecords = 20;                // table entries recorded per lane by the counting walk
-constexpr int kRawGroups = 4;               // raw groups per lane loaded after the block scan (with 256
-                                            // lanes: every whole group of a fast-path block)
+constexpr int kStep = 4;                    // lookups per wave-uniform step of the walk
+// Write-back unit: the elements of 16 output bytes, 8 (BF16) or 16 (E5M2),
+// with 8 bytes of raw plane either way; one 16-byte store per unit, so that a
+// wave's store covers 1 KB of contiguous output.
+template <int kFmt>
+struct Unit {
+    static constexpr uint32_t kElems = kFmt == ECF8V_BF16 ? 8u : 16u;
+    static constexpr int kPerLane = kFmt == ECF8V_BF16 ? 8 : 4;   // loaded per lane after the block scan:
+                                                                  // with 256 lanes, all of a fast-path block
+};
+constexpr int kRawMax = 8;                  // the larger of the two kPerLane
 constexpr int kTableSlices = (kTabMax + 255) / 256;
-static_assert(kRecords % 4 == 0, "records are taken four at a time");
+static_assert(kRecords % kStep == 0, "records are taken kStep at a time");
 
 // Per-tensor descriptor in the workspace.
 struct DescV {
@@ -305,15 +315,15 @@ __device__ __forceinline__ void load_block(const NextTensor& nt, uint64_t gblk, 
     in.gb = bld1(make_rsrc(nt.gaps + b * (kTB / 2), kTB / 2), tid >> 1);
 }
 
-// Output range of a block (or round): elements [lo, lo + nw), 16-element
-// groups counted from base = lo & ~15 (a0 = lo - base).
+// Output range of a block (or round): elements [lo, lo + nw), units of
+// `unit` elements counted from base = lo rounded down to a unit (a0 = lo - base).
 struct BlockGeo {
     uint64_t lo, base, want;
-    uint32_t nw, a0, groups;
+    uint32_t nw, a0, units;
     bool sane;          // lo <= hi <= n
 };
 
-__device__ __forceinline__ BlockGeo block_geo(uint64_t lo_raw, uint64_t hi_raw, uint64_t n)
+__device__ __forceinline__ BlockGeo block_geo(uint64_t lo_raw, uint64_t hi_raw, uint64_t n, uint32_t unit)
 {
     BlockGeo g;
     g.sane = lo_raw <= hi_raw && hi_raw <= n;
@@ -321,30 +331,18 @@ __device__ __forceinline__ BlockGeo block_geo(uint64_t lo_raw, uint64_t hi_raw, 
     g.lo = lo_raw < hi ? lo_raw : hi;
     g.want = hi - g.lo;
     g.nw = g.want < (uint64_t)kStageSyms ? (uint32_t)g.want : (uint32_t)kStageSyms;
-    g.base = g.lo & ~15ull;
+    g.base = g.lo & ~(uint64_t)(unit - 1);
     g.a0 = (uint32_t)(g.lo - g.base);
-    g.groups = (g.a0 + g.nw + 15) >> 4;
+    g.units = (g.a0 + g.nw + unit - 1) / unit;
     return g;
 }
 
-// Raw plane of a group of 16 elements: 16 bytes (BF16) or 8 (E5M2).
-template <int kFmt>
-struct RawOf {
-    using T = uint4;
-    static constexpr uint32_t kGroupBytes = 16;
-};
-template <>
-struct RawOf<ECF8V_E5M2> {
-    using T = uint2;
-    static constexpr uint32_t kGroupBytes = 8;
-};
-
-// The raw plane of the groups of a range (the resource ends with the range,
-// so loads past it read 0 without touching memory).
+// The raw plane of the units of a range, 8 bytes per unit (the resource ends
+// with the range, so loads past it read 0 without touching memory).
 template <int kFmt>
 __device__ __forceinline__ Rsrc raw_rsrc(const uint8_t* raw, const BlockGeo& g)
 {
-    return make_rsrc(raw + (kFmt == ECF8V_BF16 ? g.base : g.base >> 1), (uint64_t)RawOf<kFmt>::kGroupBytes * g.groups);
+    return make_rsrc(raw + (kFmt == ECF8V_BF16 ? g.base : g.base >> 1), 8ull * g.units);
 }
 
 // Output elements from base on, to the end of the tensor.
@@ -355,42 +353,46 @@ __device__ __forceinline__ Rsrc out_rsrc(uint8_t* out, uint64_t base, uint64_t n
     return make_rsrc(out + eb * base, eb * (n - base));
 }
 
+__device__ __forceinline__ uint2 load_raw_unit(Rsrc rr, uint32_t u) { return bld2(rr, 8u * u); }
+
+// The symbols of a unit as staged: 8 bytes (BF16) or 16 (E5M2).
 template <int kFmt>
-__device__ __forceinline__ typename RawOf<kFmt>::T load_raw_group(Rsrc rr, uint32_t g)
+__device__ __forceinline__ uint4 read_unit(const uint8_t* stage, uint32_t u)
+{
+    if constexpr (kFmt == ECF8V_BF16) {
+        const uint2 v = reinterpret_cast<const uint2*>(stage)[u];
+        return make_uint4(v.x, v.y, 0u, 0u);
+    } else {
+        return reinterpret_cast<const uint4*>(stage)[u];
+    }
+}
+template <int kFmt>
+__device__ __forceinline__ void clear_unit(uint8_t* stage, uint32_t u)
 {
     if constexpr (kFmt == ECF8V_BF16)
-        return bld4(rr, 16u * g);
+        reinterpret_cast<uint2*>(stage)[u] = make_uint2(0u, 0u);
     else
-        return bld2(rr, 8u * g);
+        reinterpret_cast<uint4*>(stage)[u] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// The 16 elements of a group from its 16 staged symbol bytes and its raw
-// plane (byte permutes and masks): 8 words (BF16, two elements a word) or 4
-// (E5M2, four a word).
+// The elements of a unit from its staged symbols and its raw plane, as the 4
+// words of its 16 output bytes (byte permutes and masks).
 template <int kFmt>
-struct GroupWords {
-    static constexpr int kWords = kFmt == ECF8V_BF16 ? 8 : 4;
-};
-
-template <int kFmt>
-__device__ __forceinline__ void assemble_group(uint4 sv, typename RawOf<kFmt>::T rv, uint32_t (&o)[GroupWords<kFmt>::kWords])
+__device__ __forceinline__ void assemble_unit(uint4 sv, uint2 rv, uint32_t (&o)[4])
 {
-    const uint32_t S[4] = {sv.x, sv.y, sv.z, sv.w};
     if constexpr (kFmt == ECF8V_BF16) {
-        const uint32_t R[4] = {rv.x, rv.y, rv.z, rv.w};
+        const uint32_t S[2] = {sv.x, sv.y}, R[2] = {rv.x, rv.y};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {     // elements 4q + 2h, 4q + 2h + 1 into one word
-                const uint32_t sel = h ? 0x0c030c02u : 0x0c010c00u;
-                const uint32_t rr = __builtin_amdgcn_perm(0u, R[q], sel);
-                const uint32_t ss = __builtin_amdgcn_perm(0u, S[q], sel);
-                o[2 * q + h] = ((rr & 0x00800080u) << 8) | (ss << 7) | (rr & 0x007F007Fu);
-            }
+        for (int q = 0; q < 4; ++q) {                     // elements 2q, 2q + 1 into word q
+            const uint32_t sel = (q & 1) ? 0x0c030c02u : 0x0c010c00u;
+            const uint32_t rr = __builtin_amdgcn_perm(0u, R[q >> 1], sel);
+            const uint32_t ss = __builtin_amdgcn_perm(0u, S[q >> 1], sel);
+            o[q] = ((rr & 0x00800080u) << 8) | (ss << 7) | (rr & 0x007F007Fu);
         }
     } else {
+        const uint32_t S[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 4; ++q) {                     // elements 4q .. 4q + 3 into word q
             uint32_t t = ((q < 2 ? rv.x : rv.y) >> (16 * (q & 1))) & 0xFFFFu;   // 4 nibbles
             t = (t | (t << 8)) & 0x00FF00FFu;
             t = (t | (t << 4)) & 0x0F0F0F0Fu;                               // one per byte
@@ -399,31 +401,26 @@ __device__ __forceinline__ void assemble_group(uint4 sv, typename RawOf<kFmt>::T
     }
 }
 
-// A whole group: one (E5M2) or two (BF16) 16-byte stores.
+// A whole unit: one 16-byte store.
 template <int kFmt>
-__device__ __forceinline__ void write_group(Rsrc ro, uint32_t g, uint4 sv, typename RawOf<kFmt>::T rv)
+__device__ __forceinline__ void write_unit(Rsrc ro, uint32_t u, uint4 sv, uint2 rv)
 {
-    uint32_t o[GroupWords<kFmt>::kWords];
-    assemble_group<kFmt>(sv, rv, o);
-    if constexpr (kFmt == ECF8V_BF16) {
-        bst4(ro, 32u * g, o[0], o[1], o[2], o[3]);
-        bst4(ro, 32u * g + 16u, o[4], o[5], o[6], o[7]);
-    } else {
-        bst4(ro, 16u * g, o[0], o[1], o[2], o[3]);
-    }
+    uint32_t o[4];
+    assemble_unit<kFmt>(sv, rv, o);
+    bst4(ro, 16u * u, o[0], o[1], o[2], o[3]);
 }
 
-// A ragged group ge of a range (range-relative elements [a0, endo)): the
-// group is assembled whole, its elements inside the range stored one by one.
+// A ragged unit ue of a range (range-relative elements [a0, endo)): the unit
+// is assembled whole, its elements inside the range stored one by one.
 template <int kFmt>
-__device__ __forceinline__ void write_edge(Rsrc ro, uint32_t ge, uint4 sv, typename RawOf<kFmt>::T rv, uint32_t a0,
-                                           uint32_t endo)
+__device__ __forceinline__ void write_edge(Rsrc ro, uint32_t ue, uint4 sv, uint2 rv, uint32_t a0, uint32_t endo)
 {
-    uint32_t o[GroupWords<kFmt>::kWords];
-    assemble_group<kFmt>(sv, rv, o);
+    constexpr uint32_t kE = Unit<kFmt>::kElems;
+    uint32_t o[4];
+    assemble_unit<kFmt>(sv, rv, o);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const uint32_t i = 16u * ge + e;
+    for (uint32_t e = 0; e < kE; ++e) {
+        const uint32_t i = kE * ue + e;
         if (i >= a0 && i < endo) {
             if constexpr (kFmt == ECF8V_BF16)
                 bst2(ro, 2u * i, (uint16_t)(o[e >> 1] >> (16 * (e & 1))));
@@ -434,45 +431,44 @@ __device__ __forceinline__ void write_edge(Rsrc ro, uint32_t ge, uint4 sv, typen
 }
 
 // Write back a range: range-relative elements [a0, endo), element i staged
-// at stage[i].  Lane tid writes the whole groups g = tid + k * kTB with
-// 16-byte stores, the first kPre of them with the raw plane already in rv;
-// lane 0 writes a ragged first group (its raw plane rv[0] when kPre > 0) and
-// lane end_full % kTB a ragged last group (its raw plane tail_raw when
-// kPre > 0) element-wise.  The lane that reads a group from the stage clears it.
+// at stage[i].  Lane tid writes the whole units u = tid + k * kTB with one
+// 16-byte store each, the first kPre of them with the raw plane already in
+// rv; lane 0 writes a ragged first unit (its raw plane rv[0] when kPre > 0)
+// and lane end_full % kTB a ragged last unit (its raw plane tail_raw when
+// kPre > 0) element-wise.  The lane that reads a unit from the stage clears it.
 template <int kFmt, int kTB, int kPre>
 __device__ __forceinline__ void write_back(uint8_t* stage, Rsrc rr, Rsrc ro, uint32_t a0, uint32_t endo, int tid,
-                                           const typename RawOf<kFmt>::T (&rv)[kRawGroups],
-                                           typename RawOf<kFmt>::T tail_raw)
+                                           const uint2 (&rv)[kRawMax], uint2 tail_raw)
 {
+    constexpr uint32_t kE = Unit<kFmt>::kElems;
     const uint32_t first_full = a0 ? 1u : 0u;
-    const uint32_t end_full = endo >> 4;                 // groups [first_full, end_full) are whole
-    const uint32_t groups = (endo + 15) >> 4;
-    uint4* const st16 = reinterpret_cast<uint4*>(stage);
-    uint32_t g = (uint32_t)tid;
+    const uint32_t end_full = endo / kE;                 // units [first_full, end_full) are whole
+    const uint32_t units = (endo + kE - 1) / kE;
+    uint32_t u = (uint32_t)tid;
 #pragma unroll
-    for (int k = 0; k < kPre; ++k, g += kTB) {
-        if (g >= first_full && g < end_full) {
-            const uint4 sv = st16[g];
-            st16[g] = make_uint4(0u, 0u, 0u, 0u);
-            write_group<kFmt>(ro, g, sv, rv[k]);
+    for (int k = 0; k < kPre; ++k, u += kTB) {
+        if (u >= first_full && u < end_full) {
+            const uint4 sv = read_unit<kFmt>(stage, u);
+            clear_unit<kFmt>(stage, u);
+            write_unit<kFmt>(ro, u, sv, rv[k]);
         }
     }
-    for (; g < end_full; g += kTB) {
-        if (g >= first_full) {
-            const uint4 sv = st16[g];
-            st16[g] = make_uint4(0u, 0u, 0u, 0u);
-            write_group<kFmt>(ro, g, sv, load_raw_group<kFmt>(rr, g));
+    for (; u < end_full; u += kTB) {
+        if (u >= first_full) {
+            const uint4 sv = read_unit<kFmt>(stage, u);
+            clear_unit<kFmt>(stage, u);
+            write_unit<kFmt>(ro, u, sv, load_raw_unit(rr, u));
         }
     }
-    if (a0 && tid == 0) {                                // group 0 (which may also be the last)
-        const uint4 sv = st16[0];
-        st16[0] = make_uint4(0u, 0u, 0u, 0u);
-        write_edge<kFmt>(ro, 0u, sv, kPre > 0 ? rv[0] : load_raw_group<kFmt>(rr, 0u), a0, endo);
+    if (a0 && tid == 0) {                                // unit 0 (which may also be the last)
+        const uint4 sv = read_unit<kFmt>(stage, 0u);
+        clear_unit<kFmt>(stage, 0u);
+        write_edge<kFmt>(ro, 0u, sv, kPre > 0 ? rv[0] : load_raw_unit(rr, 0u), a0, endo);
     }
-    if (end_full < groups && end_full >= first_full && (uint32_t)tid == end_full % kTB) {
-        const uint4 sv = st16[end_full];
-        st16[end_full] = make_uint4(0u, 0u, 0u, 0u);
-        write_edge<kFmt>(ro, end_full, sv, kPre > 0 ? tail_raw : load_raw_group<kFmt>(rr, end_full), a0, endo);
+    if (end_full < units && end_full >= first_full && (uint32_t)tid == end_full % kTB) {
+        const uint4 sv = read_unit<kFmt>(stage, end_full);
+        clear_unit<kFmt>(stage, end_full);
+        write_edge<kFmt>(ro, end_full, sv, kPre > 0 ? tail_raw : load_raw_unit(rr, end_full), a0, endo);
     }
 }
 
@@ -521,7 +517,7 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
     constexpr uint32_t kPitch = 4u * kTB;                      // bytes per row
     constexpr int kPitchShift = kTB == 256 ? 5 : (kTB == 128 ? 4 : 3);   // (r & 0xE0) << s == (r >> 5) * kPitch
     static_assert(7 * kPitch <= (uint32_t)kStageBytes, "rows inside the stage");
-    using RawT = typename RawOf<kFmt>::T;
+    constexpr uint32_t kE = Unit<kFmt>::kElems;
     extern __shared__ __align__(16) uint8_t dyn[];
     uint8_t* const stage = dyn;
     uint32_t* const stage32 = reinterpret_cast<uint32_t*>(dyn);
@@ -562,7 +558,7 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
 
     for (; blk < total_blocks; blk += gridDim.x) {
         const BlockIn in = nx;
-        RawT rc[kRawGroups];
+        uint2 rc[kRawMax];
         if (ptens != cur) {
             // every lane is past the previous block's last table read
             const DescV* d = descs + ptens;
@@ -592,7 +588,7 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
         const uint64_t cstart = (b * kTB + tid) * (uint64_t)kChunkBits;
         const uint32_t E = c_T > cstart ? (c_T - cstart < (uint64_t)kChunkBits ? (uint32_t)(c_T - cstart) : (uint32_t)kChunkBits) : 0u;
         const uint32_t gap = (in.gb >> ((tid & 1) * 4)) & 15u;
-        const BlockGeo geo = block_geo(lane_u64(in.off, 0), lane_u64(in.off, 1), c_n);
+        const BlockGeo geo = block_geo(lane_u64(in.off, 0), lane_u64(in.off, 1), c_n, kE);
 
         // prefetch the next block of this workgroup (after the last block the
         // current one is loaded again: unconditional loads keep the wait counts exact)
@@ -611,17 +607,17 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
         bool act = r > rend;
         int nq = 0;                           // four-lookup steps taken (wave-uniform)
 #pragma unroll
-        for (int q = 0; q < kRecords / 4; ++q) {
+        for (int q = 0; q < kRecords / kStep; ++q) {
             if (__builtin_amdgcn_ballot_w64(act) == 0) break;
             nq = q + 1;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < kStep; ++j) {
                 const uint32_t a = col_lo + ((r & 0xE0u) << kPitchShift);
                 const uint32_t wlo = *reinterpret_cast<const uint32_t*>(stage + a);
                 const uint32_t whi = *reinterpret_cast<const uint32_t*>(stage + a + kPitch);
                 const uint32_t e = s_tab[tab_index(__builtin_amdgcn_alignbit(whi, wlo, r), cd, last)];
                 const uint32_t em = act ? e : 0u;
-                rec[4 * q + j] = em;
+                rec[kStep * q + j] = em;
                 lastex = act ? e : lastex;
                 r -= em & 31u;
                 cnt += (em >> 5) & 3u;
@@ -688,27 +684,24 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
             // across the walk, and the loads queued behind the stores)
             const Rsrc rr = raw_rsrc<kFmt>(c_raw, geo);
 #pragma unroll
-            for (int k = 0; k < kRawGroups; ++k) {       // read once: non-temporal
-                if constexpr (kFmt == ECF8V_BF16)
-                    rc[k] = bld4_p<kNonTemporal>(rr, 16u * tid, 16u * k * kTB);
-                else
-                    rc[k] = bld2_p<kNonTemporal>(rr, 8u * tid, 8u * k * kTB);
-            }
-            // and the ragged last group's, for the lane that writes it (other
+            for (int k = 0; k < Unit<kFmt>::kPerLane; ++k)   // read once: non-temporal
+                rc[k] = bld2_p<kNonTemporal>(rr, 8u * tid, 8u * k * kTB);
+            // and the ragged last unit's, for the lane that writes it (other
             // lanes load past the range: no memory access)
-            const uint32_t endo = geo.a0 + geo.nw, end_full = endo >> 4;
-            const bool tail_lane = (endo & 15) && end_full >= (geo.a0 ? 1u : 0u) && (uint32_t)tid == end_full % kTB;
-            const RawT tail_raw = load_raw_group<kFmt>(rr, tail_lane ? end_full : 0x0FFFFFFFu);
+            const uint32_t endo = geo.a0 + geo.nw, end_full = endo / kE;
+            const bool tail_lane = (endo % kE) && end_full >= (geo.a0 ? 1u : 0u) && (uint32_t)tid == end_full % kTB;
+            const uint2 tail_raw = load_raw_unit(rr, tail_lane ? end_full : 0x0FFFFFFFu);
             // ---- replay into the stage
             uint32_t ob = geo.a0 + pos;
 #pragma unroll
-            for (int q = 0; q < kRecords / 4; ++q) {
-                if (q >= nq) break;
+            for (int q = 0; q < kRecords / kStep; ++q) {
+                if (q < nq) {                             // no early exit: the records keep static indices
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t e = rec[4 * q + j];
-                    emit_entry(stage32, ob, e);
-                    ob += (e >> 5) & 3u;
+                    for (int j = 0; j < kStep; ++j) {
+                        const uint32_t e = rec[kStep * q + j];
+                        emit_entry(stage32, ob, e);
+                        ob += (e >> 5) & 3u;
+                    }
                 }
             }
             if (r_rec > rend) {
@@ -727,15 +720,14 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
                 }
             }
             __syncthreads();
-            // ---- write back; every group read is cleared
-            write_back<kFmt, kTB, kRawGroups>(stage, rr, out_rsrc<kFmt>(c_out, geo.base, c_n), geo.a0, endo, tid, rc,
-                                              tail_raw);
+            // ---- write back; every unit read is cleared
+            write_back<kFmt, kTB, Unit<kFmt>::kPerLane>(stage, rr, out_rsrc<kFmt>(c_out, geo.base, c_n), geo.a0, endo,
+                                                        tid, rc, tail_raw);
             // symbols OR-ed past the block's end (by the last lane, or decoded
-            // from the padding after T) lie in the groups up to zend
-            const uint32_t zend0 = (geo.a0 + total + 2u + 16u) >> 4;
-            const uint32_t zend = zend0 < (uint32_t)(kStageBytes / 16) ? zend0 : (uint32_t)(kStageBytes / 16);
-            for (uint32_t g = geo.groups + tid; g < zend; g += kTB)
-                reinterpret_cast<uint4*>(stage)[g] = make_uint4(0u, 0u, 0u, 0u);
+            // from the padding after T) lie in the units up to zend
+            const uint32_t zend0 = (geo.a0 + total + 2u + 16u) / kE;
+            const uint32_t zend = zend0 < (uint32_t)kStageBytes / kE ? zend0 : (uint32_t)kStageBytes / kE;
+            for (uint32_t u = geo.units + tid; u < zend; u += kTB) clear_unit<kFmt>(stage, u);
         } else if (ok) {
             // ---- more than kStageSyms symbols: rounds, each lane walking its
             // chunk again and writing its symbols of the round
@@ -746,7 +738,7 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
             for (uint32_t base = 0; base < total; base += kStageSyms) {
                 const uint32_t lim = total - base < (uint32_t)kStageSyms ? total - base : (uint32_t)kStageSyms;
                 const uint64_t j_start = geo.lo + base;
-                const uint32_t shift = (uint32_t)(j_start & 15);
+                const uint32_t shift = (uint32_t)(j_start & (kE - 1));
                 if (pos < base + lim && pos + cnt > base) {
                     uint32_t p = gap, k = pos;
                     while (p < E && k < base + lim) {
@@ -759,7 +751,7 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
                     }
                 }
                 __syncthreads();
-                const BlockGeo rg = block_geo(j_start, j_start + lim, c_n);
+                const BlockGeo rg = block_geo(j_start, j_start + lim, c_n, kE);
                 write_back<kFmt, kTB, 0>(stage, raw_rsrc<kFmt>(c_raw, rg), out_rsrc<kFmt>(c_out, rg.base, c_n), rg.a0,
                                          rg.a0 + rg.nw, tid, rc, rc[0]);
                 __syncthreads();
