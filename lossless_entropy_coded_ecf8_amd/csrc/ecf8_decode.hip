@@ -103,17 +103,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 template <class T>
 __device__ __forceinline__ T gld(const T* p) { return *(const ECF8_GLOBAL T*)(p); }
-template <class T>
-__device__ __forceinline__ void gst(T* p, const T& v) { *(ECF8_GLOBAL T*)(p) = v; }
 __device__ __forceinline__ uint4 gld4(const void* p)
 {
     const u32x4 v = *(const ECF8_GLOBAL u32x4*)(p);
     return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint2 gld2(const void* p)
-{
-    const u32x2 v = *(const ECF8_GLOBAL u32x2*)(p);
-    return make_uint2(v.x, v.y);
 }
 
 // Buffer resources for the streaming loads and stores of the decode kernel: a

@@ -124,37 +124,6 @@ __global__ __launch_bounds__(256) void ecf8_zero_kernel(uint32_t* p, uint64_t wo
         p[i] = 0u;
 }
 
-// Symbol counts of one lane's 16 bytes as 16-bit fields of 8 words (field
-// (d, f) counts symbol count_symbol(d, f)).  Each element adds 1 << (4 s) to
-// a 64-bit register of 4-bit fields (elements 0..7 and 8..15 in two
-// registers, so no field passes 8); the fields are then widened.  `pad`
-// zero bytes past n were counted as symbol 0 and are taken off.
-__device__ __forceinline__ void lane_counts(const uint32_t (&w)[4], uint32_t pad, uint32_t (&c)[kCountWords])
-{
-    uint64_t A = 0, B = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t e = w[q] & 0x78787878u;                 // exponent fields in place
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t sh = (e >> (8 * k + 1)) & 63u;      // 4 x symbol
-            if (q < 2)
-                A += 1ull << sh;
-            else
-                B += 1ull << sh;
-        }
-    }
-    const uint64_t m8 = 0x0F0F0F0F0F0F0F0Full, m16 = 0x00FF00FF00FF00FFull;
-    const uint64_t even = (A & m8) + (B & m8);                 // byte j: symbol 2j
-    const uint64_t odd = ((A >> 4) & m8) + ((B >> 4) & m8);    // byte j: symbol 2j + 1
-    const uint64_t r[4] = {(even & m16) - pad, odd & m16, (even >> 8) & m16, (odd >> 8) & m16};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        c[2 * q] = (uint32_t)r[q];
-        c[2 * q + 1] = (uint32_t)(r[q] >> 32);
-    }
-}
-
 // Sum of v over the 64 lanes of the wave (uniform): DPP row shifts leave each
 // 16-lane row's total in its last lane; the four row totals are read out.
 __device__ __forceinline__ uint32_t wave_total(uint32_t v)
