@@ -38,10 +38,10 @@
 //     twice is exact.  The stream rows share memory with the staging.
 //   * write back: 16 elements per lane-step: 8 bytes of exponent nibbles from
 //     LDS, 8 bytes of the sign/mantissa plane from HBM (non-temporal loads
-//     issued after the count, in flight during the scan and decode), SWAR
-//     byte assembly, one non-temporal 16-byte store; byte stores only at the
-//     two ragged block edges.  The next block's inputs are taken into
-//     registers before the stores are issued.
+//     issued when the block starts, in flight during the count, scan and
+//     decode), SWAR byte assembly, one non-temporal 16-byte store; byte stores
+//     only at the two ragged block edges.  The next block's inputs are taken
+//     into registers before the stores are issued.
 //   * streaming loads and stores are buffer instructions (SGPR descriptors,
 //     32-bit offsets, hardware range checks); one persistent dispatch walks
 //     all blocks of all tensors of a batch at 6 workgroups per CU.
@@ -619,6 +619,12 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
         const uint32_t a0 = geo.a0, nw = geo.nw, groups = geo.groups;
         const uint64_t want = geo.want;
         const Rsrc nib_blk = nibble_rsrc(c_nib, geo);
+        // the block's sign/mantissa plane, in flight during the count, scan and
+        // decode.  Issued after the previous block's stores (loaded a block
+        // ahead instead, they queued behind those stores and held registers
+        // across two counts) and before the next block's inputs.
+        uint2 nv[kNibPrefetch];
+        load_nibbles<TB>(nib_blk, tid, nv);
 
         // prefetch the next block of this workgroup (after the last block, the
         // current one is re-read: unconditional loads keep the wait counts exact)
@@ -689,13 +695,8 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
             cnt -= ns - keep;
         }
 
-        // the block's sign/mantissa plane, in flight during the scan and the
-        // decode (loaded a block ahead instead, it measured slower: more
-        // registers live across the count, and loads queued behind stores);
         // the next block's inputs, issued at the top, are taken now, before
         // this block's stores
-        uint2 nv[kNibPrefetch];
-        load_nibbles<TB>(nib_blk, tid, nv);
         asm volatile("" ::"v"(nx.sv.x), "v"(nx.la), "v"(nx.gb), "v"((uint32_t)nx.off));
 
         // ---- phase 3: block-wide exclusive scan of the counts
