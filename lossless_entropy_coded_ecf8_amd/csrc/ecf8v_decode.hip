@@ -20,12 +20,19 @@
 // The index of a 32-bit window w is min(max(w >> 22, (w >> 16) - cdelta),
 // last) with cdelta = 63 * p_long: one branch-free expression picks the
 // region, and the clamp sends any window past the codes to an entry that
-// decodes nothing.  Codewords longer than 10 bits cover at most 1/8 of the
+// decodes nothing.  As w >> 22 < 1024 <= last, the two bounds are one
+// median-of-three.  Codewords longer than 10 bits cover at most 1/8 of the
 // space when there are at most 256 symbols, so a table has at most 9089
 // entries.
-// Entry bits: 4..0 bits consumed (1 for no codeword), 6..5 whole codewords
-// decoded (0..3), 7 set for no codeword, 31..8 the symbols as bytes, first
-// symbol lowest, bytes past the count zero.
+// An entry holds the bits consumed (1 for no codeword), the whole codewords
+// decoded (0..3), a no-codeword flag, and the symbols in bytes 1..3, first
+// symbol lowest, bytes past the count zero.  BF16 symbols fill their bytes,
+// so byte 0 holds the bits consumed (4..0), the count (6..5) and the flag
+// (7).  E5M2 symbols sit in bits 6..2 of their bytes, where the output byte
+// takes the exponent: byte 0 is the bits consumed alone (one byte-select
+// subtract advances the walk), the count is in bits 9..8 and the flag in bit
+// 15, around the first symbol (the write-back overwrites bits 7, 1 and 0 of
+// every staged byte with the sign and mantissa).
 //
 // Decode kernel: persistent workgroups of TB lanes walk the global block
 // index over all tensors; each block's stream chunks, gaps and offsets are
@@ -87,6 +94,16 @@ struct Unit {
 };
 constexpr int kRawMax = 8;                  // the larger of the two kPerLane
 constexpr int kTableSlices = (kTabMax + 255) / 256;
+
+// Entry fields per format (see the table description above).
+template <int kFmt>
+struct Entry {
+    static constexpr uint32_t kNb = kFmt == ECF8V_BF16 ? 31u : 255u;       // bits consumed: e & kNb
+    static constexpr int kCnt = kFmt == ECF8V_BF16 ? 5 : 8;               // codewords: (e >> kCnt) & 3
+    static constexpr uint32_t kInv = kFmt == ECF8V_BF16 ? 0x80u : 0x8000u;   // no codeword
+    static constexpr int kSymShift = kFmt == ECF8V_BF16 ? 0 : 2;          // symbol i: (e >> (8 + 8 i + kSymShift))
+    static constexpr uint32_t kSym = kFmt == ECF8V_BF16 ? 255u : 31u;     //   & kSym
+};
 static_assert(kRecords % kStep == 0, "records are taken kStep at a time");
 
 // Per-tensor descriptor in the workspace.
@@ -207,7 +224,8 @@ __device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l)
 // places symbol s in canonical order (its rank and the left-justified start
 // of its code range); an entry is then decoded greedily from its known bits
 // (10 in region 1, 16 in region 2) by binary search over the code starts.
-__global__ __launch_bounds__(256) void ecf8v_table_kernel(const DescV* __restrict__ descs, uint32_t* __restrict__ tables)
+__global__ __launch_bounds__(256) void ecf8v_table_kernel(const DescV* __restrict__ descs, uint32_t* __restrict__ tables,
+                                                          uint32_t fmt)
 {
     __shared__ uint32_t s_start[ECF8V_MAX_SYM];
     __shared__ uint8_t s_len[ECF8V_MAX_SYM];
@@ -262,7 +280,11 @@ __global__ __launch_bounds__(256) void ecf8v_table_kernel(const DescV* __restric
         ++ns;
         pos += ll;
     }
-    tables[(uint64_t)blockIdx.x * kTabMax + idx] = ns ? (pos | (ns << 5) | (sy << 8)) : 0x81u;
+    const bool bf = fmt == ECF8V_BF16;
+    const uint32_t cnt_shift = bf ? (uint32_t)Entry<ECF8V_BF16>::kCnt : (uint32_t)Entry<ECF8V_E5M2>::kCnt;
+    const uint32_t sym_shift = bf ? (uint32_t)Entry<ECF8V_BF16>::kSymShift : (uint32_t)Entry<ECF8V_E5M2>::kSymShift;
+    const uint32_t inv = 1u | (bf ? Entry<ECF8V_BF16>::kInv : Entry<ECF8V_E5M2>::kInv);
+    tables[(uint64_t)blockIdx.x * kTabMax + idx] = ns ? (pos | (ns << cnt_shift) | (sy << (8 + sym_shift))) : inv;
 }
 
 __global__ __launch_bounds__(64) void ecf8v_clear_kernel(unsigned long long* status, uint32_t words)
@@ -375,28 +397,38 @@ __device__ __forceinline__ void clear_unit(uint8_t* stage, uint32_t u)
         reinterpret_cast<uint4*>(stage)[u] = make_uint4(0u, 0u, 0u, 0u);
 }
 
+// Bit-field insert: the bits of a where m is set, of b elsewhere.  One
+// three-input bitwise instruction (truth table 0xca: m ? a : b); written as
+// (a & m) | (b & ~m) the compiler splits it into masks and ORs.
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b)
+{
+    return __builtin_amdgcn_bitop3_b32(m, a, b, 0xca);
+}
+
 // The elements of a unit from its staged symbols and its raw plane, as the 4
-// words of its 16 output bytes (byte permutes and masks).
+// words of its 16 output bytes: byte permutes, shifts and bit-field inserts.
 template <int kFmt>
 __device__ __forceinline__ void assemble_unit(uint4 sv, uint2 rv, uint32_t (&o)[4])
 {
     if constexpr (kFmt == ECF8V_BF16) {
+        // element = raw bit 7 (sign) << 15 | exponent << 7 | raw bits 6..0
         const uint32_t S[2] = {sv.x, sv.y}, R[2] = {rv.x, rv.y};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {                     // elements 2q, 2q + 1 into word q
-            const uint32_t sel = (q & 1) ? 0x0c030c02u : 0x0c010c00u;
-            const uint32_t rr = __builtin_amdgcn_perm(0u, R[q >> 1], sel);
-            const uint32_t ss = __builtin_amdgcn_perm(0u, S[q >> 1], sel);
-            o[q] = ((rr & 0x00800080u) << 8) | (ss << 7) | (rr & 0x007F007Fu);
+            const uint32_t rr = __builtin_amdgcn_perm(0u, R[q >> 1], (q & 1) ? 0x03030202u : 0x01010000u);
+            const uint32_t ss = __builtin_amdgcn_perm(0u, S[q >> 1], (q & 1) ? 0x0c030c02u : 0x0c010c00u);
+            o[q] = bfi(0x807F807Fu, rr, ss << 7);         // each half: raw byte twice | exponent byte at bit 7
         }
     } else {
+        // element = nibble bit 2 (sign) << 7 | exponent << 2 | nibble bits 1..0;
+        // the staged bytes hold the exponent in bits 6..2 already (bits 7, 1,
+        // 0 may carry entry flags: the two inserts overwrite them)
         const uint32_t S[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {                     // elements 4q .. 4q + 3 into word q
-            uint32_t t = ((q < 2 ? rv.x : rv.y) >> (16 * (q & 1))) & 0xFFFFu;   // 4 nibbles
-            t = (t | (t << 8)) & 0x00FF00FFu;
-            t = (t | (t << 4)) & 0x0F0F0F0Fu;                               // one per byte
-            o[q] = ((t & 0x04040404u) << 5) | ((S[q] & 0x1F1F1F1Fu) << 2) | (t & 0x03030303u);
+            const uint32_t y = __builtin_amdgcn_perm(0u, q < 2 ? rv.x : rv.y, (q & 1) ? 0x03030202u : 0x01010000u);
+            const uint32_t t = bfi(0x00FF00FFu, y, y >> 4);   // nibble j in bits 3..0 of byte j
+            o[q] = bfi(0x80808080u, t << 5, bfi(0x03030303u, t, S[q]));
         }
     }
 }
@@ -493,23 +525,36 @@ __device__ __forceinline__ uint32_t reg_window(const uint32_t (&w)[5], uint32_t 
     return (uint32_t)(((((uint64_t)hi << 32) | lo) << (p & 31)) >> 32);
 }
 
+// min(max(a, b), last) for a = win >> 22 <= 1023 < last: the median of the
+// three (one instruction).
 __device__ __forceinline__ uint32_t tab_index(uint32_t win, int cd, int last)
 {
     const int a = (int)(win >> (32 - kWin));
     const int b = (int)(win >> 16) - cd;
-    const int m = a > b ? a : b;
-    return (uint32_t)(m < last ? m : last);
+    int m;
+    asm("v_med3_i32 %0, %1, %2, %3" : "=v"(m) : "v"(b), "v"(a), "s"(last));
+    return (uint32_t)m;
 }
 
-// Waves per SIMD the register allocation must allow (measured best: BF16
-// keeps its 16 raw-plane registers per lane unspilled at 5, E5M2 fits 6).
-template <int kFmt>
-constexpr int kMinWaves = kFmt == ECF8V_BF16 ? 5 : 6;
-
-// Dynamic LDS: the stage (the stream rows live inside it) | code lengths
-// (256 bytes) | table (tab_n entries).
+// Waves per SIMD the register allocation must allow (measured best with 256
+// lanes: BF16 keeps its 16 raw-plane registers per lane unspilled at 5, E5M2
+// fits 6); smaller workgroups are held lower by the stage's LDS (16 KB per
+// workgroup of any size, 160 KB per compute unit of 4 SIMDs).
 template <int kFmt, int kTB>
-__global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<kFmt>))) void ecf8v_decode_kernel(
+constexpr int kMinWaves = (kFmt == ECF8V_BF16 ? 5 : 6) < (160 * 1024 / (kStageBytes + 64)) * (kTB / 64) / 4
+                              ? (kFmt == ECF8V_BF16 ? 5 : 6)
+                              : (160 * 1024 / (kStageBytes + 64)) * (kTB / 64) / 4;
+
+// Static LDS: the stage (the stream rows live inside it) at address 0, so a
+// row address is a lane offset OR-ed with a row offset; then the wave sums.
+// Dynamic LDS: code lengths (256 bytes) | table (tab_n entries).
+template <int kWaves>
+struct StageLds {
+    uint8_t stage[kStageBytes];
+    uint32_t wsum[kWaves];
+};
+template <int kFmt, int kTB>
+__global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<kFmt, kTB>))) void ecf8v_decode_kernel(
     const DescV* __restrict__ descs, int count, const uint32_t* __restrict__ tables, uint64_t total_blocks,
     unsigned long long* __restrict__ status, uint32_t tab_n)
 {
@@ -518,12 +563,14 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
     constexpr int kPitchShift = kTB == 256 ? 5 : (kTB == 128 ? 4 : 3);   // (r & 0xE0) << s == (r >> 5) * kPitch
     static_assert(7 * kPitch <= (uint32_t)kStageBytes, "rows inside the stage");
     constexpr uint32_t kE = Unit<kFmt>::kElems;
+    using En = Entry<kFmt>;
+    __shared__ __align__(16) StageLds<kWaves> s_lds;
     extern __shared__ __align__(16) uint8_t dyn[];
-    uint8_t* const stage = dyn;
-    uint32_t* const stage32 = reinterpret_cast<uint32_t*>(dyn);
-    uint8_t* const s_len = dyn + kStageBytes;
-    uint32_t* const s_tab = reinterpret_cast<uint32_t*>(dyn + kStageBytes + ECF8V_MAX_SYM);
-    __shared__ uint32_t s_wsum[kWaves];
+    uint8_t* const stage = s_lds.stage;
+    uint32_t* const stage32 = reinterpret_cast<uint32_t*>(s_lds.stage);
+    uint32_t* const s_wsum = s_lds.wsum;
+    uint8_t* const s_len = dyn;
+    uint32_t* const s_tab = reinterpret_cast<uint32_t*>(dyn + ECF8V_MAX_SYM);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -612,28 +659,28 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
             nq = q + 1;
 #pragma unroll
             for (int j = 0; j < kStep; ++j) {
-                const uint32_t a = col_lo + ((r & 0xE0u) << kPitchShift);
+                const uint32_t a = col_lo | ((r & 0xE0u) << kPitchShift);   // col_lo < kPitch
                 const uint32_t wlo = *reinterpret_cast<const uint32_t*>(stage + a);
                 const uint32_t whi = *reinterpret_cast<const uint32_t*>(stage + a + kPitch);
                 const uint32_t e = s_tab[tab_index(__builtin_amdgcn_alignbit(whi, wlo, r), cd, last)];
                 const uint32_t em = act ? e : 0u;
                 rec[kStep * q + j] = em;
                 lastex = act ? e : lastex;
-                r -= em & 31u;
-                cnt += (em >> 5) & 3u;
+                r -= em & En::kNb;
+                cnt += (em >> En::kCnt) & 3u;
                 inv |= em;
                 act = r > rend;
             }
         }
         const uint32_t r_rec = r;            // where the recorded lookups end
         while (r > rend) {
-            const uint32_t a = col_lo + ((r & 0xE0u) << kPitchShift);
+            const uint32_t a = col_lo | ((r & 0xE0u) << kPitchShift);
             const uint32_t wlo = *reinterpret_cast<const uint32_t*>(stage + a);
             const uint32_t whi = *reinterpret_cast<const uint32_t*>(stage + a + kPitch);
             const uint32_t e = s_tab[tab_index(__builtin_amdgcn_alignbit(whi, wlo, r), cd, last)];
             lastex = e;
-            r -= e & 31u;
-            cnt += (e >> 5) & 3u;
+            r -= e & En::kNb;
+            cnt += (e >> En::kCnt) & 3u;
             inv |= e;
         }
         // the lane's rows are stage memory from here on: leave them cleared
@@ -642,14 +689,15 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
         if (r != r0) {
             // the last lookup started `room` bits before the chunk end: keep
             // its codewords that start before it
-            const uint32_t ns = (lastex >> 5) & 3u;
-            const uint32_t room = r + (lastex & 31u) - rend;
-            const uint32_t l1 = s_len[(lastex >> 8) & 255u], l2 = s_len[(lastex >> 16) & 255u];
+            const uint32_t ns = (lastex >> En::kCnt) & 3u;
+            const uint32_t room = r + (lastex & En::kNb) - rend;
+            const uint32_t l1 = s_len[(lastex >> (8 + En::kSymShift)) & En::kSym];
+            const uint32_t l2 = s_len[(lastex >> (16 + En::kSymShift)) & En::kSym];
             const uint32_t keep = 1u + (ns >= 2 && l1 < room ? 1u : 0u) + (ns >= 3 && l1 + l2 < room ? 1u : 0u);
             cnt -= ns - keep;
         }
         // a window with no codeword spoils the block's total
-        if (inv & 0x80u) cnt += 1u << 22;
+        if (inv & En::kInv) cnt += 1u << 22;
 
         // ---- block scan of the counts
         uint32_t x = cnt;
@@ -700,7 +748,7 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
                     for (int j = 0; j < kStep; ++j) {
                         const uint32_t e = rec[kStep * q + j];
                         emit_entry(stage32, ob, e);
-                        ob += (e >> 5) & 3u;
+                        ob += (e >> En::kCnt) & 3u;
                     }
                 }
             }
@@ -715,8 +763,8 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
                 while (r2 > rend) {
                     const uint32_t e = s_tab[tab_index(reg_window(w, 160u - r2), cd, last)];
                     emit_entry(stage32, ob, e);
-                    ob += (e >> 5) & 3u;
-                    r2 -= e & 31u;
+                    ob += (e >> En::kCnt) & 3u;
+                    r2 -= e & En::kNb;
                 }
             }
             __syncthreads();
@@ -743,11 +791,11 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
                     uint32_t p = gap, k = pos;
                     while (p < E && k < base + lim) {
                         const uint32_t e = s_tab[tab_index(reg_window(w, p), cd, last)];
-                        const uint32_t ns = (e >> 5) & 3u;
+                        const uint32_t ns = (e >> En::kCnt) & 3u;
                         for (uint32_t i = 0; i < ns; ++i, ++k)
                             if (k >= base && k < base + lim && k < pos + cnt)
                                 stage[k - base + shift] = (uint8_t)(e >> (8 + 8 * i));
-                        p += e & 31u;
+                        p += e & En::kNb;
                     }
                 }
                 __syncthreads();
@@ -806,7 +854,7 @@ int kernel_slots(uint32_t fmt, uint32_t tb, uint32_t lds, uint32_t* out)
     return ECF8_OK;
 }
 
-uint32_t decode_lds_bytes(uint32_t tab_n) { return (uint32_t)(kStageBytes + ECF8V_MAX_SYM) + 4 * tab_n; }
+uint32_t decode_lds_bytes(uint32_t tab_n) { return (uint32_t)ECF8V_MAX_SYM + 4 * tab_n; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -870,7 +918,7 @@ extern "C" int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, u
     if (count)
         hipLaunchKernelGGL(ecf8v_table_kernel, dim3((uint32_t)count, (uint32_t)kTableSlices), dim3(256), 0, st,
                            reinterpret_cast<const DescV*>(ws + desc_offset()),
-                           reinterpret_cast<uint32_t*>(ws + table_offset(count)));
+                           reinterpret_cast<uint32_t*>(ws + table_offset(count)), fmt);
     if (hipGetLastError() != hipSuccess || hipStreamSynchronize(st) != hipSuccess) return ECF8_ERR_HIP;
     plan->workspace = workspace;
     plan->workspace_bytes = workspace_bytes;
