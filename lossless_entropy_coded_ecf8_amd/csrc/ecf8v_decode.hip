@@ -479,6 +479,10 @@ __device__ __forceinline__ void write_back(uint8_t* stage, Rsrc rr, Rsrc ro, uin
     uint32_t u = (uint32_t)tid;
 #pragma unroll
     for (int k = 0; k < kPre; ++k, u += kTB) {
+        // E5M2 runs 7 waves per SIMD (72 registers): the unit indices are
+        // recomputed per block rather than kept across it, where the register
+        // allocator would put them in scratch
+        if constexpr (kFmt == ECF8V_E5M2) asm volatile("" : "+v"(u));
         if (u >= first_full && u < end_full) {
             const uint4 sv = read_unit<kFmt>(stage, u);
             clear_unit<kFmt>(stage, u);
@@ -537,12 +541,13 @@ __device__ __forceinline__ uint32_t tab_index(uint32_t win, int cd, int last)
 }
 
 // Waves per SIMD the register allocation must allow (measured best with 256
-// lanes: BF16 keeps its 16 raw-plane registers per lane unspilled at 5, E5M2
-// fits 6); smaller workgroups are held lower by the stage's LDS (16 KB per
-// workgroup of any size, 160 KB per compute unit of 4 SIMDs).
+// lanes: BF16 keeps its 16 raw-plane registers per lane unspilled at 5 (at 6
+// a record spills), E5M2 fits 7); smaller workgroups are held lower by the
+// stage's LDS (16 KB per workgroup of any size, 160 KB per compute unit of 4
+// SIMDs).
 template <int kFmt, int kTB>
-constexpr int kMinWaves = (kFmt == ECF8V_BF16 ? 5 : 6) < (160 * 1024 / (kStageBytes + 64)) * (kTB / 64) / 4
-                              ? (kFmt == ECF8V_BF16 ? 5 : 6)
+constexpr int kMinWaves = (kFmt == ECF8V_BF16 ? 5 : 7) < (160 * 1024 / (kStageBytes + 64)) * (kTB / 64) / 4
+                              ? (kFmt == ECF8V_BF16 ? 5 : 7)
                               : (160 * 1024 / (kStageBytes + 64)) * (kTB / 64) / 4;
 
 // Static LDS: the stage (the stream rows live inside it) at address 0, so a
@@ -709,7 +714,7 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
                        q2 = __builtin_amdgcn_readlane(x, 47), q3 = __builtin_amdgcn_readlane(x, 63);
         const int row = lane >> 4;
         x += (row >= 1 ? q0 : 0u) + (row >= 2 ? q1 : 0u) + (row >= 3 ? q2 : 0u);
-        if (lane == 0) s_wsum[wave] = q0 + q1 + q2 + q3;
+        if (lane == 0) s_wsum[__builtin_amdgcn_readfirstlane(tid) >> 6] = q0 + q1 + q2 + q3;   // this wave's
         __syncthreads();
         uint32_t before = 0, total = 0;
 #pragma unroll
