@@ -41,17 +41,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the decode kernel source with comments and blank lines removed."""
+def kernel_source_hash(source: str = "ecf8_decode.hip") -> str:
+    """Hash of a kernel source file with comments and blank lines removed."""
     import re
-    p = os.path.join(ROOT, "lossless_entropy_coded_ecf8_amd", "csrc", "ecf8_decode.hip")
+    p = os.path.join(ROOT, "lossless_entropy_coded_ecf8_amd", "csrc", source)
     text = re.sub(r"//[^\n]*", "", open(p).read())
     code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def load_traffic(workload: str, kernel_hash: str, launches_bytes: float):
-    """HBM traffic per launch from committed rocprofv3 counter summaries, if they match this kernel."""
+def load_traffic(workload: str, kernel_hash: str, launches_bytes: float = 0.0):
+    """HBM traffic per launch from committed rocprofv3 counter summaries, if they match this kernel
+    (`workload` names the summary: traffic_<workload>.json under profiles/)."""
     p = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(p):
         return None
@@ -326,6 +327,8 @@ def variant_bench(args):
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / args.steps
     eb = 2 if fmt == "bf16" else 1
+    khash = kernel_source_hash("ecf8v_decode.hip")
+    traffic = load_traffic("variant_%s_%s" % (fmt, args.workload), khash)
     n = sum(h.n for h in hs)
     read = sum(h.compressed_bytes() for h in hs)
     written = n * eb
@@ -341,8 +344,8 @@ def variant_bench(args):
            "roofline": {"bound": "hbm", "achieved": round((read + written) / (ms * 1e-3) / 1e9, 2),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round((read + written) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                        "traffic": None, "kernel": "ecf8v_decode_kernel (+ table kernel, one run)",
-                        "algorithmic_bytes": read + written}}
+                        "traffic": traffic, "kernel": "ecf8v_decode_kernel (+ table kernel, one run)",
+                        "algorithmic_bytes": read + written, "kernel_sha": khash}}
     print(json.dumps(res), flush=True)
 
 
