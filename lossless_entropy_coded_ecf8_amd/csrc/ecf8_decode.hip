@@ -44,7 +44,9 @@
 //     into registers before the stores are issued.
 //   * streaming loads and stores are buffer instructions (SGPR descriptors,
 //     32-bit offsets, hardware range checks); one persistent dispatch walks
-//     all blocks of all tensors of a batch at 6 workgroups per CU.
+//     all blocks of all tensors of a batch at 6 workgroups per CU;
+//   * wave priority rises through a block (count 1, scan and decode 2,
+//     write-back 3), so the wave of a SIMD nearest its stores issues first.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -634,7 +636,12 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
         load_block(nt, nbe, tid, nx);
         ptens = nt.t;
 
-        __builtin_amdgcn_s_setprio(3);
+        // Wave priorities rise through the block: count 1, scan and decode 2,
+        // write-back 3, then 0 until the next count.  Among the waves of a SIMD
+        // (each from another workgroup, at another point of its block), the one
+        // nearest its stores issues first, so stores leave earlier and the
+        // next blocks' loads start sooner (4% faster than one raised count).
+        __builtin_amdgcn_s_setprio(1);
         // ---- phase 2: count the codewords that start inside [gap, E)
         // The walk runs in steps of four lookups with one wave-uniform exit test
         // per step; a lane that has passed E keeps looking up at its final
@@ -672,7 +679,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
             r -= e & 0xFFu;
             cnt4 += (e >> 8) & 0xFFu;
         }
-        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_s_setprio(2);
         // the lane's rows are staging memory from here on: leave them cleared
 #pragma unroll
         for (int k = 0; k < S; ++k) col[(S - k) * TB] = 0u;
@@ -739,6 +746,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
         }
         __syncthreads();
 
+        __builtin_amdgcn_s_setprio(3);
         // ---- phase 5: write back [lo, lo + nw) as 16-element groups
         if (tid == 0 && (want != total || !c_ok)) atomicAdd(status, 1ull);
         const Rsrc out_blk = make_rsrc(c_out + base, c_n - base);
@@ -775,6 +783,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
             if (k >= (uint32_t)kNibPrefetch) nm = bld2(nib_blk, 8u * end_full);
             write_edge(s_out, out_blk, end_full, nm, a0, endo);
         }
+        __builtin_amdgcn_s_setprio(0);
         // clear the staging the decode wrote: groups [0, zend) cover every
         // nibble OR-ed in, the codewords a last lane decodes past the end included
         // (each group is cleared by the lane that read it above)

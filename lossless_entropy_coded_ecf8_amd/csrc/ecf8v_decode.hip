@@ -60,6 +60,8 @@
 //     group clears it for the next block.
 // Blocks of more than 16384 symbols (codes averaging under 2 bits) take a
 // slower path: rounds of 16384 symbols, each lane walking its chunk again.
+// Wave priority rises through a block (walk 1, scan and replay 2, write-back
+// 3), so the wave of a SIMD nearest its stores issues first.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -650,6 +652,10 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
         load_block<kTB>(nt, nbe, tid, nx);
         ptens = nt.t;
 
+        // Wave priorities rise through the block: walk 1, scan and replay 2,
+        // write-back 3, then 0 until the next walk, so the wave of a SIMD
+        // nearest its stores issues first.
+        __builtin_amdgcn_s_setprio(1);
         // ---- counting walk, recording each lookup's entry
         const int cd = c_cd, last = c_last;
         const uint32_t rend = 160u - E;
@@ -688,6 +694,7 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
             cnt += (e >> En::kCnt) & 3u;
             inv |= e;
         }
+        __builtin_amdgcn_s_setprio(2);
         // the lane's rows are stage memory from here on: leave them cleared
 #pragma unroll
         for (int k = 0; k < 5; ++k) col[k * kTB] = 0u;
@@ -773,9 +780,11 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
                 }
             }
             __syncthreads();
+            __builtin_amdgcn_s_setprio(3);
             // ---- write back; every unit read is cleared
             write_back<kFmt, kTB, Unit<kFmt>::kPerLane>(stage, rr, out_rsrc<kFmt>(c_out, geo.base, c_n), geo.a0, endo,
                                                         tid, rc, tail_raw);
+            __builtin_amdgcn_s_setprio(0);
             // symbols OR-ed past the block's end (by the last lane, or decoded
             // from the padding after T) lie in the units up to zend
             const uint32_t zend0 = (geo.a0 + total + 2u + 16u) / kE;
