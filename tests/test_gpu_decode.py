@@ -135,6 +135,44 @@ def test_batched_mixed_tensors_and_buffer_reuse():
     assert plan2.status() == 0
 
 
+def test_split_calls_and_decode_without_tables():
+    """ecf8_build_tables then ecf8_decode_blocks equals ecf8_decode_run, on a batch whose tensors'
+    tables differ in size (each workgroup reloads its LDS table, in 16-byte loads, whenever its
+    next block belongs to another tensor); ecf8_decode_blocks on a plan whose tables were never
+    built flags every block, ends, and writes nothing outside the tensors' ranges."""
+    d = dev()
+    kinds = [("stable", 500_001), ("long12x6", 300_000), ("fib15", 200_003), ("two", 150_000),
+             ("uniform4", 262_144), ("gauss", 400_000)]
+    xs, encs, offs, off = [], [], [], 0
+    for i, (k, n) in enumerate(kinds):
+        x, L = make_input(k, n, 2000 + i)
+        xs.append(x)
+        encs.append(E.encode(x, lengths=L).to(d))
+        offs.append(off)
+        off += (n + 15) // 16 * 16 + 32
+    inside = np.zeros(off + 64, dtype=bool)
+    for o, (_, n) in zip(offs, kinds):
+        inside[o:o + n] = True
+    # tables never built: every block is flagged, no byte outside the ranges is touched
+    out0 = torch.full((off + 64,), CANARY, dtype=torch.uint8, device=d)
+    plan0 = E.DecodePlan(encs, out=out0, offsets=offs)
+    plan0.decode_blocks()
+    assert plan0.status() == int(plan0.plan.total_blocks)
+    b0 = out0.cpu().numpy()
+    assert (b0[~inside] == CANARY).all()
+    # the two calls in order decode every tensor exactly
+    out = torch.full((off + 64,), CANARY, dtype=torch.uint8, device=d)
+    plan = E.DecodePlan(encs, out=out, offsets=offs)
+    plan.build_tables()
+    plan.decode_blocks()
+    torch.cuda.synchronize()
+    assert plan.status() == 0
+    b = out.cpu().numpy()
+    assert (b[~inside] == CANARY).all()
+    for i, x in enumerate(xs):
+        assert np.array_equal(b[offs[i]:offs[i] + x.size], x), kinds[i]
+
+
 def test_corrupt_block_offset_is_flagged_and_contained():
     """Checked mode: a wrong blk_off entry is reported, and no byte outside [0, n) is written."""
     d = dev()
