@@ -218,7 +218,7 @@ def pipeline_bench(args):
            "value": results[-1][main_cfg + "_vs_resident"], "unit": "ratio", "n_gpus": 1,
            "higher_is_better": False, "dtype": "fp8 e4m3 GEMM, u8 decode", "data": "synthetic",
            "config": {"workload": WORKLOAD_TEXT[args.workload], "layers": len(layers), "repeats": args.repeats,
-                      "gemm": "torch._scaled_mm" if P._scaled_mm_ok(d) else "bf16 matmul"},
+                      "gemm": "torch._scaled_mm (hipBLASLt FP8 E4M3)"},
            "memory": {"resident_fp8_bytes": resident, "compressed_bytes": compressed, "pool_bytes": pool,
                       "ecf8_total_bytes": compressed + pool},
            "results": results}

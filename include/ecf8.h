@@ -284,6 +284,18 @@ int ecf8_alpha_hat(const float* w, uint64_t n, double gamma, double* alpha_hat);
  * α <= 0. */
 double ecf8_exponent_entropy_bound(double alpha);
 
+/* ------------------------------ measurement ------------------------------ */
+
+/* A plain streaming copy of `bytes` bytes from src to dst (device memory,
+ * both 16-byte aligned, not overlapping): dwordx4 loads and stores, four in
+ * flight per lane, non-temporal hints, a persistent grid of 8 workgroups per
+ * compute unit.  It is not part of the method: the decode is bound by HBM
+ * traffic, and this copy is the ceiling its traffic is compared with (its
+ * rate, and the FETCH_SIZE / WRITE_SIZE counters it reads for a known size,
+ * calibrate the decode's measurements).  Asynchronous on hip_stream.
+ * Errors: ECF8_ERR_ARG (NULL or misaligned with bytes > 0), ECF8_ERR_HIP. */
+int ecf8_hbm_copy(const void* src, void* dst, uint64_t bytes, void* hip_stream);
+
 /* Human-readable name of an error code (static string). */
 const char* ecf8_strerror(int code);
 

@@ -97,8 +97,8 @@ EXPORTS = ["ecf8_histogram", "ecf8_codebook_from_freq", "ecf8_build_codebook", "
            "ecf8_decode_prepare", "ecf8_decode_run", "ecf8_build_tables", "ecf8_decode_blocks",
            "ecf8_decode_batched", "ecf8_decode",
            "ecf8_decode_status", "ecf8_histogram_device", "ecf8_meta_from_freq", "ecf8_encode_workspace_bytes",
-           "ecf8_encode_device", "ecf8_alpha_hat", "ecf8_exponent_entropy_bound", "ecf8_strerror",
-           "ecf8_version"]
+           "ecf8_encode_device", "ecf8_alpha_hat", "ecf8_exponent_entropy_bound", "ecf8_hbm_copy",
+           "ecf8_strerror", "ecf8_version"]
 
 _lib = None
 
@@ -142,6 +142,7 @@ def lib() -> ctypes.CDLL:
         "ecf8_encode_device": (i, [vp, ctypes.POINTER(Meta), vp, vp, vp, vp, vp, ctypes.c_uint64, vp]),
         "ecf8_alpha_hat": (i, [vp, ctypes.c_uint64, ctypes.c_double, ctypes.POINTER(ctypes.c_double)]),
         "ecf8_exponent_entropy_bound": (ctypes.c_double, [ctypes.c_double]),
+        "ecf8_hbm_copy": (i, [vp, vp, ctypes.c_uint64, vp]),
         "ecf8_strerror": (ctypes.c_char_p, [i]),
         "ecf8_version": (i, []),
     }
@@ -352,12 +353,49 @@ def _stream_handle(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _workspace(count: int, device, workspace=None):
+def _torch_stream(stream):
+    import torch
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _workspace(count: int, device, workspace=None, stream=None):
+    """A caller's workspace if it is large enough, else a new one.  A new one is
+    allocated while `stream` (the launch stream) is current, so that the caching
+    allocator does not hand its memory to other work before the launch ends."""
     import torch
     need = workspace_bytes(count)
     if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(_torch_stream(stream)):
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    else:
+        _check_buffer(workspace, device, "workspace")
     return workspace
+
+
+def _check_buffer(t, device, what: str):
+    """A device buffer handed to the library: uint8, contiguous, on `device`."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % what)
+    if t.dtype != torch.uint8 or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous uint8 tensor (got %s, contiguous=%s)"
+                         % (what, t.dtype, t.is_contiguous()))
+    if t.device != torch.device(device):
+        raise ValueError("%s is on %s, the encoded tensors on %s" % (what, t.device, device))
+
+
+def _check_out_ranges(out, offsets, sizes, device):
+    """out must hold every tensor's range [offset, offset + n) and the ranges must not overlap."""
+    _check_buffer(out, device, "out")
+    spans = sorted((int(o), int(o) + int(n)) for o, n in zip(offsets, sizes) if int(n) > 0)
+    for o, n in zip(offsets, sizes):
+        if int(o) < 0:
+            raise ValueError("negative output offset %d" % int(o))
+    if spans and spans[-1][1] > out.numel():
+        raise ValueError("out holds %d bytes; the tensors need %d" % (out.numel(), max(e for _, e in spans)))
+    for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+        if b0 < a1:
+            raise ValueError("output ranges [%d, %d) and [%d, %d) overlap" % (a0, a1, b0, b1))
 
 
 def encode_workspace(n: int, device):
@@ -430,15 +468,22 @@ def encode_device(x, lengths=None, chunk_bytes: int = DEFAULT_CHUNK_BYTES,
 
 
 def decode(enc: DeviceEncoded, out=None, workspace=None, stream=None):
-    """Single-tensor GPU decode (ecf8_decode).  Returns the uint8 output tensor."""
+    """Single-tensor GPU decode (ecf8_decode).  Returns the uint8 output tensor.
+
+    out, if given, must be a contiguous uint8 tensor of exactly n bytes on the
+    encoded tensor's device (its size is passed as n and checked against the
+    metadata).  Buffers allocated here are allocated on the launch stream."""
     import torch
     dev = enc.stream.device
     if out is None:
-        out = torch.empty(max(enc.n, 1), dtype=torch.uint8, device=dev)[: enc.n]
-    ws = _workspace(1, dev, workspace)
+        with torch.cuda.stream(_torch_stream(stream)):
+            out = torch.empty(max(enc.n, 1), dtype=torch.uint8, device=dev)[: enc.n]
+    else:
+        _check_buffer(out, dev, "out")
+    ws = _workspace(1, dev, workspace, stream)
     s = enc.c_stream()
     m = enc.meta
-    _check(lib().ecf8_decode(ctypes.byref(s), ctypes.byref(m), ctypes.c_void_p(out.data_ptr()), enc.n,
+    _check(lib().ecf8_decode(ctypes.byref(s), ctypes.byref(m), ctypes.c_void_p(out.data_ptr()), out.numel(),
                              ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_handle(stream)),
            "ecf8_decode")
     return out
@@ -468,8 +513,14 @@ class DecodePlan:
         else:
             total = max([o + e.n for o, e in zip(offsets, self.encs)] + [0])
         self.offsets = list(offsets)
-        self.out = out if out is not None else torch.empty(max(total, 1), dtype=torch.uint8, device=dev)
-        self.workspace = _workspace(len(self.encs), dev, workspace)
+        if len(self.offsets) != len(self.encs):
+            raise ValueError("%d offsets for %d tensors" % (len(self.offsets), len(self.encs)))
+        if out is None:
+            with torch.cuda.stream(_torch_stream(stream)):
+                out = torch.empty(max(total, 1), dtype=torch.uint8, device=dev)
+        _check_out_ranges(out, self.offsets, [e.n for e in self.encs], dev)
+        self.out = out
+        self.workspace = _workspace(len(self.encs), dev, workspace, stream)
         arr = (TensorDesc * max(1, len(self.encs)))()
         for i, (e, o) in enumerate(zip(self.encs, self.offsets)):
             arr[i].s = e.c_stream()
@@ -483,16 +534,30 @@ class DecodePlan:
                "ecf8_decode_prepare")
         if workgroups is not None:
             self.plan.grid = max(1, min(int(self.plan.grid), int(workgroups)))
+        # the descriptor upload is ordered on the prepare stream; a launch on
+        # another stream first waits for it (once per stream)
+        self._prep_stream = _torch_stream(stream)
+        self._ready = torch.cuda.Event()
+        self._ready.record(self._prep_stream)
+        self._synced = {self._prep_stream.cuda_stream}
+
+    def _launch_stream(self, stream):
+        s = _torch_stream(stream)
+        if s.cuda_stream not in self._synced:
+            s.wait_event(self._ready)
+            self._synced.add(s.cuda_stream)
+        return ctypes.c_void_p(s.cuda_stream)
 
     def run(self, stream=None):
-        _check(lib().ecf8_decode_run(ctypes.byref(self.plan), _stream_handle(stream)), "ecf8_decode_run")
+        _check(lib().ecf8_decode_run(ctypes.byref(self.plan), self._launch_stream(stream)), "ecf8_decode_run")
         return self.out
 
     def build_tables(self, stream=None):
-        _check(lib().ecf8_build_tables(ctypes.byref(self.plan), _stream_handle(stream)), "ecf8_build_tables")
+        _check(lib().ecf8_build_tables(ctypes.byref(self.plan), self._launch_stream(stream)), "ecf8_build_tables")
 
     def decode_blocks(self, stream=None):
-        _check(lib().ecf8_decode_blocks(ctypes.byref(self.plan), _stream_handle(stream)), "ecf8_decode_blocks")
+        _check(lib().ecf8_decode_blocks(ctypes.byref(self.plan), self._launch_stream(stream)),
+               "ecf8_decode_blocks")
         return self.out
 
     def status(self, stream=None) -> int:
@@ -506,6 +571,16 @@ class DecodePlan:
 
     def view(self, i: int):
         return self.out[self.offsets[i]: self.offsets[i] + self.encs[i].n]
+
+
+def hbm_copy(src, dst, stream=None):
+    """Plain streaming device copy src -> dst (ecf8_hbm_copy), the HBM ceiling the decode is compared with."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst holds fewer bytes than src")
+    _check(lib().ecf8_hbm_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n,
+                               _stream_handle(stream)), "ecf8_hbm_copy")
+    return dst
 
 
 def decode_batched(encs: Sequence[DeviceEncoded], out=None, offsets=None, workspace=None, stream=None):
@@ -680,10 +755,19 @@ class DecodePlanV:
         else:
             total = max([o + e.n * e.elem_bytes for o, e in zip(offsets, self.encs)] + [0])
         self.offsets = list(offsets)
-        self.out = out if out is not None else torch.empty(max(total, 1), dtype=torch.uint8, device=dev)
+        if len(self.offsets) != len(self.encs):
+            raise ValueError("%d offsets for %d tensors" % (len(self.offsets), len(self.encs)))
+        if out is None:
+            with torch.cuda.stream(_torch_stream(stream)):
+                out = torch.empty(max(total, 1), dtype=torch.uint8, device=dev)
+        _check_out_ranges(out, self.offsets, [e.n * e.elem_bytes for e in self.encs], dev)
+        self.out = out
         need = int(lib().ecf8v_workspace_bytes(len(self.encs)))
         if workspace is None or workspace.numel() < need:
-            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+            with torch.cuda.stream(_torch_stream(stream)):
+                workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        else:
+            _check_buffer(workspace, dev, "workspace")
         self.workspace = workspace
         arr = (TensorDescV * max(1, len(self.encs)))()
         for i, (e, o) in enumerate(zip(self.encs, self.offsets)):
@@ -700,9 +784,15 @@ class DecodePlanV:
                                           _stream_handle(stream), ctypes.byref(self.plan)), "ecf8v_decode_prepare")
         if workgroups is not None:
             self.plan.grid = max(1, min(int(self.plan.grid), int(workgroups)))
+        self._prep_stream = _torch_stream(stream)
+        self._ready = torch.cuda.Event()
+        self._ready.record(self._prep_stream)
+        self._synced = {self._prep_stream.cuda_stream}
+
+    _launch_stream = DecodePlan._launch_stream
 
     def run(self, stream=None):
-        _check(lib().ecf8v_decode_run(ctypes.byref(self.plan), _stream_handle(stream)), "ecf8v_decode_run")
+        _check(lib().ecf8v_decode_run(ctypes.byref(self.plan), self._launch_stream(stream)), "ecf8v_decode_run")
         return self.out
 
     def status(self, stream=None) -> int:

@@ -170,8 +170,12 @@ __device__ __forceinline__ void bst1(Rsrc r, uint32_t off, uint8_t v)
 constexpr int kTableSlices = (kTableMax + kTableThreads - 1) / kTableThreads;   // 9
 
 __global__ __launch_bounds__(kTableThreads) void ecf8_table_kernel(DevDesc* __restrict__ descs,
-                                                                   uint32_t* __restrict__ tables)
+                                                                   uint32_t* __restrict__ tables,
+                                                                   unsigned long long* __restrict__ status)
 {
+    // each run's block check counts from zero (the decode dispatch that follows
+    // on the same stream adds to it)
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0ull;
     __shared__ uint32_t s_start[16];   // canonical order: left-justified start of the k-th codeword range
     __shared__ uint32_t s_len[16];
     __shared__ uint32_t s_sym[16];
@@ -330,6 +334,22 @@ __device__ __forceinline__ void write_edge(const uint32_t* s_out, Rsrc out_blk, 
         if (q >= kb && q < ke) bst1(out_blk, e0 + q, (uint8_t)(w[q >> 2] >> (8 * (q & 3))));
 }
 
+// Table index of a 32-bit window: max(prefix11, prefix16 - cd), clamped to
+// the last entry.  For every complete code the unclamped index is already
+// below the built entry count; the clamp matters for the one incomplete code
+// that validates (a single symbol of length 1), whose windows starting with a
+// 1 bit are no codeword: there it selects an entry that consumes one bit and
+// decodes nothing (every built entry consumes at least one bit), so a
+// corrupted single-symbol stream still ends each walk and is counted by the
+// block check.  prefix11 <= 2047 < kTableMax - 1, so the clamp is one
+// v_med3_i32 in place of the v_max_i32.
+__device__ __forceinline__ int table_index(uint32_t win, int cd)
+{
+    const int a = (int)(win >> (32 - kWin));
+    const int b = (int)(win >> 16) - cd;
+    return min(max(a, b), kTableMax - 1);
+}
+
 // One table lookup at stream position r (r = 192 - bit position within the
 // lane's chunk): 32-bit window from the lane's two LDS rows, then the index
 // max(prefix11, prefix16 - cd) into the packed table.
@@ -343,8 +363,7 @@ __device__ __forceinline__ uint32_t lookup(const char* s_stream_b, const uint32_
     const uint32_t w1 = *reinterpret_cast<const uint32_t*>(s_stream_b + a);
     const uint32_t w0 = *reinterpret_cast<const uint32_t*>(s_stream_b + a + 4u * kLanes);
     const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, r);
-    const int idx = max((int)(win >> (32 - kWin)), (int)(win >> 16) - cd);
-    return s_tx[idx];
+    return s_tx[table_index(win, cd)];
 }
 
 // OR the symbols of one table entry, as packed nibbles, into the zeroed
@@ -741,8 +760,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
             r = r_rec;
             while (r > rend) {
                 const uint32_t win = reg_window(w, 192u - r);
-                const int idx = max((int)(win >> (32 - kWin)), (int)(win >> 16) - cd);
-                const uint32_t ex = s_tx[idx];
+                const uint32_t ex = s_tx[table_index(win, cd)];
                 emit_symbols(s_out, ob, ex);
                 ob += (ex >> 8) & 0xFFu;
                 r -= ex & 0xFFu;
@@ -916,8 +934,9 @@ extern "C" int ecf8_build_tables(const ecf8_plan* plan, void* hip_stream)
     unsigned char* ws = static_cast<unsigned char*>(plan->workspace);
     DevDesc* dd = reinterpret_cast<DevDesc*>(ws + desc_offset());
     uint32_t* tables = reinterpret_cast<uint32_t*>(ws + table_offset((int)plan->count));
+    auto* status = reinterpret_cast<unsigned long long*>(ws);
     hipLaunchKernelGGL(ecf8_table_kernel, dim3(plan->count, kTableSlices), dim3(kTableThreads), 0,
-                       reinterpret_cast<hipStream_t>(hip_stream), dd, tables);
+                       reinterpret_cast<hipStream_t>(hip_stream), dd, tables, status);
     return hipGetLastError() == hipSuccess ? ECF8_OK : ECF8_ERR_HIP;
 }
 

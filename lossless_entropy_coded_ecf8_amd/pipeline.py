@@ -61,17 +61,24 @@ def linear_fp8(x_fp8: torch.Tensor, x_scale: torch.Tensor, w_u8: torch.Tensor, w
                bias: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16) -> torch.Tensor:
     """y = (x * x_scale) @ (w * w_scale)^T + bias for FP8 E4M3 x (T x K) and w (N x K).
 
-    hipBLASLt FP8 GEMM through torch._scaled_mm where it runs; otherwise the
-    operands are widened to bfloat16 for a plain GEMM.
+    The FP8 GEMM is hipBLASLt's, through torch._scaled_mm.  There is no other
+    GEMM path: where torch._scaled_mm does not run FP8 E4M3 this raises.
     """
     w = w_u8.view(torch.float8_e4m3fn)
-    if _scaled_mm_ok(x_fp8.device):
-        y = torch._scaled_mm(x_fp8, w.t(), scale_a=x_scale, scale_b=w_scale, out_dtype=out_dtype)
-    else:
-        y = ((x_fp8.to(torch.bfloat16) @ w.to(torch.bfloat16).t()).float() * (x_scale * w_scale)).to(out_dtype)
+    if not _scaled_mm_ok(x_fp8.device):
+        raise RuntimeError("torch._scaled_mm does not run FP8 E4M3 GEMMs on %s" % x_fp8.device)
+    y = torch._scaled_mm(x_fp8, w.t(), scale_a=x_scale, scale_b=w_scale, out_dtype=out_dtype)
     if bias is not None:
         y = y + bias.to(out_dtype)
     return y
+
+
+def check_decode(plan: binding.DecodePlan, stream=None):
+    """Checked mode: synchronize `stream` and raise if the last run of `plan`
+    flagged any block (its decoded symbol count disagreed with blk_off)."""
+    bad = plan.status(stream)
+    if bad:
+        raise binding.Ecf8Error(-5, "ECF8 decode (%d corrupt blocks)" % bad)
 
 
 class ECF8Linear(torch.nn.Module):
@@ -85,8 +92,12 @@ class ECF8Linear(torch.nn.Module):
     """
 
     def __init__(self, weight_u8: torch.Tensor, scale: float, bias: Optional[torch.Tensor] = None,
-                 device="cuda"):
+                 device="cuda", checked: bool = False):
+        """checked: after each decode into the layer's own buffer, synchronize
+        and raise if the decode's block check flagged a block (a corrupt
+        stream, gap or block offset) instead of feeding the GEMM."""
         super().__init__()
+        self.checked = checked
         if weight_u8.dim() != 2 or weight_u8.dtype != torch.uint8:
             raise ValueError("weight_u8 must be a 2-D uint8 tensor of FP8 E4M3 bytes")
         self.out_features, self.in_features = (int(s) for s in weight_u8.shape)
@@ -122,6 +133,8 @@ class ECF8Linear(torch.nn.Module):
             self._own = torch.empty(self.numel, dtype=torch.uint8, device=self.device)
             self._own_plan = self.plan_into(self._own, stream=stream)
         self._own_plan.run(stream)
+        if self.checked:
+            check_decode(self._own_plan, stream)
         return self._own.view(self.out_features, self.in_features)
 
     def forward(self, x_fp8: torch.Tensor, x_scale: torch.Tensor,
@@ -144,7 +157,11 @@ class DecodePipeline:
     """
 
     def __init__(self, layers: Sequence[ECF8Linear], slots: int = 3, ahead: int = 2,
-                 workgroups: Optional[int] = None):
+                 workgroups: Optional[int] = None, checked: bool = False):
+        """checked: at the end of each run, synchronize and raise if any layer's
+        decode flagged a block (every plan has its own workspace, so each
+        layer's block check is read separately)."""
+        self.checked = checked
         if not layers:
             raise ValueError("no layers")
         if ahead < 0 or (ahead > 0 and ahead > slots - 1) or slots < 1:
@@ -179,6 +196,7 @@ class DecodePipeline:
             for i in range(L):
                 self.plans[i].run(main)
                 outs.append(self.layers[i](xs[i], x_scales[i], weight_u8=self.slot(i)))
+            self._check(main)
             return outs
         side = self.side
         side.wait_stream(main)          # inputs and the pool are ready on the caller's stream
@@ -196,4 +214,10 @@ class DecodePipeline:
             outs.append(self.layers[i](xs[i], x_scales[i], weight_u8=self.slot(i)))
             self.used[i].record(main)
         main.wait_stream(side)
+        self._check(main)
         return outs
+
+    def _check(self, stream):
+        if self.checked:
+            for p in self.plans:
+                check_decode(p, stream)

@@ -74,6 +74,9 @@ def lib():
         L.oracle_check_layout.argtypes = [_u8p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
                                           _intp, ctypes.c_uint32, ctypes.c_uint32, _u8p, _u64p]
         L.oracle_check_layout.restype = ctypes.c_int64
+        L.oracle_chunk_count.argtypes = [_u8p, ctypes.c_uint64, ctypes.c_uint64, _intp, ctypes.c_uint32,
+                                         ctypes.c_uint64, ctypes.c_uint32]
+        L.oracle_chunk_count.restype = ctypes.c_int64
         # format variants (ecf8v_oracle.c)
         L.oraclev_nsym.argtypes = [ctypes.c_int]
         L.oraclev_nsym.restype = ctypes.c_int
@@ -198,6 +201,32 @@ def check_layout(stream, n: int, total_bits: int, lengths, chunk_bytes: int, tb:
     L = np.ascontiguousarray(np.asarray(lengths, dtype=np.intc))
     return int(lib().oracle_check_layout(_p(stream, _u8p), stream.size, n, total_bits, _p(L, _intp),
                                          chunk_bytes, tb, _p(gaps, _u8p), _p(blk, _u64p)))
+
+
+def chunk_count(stream, total_bits: int, lengths, chunk_bytes: int, t: int, gap: int) -> int:
+    """Codewords a thread counts in chunk t from stored gap `gap` (ECF8 blog §3.2.1 count step);
+    -1 on an invalid codeword."""
+    stream = _c8(stream)
+    L = np.ascontiguousarray(np.asarray(lengths, dtype=np.intc))
+    return int(lib().oracle_chunk_count(_p(stream, _u8p), stream.size, total_bits, _p(L, _intp), chunk_bytes,
+                                        t, gap))
+
+
+def block_counts(stream, gaps, total_bits: int, lengths, chunk_bytes: int, tb: int, n_blocks: int):
+    """Per block, the sum of its chunks' counts from their stored gaps (what a block-wide reduction of
+    the count step gives); None for a block with an invalid codeword."""
+    gaps = _c8(gaps)
+    out = []
+    for b in range(n_blocks):
+        tot = 0
+        for t in range(b * tb, (b + 1) * tb):
+            c = chunk_count(stream, total_bits, lengths, chunk_bytes, t, (int(gaps[t >> 1]) >> (4 * (t & 1))) & 15)
+            if c < 0:
+                tot = None
+                break
+            tot += c
+        out.append(tot)
+    return out
 
 
 # ---- format variants: BF16 (DFloat11 layout) and FP8 E5M2 (ecf8v_oracle.c) ----

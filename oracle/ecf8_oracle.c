@@ -266,6 +266,32 @@ uint64_t oracle_decode(const uint8_t* stream, uint64_t stream_bytes, const uint8
     return oracle_decode_range(stream, stream_bytes, nibbles, len, 0, 0, n, out);
 }
 
+/* [ECF8 blog §3.2.1] the count step of the parallel decode, bit-serial: the
+ * thread that owns chunk t starts at its stored gap (bit 8Ct + gap) and
+ * decodes codewords one bit at a time; it counts every codeword that starts
+ * before the end of its chunk, min(8C(t+1), T).  A chunk whose start is at or
+ * past T counts nothing.  The stored gap is taken as given (it may be
+ * corrupt), so this is also what a decoder that trusts it finds.  Returns the
+ * count, or -1 if a codeword is invalid (possible only for an incomplete
+ * code) or runs past the stream. */
+int64_t oracle_chunk_count(const uint8_t* stream, uint64_t stream_bytes, uint64_t total_bits,
+                           const int len[OR_NSYM], uint32_t chunk_bytes, uint64_t t, uint32_t gap)
+{
+    uint32_t code[OR_NSYM];
+    if (oracle_canonical_codes(len, code) != 0) return -1;
+    uint64_t chunk_bits = 8ull * chunk_bytes;
+    uint64_t begin = chunk_bits * t;
+    uint64_t end = begin + chunk_bits;
+    if (end > total_bits) end = total_bits;
+    uint64_t pos = begin + gap;
+    int64_t count = 0;
+    while (pos < end) {
+        if (or_read_symbol(stream, stream_bytes, &pos, len, code) < 0) return -1;
+        count++;
+    }
+    return count;
+}
+
 /* Re-derive gaps and block offsets from a bit walk of an existing stream and
  * compare them with the stored ones.  Returns 0 if all agree, else 1 + the
  * index of the first mismatching chunk (gaps) or -(1 + block) (offsets). */

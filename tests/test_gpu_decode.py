@@ -193,6 +193,129 @@ def test_corrupt_block_offset_is_flagged_and_contained():
     assert np.array_equal(b[16 + lo2:16 + n], x[lo2:])
 
 
+def decode_plan_with_canaries(denc, d):
+    """Run a one-tensor plan into a canary-guarded buffer; returns (plan, host bytes of the buffer)."""
+    n = denc.n
+    buf = torch.full((n + 64,), CANARY, dtype=torch.uint8, device=d)
+    plan = E.DecodePlan([denc], out=buf[16:16 + n], offsets=[0])
+    plan.run()
+    bad = plan.status()
+    return plan, bad, buf
+
+
+def expected_bad_blocks(stream, gaps, enc):
+    """Blocks whose count-step total (oracle, from the stored gaps) disagrees with blk_off."""
+    m = enc.meta
+    bc = oracle.block_counts(stream, gaps, int(m.total_bits), enc.lengths, int(m.chunk_bytes),
+                             int(m.threads_per_block), int(m.n_blocks))
+    want = np.diff(enc.blk_off.astype(np.int64))
+    return [b for b, c in enumerate(bc) if c is None or c != want[b]]
+
+
+def check_contained(buf, x, enc, bad_blocks):
+    """Canaries intact; every block outside bad_blocks decodes exactly."""
+    n = x.size
+    b = buf.cpu().numpy()
+    assert (b[:16] == CANARY).all() and (b[16 + n:] == CANARY).all(), "decode wrote outside [0, n)"
+    blk = enc.blk_off.astype(np.int64)
+    for k in range(int(enc.meta.n_blocks)):
+        if k not in bad_blocks:
+            assert np.array_equal(b[16 + blk[k]:16 + blk[k + 1]], x[blk[k]:blk[k + 1]]), ("block", k)
+
+
+def test_corrupt_gap_is_flagged_and_contained():
+    """Checked mode (ECF8 blog §5.3: wrong output -> check the gap synchronisation): a corrupted gap
+    nibble desynchronises one lane's walk.  The blocks the device flags are exactly those whose
+    count-step totals, recomputed by the oracle from the corrupted gaps, disagree with blk_off; nothing
+    is written outside [0, n); every other block decodes exactly."""
+    d = dev()
+    x, _ = make_input("stable", 400_000, 11)
+    enc = E.encode(x)
+    TB = int(enc.meta.threads_per_block)
+    assert enc.meta.n_blocks >= 4
+    for t in (TB + 37, 2 * TB + 200):
+        g0 = (int(enc.gaps[t >> 1]) >> (4 * (t & 1))) & 15
+        for delta in range(1, 16):
+            gaps = enc.gaps.copy()
+            g1 = (g0 + delta) % 16
+            gaps[t >> 1] = (gaps[t >> 1] & (0xF0 if t % 2 == 0 else 0x0F)) | (g1 << (4 * (t & 1)))
+            want_bad = expected_bad_blocks(enc.stream, gaps, enc)
+            if want_bad:
+                break
+        assert want_bad == [t // TB]
+        denc = enc.to(d)
+        denc.gaps.copy_(torch.from_numpy(gaps).to(d))
+        plan, bad, buf = decode_plan_with_canaries(denc, d)
+        assert bad == len(want_bad), (t, g0, g1)
+        check_contained(buf, x, enc, want_bad)
+
+
+def test_corrupt_stream_byte_is_flagged_and_contained():
+    """A corrupted stream byte (a complete code: every bit string still parses) changes the codewords
+    one or two lanes find; the device flags exactly the blocks whose oracle count-step totals change,
+    writes nothing outside [0, n), and decodes every other block exactly.  A later run on the repaired
+    stream reports no corrupt block (the counter restarts with every run)."""
+    d = dev()
+    x, _ = make_input("stable", 400_000, 12)
+    enc = E.encode(x)
+    C, TB = int(enc.meta.chunk_bytes), int(enc.meta.threads_per_block)
+    for pos in (C * TB + 16 * 5 + 3, 3 * C * TB + 16 * 100 + 9):
+        for flip in (0x01, 0x10, 0x80, 0xFF, 0x5A):
+            stream = enc.stream.copy()
+            stream[pos] ^= flip
+            want_bad = expected_bad_blocks(stream, enc.gaps, enc)
+            if want_bad:
+                break
+        assert want_bad == [pos // (C * TB)]
+        denc = enc.to(d)
+        denc.stream.copy_(torch.from_numpy(stream).to(d))
+        plan, bad, buf = decode_plan_with_canaries(denc, d)
+        assert bad == len(want_bad), (pos, flip)
+        check_contained(buf, x, enc, want_bad)
+        denc.stream.copy_(torch.from_numpy(enc.stream).to(d))
+        plan.run()
+        assert plan.status() == 0
+        assert np.array_equal(buf.cpu().numpy()[16:16 + x.size], x)
+
+
+def test_corrupt_single_symbol_stream_is_flagged_and_contained():
+    """The one incomplete code that validates (a single symbol, code '0'): a 1 bit in its stream is no
+    codeword.  The decode table maps it to an entry that consumes the bit and decodes nothing, so the
+    walk ends, the chunk counts one codeword fewer and the block is flagged; nothing is written outside
+    [0, n) and the other blocks decode exactly."""
+    d = dev()
+    n = 300_000
+    x, _ = make_input("single", n, 3)
+    enc = E.encode(x)
+    C, TB = int(enc.meta.chunk_bytes), int(enc.meta.threads_per_block)
+    assert enc.meta.n_blocks >= 3 and sum(1 for l in enc.lengths if l) == 1
+    stream = enc.stream.copy()
+    stream[C * TB + 777] |= 0x08                     # one bit, block 1
+    stream[2 * C * TB + 5] = 0xFF                    # eight bits, block 2
+    denc = enc.to(d)
+    denc.stream.copy_(torch.from_numpy(stream).to(d))
+    plan, bad, buf = decode_plan_with_canaries(denc, d)
+    assert bad == 2
+    check_contained(buf, x, enc, [1, 2])
+
+
+def test_out_buffer_checks():
+    """The binding rejects an output buffer that is too small, not uint8, or whose ranges overlap, and a
+    single-tensor decode whose output size is not n."""
+    d = dev()
+    x, _ = make_input("stable", 10_000, 13)
+    e = E.encode(x).to(d)
+    with pytest.raises(ValueError):
+        E.DecodePlan([e], out=torch.empty(x.size - 1, dtype=torch.uint8, device=d), offsets=[0])
+    with pytest.raises(ValueError):
+        E.DecodePlan([e], out=torch.empty(x.size, dtype=torch.int16, device=d), offsets=[0])
+    with pytest.raises(ValueError):
+        E.DecodePlan([e, e], out=torch.empty(3 * x.size, dtype=torch.uint8, device=d), offsets=[0, x.size - 16])
+    with pytest.raises(E.Ecf8Error) as ei:
+        E.decode(e, out=torch.empty(x.size + 16, dtype=torch.uint8, device=d))
+    assert ei.value.code == -2
+
+
 def test_unsupported_and_misaligned_arguments():
     d = dev()
     x, _ = make_input("stable", 10_000, 8)

@@ -224,6 +224,68 @@ def test_gaps_and_block_offsets_by_definition(seed):
                                enc["gaps"], enc["blk_off"]) == 0
 
 
+def set_gap(gaps, t, v):
+    g = gaps.copy()
+    g[t >> 1] = (g[t >> 1] & (0xF0 if t % 2 == 0 else 0x0F)) | (v << (4 * (t & 1)))
+    return g
+
+
+def test_check_layout_reports_the_first_corrupt_gap_and_offset():
+    """oracle.check_layout names what it finds: t + 1 for a stored gap that is not the offset of chunk
+    t's first codeword start (an interior chunk, a block's first chunk, a chunk past T), and -(b + 1) for
+    a block offset that is not the count of codewords before block b (an interior and the final one)."""
+    x = synth.small_stable(30_000, 1.7, 21)
+    C, TB = 4, 64
+    enc = oracle.encode(x, chunk_bytes=C, tb=TB)
+    n, T, L = x.size, enc["total_bits"], enc["lengths"]
+    assert enc["n_blocks"] >= 4 and enc["n_blocks"] * TB > enc["n_chunks"]
+    chk = lambda gaps, blk: oracle.check_layout(enc["stream"], n, T, L, C, TB, gaps, blk)
+    assert chk(enc["gaps"], enc["blk_off"]) == 0
+    gaps_bf, _ = brute_force_layout(x, L, C, TB)
+    for t in (5, 2 * TB, 3 * TB + 17, enc["n_chunks"] - 1, enc["n_blocks"] * TB - 1):
+        bad = (gaps_bf[t] + 1) % 16
+        assert chk(set_gap(enc["gaps"], t, bad), enc["blk_off"]) == t + 1, t
+    for b in (1, 2, enc["n_blocks"]):
+        blk = enc["blk_off"].copy()
+        blk[b] += 1
+        assert chk(enc["gaps"], blk) == -(b + 1), b
+    # with both corrupt, the walk meets the earlier one first
+    blk = enc["blk_off"].copy()
+    blk[3] -= 1
+    assert chk(set_gap(enc["gaps"], 3 * TB + 17, (gaps_bf[3 * TB + 17] + 3) % 16), blk) == -(3 + 1)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_chunk_counts_by_definition(seed):
+    """The count step from stored gaps (oracle.chunk_count) equals, per chunk, the number of codeword
+    starts in [8Ct, min(8C(t+1), T)) counted by brute force; per block the counts sum to the block-offset
+    difference.  A gap moved off its codeword changes the count the way a bit walk from there does."""
+    rng = np.random.default_rng(90 + seed)
+    n = int(rng.integers(500, 6000))
+    x = synth.small_stable(n, 1.5 + 0.1 * seed, seed) if seed % 2 else synth.random_bytes(n, seed)
+    C, TB = [(4, 64), (8, 64)][seed % 2]
+    enc = oracle.encode(x, chunk_bytes=C, tb=TB)
+    L = enc["lengths"]
+    e = (x >> 3) & 15
+    lens = np.asarray(L)[e]
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    T = enc["total_bits"]
+    gaps = [(int(enc["gaps"][t >> 1]) >> (4 * (t & 1))) & 15 for t in range(enc["n_blocks"] * TB)]
+    for t in range(enc["n_blocks"] * TB):
+        lo, hi = 8 * C * t, min(8 * C * (t + 1), T)
+        want = int(((starts >= lo) & (starts < hi)).sum()) if lo < T else 0
+        assert oracle.chunk_count(enc["stream"], T, L, C, t, gaps[t]) == want, t
+    bc = oracle.block_counts(enc["stream"], enc["gaps"], T, L, C, TB, enc["n_blocks"])
+    assert bc == np.diff(enc["blk_off"].astype(np.int64)).tolist()
+    # a gap one codeword later: one fewer codeword counted in that chunk
+    t = next(t for t in range(1, enc["n_chunks"] - 1)
+             if gaps[t] + int(lens[np.searchsorted(starts, 8 * C * t + gaps[t])]) < 16
+             and 8 * C * t + gaps[t] + int(lens[np.searchsorted(starts, 8 * C * t + gaps[t])]) < 8 * C * (t + 1))
+    j = int(np.searchsorted(starts, 8 * C * t + gaps[t]))
+    c0 = oracle.chunk_count(enc["stream"], T, L, C, t, gaps[t])
+    assert oracle.chunk_count(enc["stream"], T, L, C, t, gaps[t] + int(lens[j])) == c0 - 1
+
+
 def test_sentinel_gap_for_chunk_without_codeword_start():
     """A last chunk that holds only the tail of the final codeword gets gap = T - 8Ct."""
     # lengths: symbol 0 -> 1 bit, symbol 1 -> 2 bits, symbol 2,3 -> 3 bits ... craft T = 33

@@ -18,11 +18,12 @@ import torch
 import oracle
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "bf16_worked_example.txt")
+GOLDEN_E5M2 = os.path.join(os.path.dirname(__file__), "golden", "e5m2_worked_example.txt")
 
 
-def read_golden():
+def read_golden(path=GOLDEN):
     d = {}
-    for line in open(GOLDEN):
+    for line in open(path):
         line = line.strip()
         if not line or line.startswith("#"):
             continue
@@ -171,3 +172,87 @@ def test_bf16_gaussian_compresses_to_about_eleven_bits():
     e = oracle.v_encode("bf16", x)
     bits = (e["total_bits"] + 8 * x.size) / x.size
     assert 10.3 < bits < 11.2, bits
+
+
+def test_e5m2_worked_example():
+    """Hand-worked E5M2 example (tests/golden/e5m2_worked_example.txt): symbol (b >> 2) & 31, the raw
+    nibble (s << 2) | m in the E4M3 nibble layout, canonical codes, stream bytes and T.  The byte values
+    are also checked against torch's own E5M2 cast of the listed floats."""
+    g = read_golden(GOLDEN_E5M2)
+    x = np.array([int(v, 16) for v in g["values"]], dtype=np.uint8)
+    fl = torch.tensor([float(v) for v in g["floats"]]).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(fl, x)
+    assert [int(s) for s in g["symbols"]] == [int((v >> 2) & 31) for v in x]
+    L = oracle.v_lengths("e5m2", x)
+    want = {int(a): int(b) for a, b in (kv.split(":") for kv in g["lengths"])}
+    assert {int(s): int(L[s]) for s in np.nonzero(L)[0]} == want
+    codes = oracle.v_canonical_codes(L)
+    for kv in g["codes"]:
+        s, bits = kv.split(":")
+        assert int(codes[int(s)]) == int(bits, 2) and int(L[int(s)]) == len(bits)
+    e = oracle.v_encode("e5m2", x)
+    assert e["total_bits"] == int(g["total_bits"][0])
+    assert int(e["stream"][0]) == int(g["stream"][0], 16) and not e["stream"][1:].any()
+    raw = [int(v, 16) for v in g["raw"]]
+    assert [int(v) for v in e["raw"][:len(raw)]] == raw and not e["raw"][len(raw):].any()
+    assert e["blk_off"].tolist() == [0, x.size]
+    assert np.array_equal(oracle.v_decode("e5m2", e["stream"], e["raw"], x.size, e["lengths"]), x)
+
+
+def v_symbols(fmt, x):
+    x = np.asarray(x)
+    return ((x.astype(np.int64) >> 7) & 255) if fmt == "bf16" else ((x.astype(np.int64) >> 2) & 31)
+
+
+def brute_force_layout_v(fmt, x, lengths, C, TB):
+    """Gaps and block offsets from the definitions (ECF8 blog §3.2.1 per-thread gap), by brute force over
+    the codeword start positions: gap_t = (first start >= 8Ct, T counting as a start) - 8Ct for 8Ct < T,
+    else 0; blk_off_b = number of starts before 8*C*TB*b; blk_off[n_blocks] = n."""
+    lens = np.asarray(lengths)[v_symbols(fmt, x)]
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]) if len(lens) else np.zeros(0, np.int64)
+    T = int(lens.sum())
+    nc = -(-T // (8 * C))
+    nb = -(-nc // TB)
+    gaps = []
+    for t in range(nb * TB):
+        s0 = 8 * C * t
+        if s0 >= T:
+            gaps.append(0)
+            continue
+        later = starts[starts >= s0]
+        gaps.append(int(min(later.min(), T) if later.size else T) - s0)
+    blk = [int((starts < 8 * C * TB * b).sum()) for b in range(nb)] + [len(lens)]
+    return gaps, blk
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "e5m2"])
+@pytest.mark.parametrize("seed", range(6))
+def test_variant_gaps_and_block_offsets_by_definition(fmt, seed):
+    """Every chunk's gap and every block offset of oraclev_encode equal a brute-force recomputation from
+    codeword starts, interior chunks included, at several (C, TB) and sizes."""
+    rng = np.random.default_rng(700 + seed)
+    n = int(rng.integers(1, 4000))
+    C, TB = [(4, 64), (8, 64), (16, 64)][seed % 3]
+    if fmt == "bf16":
+        x = bf16_weights(n, seed, scale=0.02 if seed % 2 else 3.0)
+    else:
+        x = torch.from_numpy((rng.standard_normal(n) * (10.0 ** rng.uniform(-3, 3, n))).astype(np.float32)) \
+            .to(torch.float8_e5m2).view(torch.uint8).numpy()
+    e = oracle.v_encode(fmt, x, chunk_bytes=C, tb=TB)
+    gaps, blk = brute_force_layout_v(fmt, x, e["lengths"], C, TB)
+    assert all(0 <= v <= 15 for v in gaps)
+    g = e["gaps"]
+    stored = [(int(g[t >> 1]) >> (4 * (t & 1))) & 15 for t in range(len(gaps))]
+    assert stored == gaps
+    assert e["blk_off"].tolist() == blk
+    # every chunk decodes its own codewords from its stored gap: the first codeword it reads is the
+    # element whose start the gap names
+    starts = np.concatenate([[0], np.cumsum(np.asarray(e["lengths"])[v_symbols(fmt, x)])[:-1]])
+    for t in range(0, e["n_chunks"], max(1, e["n_chunks"] // 40)):
+        p = 8 * C * t + gaps[t]
+        if p >= e["total_bits"]:
+            continue
+        j = int(np.searchsorted(starts, p))
+        assert starts[j] == p
+        got, _ = oracle.v_decode_range(fmt, e["stream"], e["raw"], e["lengths"], p, j, 1)
+        assert int(got[0]) == int(x[j])
