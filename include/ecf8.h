@@ -155,9 +155,13 @@ int ecf8_build_codebook(const uint8_t* fp8, uint64_t n, uint32_t max_len, ecf8_c
 /* Canonical codes of a codebook (MSB-first values, length in cb->len). */
 int ecf8_canonical_codes(const ecf8_codebook* cb, uint32_t code[ECF8_NSYM]);
 
-/* Size query: fills *out (T, chunk/block counts, the four buffer sizes) for
- * encoding fp8 with cb and params.  ECF8_ERR_META if an element's exponent has
- * length 0 in cb or cb is not a prefix code; ECF8_ERR_ARG on bad params. */
+/* Size query for ECF8 blog §3.1.1 (the exponent stream T = sum of code
+ * lengths) and §3.2.1 (the stream cut into per-thread chunks of C bytes, each
+ * with a stored gap, and blocks of TB threads): fills *out (T, chunk/block
+ * counts, the four buffer sizes) for encoding fp8 with cb and params.
+ * fp8: host, n bytes (not modified); out: host, overwritten.
+ * Errors: ECF8_ERR_META if an element's exponent has length 0 in cb or cb is
+ * not a prefix code; ECF8_ERR_ARG on NULL pointers or bad params. */
 int ecf8_encode_sizes(const uint8_t* fp8, uint64_t n, const ecf8_codebook* cb,
                       const ecf8_params* params, ecf8_meta* out);
 
@@ -171,15 +175,22 @@ int ecf8_encode(const uint8_t* fp8, uint64_t n, const ecf8_codebook* cb, const e
                 uint8_t* gaps, uint64_t gap_cap, uint64_t* blk_off, uint64_t blk_cap,
                 ecf8_meta* meta);
 
-/* Structural check of metadata: sizes consistent with n, T, C, TB; code
- * lengths 0..16 forming a prefix code (Kraft sum 1 with >= 2 symbols, one
- * symbol of length 1 otherwise); max_len correct.  ECF8_OK or ECF8_ERR_META. */
+/* ECF8 blog §5.3 (troubleshooting: wrong output -> check that the gap values
+ * agree with the stream): the host-side part of that check, a structural
+ * check of metadata before any decode: sizes consistent with n, T, C, TB
+ * (§3.2.1 chunk and block counts); code lengths 0..16 forming a prefix code
+ * (§3.1.1: optimal prefix code, at most 16 bits; Kraft sum 1 with >= 2
+ * symbols, one symbol of length 1 otherwise); max_len correct.  meta: host,
+ * read only.  Returns ECF8_OK, or ECF8_ERR_META (ECF8_ERR_ARG if NULL). */
 int ecf8_validate_meta(const ecf8_meta* meta);
 
 /* -------------------------- device decode ----------------------------- */
 
 /* Workspace bytes a decode of `count` tensors needs (256-byte aligned
- * device memory, owned by the caller, reusable across calls). */
+ * device memory, owned by the caller, sized once and reused across calls, as
+ * ECF8 blog §3.2.2 sizes its pool once): a 256-byte block-check counter,
+ * 128 bytes of descriptor and 9,216 bytes of decode table per tensor.
+ * Returns 0 for count < 0. */
 uint64_t ecf8_workspace_bytes(int count);
 
 /* Batched-decode setup (ECF8 blog §3.3, "resident weights + batched decode"):
@@ -202,26 +213,52 @@ int ecf8_decode_prepare(const ecf8_tensor_desc* descs, int count, uint8_t* out_b
 int ecf8_decode_run(const ecf8_plan* plan, void* hip_stream);
 
 /* The two launches of ecf8_decode_run, for callers that schedule or time
- * them separately: ecf8_build_tables (one workgroup per tensor, ECF8 blog
- * §3.1.2) must precede ecf8_decode_blocks (the persistent decode dispatch,
- * ECF8 blog §3.2.1) on the same stream.  Same arguments and errors as
- * ecf8_decode_run. */
+ * them separately: ecf8_build_tables (grid = tensors x 9 workgroups, one per
+ * 256-entry slice of a tensor's table, ECF8 blog §3.1.2; it also restarts the
+ * workspace's block-check counter) must precede ecf8_decode_blocks (the
+ * persistent decode dispatch, ECF8 blog §3.2.1) on the same stream.  Same
+ * arguments and errors as ecf8_decode_run. */
 int ecf8_build_tables(const ecf8_plan* plan, void* hip_stream);
 int ecf8_decode_blocks(const ecf8_plan* plan, void* hip_stream);
 
-/* prepare + run. */
+/* ECF8 blog §3.3 (data-centre mode: every weight resident, decoded in
+ * batches) and §3.2.2 (one preallocated output pool, reused, no allocation);
+ * DFloat11 blog §3.3 (the weights of a whole transformer block decoded
+ * together): decode `count` tensors in one persistent dispatch into
+ * out_base (tensor i at out_base + descs[i].out_offset, n_i bytes, 16-byte
+ * aligned, ranges must not overlap).  = ecf8_decode_prepare +
+ * ecf8_decode_run.  descs: host, read during the call only; buffers and
+ * workspace: device, caller-owned.  Asynchronous on hip_stream.
+ * Errors: those of ecf8_decode_prepare and ecf8_decode_run. */
 int ecf8_decode_batched(const ecf8_tensor_desc* descs, int count, uint8_t* out_base,
                         void* workspace, uint64_t workspace_bytes, void* hip_stream);
 
-/* Single-tensor decode: stream/nibbles/gaps/blk_off and out_fp8 are device
- * pointers; n must equal meta->n; out_fp8 must be 16-byte aligned and hold n
- * bytes.  Equivalent to ecf8_decode_batched with count = 1. */
+/* ECF8 blog §3.2.1, the decode kernel of one bitstream and its metadata
+ * (per-thread chunk load, gap-based symbol count, block-wide scan,
+ * cooperative decode into shared memory, write-back): decode one tensor.
+ * s: host struct of device pointers (stream 16-byte aligned, nibbles and
+ * blk_off 8-byte aligned); meta: host; out_fp8: device, 16-byte aligned,
+ * receives exactly n bytes; n must equal meta->n (ECF8_ERR_SIZE otherwise).
+ * workspace: device, >= ecf8_workspace_bytes(1) bytes, 256-byte aligned,
+ * caller-owned (descriptor, decode table and block-check counter; the
+ * library allocates nothing).  Equivalent to ecf8_decode_batched with
+ * count = 1.  Asynchronous on hip_stream; the return code covers argument
+ * and metadata checks and launch errors (ECF8_ERR_ARG/SIZE/META/
+ * UNSUPPORTED/WORKSPACE/HIP). */
 int ecf8_decode(const ecf8_stream* s, const ecf8_meta* meta, uint8_t* out_fp8, uint64_t n,
                 void* workspace, uint64_t workspace_bytes, void* hip_stream);
 
-/* Checked mode: synchronizes hip_stream, reads the workspace's error counter
- * (blocks whose decoded symbol count disagreed with blk_off since the last
- * prepare) into *bad_blocks and returns ECF8_ERR_CORRUPT if it is non-zero. */
+/* Checked mode, after ECF8 blog §5.3 (wrong output -> verify the gap
+ * synchronisation): every decoded block compares the sum of its threads'
+ * symbol counts (each counted from the thread's stored gap) with its stored
+ * offsets blk_off[b + 1] - blk_off[b].  This call synchronizes hip_stream,
+ * reads the workspace's counter of disagreeing blocks for the last run (the
+ * table launch of each run restarts it; a plan whose tables were never built
+ * flags every block) into *bad_blocks (host) and returns ECF8_ERR_CORRUPT if
+ * it is non-zero.  A corrupt stream, gap or offset that keeps every block's
+ * count is not detected (the format carries no checksum); whatever the
+ * corruption, no byte outside each tensor's output range is written.
+ * Errors: ECF8_ERR_ARG (NULL), ECF8_ERR_HIP. */
 int ecf8_decode_status(const void* workspace, void* hip_stream, uint64_t* bad_blocks);
 
 /* ---------------------------- device encode ---------------------------- */

@@ -164,8 +164,9 @@ __device__ __forceinline__ void bst1(Rsrc r, uint32_t off, uint8_t v)
 // (length, symbol) order, so symbol s starts at the sum of 2^(16 - len) over
 // the symbols before it; each of 16 lanes computes one symbol's range.
 // Entry layout (one dword, so a lookup is a single 4-byte LDS read):
-//   bits  7..0   bits consumed (1..16)
-//   bits 15..8   4 * symbols decoded (0..16)
+//   bits  7..0   4 * symbols decoded (0..16): the nibble count of the entry's
+//                output, also usable directly as a shift amount (bits 4..0)
+//   bits 15..8   bits consumed (1..16)
 //   bits 31..16  the symbols as nibbles, first symbol in bits 19..16.
 constexpr int kTableSlices = (kTableMax + kTableThreads - 1) / kTableThreads;   // 9
 
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(kTableThreads) void ecf8_table_kernel(DevDesc* __re
         ns++;
         pos += l;
     }
-    tables[(uint64_t)blockIdx.x * kTabStride + idx] = (pos ? pos : 1u) | ((4 * ns) << 8) | (sy << 16);
+    tables[(uint64_t)blockIdx.x * kTabStride + idx] = (4 * ns) | ((pos ? pos : 1u) << 8) | (sy << 16);
 }
 
 // ------------------------------------------------------------ helpers
@@ -347,7 +348,9 @@ __device__ __forceinline__ int table_index(uint32_t win, int cd)
 {
     const int a = (int)(win >> (32 - kWin));
     const int b = (int)(win >> 16) - cd;
-    return min(max(a, b), kTableMax - 1);
+    int m;
+    asm("v_med3_i32 %0, %1, %2, %3" : "=v"(m) : "v"(a), "v"(b), "v"(kTableMax - 1));
+    return m;
 }
 
 // One table lookup at stream position r (r = 192 - bit position within the
@@ -379,25 +382,31 @@ __device__ __forceinline__ void emit_symbols(uint32_t* s_out, uint32_t ob, uint3
 
 // OR the symbols of two consecutive table entries of a lane (an entry of 0
 // contributes nothing) into the staging at bit offset ob: their packets joined
-// into one bit string of at most 32 bits, spread over two dwords.  Returns the
-// bit offset after them.
-__device__ __forceinline__ uint32_t emit_pair(uint32_t* s_out, uint32_t ob, uint32_t e0, uint32_t e1)
+// into one bit string of at most 32 bits, which covers dword ob / 32 and, when
+// it crosses, part of the next.  Only the first of those dwords is written
+// here, together with `carry`, the spill of the previous pair into this same
+// dword; this pair's own spill is returned in `carry` for the next pair (or
+// the final flush).  A pair adds at most 32 bits, so the next pair starts in
+// this dword or the next one, and a spill is non-zero only if it starts in the
+// next: the carry always lands in the dword it belongs to, with one LDS atomic
+// per pair instead of two.  Returns the bit offset after the pair.
+__device__ __forceinline__ uint32_t emit_pair(uint32_t* s_out, uint32_t ob, uint32_t e0, uint32_t e1,
+                                              uint32_t& carry)
 {
-    // p01 = ((e1 >> 16) << n0) | (e0 >> 16), n0 = 4 * symbols of e0 (<= 16, the low
-    // five bits of e0 >> 8), with word selects instead of shifts
-    const uint32_t n0s = e0 >> 8;
+    // p01 = ((e1 >> 16) << n0) | (e0 >> 16), n0 = 4 * symbols of e0 (<= 16: the
+    // shift takes the low five bits of e0 itself), with word selects
+    const uint32_t n0s = e0;
     uint32_t p01;
     asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1\n\t"
         "v_or_b32_sdwa %0, %0, %3 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
         : "=&v"(p01) : "v"(n0s), "v"(e1), "v"(e0));
     const uint64_t v = (uint64_t)p01 << (ob & 31u);
-    const uint32_t wa = ob >> 5;
-    atomicOr(&s_out[wa], (uint32_t)v);
-    atomicOr(&s_out[wa + 1], (uint32_t)(v >> 32));
+    atomicOr(&s_out[ob >> 5], (uint32_t)v | carry);
+    carry = (uint32_t)(v >> 32);
     // ob + (4 * symbols of e0) + (4 * symbols of e1), with byte selects
     uint32_t nob;
-    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD\n\t"
-        "v_add_u32_sdwa %0, %3, %0 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD"
+    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD\n\t"
+        "v_add_u32_sdwa %0, %3, %0 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD"
         : "=&v"(nob) : "v"(e0), "v"(ob), "v"(e1));
     return nob;
 }
@@ -407,7 +416,59 @@ __device__ __forceinline__ uint32_t emit_pair(uint32_t* s_out, uint32_t ob, uint
 #define ECF8_RECORDS 20
 #endif
 constexpr int kRecords = ECF8_RECORDS;   // table entries recorded per lane by the count pass
-static_assert(kRecords % 4 == 0, "records are taken four at a time");
+constexpr int kStep = 2;                 // lookups per wave-uniform step of the count pass
+static_assert(kRecords % kStep == 0 && kStep % 2 == 0, "records are taken a step at a time, emitted in pairs");
+
+// acc + (e & 0xFF) as one byte-select add
+__device__ __forceinline__ uint32_t add_byte0(uint32_t acc, uint32_t e)
+{
+    uint32_t r;
+    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD"
+        : "=v"(r) : "v"(e), "v"(acc));
+    return r;
+}
+
+// The count pass in wave-uniform steps of kStep lookups, unrolled at compile
+// time so that every record index is static (the records stay in registers).
+// A lane past its end keeps looking up at its final position but records 0
+// (no bits, no symbols); the step loop ends when no lane of the wave is active.
+template <int Q>
+__device__ __forceinline__ void count_steps(const char* s_stream_b, const uint32_t* s_tx, uint32_t col_addr, int cd,
+                                            uint32_t rend, uint32_t& r, uint32_t& cnt4, uint32_t& lastex, bool& act,
+                                            int& nq, uint32_t (&rec)[kRecords])
+{
+    if constexpr (Q < kRecords / kStep) {
+        if (__builtin_amdgcn_ballot_w64(act) == 0) return;
+        nq = Q + 1;
+#pragma unroll
+        for (int j = 0; j < kStep; ++j) {
+            const uint32_t e = lookup(s_stream_b, s_tx, col_addr, r, cd);
+            const uint32_t em = act ? e : 0u;
+            lastex = act ? e : lastex;
+            rec[kStep * Q + j] = em;
+            r -= (em >> 8) & 0xFFu;
+            cnt4 = add_byte0(cnt4, em);
+            act = r > rend;
+        }
+        count_steps<Q + 1>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
+    }
+}
+
+// The decode pass over the recorded entries, two at a time, for the nq steps
+// the count pass took (compile-time unrolled like count_steps).
+template <int Q>
+__device__ __forceinline__ uint32_t emit_steps(uint32_t* s_out, uint32_t ob, int nq, const uint32_t (&rec)[kRecords],
+                                               uint32_t& carry)
+{
+    if constexpr (Q < kRecords / kStep) {
+        if (Q >= nq) return ob;
+#pragma unroll
+        for (int j = 0; j < kStep; j += 2)
+            ob = emit_pair(s_out, ob, rec[kStep * Q + j], rec[kStep * Q + j + 1], carry);
+        return emit_steps<Q + 1>(s_out, ob, nq, rec, carry);
+    }
+    return ob;
+}
 
 template <int C, int TB>
 struct DecodeLds {
@@ -666,7 +727,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
         // next blocks' loads start sooner (4% faster than one raised count).
         __builtin_amdgcn_s_setprio(1);
         // ---- phase 2: count the codewords that start inside [gap, E)
-        // The walk runs in steps of four lookups with one wave-uniform exit test
+        // The walk runs in steps of kStep lookups with one wave-uniform exit test
         // per step; a lane that has passed E keeps looking up at its final
         // position but records 0 (no bits, no symbols).  The recorded entries sit
         // in statically indexed registers and are replayed by phase 4, so the
@@ -679,28 +740,14 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
         uint32_t r = r0;
         uint32_t cnt4 = 0, lastex = 0;
         bool act = r > rend;
-        int nq = 0;                        // four-lookup steps taken (wave-uniform)
-#pragma unroll
-        for (int q = 0; q < kRecords / 4; ++q) {
-            if (__builtin_amdgcn_ballot_w64(act) == 0) break;
-            nq = q + 1;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t e = lookup(s_stream_b, s_tx, col_addr, r, cd);
-                const uint32_t em = act ? e : 0u;
-                lastex = act ? e : lastex;
-                rec[4 * q + j] = em;
-                r -= em & 0xFFu;
-                cnt4 += (em >> 8) & 0xFFu;
-                act = r > rend;
-            }
-        }
+        int nq = 0;                        // steps taken (wave-uniform)
+        count_steps<0>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
         const uint32_t r_rec = r;          // where the recorded lookups end
         while (r > rend) {
             const uint32_t e = lookup(s_stream_b, s_tx, col_addr, r, cd);
             lastex = e;
-            r -= e & 0xFFu;
-            cnt4 += (e >> 8) & 0xFFu;
+            r -= (e >> 8) & 0xFFu;
+            cnt4 += e & 0xFFu;
         }
         __builtin_amdgcn_s_setprio(2);
         // the lane's rows are staging memory from here on: leave them cleared
@@ -711,8 +758,8 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
             // the last lookup (at r + its bit count) may have decoded codewords
             // that start at or after E: keep those starting before E
             const uint32_t ex = lastex;
-            const uint32_t ns = (ex >> 10) & 0x3Fu;
-            const uint32_t room = r + (ex & 0xFFu) - rend;
+            const uint32_t ns = (ex & 0xFFu) >> 2;
+            const uint32_t room = r + ((ex >> 8) & 0xFFu) - rend;
             uint32_t sy = ex >> 16, start = 0, keep = 0;
 #pragma unroll
             for (int i = 0; i < kMaxSymPerEntry; ++i) {
@@ -744,12 +791,12 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
 
         // ---- phase 4: cooperative decode into the LDS staging (packed nibbles)
         uint32_t ob = (a0 + pos) * 4;      // bit offset of the lane's first nibble in the staging
-#pragma unroll
-        for (int q = 0; q < kRecords / 4; ++q) {
-            if (q >= nq) break;
-            ob = emit_pair(s_out, ob, rec[4 * q], rec[4 * q + 1]);
-            ob = emit_pair(s_out, ob, rec[4 * q + 2], rec[4 * q + 3]);
-        }
+        uint32_t carry = 0;
+        ob = emit_steps<0>(s_out, ob, nq, rec, carry);
+        // the last pair's spill belongs to the dword after the one ob was in
+        // before that pair; that is the dword of ob or the one before it, and
+        // ob's dword when the spill is non-zero (a spill means the pair crossed)
+        if (nq) atomicOr(&s_out[ob >> 5], carry);
         if (r_rec > rend) {
             // lanes with more than kRecords lookups walk the rest from registers
             // (their rows are staging memory now): reload the chunk (L2-resident)
@@ -762,8 +809,8 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
                 const uint32_t win = reg_window(w, 192u - r);
                 const uint32_t ex = s_tx[table_index(win, cd)];
                 emit_symbols(s_out, ob, ex);
-                ob += (ex >> 8) & 0xFFu;
-                r -= ex & 0xFFu;
+                ob += ex & 0xFFu;
+                r -= (ex >> 8) & 0xFFu;
             }
         }
         __syncthreads();
