@@ -45,7 +45,8 @@
  * functions take device pointers (HIP device memory) and run asynchronously
  * on the given hipStream_t (passed as void*; NULL = the null stream).  The
  * decode entry points allocate no device memory: scratch space is the
- * caller's workspace.
+ * caller's workspace, or, for ecf8_decode_batched_noalloc, a fixed device
+ * array of the library.
  */
 #ifndef ECF8_H
 #define ECF8_H
@@ -260,6 +261,26 @@ int ecf8_decode(const ecf8_stream* s, const ecf8_meta* meta, uint8_t* out_fp8, u
  * corruption, no byte outside each tensor's output range is written.
  * Errors: ECF8_ERR_ARG (NULL), ECF8_ERR_HIP. */
 int ecf8_decode_status(const void* workspace, void* hip_stream, uint64_t* bad_blocks);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc): the same
+ * decode as ecf8_decode_batched, with no workspace argument.  Its block-check
+ * counter, descriptors and decode tables live in a fixed device array of the
+ * library, 149,760 bytes per GPU, held by each GPU the library runs on until
+ * the process ends; it holds at most 16 tensors (count > 16 returns
+ * ECF8_ERR_WORKSPACE).  The descriptors reach the device as kernel arguments,
+ * so the call allocates nothing, copies nothing and issues no memset:
+ * launches only (a setup kernel per 8 tensors, the table kernel, the decode).
+ * Every call on one GPU shares that array: calls that overlap on one GPU (on
+ * different streams, unordered) race and must not be issued; calls ordered on
+ * one stream are safe (each rewrites what it uses).  bad_blocks: NULL, or a
+ * device uint64 (8-byte aligned, caller-owned) that receives the number of
+ * blocks whose symbol count disagreed with blk_off (checked mode; zeroed at
+ * the start of each call, complete when the stream reaches the end of the
+ * decode).  Other arguments, alignment and errors as ecf8_decode_batched.
+ * Asynchronous on hip_stream. */
+int ecf8_decode_batched_noalloc(const ecf8_tensor_desc* descs, int count, uint8_t* out_base,
+                                uint64_t* bad_blocks, void* hip_stream);
 
 /* ---------------------------- device encode ---------------------------- */
 

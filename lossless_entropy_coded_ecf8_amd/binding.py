@@ -95,7 +95,7 @@ EXPORTS_V = ["ecf8v_nsym", "ecf8v_histogram", "ecf8v_code_lengths", "ecf8v_canon
 EXPORTS = ["ecf8_histogram", "ecf8_codebook_from_freq", "ecf8_build_codebook", "ecf8_canonical_codes",
            "ecf8_encode_sizes", "ecf8_encode", "ecf8_validate_meta", "ecf8_workspace_bytes",
            "ecf8_decode_prepare", "ecf8_decode_run", "ecf8_build_tables", "ecf8_decode_blocks",
-           "ecf8_decode_batched", "ecf8_decode",
+           "ecf8_decode_batched", "ecf8_decode", "ecf8_decode_batched_noalloc",
            "ecf8_decode_status", "ecf8_histogram_device", "ecf8_meta_from_freq", "ecf8_encode_workspace_bytes",
            "ecf8_encode_device", "ecf8_alpha_hat", "ecf8_exponent_entropy_bound", "ecf8_hbm_copy",
            "ecf8_strerror", "ecf8_version"]
@@ -134,6 +134,7 @@ def lib() -> ctypes.CDLL:
         "ecf8_decode_batched": (i, [ctypes.POINTER(TensorDesc), i, vp, vp, ctypes.c_uint64, vp]),
         "ecf8_decode": (i, [ctypes.POINTER(Stream), ctypes.POINTER(Meta), vp, ctypes.c_uint64, vp,
                             ctypes.c_uint64, vp]),
+        "ecf8_decode_batched_noalloc": (i, [ctypes.POINTER(TensorDesc), i, vp, vp, vp]),
         "ecf8_decode_status": (i, [vp, vp, u64p]),
         "ecf8_histogram_device": (i, [vp, ctypes.c_uint64, vp, vp, ctypes.c_uint64, vp]),
         "ecf8_meta_from_freq": (i, [u64p, ctypes.c_uint64, ctypes.POINTER(Codebook), ctypes.POINTER(Params),
@@ -581,6 +582,26 @@ def hbm_copy(src, dst, stream=None):
     _check(lib().ecf8_hbm_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n,
                                _stream_handle(stream)), "ecf8_hbm_copy")
     return dst
+
+
+def decode_batched_noalloc(encs: Sequence[DeviceEncoded], out, offsets, bad_blocks=None, stream=None):
+    """ecf8_decode_batched_noalloc: decode up to 16 tensors into out[offsets[i]:] with no workspace and no
+    allocation (the library's fixed device scratch).  bad_blocks: None or a device int64 tensor of one
+    element that receives the block-check count."""
+    encs = list(encs)
+    dev = encs[0].stream.device if encs else out.device
+    if len(offsets) != len(encs):
+        raise ValueError("%d offsets for %d tensors" % (len(offsets), len(encs)))
+    _check_out_ranges(out, offsets, [e.n for e in encs], dev)
+    arr = (TensorDesc * max(1, len(encs)))()
+    for i, (e, o) in enumerate(zip(encs, offsets)):
+        arr[i].s = e.c_stream()
+        arr[i].meta = e.meta
+        arr[i].out_offset = o
+    bb = ctypes.c_void_p(bad_blocks.data_ptr()) if bad_blocks is not None else ctypes.c_void_p(0)
+    _check(lib().ecf8_decode_batched_noalloc(arr, len(encs), ctypes.c_void_p(out.data_ptr()), bb,
+                                             _stream_handle(stream)), "ecf8_decode_batched_noalloc")
+    return out
 
 
 def decode_batched(encs: Sequence[DeviceEncoded], out=None, offsets=None, workspace=None, stream=None):

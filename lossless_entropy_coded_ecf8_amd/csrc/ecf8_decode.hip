@@ -870,15 +870,16 @@ struct DeviceInfo {
     int occupancy = 0;
 };
 
+constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
-std::vector<DeviceInfo> g_dev;
+DeviceInfo g_dev[kMaxDevices];     // fixed size: the decode paths allocate no host memory either
 
 int device_info(DeviceInfo* out)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return ECF8_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return ECF8_ERR_HIP;
     std::lock_guard<std::mutex> lk(g_dev_mu);
-    if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
     DeviceInfo& di = g_dev[dev];
     if (di.cus == 0) {
         int cus = 0, occ = 0;
@@ -895,6 +896,36 @@ int device_info(DeviceInfo* out)
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Validates one tensor of a batch and writes its device descriptor (host
+// memory, copied to the device by the caller); `blocks` is the running block
+// count of the batch.
+int fill_desc(const ecf8_tensor_desc& td, uint8_t* out_base, uint64_t& blocks, DevDesc& dd)
+{
+    const ecf8_meta& m = td.meta;
+    int rc = ecf8_validate_meta(&m);
+    if (rc) return rc;
+    if (m.chunk_bytes != (uint32_t)kChunk || m.threads_per_block != (uint32_t)kLanes) return ECF8_ERR_UNSUPPORTED;
+    if (m.n > 0) {
+        if (!out_base || !td.s.stream || !td.s.nibbles || !td.s.gaps || !td.s.blk_off) return ECF8_ERR_ARG;
+        if (!aligned(td.s.stream, 16) || !aligned(td.s.nibbles, 8) || !aligned(td.s.blk_off, 8) ||
+            !aligned(out_base + td.out_offset, 16))
+            return ECF8_ERR_ARG;
+    }
+    std::memset(&dd, 0, sizeof(dd));
+    dd.stream = td.s.stream;
+    dd.nibbles = td.s.nibbles;
+    dd.gaps = td.s.gaps;
+    dd.blk_off = td.s.blk_off;
+    dd.out = out_base ? out_base + td.out_offset : nullptr;
+    dd.n = m.n;
+    dd.total_bits = m.total_bits;
+    dd.block_begin = blocks;
+    blocks += m.n_blocks;
+    dd.block_end = blocks;
+    for (int s = 0; s < 16; ++s) dd.len[s] = m.cb.len[s];
+    return ECF8_OK;
+}
 
 }  // namespace
 
@@ -916,30 +947,8 @@ extern "C" int ecf8_decode_prepare(const ecf8_tensor_desc* descs, int count, uin
     DevDesc* hd = reinterpret_cast<DevDesc*>(host.data() + desc_offset());
     uint64_t blocks = 0;
     for (int i = 0; i < count; ++i) {
-        const ecf8_tensor_desc& td = descs[i];
-        const ecf8_meta& m = td.meta;
-        int rc = ecf8_validate_meta(&m);
+        int rc = fill_desc(descs[i], out_base, blocks, hd[i]);
         if (rc) return rc;
-        if (m.chunk_bytes != (uint32_t)kChunk || m.threads_per_block != (uint32_t)kLanes)
-            return ECF8_ERR_UNSUPPORTED;
-        if (m.n > 0) {
-            if (!out_base || !td.s.stream || !td.s.nibbles || !td.s.gaps || !td.s.blk_off) return ECF8_ERR_ARG;
-            if (!aligned(td.s.stream, 16) || !aligned(td.s.nibbles, 8) || !aligned(td.s.blk_off, 8) ||
-                !aligned(out_base + td.out_offset, 16))
-                return ECF8_ERR_ARG;
-        }
-        DevDesc& dd = hd[i];
-        dd.stream = td.s.stream;
-        dd.nibbles = td.s.nibbles;
-        dd.gaps = td.s.gaps;
-        dd.blk_off = td.s.blk_off;
-        dd.out = out_base ? out_base + td.out_offset : nullptr;
-        dd.n = m.n;
-        dd.total_bits = m.total_bits;
-        dd.block_begin = blocks;
-        blocks += m.n_blocks;
-        dd.block_end = blocks;
-        for (int s = 0; s < 16; ++s) dd.len[s] = m.cb.len[s];
     }
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     if (hipMemcpyAsync(workspace, host.data(), host.size(), hipMemcpyHostToDevice, st) != hipSuccess)
@@ -1038,4 +1047,107 @@ extern "C" int ecf8_decode_status(const void* workspace, void* hip_stream, uint6
     if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return ECF8_ERR_HIP;
     *bad_blocks = v;
     return v ? ECF8_ERR_CORRUPT : ECF8_OK;
+}
+
+// ------------------------------------------------------------ no-allocation entry point
+// ecf8_decode_batched without a workspace argument, for callers that cannot
+// allocate (HIP graph capture, serving loops that forbid allocation): the
+// status word, descriptors and decode tables live in `scratch`, a fixed
+// device array of this library (one copy per GPU, held until the process
+// ends).  The descriptors reach the device as kernel arguments of a small
+// setup launch, so the call makes no allocation, no copy and no memset.
+namespace {
+
+constexpr int kNoAllocMaxTensors = 16;
+constexpr int kSetupDescs = 8;                          // descriptors per setup launch (1 KiB of arguments)
+constexpr uint64_t kNoAllocScratchBytes =
+    kStatusBytes + (kNoAllocMaxTensors * sizeof(DevDesc) + 255) / 256 * 256 + kNoAllocMaxTensors * kTableBytes;
+static_assert(kNoAllocScratchBytes == 149760, "scratch size stated in the header");
+
+struct SetupArgs {
+    DevDesc d[kSetupDescs];
+};
+
+// Copies n descriptors from the kernel arguments to dst (one dword per lane)
+// and, with clear set, zeroes the block-check counter.
+__global__ __launch_bounds__(256) void ecf8_noalloc_setup_kernel(SetupArgs a, int n, DevDesc* __restrict__ dst,
+                                                                 unsigned long long* __restrict__ status, int clear)
+{
+    constexpr int kDw = (int)(sizeof(DevDesc) / 4);
+    const int t = threadIdx.x;
+    if (t < n * kDw) reinterpret_cast<uint32_t*>(dst)[t] = reinterpret_cast<const uint32_t*>(a.d)[t];
+    if (clear && t == 0) *status = 0ull;
+}
+
+struct NoAllocDevice {
+    unsigned char* ptr = nullptr;   // device address of this GPU's copy of scratch
+    bool ready = false;
+};
+NoAllocDevice g_noalloc[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// The device address of the current GPU's scratch, resolved once per device
+// with that device current (the array's host-side name is not a device address).
+int noalloc_scratch(unsigned char** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ECF8_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    NoAllocDevice& d = g_noalloc[dev];
+    if (!d.ready) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ECF8_ERR_HIP;
+        d.ptr = static_cast<unsigned char*>(p);
+        d.ready = true;
+    }
+    *out = d.ptr;
+    return ECF8_OK;
+}
+
+}  // namespace
+
+extern "C" int ecf8_decode_batched_noalloc(const ecf8_tensor_desc* descs, int count, uint8_t* out_base,
+                                           uint64_t* bad_blocks, void* hip_stream)
+{
+    if (count < 0 || (count > 0 && !descs)) return ECF8_ERR_ARG;
+    if (count > kNoAllocMaxTensors) return ECF8_ERR_WORKSPACE;
+    if (bad_blocks && !aligned(bad_blocks, 8)) return ECF8_ERR_ARG;
+    DevDesc hd[kNoAllocMaxTensors];
+    uint64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        int rc = fill_desc(descs[i], out_base, blocks, hd[i]);
+        if (rc) return rc;
+    }
+    unsigned char* ws = nullptr;
+    int rc = noalloc_scratch(&ws);
+    if (rc) return rc;
+    DeviceInfo di;
+    rc = device_info(&di);
+    if (rc) return rc;
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    auto* status = bad_blocks ? reinterpret_cast<unsigned long long*>(bad_blocks)
+                              : reinterpret_cast<unsigned long long*>(ws);
+    DevDesc* dd = reinterpret_cast<DevDesc*>(ws + desc_offset());
+    uint32_t* tables = reinterpret_cast<uint32_t*>(ws + table_offset(count));
+    // descriptors (and the cleared counter) first, in launches of kSetupDescs
+    for (int c = 0; c < count || c == 0; c += kSetupDescs) {
+        SetupArgs a;
+        const int nc = count - c < kSetupDescs ? count - c : kSetupDescs;
+        for (int k = 0; k < kSetupDescs; ++k) a.d[k] = k < nc ? hd[c + k] : DevDesc{};
+        hipLaunchKernelGGL(ecf8_noalloc_setup_kernel, dim3(1), dim3(256), 0, st, a, nc, dd + c, status, c == 0 ? 1 : 0);
+        if (count == 0) break;
+    }
+    if (blocks > 0) {
+        hipLaunchKernelGGL(ecf8_table_kernel, dim3(count, kTableSlices), dim3(kTableThreads), 0, st, dd, tables, status);
+        uint64_t grid = (uint64_t)di.cus * (uint64_t)di.occupancy;
+        if (grid > blocks) grid = blocks;
+        hipLaunchKernelGGL((ecf8_decode_kernel<kChunk, kLanes>), dim3((uint32_t)grid), dim3(kLanes), 0, st, dd, count,
+                           blocks, tables, status);
+    }
+    return hipGetLastError() == hipSuccess ? ECF8_OK : ECF8_ERR_HIP;
 }
