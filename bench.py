@@ -30,11 +30,20 @@ METRIC = "ECF8 decoded GB/s on 1 MI355X, % of HBM roofline; bit-exact vs oracle"
 WORKLOAD_TEXT = {
     "llama70b": "Llama-3-70B transformer block FP8 E4M3 (q,o 8192x8192; k,v 8192x1024; gate,up 8192x28672; "
                 "down 28672x8192), alpha-stable alpha=1.9, per-tensor codebooks, one batched dispatch",
-    "llama8b": "Llama-3-8B attention+MLP FP8 E4M3, alpha=1.8, per-tensor codebooks, one batched dispatch",
-    "dit14b": "14B-DiT block FP8 E4M3 (hidden 5120), alpha=1.5 + 2% outliers, per-128x128 scaling, batched",
-    "moe8": "MoE layer, 8 routed experts x (gate, up 7168x2048; down 2048x7168), per-expert codebooks, batched",
-    "gauss1m": "single 1024x1024 N(0,0.02) FP8 E4M3 tensor",
+    "llama8b": "Llama-3-8B attention+MLP weights FP8 E4M3 (q,o 4096x4096; k,v 4096x1024; gate,up 4096x14336; "
+               "down 14336x4096), alpha-stable alpha=1.8, per-tensor codebooks, one decode launch per tensor",
+    "dit14b": "14B-DiT block FP8 E4M3 (hidden 5120: self/cross-attn qkvo 8x 5120x5120, FFN 5120x13824 and "
+              "13824x5120), alpha-stable alpha=1.5 + 2% N(0,0.2) outliers, per-128x128-tile scaling, one batched dispatch",
+    "moe8": "MoE layer, the 8 experts of a seeded routing draw x (gate, up 7168x2048; down 2048x7168), FP8 E4M3, "
+            "alpha ~ U[1.5,2.0] per expert, per-expert codebooks, one batched dispatch",
+    "moe256": "MoE layer, all 256 experts x (gate, up 7168x2048; down 2048x7168) = 11.27 G FP8 E4M3 weights, "
+              "alpha ~ U[1.5,2.0] per expert, per-expert codebooks, one batched dispatch",
+    "gauss1m": "single 1024x1024 FP8 E4M3 tensor, N(0,0.02), per-tensor max-abs scaling, one decode launch",
 }
+# configs whose decode reads and writes fit the 256 MB Infinity Cache: their timings are cache-resident
+CACHE_RESIDENT = {"gauss1m"}
+# configs decoded with one launch per tensor (the others: one batched dispatch per step)
+PER_TENSOR = {"llama8b", "gauss1m"}
 
 
 def log(*a):
@@ -65,26 +74,40 @@ def load_traffic(workload: str, kernel_hash: str, launches_bytes: float = 0.0):
     return rec.get("traffic_bytes_per_launch")
 
 
-def copy_ceiling(torch, d, gib: float = 1.0, reps: int = 5):
-    """Event-timed plain streaming kernel (uint8 bitwise_not: reads and writes `gib` GiB each)."""
+def dispatch_stats(ms_list):
+    """Mean, median, min and max (ms) of per-dispatch times."""
+    v = sorted(ms_list)
+    n = len(v)
+    med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return {"mean": round(sum(v) / n, 5), "median": round(med, 5), "min": round(v[0], 5), "max": round(v[-1], 5)}
+
+
+def copy_ceiling(torch, d, gib: float = 1.0, reps: int = 10):
+    """The plain dwordx4 streaming copy of the library (ecf8_hbm_copy), `gib` GiB in and out, back to back:
+    median per-dispatch rate in GB/s (bytes read + written)."""
+    from lossless_entropy_coded_ecf8_amd import binding as B
     n = int(gib * (1 << 30))
-    a = torch.empty(n, dtype=torch.uint8, device=d).fill_(0x5A)
+    a = torch.randint(0, 256, (n,), dtype=torch.uint8, device=d)
     b = torch.empty_like(a)
-    torch.bitwise_not(a, out=b)
+    B.hbm_copy(a, b)
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(reps):
-        torch.bitwise_not(a, out=b)
-    e.record()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for s, e in ev:
+        s.record()
+        B.hbm_copy(a, b)
+        e.record()
     torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / reps
+    ok = torch.equal(a, b)
     del a, b
-    return 2.0 * n / (ms * 1e-3) / 1e9
+    if not ok:
+        raise RuntimeError("copy kernel mismatch")
+    st = dispatch_stats([s.elapsed_time(e) for s, e in ev])
+    return 2.0 * n / (st["median"] * 1e-3) / 1e9
 
 
 def cpu_baseline(encs_host, seconds: float):
-    """Time the C oracle decoding whole blocks of the largest tensor, all host cores."""
+    """Time the C oracle decoding whole blocks of the largest tensor: all host cores (thread pool), then
+    one core, each on a bounded sample sized to about `seconds` / 2 of wall time."""
     import numpy as np
     import oracle
     enc = max(encs_host, key=lambda e: e.n)
@@ -101,22 +124,29 @@ def cpu_baseline(encs_host, seconds: float):
         out, _ = oracle.decode_range(stream, nib, L, 8 * C * t + gap, lo, hi - lo)
         return hi - lo
 
+    def timed(blocks, threads):
+        t0 = time.perf_counter()
+        with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+            done = sum(ex.map(one, blocks))
+        return done, time.perf_counter() - t0
+
     oracle.lib()
-    # calibrate on 32 blocks per core, then size the sample to ~`seconds` of wall time
-    cal = min(int(m.n_blocks) // 2, 32 * cores)
-    t0 = time.perf_counter()
-    with concurrent.futures.ThreadPoolExecutor(cores) as ex:
-        done = sum(ex.map(one, range(cal)))
-    dt = time.perf_counter() - t0
-    nblk = int(max(cores, min(int(m.n_blocks) - cal, cal * seconds / max(dt, 1e-6))))
-    blocks = list(range(cal, cal + nblk))
-    t0 = time.perf_counter()
-    with concurrent.futures.ThreadPoolExecutor(cores) as ex:
-        done = sum(ex.map(one, blocks))
-    dt = time.perf_counter() - t0
-    return {"value": round(done / dt / 1e9, 6), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": "%d whole blocks (%d elements) of the largest tensor, bit-serial C oracle decode, "
-                      "one thread per core, %.1f s" % (len(blocks), done, dt)}
+    nb = int(m.n_blocks)
+    # all cores: calibrate on 16 blocks per core, then size the sample
+    cal = min(nb // 2, 16 * cores)
+    _, dt = timed(range(cal), cores)
+    nblk = int(max(cores, min(nb - cal, cal * 0.5 * seconds / max(dt, 1e-6))))
+    done, dt = timed(range(cal, cal + nblk), cores)
+    res = {"value": round(done / dt / 1e9, 6), "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "sample": "%d whole blocks (%d elements) of the largest tensor, bit-serial C oracle decode, "
+                     "one thread per core, %.1f s" % (nblk, done, dt)}
+    # one core
+    _, dt1 = timed(range(4), 1)
+    n1 = int(max(2, min(nb, 4 * 0.5 * seconds / max(dt1, 1e-6))))
+    done1, dt1 = timed(range(n1), 1)
+    res["single_core"] = {"value": round(done1 / dt1 / 1e9, 6), "unit": "GB/s", "cores": 1,
+                          "sample": "%d whole blocks (%d elements), %.1f s" % (n1, done1, dt1)}
+    return res
 
 
 def alpha_report(n: int = 1 << 24):
@@ -355,7 +385,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="llama70b", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", default="decode", choices=["decode", "pipeline", "alpha", "encode", "variant"],
                     help="decode: the batched decode step (default); pipeline: decode-on-use of the "
@@ -400,64 +430,79 @@ def main():
         h = E.encode(x.cpu())
         names.append(name)
         xs.append(x.reshape(-1))
-        encs_host.append(h)
+        if wl != "moe256":
+            encs_host.append(h)
+        elif not encs_host or h.n > encs_host[0].n:
+            encs_host = [h]                                   # the CPU leg needs one tensor only
         encs.append(h.to(d))
-        log("encoded %-12s n=%d  %.3f bits/exponent" % (name, h.n, h.meta.total_bits / max(h.n, 1)))
-    log("setup %.1f s" % (time.time() - t0))
+        if len(names) <= 16:
+            log("encoded %-12s n=%d  %.3f bits/exponent" % (name, h.n, h.meta.total_bits / max(h.n, 1)))
+    log("setup %.1f s, %d tensors" % (time.time() - t0, len(encs)))
 
-    plan = E.DecodePlan(encs)
-    plan.run()
+    # one step: one batched dispatch of all tensors, or one launch per tensor (each a table kernel and a
+    # decode dispatch); the decode dispatches are bracketed by events on the launch stream
+    plans = [E.DecodePlan([e]) for e in encs] if wl in PER_TENSOR else [E.DecodePlan(encs)]
+    for p in plans:
+        p.run()
     torch.cuda.synchronize()
-    bad = plan.status()
-    for i, x in enumerate(xs):
-        if not torch.equal(plan.view(i), x):
-            log("MISMATCH in tensor", names[i])
+    bad = sum(p.status() for p in plans)
+    views = [p.view(0) for p in plans] if wl in PER_TENSOR else [plans[0].view(i) for i in range(len(encs))]
+    for nm, v, x in zip(names, views, xs):
+        if not torch.equal(v, x):
+            log("MISMATCH in tensor", nm)
             sys.exit(1)
     if bad:
         log("block offset check failed on", bad, "blocks")
         sys.exit(1)
     log("bit-exact check passed on %d tensors" % len(xs))
+    del xs, views
+
+    def step(evs):
+        for p, (a, b) in zip(plans, evs):
+            p.build_tables()
+            a.record()
+            p.decode_blocks()
+            b.record()
+
+    def new_events():
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in plans]
 
     for _ in range(args.warmup):
-        plan.run()
+        step(new_events())
     torch.cuda.synchronize()
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    ev = [new_events() for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for k in range(K):
-        plan.build_tables()
-        ev[k][0].record()
-        plan.decode_blocks()
-        ev[k][1].record()
+        step(ev[k])
     end.record()
     torch.cuda.synchronize()
     step_ms = start.elapsed_time(end) / K
-    dec_ms = sum(a.elapsed_time(b) for a, b in ev) / K
+    dec = [sum(a.elapsed_time(b) for a, b in e) for e in ev]      # decode time of each step
+    st = dispatch_stats(dec)
 
-    # the same decode with a 1 GiB read before each dispatch: the 256 MB Infinity Cache then holds
-    # only clean lines of that buffer (a write would leave dirty lines for the decode to write back)
+    # the same decode with a 1 GiB read before each step: the 256 MB Infinity Cache then holds only
+    # clean lines of that buffer (a write would leave dirty lines for the decode to write back)
     scratch = torch.ones(1 << 27, dtype=torch.int64, device=d)
     kc = min(K, 20)
-    evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(kc)]
+    evc = [new_events() for _ in range(kc)]
     for k in range(kc):
         scratch.sum()
-        plan.build_tables()
-        evc[k][0].record()
-        plan.decode_blocks()
-        evc[k][1].record()
+        step(evc[k])
     torch.cuda.synchronize()
-    cold_ms = sum(a.elapsed_time(b) for a, b in evc) / kc
+    stc = dispatch_stats([sum(a.elapsed_time(b) for a, b in e) for e in evc])
     del scratch
 
     copy_gbs = copy_ceiling(torch, d)
     bb = batch_bytes(encs)
     n_total = bb["written"]
     value = n_total / (step_ms * 1e-3) / 1e9
-    achieved = bb["total"] / (dec_ms * 1e-3) / 1e9
+    achieved = bb["total"] / (st["mean"] * 1e-3) / 1e9
     khash = kernel_source_hash()
     traffic = load_traffic(wl, khash, bb["total"])
+    gbs = lambda ms: round(bb["total"] / (ms * 1e-3) / 1e9, 2)
     res = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -473,22 +518,28 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[wl], "name": wl, "tensors": len(encs), "elements": n_total,
                    "compressed_bytes": bb["read"], "bits_per_element": round(8.0 * bb["read"] / n_total, 4),
-                   "chunk_bytes": 16, "lanes_per_block": 256, "grid": int(plan.plan.grid)},
+                   "chunk_bytes": 16, "lanes_per_block": 256, "launches_per_step": len(plans),
+                   "grid": int(max(p.plan.grid for p in plans))},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "ecf8_decode_kernel", "kernel_ms": round(dec_ms, 5),
+                     "kernel": "ecf8_decode_kernel", "kernel_ms": st["mean"], "kernel_ms_median": st["median"],
+                     "kernel_ms_min": st["min"], "kernel_ms_max": st["max"],
+                     "frac_median": round(gbs(st["median"]) / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes": bb["total"], "kernel_sha": khash,
                      "copy_ceiling_gbs": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4),
-                     "cache": "kernel_ms: back-to-back dispatches (part of one step's data stays in the 256 MB "
-                              "Infinity Cache for the next); kernel_ms_cache_evicted: each dispatch after a 1 GiB read",
-                     "kernel_ms_cache_evicted": round(cold_ms, 5),
-                     "frac_cache_evicted": round(bb["total"] / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                     "cache": ("every byte the decode reads and writes fits the 256 MB Infinity Cache: cache-resident "
+                               "timings" if wl in CACHE_RESIDENT else
+                               "kernel_ms*: back-to-back steps (part of one step's data stays in the 256 MB Infinity "
+                               "Cache for the next); kernel_ms_cache_evicted*: each step after a 1 GiB read"),
+                     "kernel_ms_cache_evicted": stc["mean"], "kernel_ms_cache_evicted_median": stc["median"],
+                     "kernel_ms_cache_evicted_min": stc["min"], "kernel_ms_cache_evicted_max": stc["max"],
+                     "frac_cache_evicted": round(gbs(stc["mean"]) / HBM_PEAK_GBS, 4),
+                     "decode_us_per_step": [round(1000 * t, 1) for t in dec[:50]]},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(encs_host, args.cpu_seconds)
     print(json.dumps(res), flush=True)
-
 
 if __name__ == "__main__":
     main()
