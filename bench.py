@@ -149,6 +149,40 @@ def cpu_baseline(encs_host, seconds: float):
     return res
 
 
+def copy_calibration(args):
+    """The library's plain copy kernel (ecf8_hbm_copy) at several sizes, each dispatch preceded by a 1 GiB
+    read that evicts the Infinity Cache: what FETCH_SIZE / WRITE_SIZE read for copies of known size
+    calibrates the decode's traffic counters; the event-timed rates are the copy ceiling at each size."""
+    import torch
+    from lossless_entropy_coded_ecf8_amd import binding as B
+    d = torch.device("cuda:0")
+    scratch = torch.ones(1 << 27, dtype=torch.int64, device=d)
+    rows = []
+    for mib in [int(v) for v in args.copy_mib.split(",")]:
+        n = mib << 20
+        a = torch.randint(0, 256, (n,), dtype=torch.uint8, device=d)
+        b = torch.empty_like(a)
+        ms = []
+        for _ in range(args.steps):
+            scratch.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            B.hbm_copy(a, b)
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        if not torch.equal(a, b):
+            log("copy mismatch at", mib, "MiB")
+            sys.exit(1)
+        st = dispatch_stats(ms)
+        rows.append({"mib": mib, "bytes_read": n, "bytes_written": n, "ms": st,
+                     "gbs_median": round(2 * n / (st["median"] * 1e-3) / 1e9, 1)})
+        log(json.dumps(rows[-1]))
+        del a, b
+    print(json.dumps({"report": "ecf8_hbm_copy calibration, each dispatch after a 1 GiB read", "rows": rows}),
+          flush=True)
+
+
 def alpha_report(n: int = 1 << 24):
     """Tail index vs exponent entropy (ECF8 blog §2.2 bound, §6 estimator) on seeded CMS samples."""
     import math
@@ -387,7 +421,8 @@ def main():
     ap.add_argument("--workload", default="llama70b", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="decode", choices=["decode", "pipeline", "alpha", "encode", "variant"],
+    ap.add_argument("--copy-mib", default="512,2048", help="copycal mode: copy sizes in MiB (comma list)")
+    ap.add_argument("--mode", default="decode", choices=["decode", "pipeline", "alpha", "encode", "variant", "copycal"],
                     help="decode: the batched decode step (default); pipeline: decode-on-use of the "
                          "block's layers beside FP8 GEMMs, against resident FP8 weights")
     ap.add_argument("--format", default="bf16", choices=["bf16", "e5m2"], help="variant mode: the float format")
@@ -411,6 +446,9 @@ def main():
         return
     if args.mode == "variant":
         variant_bench(args)
+        return
+    if args.mode == "copycal":
+        copy_calibration(args)
         return
 
     import torch

@@ -416,7 +416,10 @@ __device__ __forceinline__ uint32_t emit_pair(uint32_t* s_out, uint32_t ob, uint
 #define ECF8_RECORDS 20
 #endif
 constexpr int kRecords = ECF8_RECORDS;   // table entries recorded per lane by the count pass
-constexpr int kStep = 2;                 // lookups per wave-uniform step of the count pass
+#ifndef ECF8_STEP
+#define ECF8_STEP 4
+#endif
+constexpr int kStep = ECF8_STEP;         // lookups per wave-uniform step of the count pass
 static_assert(kRecords % kStep == 0 && kStep % 2 == 0, "records are taken a step at a time, emitted in pairs");
 
 // acc + (e & 0xFF) as one byte-select add

@@ -34,7 +34,7 @@ import lossless_entropy_coded_ecf8_amd as E
 C, TB = 16, 256
 K_WIN = 11
 K_TABLE_MAX = (1 << K_WIN) + ((1 << (16 - K_WIN)) - 1) * 8
-RECORDS, STEP = 20, 2
+RECORDS, STEP = 20, 4
 OUT_DW = ((8 * C * TB + 15 + 8 + 16) // 8 + 2 + 3) // 4 * 4        # staging dwords in the kernel
 
 
