@@ -380,16 +380,21 @@ def variant_bench(args):
         log("MISMATCH in the variant decode")
         sys.exit(1)
     log("bit-exact check passed on %d tensors" % len(xs))
+    del xs
     for _ in range(args.warmup):
         plan.run()
     torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
-    for _ in range(args.steps):
+    for e0, e1 in ev:
+        e0.record()
         plan.run()
+        e1.record()
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / args.steps
+    st = dispatch_stats([e0.elapsed_time(e1) for e0, e1 in ev])
     eb = 2 if fmt == "bf16" else 1
     khash = kernel_source_hash("ecf8v_decode.hip")
     traffic = load_traffic("variant_%s_%s" % (fmt, args.workload), khash)
@@ -405,10 +410,13 @@ def variant_bench(args):
                       "tensors": len(hs), "elements": n, "compressed_bytes": read,
                       "compressed_ratio": round(read / written, 4), "chunk_bytes": 16, "lanes_per_block": 256,
                       "grid": int(plan.plan.grid)},
-           "roofline": {"bound": "hbm", "achieved": round((read + written) / (ms * 1e-3) / 1e9, 2),
+           "roofline": {"bound": "hbm", "achieved": round((read + written) / (st["mean"] * 1e-3) / 1e9, 2),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round((read + written) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                        "traffic": traffic, "kernel": "ecf8v_decode_kernel (+ table kernel, one run)",
+                        "frac": round((read + written) / (st["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "frac_median": round((read + written) / (st["median"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "run_ms": st["mean"], "run_ms_median": st["median"], "run_ms_min": st["min"],
+                        "run_ms_max": st["max"],
+                        "traffic": traffic, "kernel": "ecf8v_decode_kernel (+ clear and table kernels: one run)",
                         "algorithmic_bytes": read + written, "kernel_sha": khash}}
     print(json.dumps(res), flush=True)
 

@@ -626,8 +626,14 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
             const uint32_t ne = d->entries <= tab_n ? d->entries : tab_n;
             c_last = (int)ne - 1;
             const uint32_t* tx = tables + (uint64_t)ptens * kTabMax;
-            for (uint32_t i = tid; i < ne / 4; i += kTB) reinterpret_cast<uint4*>(s_tab)[i] = gld16(tx + 4 * i);
-            for (int i = tid; i < ECF8V_MAX_SYM; i += kTB) s_len[i] = d->len[i];
+            // the lane index passes through an empty asm so that the per-lane
+            // addresses of these copies are formed here, when a tensor
+            // changes, instead of being hoisted out of the block loop and
+            // kept live (at 7 waves per SIMD they would be spilled)
+            int lt = tid;
+            asm volatile("" : "+v"(lt));
+            for (uint32_t i = lt; i < ne / 4; i += kTB) reinterpret_cast<uint4*>(s_tab)[i] = gld16(tx + 4 * i);
+            for (int i = lt; i < ECF8V_MAX_SYM; i += kTB) s_len[i] = d->len[i];
             cur = ptens;
         }
         // the table is in place and the previous block's write-back (which
