@@ -430,6 +430,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", default="512,2048", help="copycal mode: copy sizes in MiB (comma list)")
+    ap.add_argument("--chunk-bytes", type=int, default=16, help="decode mode: stream bytes per lane (C)")
+    ap.add_argument("--lanes", type=int, default=256, help="decode mode: lanes per block (TB)")
     ap.add_argument("--mode", default="decode", choices=["decode", "pipeline", "alpha", "encode", "variant", "copycal"],
                     help="decode: the batched decode step (default); pipeline: decode-on-use of the "
                          "block's layers beside FP8 GEMMs, against resident FP8 weights")
@@ -473,7 +475,7 @@ def main():
         gen = synth.workload_tensors(wl, device=d)
     names, xs, encs_host, encs = [], [], [], []
     for name, x in gen:
-        h = E.encode(x.cpu())
+        h = E.encode(x.cpu(), chunk_bytes=args.chunk_bytes, threads_per_block=args.lanes)
         names.append(name)
         xs.append(x.reshape(-1))
         if wl != "moe256":
@@ -564,7 +566,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[wl], "name": wl, "tensors": len(encs), "elements": n_total,
                    "compressed_bytes": bb["read"], "bits_per_element": round(8.0 * bb["read"] / n_total, 4),
-                   "chunk_bytes": 16, "lanes_per_block": 256, "launches_per_step": len(plans),
+                   "chunk_bytes": args.chunk_bytes, "lanes_per_block": args.lanes, "launches_per_step": len(plans),
                    "grid": int(max(p.plan.grid for p in plans))},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

@@ -78,10 +78,13 @@ typedef struct {
 } ecf8_codebook;
 
 /* Chunk bytes per lane (C) and lanes per block (TB).  ECF8 blog §3.2.1 / §5.2
- * describe per-thread chunks and 128-thread blocks on their hardware; here
- * they are format parameters.  Encode accepts C in {4,8,...,64} (multiple of 4)
- * and TB in {64,128,...,1024} (multiple of 64).  Decode kernels exist for
- * (C, TB) = (16, 256); other pairs decode with ECF8_ERR_UNSUPPORTED. */
+ * describe 64-byte per-thread chunks and 128-thread blocks on their hardware;
+ * here they are format parameters.  Encode accepts C in {4,8,...,64}
+ * (multiple of 4) and TB in {64,128,...,1024} (multiple of 64).  Decode
+ * kernels exist for (C, TB) = (16, 256) (the tuned shape), (32, 256),
+ * (64, 128) (the pages' shape), (16, 128), (8, 256) and (16, 512); other
+ * pairs decode with ECF8_ERR_UNSUPPORTED.  All tensors of one batched decode
+ * share one shape (ECF8_ERR_UNSUPPORTED otherwise). */
 typedef struct {
     uint32_t chunk_bytes;
     uint32_t threads_per_block;

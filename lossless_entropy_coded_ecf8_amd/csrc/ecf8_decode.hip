@@ -62,8 +62,8 @@ constexpr int kWin = 11;                                            // primary w
 constexpr int kLongPrefixMax = 8;                                   // prefixes of codes > kWin bits
 constexpr int kTableMax = (1 << kWin) + ((1 << (16 - kWin)) - 1) * kLongPrefixMax;  // 2296
 constexpr uint32_t kTabStride = 2304;                               // entries per table array
-constexpr int kChunk = 16;                                          // C
-constexpr int kLanes = 256;                                         // TB
+constexpr int kChunk = 16;                                          // the tuned shape: C
+constexpr int kLanes = 256;                                         // and TB
 constexpr uint64_t kStatusBytes = 256;
 constexpr int kTableThreads = 256;
 constexpr int kNibPrefetch = 4;                                     // write-back groups prefetched per lane
@@ -353,18 +353,25 @@ __device__ __forceinline__ int table_index(uint32_t win, int cd)
     return m;
 }
 
-// One table lookup at stream position r (r = 192 - bit position within the
-// lane's chunk): 32-bit window from the lane's two LDS rows, then the index
-// max(prefix11, prefix16 - cd) into the packed table.
+// log2 of TB / 8: (r & ~31) << kPitchShift<TB> = (r >> 5) * (4 * TB), the byte
+// offset of row r >> 5 in rows of TB dwords
+template <int TB>
+constexpr int kPitchShift = TB == 64 ? 3 : TB == 128 ? 4 : TB == 256 ? 5 : TB == 512 ? 6 : 7;
+
+// One table lookup at stream position r (r = 32 (S + 1) - bit position within
+// the lane's chunk, S = C / 4 + 1 words per lane): 32-bit window from the
+// lane's two LDS rows, then the index max(prefix11, prefix16 - cd) into the
+// packed table.
+template <int TB>
 __device__ __forceinline__ uint32_t lookup(const char* s_stream_b, const uint32_t* s_tx, uint32_t col_addr,
                                            uint32_t r, int cd)
 {
-    // a = col_addr + 4 * kLanes * ((r >> 5) - 2), as one v_and + one v_lshl_add
-    static_assert(4 * kLanes == 32 << 5, "row pitch");
+    // a = col_addr + 4 * TB * ((r >> 5) - 2), as one v_and + one v_lshl_add
+    static_assert((4 * TB) == (32 << kPitchShift<TB>), "row pitch");
     uint32_t a;
-    asm("v_lshl_add_u32 %0, %1, 5, %2" : "=v"(a) : "v"(r & 0xE0u), "v"(col_addr - 2u * 4u * kLanes));
+    asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(a) : "v"(r & ~31u), "i"(kPitchShift<TB>), "v"(col_addr - 2u * 4u * TB));
     const uint32_t w1 = *reinterpret_cast<const uint32_t*>(s_stream_b + a);
-    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(s_stream_b + a + 4u * kLanes);
+    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(s_stream_b + a + 4u * TB);
     const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, r);
     return s_tx[table_index(win, cd)];
 }
@@ -435,7 +442,7 @@ __device__ __forceinline__ uint32_t add_byte0(uint32_t acc, uint32_t e)
 // time so that every record index is static (the records stay in registers).
 // A lane past its end keeps looking up at its final position but records 0
 // (no bits, no symbols); the step loop ends when no lane of the wave is active.
-template <int Q>
+template <int TB, int Q>
 __device__ __forceinline__ void count_steps(const char* s_stream_b, const uint32_t* s_tx, uint32_t col_addr, int cd,
                                             uint32_t rend, uint32_t& r, uint32_t& cnt4, uint32_t& lastex, bool& act,
                                             int& nq, uint32_t (&rec)[kRecords])
@@ -445,7 +452,7 @@ __device__ __forceinline__ void count_steps(const char* s_stream_b, const uint32
         nq = Q + 1;
 #pragma unroll
         for (int j = 0; j < kStep; ++j) {
-            const uint32_t e = lookup(s_stream_b, s_tx, col_addr, r, cd);
+            const uint32_t e = lookup<TB>(s_stream_b, s_tx, col_addr, r, cd);
             const uint32_t em = act ? e : 0u;
             lastex = act ? e : lastex;
             rec[kStep * Q + j] = em;
@@ -453,7 +460,7 @@ __device__ __forceinline__ void count_steps(const char* s_stream_b, const uint32
             cnt4 = add_byte0(cnt4, em);
             act = r > rend;
         }
-        count_steps<Q + 1>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
+        count_steps<TB, Q + 1>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
     }
 }
 
@@ -473,13 +480,24 @@ __device__ __forceinline__ uint32_t emit_steps(uint32_t* s_out, uint32_t ob, int
     return ob;
 }
 
+// LDS of one decode workgroup, in dwords: decode table | nibble staging |
+// stream rows | wave sums.  For the tuned shape (C = 16) the stream rows are
+// the first dwords of the staging (the rows are read only by the count pass,
+// the staging written only after the scan), which keeps 6 workgroups on a
+// compute unit.  For other chunk sizes the rows have their own memory, so
+// that lanes with more lookups than records can walk the rest from LDS.
 template <int C, int TB>
 struct DecodeLds {
     static constexpr int kSlot = C / 4 + 1;                                   // dwords per lane: chunk + look-ahead
     static constexpr int kStreamDw = TB * (kSlot + 1);                        // rows, + one row only read at shift 0
     static constexpr int kOutDw = ((8 * C * TB + 15 + 8 + 16) / 8 + 2 + 3) / 4 * 4;   // nibble staging
-    static constexpr int kUnionDw = kOutDw > kStreamDw ? kOutDw : kStreamDw;
+    static constexpr bool kShared = C == kChunk;                              // rows inside the staging
+    static constexpr int kUnionDw = kShared ? (kOutDw > kStreamDw ? kOutDw : kStreamDw) : kOutDw;
+    static constexpr int kRowsOff = (int)kTabStride + (kShared ? 0 : kUnionDw);
+    static constexpr int kSumOff = (int)kTabStride + kUnionDw + (kShared ? 0 : (kStreamDw + 3) / 4 * 4);
+    static constexpr int kDw = kSumOff + TB / 64;
     static_assert(kUnionDw % 4 == 0, "cleared as 16-byte words");
+    static_assert(kShared || C == 4 || C == 8 || C % 16 == 0, "chunk loads of 4, 8 or a multiple of 16 bytes");
 };
 
 // Window at bit position p (p < 128 + 16) of a lane's chunk held in registers
@@ -499,8 +517,9 @@ __device__ __forceinline__ uint32_t reg_window(const uint32_t (&w)[5], uint32_t 
 // block offsets are loaded lane-parallel (lane 0: blk_off[b], lane 1:
 // blk_off[b+1]) and broadcast with readlane where they are first needed, so
 // that no wait for the prefetch is forced right after it is issued.
+template <int C>
 struct BlockIn {
-    uint4 sv;          // the lane's 16 stream bytes
+    uint32_t sv[C / 4];   // the lane's C stream bytes (little-endian words)
     uint32_t la;       // first dword of the next lane's chunk (look-ahead)
     uint32_t gb;       // byte holding the lane's gap
     uint64_t off;      // lane 0: blk_off[b]; lane 1: blk_off[b + 1]
@@ -569,7 +588,8 @@ __device__ __forceinline__ void load_nibbles(Rsrc rn, int tid, uint2 (&nv)[kNibP
     }
 }
 
-__device__ __forceinline__ void load_block(const NextTensor& nt, uint64_t gblk, int tid, BlockIn& in)
+template <int C, int TB>
+__device__ __forceinline__ void load_block(const NextTensor& nt, uint64_t gblk, int tid, BlockIn<C>& in)
 {
     const uint64_t b = gblk - nt.begin;
     // block offsets first: they are the first of these loads to be needed
@@ -577,10 +597,25 @@ __device__ __forceinline__ void load_block(const NextTensor& nt, uint64_t gblk, 
     in.off = ((uint64_t)o.y << 32) | o.x;
     // the block's chunks and the look-ahead word of its last lane (the stream
     // has 16 bytes past its last block)
-    const Rsrc rs = make_rsrc(nt.stream + b * (kLanes * kChunk), kLanes * kChunk + 16);
-    in.sv = bld4(rs, tid * kChunk);
-    in.la = bld(rs, tid * kChunk + kChunk);
-    in.gb = bld1(make_rsrc(nt.gaps + b * (kLanes / 2), kLanes / 2), tid >> 1);
+    const Rsrc rs = make_rsrc(nt.stream + b * ((uint64_t)TB * C), (uint64_t)TB * C + 16);
+    if constexpr (C % 16 == 0) {
+#pragma unroll
+        for (int k = 0; k < C / 16; ++k) {
+            const uint4 v = bld4(rs, tid * C + 16 * k);
+            in.sv[4 * k] = v.x;
+            in.sv[4 * k + 1] = v.y;
+            in.sv[4 * k + 2] = v.z;
+            in.sv[4 * k + 3] = v.w;
+        }
+    } else if constexpr (C == 8) {
+        const uint2 v = bld2(rs, tid * C);
+        in.sv[0] = v.x;
+        in.sv[1] = v.y;
+    } else {
+        in.sv[0] = bld(rs, tid * C);
+    }
+    in.la = bld(rs, tid * C + C);
+    in.gb = bld1(make_rsrc(nt.gaps + b * (TB / 2), TB / 2), tid >> 1);
 }
 
 __device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l)
@@ -594,40 +629,48 @@ __device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l)
 #define ECF8_MIN_WAVES 6
 #endif
 
+// Waves per SIMD the register allocation aims for: ECF8_MIN_WAVES, or fewer
+// where the workgroup's LDS already allows fewer (160 KB per compute unit).
 template <int C, int TB>
-__global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAVES))) void ecf8_decode_kernel(const DevDesc* __restrict__ descs, int count,
+constexpr int kWavesTarget = [] {
+    const int wgs = 160 * 1024 / (DecodeLds<C, TB>::kDw * 4);
+    const int w = wgs * (TB / 64) / 4;
+    return w < 1 ? 1 : (w < ECF8_MIN_WAVES ? w : ECF8_MIN_WAVES);
+}();
+
+template <int C, int TB>
+__global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(kWavesTarget<C, TB>))) void ecf8_decode_kernel(const DevDesc* __restrict__ descs, int count,
                                                          uint64_t total_blocks,
                                                          const uint32_t* __restrict__ tables,
                                                          unsigned long long* __restrict__ status)
 {
-    static_assert(C == kChunk && TB == kLanes, "one instantiation");
     using L = DecodeLds<C, TB>;
     constexpr int kWaves = TB / 64;
     constexpr int S = L::kSlot;
-    // One LDS arena: decode table | nibble staging, whose first S * TB dwords
-    // double as the stream rows | wave sums.  The stream rows are read only by
-    // the count pass and the staging is written only after the block-wide
-    // scan, so the two share memory: a lane clears its own rows once it has
-    // counted, the write-back clears what the decode wrote, and a barrier at
-    // the top of each block orders the previous block's write-back before the
-    // new rows are written.
+    constexpr uint32_t R0 = 32u * (S + 1);     // r = R0 - bit position in the lane's chunk
+    // One LDS arena: decode table | nibble staging | (stream rows) | wave
+    // sums.  For C = 16 the first S * TB dwords of the staging double as the
+    // stream rows: they are read only by the count pass and the staging is
+    // written only after the block-wide scan, so a lane clears its own rows
+    // once it has counted, the write-back clears what the decode wrote, and a
+    // barrier at the top of each block orders the previous block's write-back
+    // before the new rows are written.
     constexpr int kUnionOff = (int)kTabStride;
-    constexpr int kSumOff = kUnionOff + L::kUnionDw;
-    __shared__ __align__(256) uint32_t lds[kSumOff + kWaves];
+    __shared__ __align__(256) uint32_t lds[L::kDw];
     uint32_t* const s_tx = lds;
     uint32_t* const s_out = lds + kUnionOff;
-    uint32_t* const s_stream = lds + kUnionOff;
-    uint32_t* const s_wsum = lds + kSumOff;
+    uint32_t* const s_stream = lds + L::kRowsOff;
+    uint32_t* const s_wsum = lds + L::kSumOff;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     // Lane words in word-major, reversed order: word k of the lane's chunk
     // (k = 0..S-1, k = S-1 the look-ahead) lives in row S - k, element tid;
     // row S + 1 (staging memory) is only read with a zero funnel shift, and a
-    // finished lane may read row 0 (the last table dwords) for a window it drops.  With
-    // r = 192 - bitpos, the window pair (word ceil(bitpos/32)-1, next word) is
-    // rows (r >> 5) and (r >> 5) - 1, and the funnel shift is r & 31.
-    static_assert(S == 5, "r = 192 - bitpos assumes 4 chunk words + look-ahead");
+    // finished lane may read row 0 (dwords before the rows) for a window it
+    // drops.  With r = R0 - bitpos, the window pair (word ceil(bitpos/32)-1,
+    // next word) is rows (r >> 5) and (r >> 5) - 1, and the funnel shift is
+    // r & 31.
     uint32_t* const col = s_stream - TB + tid;                 // col[row * TB] = row `row`, rows 1..S+1
     const uint32_t col_addr = (uint32_t)tid * 4u;              // byte address of row 1, this lane
     const char* const s_stream_b = reinterpret_cast<const char*>(s_stream);
@@ -639,13 +682,13 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
     NextTensor nt;
     fetch_next_tensor(descs, 0, nt);
     while (nt.t + 1 < count && blk >= nt.end) fetch_next_tensor(descs, nt.t + 1, nt);
-    BlockIn nx;
-    load_block(nt, blk, tid, nx);
+    BlockIn<C> nx;
+    load_block<C, TB>(nt, blk, tid, nx);
     int ptens = nt.t;                  // tensor of the prefetched block
     const uint32_t cap = 8u * C * TB;  // staging capacity in elements
     // wait for the first block's loads here, so that at the loop head only the
     // back edge has loads in flight and the compiler can count them exactly
-    asm volatile("" ::"v"(nx.sv.x), "v"(nx.la), "v"(nx.gb), "v"((uint32_t)nx.off));
+    asm volatile("" ::"v"(nx.sv[0]), "v"(nx.la), "v"(nx.gb), "v"((uint32_t)nx.off));
 
     // fields of the tensor being decoded
     int cur = -1;
@@ -657,7 +700,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
     uint32_t c_ok = 0;
 
     for (; blk < total_blocks; blk += gridDim.x) {
-        const BlockIn in = nx;
+        const BlockIn<C> in = nx;
         if (ptens != cur) {
             const DevDesc* d = descs + ptens;
             c_begin = d->block_begin;
@@ -687,11 +730,9 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
         // write-back, whose staging memory the stream rows reuse
         __syncthreads();
         // stage the chunk (big-endian words, reversed order) into the lane's rows
-        col[S * TB] = __builtin_bswap32(in.sv.x);
-        col[(S - 1) * TB] = __builtin_bswap32(in.sv.y);
-        col[(S - 2) * TB] = __builtin_bswap32(in.sv.z);
-        col[(S - 3) * TB] = __builtin_bswap32(in.sv.w);
-        col[(S - 4) * TB] = __builtin_bswap32(in.la);
+#pragma unroll
+        for (int k = 0; k < C / 4; ++k) col[(S - k) * TB] = __builtin_bswap32(in.sv[k]);
+        col[TB] = __builtin_bswap32(in.la);                   // row 1: the look-ahead word
         const uint64_t b = blk - c_begin;
         // stream bits of the tensor from this block's start (uniform), then the
         // lane's own: E = bits of its chunk before the end of the stream
@@ -720,7 +761,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
         const uint64_t nb = blk + gridDim.x;
         const uint64_t nbe = nb < total_blocks ? nb : blk;
         while (nt.t + 1 < count && nbe >= nt.end) fetch_next_tensor(descs, nt.t + 1, nt);
-        load_block(nt, nbe, tid, nx);
+        load_block<C, TB>(nt, nbe, tid, nx);
         ptens = nt.t;
 
         // Wave priorities rise through the block: count 1, scan and decode 2,
@@ -737,25 +778,27 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
         // stream is walked once (lanes with more than kRecords lookups finish with
         // a plain walk).
         const int cd = c_cd;
-        const uint32_t rend = 192u - E;
-        const uint32_t r0 = 192u - gap;
+        const uint32_t rend = R0 - E;
+        const uint32_t r0 = R0 - gap;
         uint32_t rec[kRecords];
         uint32_t r = r0;
         uint32_t cnt4 = 0, lastex = 0;
         bool act = r > rend;
         int nq = 0;                        // steps taken (wave-uniform)
-        count_steps<0>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
+        count_steps<TB, 0>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
         const uint32_t r_rec = r;          // where the recorded lookups end
         while (r > rend) {
-            const uint32_t e = lookup(s_stream_b, s_tx, col_addr, r, cd);
+            const uint32_t e = lookup<TB>(s_stream_b, s_tx, col_addr, r, cd);
             lastex = e;
             r -= (e >> 8) & 0xFFu;
             cnt4 += e & 0xFFu;
         }
         __builtin_amdgcn_s_setprio(2);
-        // the lane's rows are staging memory from here on: leave them cleared
+        if constexpr (L::kShared) {
+            // the lane's rows are staging memory from here on: leave them cleared
 #pragma unroll
-        for (int k = 0; k < S; ++k) col[(S - k) * TB] = 0u;
+            for (int k = 0; k < S; ++k) col[(S - k) * TB] = 0u;
+        }
         uint32_t cnt = cnt4 >> 2;
         if (r != r0) {
             // the last lookup (at r + its bit count) may have decoded codewords
@@ -777,7 +820,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
 
         // the next block's inputs, issued at the top, are taken now, before
         // this block's stores
-        asm volatile("" ::"v"(nx.sv.x), "v"(nx.la), "v"(nx.gb), "v"((uint32_t)nx.off));
+        asm volatile("" ::"v"(nx.sv[0]), "v"(nx.la), "v"(nx.gb), "v"((uint32_t)nx.off));
 
         // ---- phase 3: block-wide exclusive scan of the counts
         const uint32_t incl = wave_inclusive_scan(cnt, lane);
@@ -801,19 +844,31 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
         // ob's dword when the spill is non-zero (a spill means the pair crossed)
         if (nq) atomicOr(&s_out[ob >> 5], carry);
         if (r_rec > rend) {
-            // lanes with more than kRecords lookups walk the rest from registers
-            // (their rows are staging memory now): reload the chunk (L2-resident)
-            const uint8_t* sp = c_stream + (b * TB + tid) * kChunk;
-            const uint4 cv = gld4(sp);
-            const uint32_t w[5] = {__builtin_bswap32(cv.x), __builtin_bswap32(cv.y), __builtin_bswap32(cv.z),
-                                   __builtin_bswap32(cv.w), __builtin_bswap32(gld(reinterpret_cast<const uint32_t*>(sp + kChunk)))};
+            // lanes with more than kRecords lookups walk the rest
             r = r_rec;
-            while (r > rend) {
-                const uint32_t win = reg_window(w, 192u - r);
-                const uint32_t ex = s_tx[table_index(win, cd)];
-                emit_symbols(s_out, ob, ex);
-                ob += ex & 0xFFu;
-                r -= (ex >> 8) & 0xFFu;
+            if constexpr (L::kShared) {
+                // their rows are staging memory now: reload the chunk (L2-resident)
+                // into registers and take windows from there
+                const uint8_t* sp = c_stream + (b * TB + tid) * C;
+                const uint4 cv = gld4(sp);
+                const uint32_t w[5] = {__builtin_bswap32(cv.x), __builtin_bswap32(cv.y), __builtin_bswap32(cv.z),
+                                       __builtin_bswap32(cv.w),
+                                       __builtin_bswap32(gld(reinterpret_cast<const uint32_t*>(sp + C)))};
+                while (r > rend) {
+                    const uint32_t win = reg_window(w, R0 - r);
+                    const uint32_t ex = s_tx[table_index(win, cd)];
+                    emit_symbols(s_out, ob, ex);
+                    ob += ex & 0xFFu;
+                    r -= (ex >> 8) & 0xFFu;
+                }
+            } else {
+                // their rows are intact: take windows from LDS
+                while (r > rend) {
+                    const uint32_t ex = lookup<TB>(s_stream_b, s_tx, col_addr, r, cd);
+                    emit_symbols(s_out, ob, ex);
+                    ob += ex & 0xFFu;
+                    r -= (ex >> 8) & 0xFFu;
+                }
             }
         }
         __syncthreads();
@@ -868,6 +923,49 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(ECF8_MIN_WAV
 }
 
 // ------------------------------------------------------------ host helpers
+// The (C, TB) shapes with a decode kernel.  (16, 256) is the tuned one; the
+// others decode the same format with the same steps (the pages' own 64-byte
+// chunks on 128 lanes among them).
+#define ECF8_DECODE_SHAPES(X) X(16, 256) X(32, 256) X(64, 128) X(16, 128) X(8, 256) X(16, 512)
+
+// Index of a supported shape, or -1.
+int shape_index(uint32_t C, uint32_t TB)
+{
+    int i = 0;
+#define ECF8_X(c, t) \
+    if (C == (c) && TB == (t)) return i; \
+    ++i;
+    ECF8_DECODE_SHAPES(ECF8_X)
+#undef ECF8_X
+    return -1;
+}
+
+const void* decode_kernel_ptr(int shape)
+{
+    int i = 0;
+#define ECF8_X(c, t) \
+    if (shape == i) return reinterpret_cast<const void*>(ecf8_decode_kernel<c, t>); \
+    ++i;
+    ECF8_DECODE_SHAPES(ECF8_X)
+#undef ECF8_X
+    return nullptr;
+}
+
+int launch_decode(uint32_t C, uint32_t TB, uint32_t grid, hipStream_t st, const DevDesc* dd, int count,
+                  uint64_t blocks, const uint32_t* tables, unsigned long long* status)
+{
+#define ECF8_X(c, t)                                                                                          \
+    if (C == (c) && TB == (t)) {                                                                              \
+        hipLaunchKernelGGL((ecf8_decode_kernel<c, t>), dim3(grid), dim3(t), 0, st, dd, count, blocks, tables, \
+                           status);                                                                           \
+        return hipGetLastError() == hipSuccess ? ECF8_OK : ECF8_ERR_HIP;                                      \
+    }
+    ECF8_DECODE_SHAPES(ECF8_X)
+#undef ECF8_X
+    return ECF8_ERR_UNSUPPORTED;
+}
+
+constexpr int kShapes = 6;
 struct DeviceInfo {
     int cus = 0;
     int occupancy = 0;
@@ -875,21 +973,22 @@ struct DeviceInfo {
 
 constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
-DeviceInfo g_dev[kMaxDevices];     // fixed size: the decode paths allocate no host memory either
+DeviceInfo g_dev[kMaxDevices][kShapes];   // fixed size: the decode paths allocate no host memory either
 
-int device_info(DeviceInfo* out)
+int device_info(uint32_t C, uint32_t TB, DeviceInfo* out)
 {
+    const int shape = shape_index(C, TB);
+    if (shape < 0 || shape >= kShapes) return ECF8_ERR_UNSUPPORTED;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return ECF8_ERR_HIP;
     if (dev < 0 || dev >= kMaxDevices) return ECF8_ERR_HIP;
     std::lock_guard<std::mutex> lk(g_dev_mu);
-    DeviceInfo& di = g_dev[dev];
+    DeviceInfo& di = g_dev[dev][shape];
     if (di.cus == 0) {
         int cus = 0, occ = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return ECF8_ERR_HIP;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &occ, reinterpret_cast<const void*>(ecf8_decode_kernel<kChunk, kLanes>), kLanes, 0) != hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_kernel_ptr(shape), (int)TB, 0) != hipSuccess)
             return ECF8_ERR_HIP;
         di.cus = cus > 0 ? cus : 1;
         di.occupancy = occ > 0 ? occ : 1;
@@ -908,7 +1007,7 @@ int fill_desc(const ecf8_tensor_desc& td, uint8_t* out_base, uint64_t& blocks, D
     const ecf8_meta& m = td.meta;
     int rc = ecf8_validate_meta(&m);
     if (rc) return rc;
-    if (m.chunk_bytes != (uint32_t)kChunk || m.threads_per_block != (uint32_t)kLanes) return ECF8_ERR_UNSUPPORTED;
+    if (shape_index(m.chunk_bytes, m.threads_per_block) < 0) return ECF8_ERR_UNSUPPORTED;
     if (m.n > 0) {
         if (!out_base || !td.s.stream || !td.s.nibbles || !td.s.gaps || !td.s.blk_off) return ECF8_ERR_ARG;
         if (!aligned(td.s.stream, 16) || !aligned(td.s.nibbles, 8) || !aligned(td.s.blk_off, 8) ||
@@ -930,6 +1029,25 @@ int fill_desc(const ecf8_tensor_desc& td, uint8_t* out_base, uint64_t& blocks, D
     return ECF8_OK;
 }
 
+// The (C, TB) all tensors of a batch share: every tensor's own, which must be
+// a supported shape and the same for all (ECF8_ERR_UNSUPPORTED otherwise).
+// An empty batch takes the tuned shape.
+int batch_shape(const ecf8_tensor_desc* descs, int count, uint32_t* C, uint32_t* TB)
+{
+    *C = kChunk;
+    *TB = kLanes;
+    for (int i = 0; i < count; ++i) {
+        const ecf8_meta& m = descs[i].meta;
+        if (i == 0) {
+            *C = m.chunk_bytes;
+            *TB = m.threads_per_block;
+        } else if (m.chunk_bytes != *C || m.threads_per_block != *TB) {
+            return ECF8_ERR_UNSUPPORTED;
+        }
+    }
+    return shape_index(*C, *TB) >= 0 || count == 0 ? ECF8_OK : ECF8_ERR_UNSUPPORTED;
+}
+
 }  // namespace
 
 extern "C" uint64_t ecf8_workspace_bytes(int count)
@@ -949,15 +1067,18 @@ extern "C" int ecf8_decode_prepare(const ecf8_tensor_desc* descs, int count, uin
     std::vector<unsigned char> host(table_offset(count) - 0, 0);   // status + descriptors
     DevDesc* hd = reinterpret_cast<DevDesc*>(host.data() + desc_offset());
     uint64_t blocks = 0;
+    uint32_t C = kChunk, TB = kLanes;
+    int rc = batch_shape(descs, count, &C, &TB);
+    if (rc) return rc;
     for (int i = 0; i < count; ++i) {
-        int rc = fill_desc(descs[i], out_base, blocks, hd[i]);
+        rc = fill_desc(descs[i], out_base, blocks, hd[i]);
         if (rc) return rc;
     }
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     if (hipMemcpyAsync(workspace, host.data(), host.size(), hipMemcpyHostToDevice, st) != hipSuccess)
         return ECF8_ERR_HIP;
     DeviceInfo di;
-    int rc = device_info(&di);
+    rc = device_info(C, TB, &di);
     if (rc) return rc;
     uint64_t grid = (uint64_t)di.cus * (uint64_t)di.occupancy;
     if (grid > blocks) grid = blocks;
@@ -965,8 +1086,8 @@ extern "C" int ecf8_decode_prepare(const ecf8_tensor_desc* descs, int count, uin
     plan->workspace_bytes = workspace_bytes;
     plan->total_blocks = blocks;
     plan->count = (uint32_t)count;
-    plan->chunk_bytes = kChunk;
-    plan->threads_per_block = kLanes;
+    plan->chunk_bytes = C;
+    plan->threads_per_block = TB;
     plan->grid = (uint32_t)grid;
     return ECF8_OK;
 }
@@ -979,8 +1100,7 @@ int check_plan(const ecf8_plan* plan)
     if (plan->count == 0 || plan->total_blocks == 0) return ECF8_OK;
     if (!plan->workspace || plan->workspace_bytes < ecf8_workspace_bytes((int)plan->count))
         return ECF8_ERR_WORKSPACE;
-    if (plan->chunk_bytes != (uint32_t)kChunk || plan->threads_per_block != (uint32_t)kLanes || plan->grid == 0)
-        return ECF8_ERR_ARG;
+    if (shape_index(plan->chunk_bytes, plan->threads_per_block) < 0 || plan->grid == 0) return ECF8_ERR_ARG;
     return ECF8_OK;
 }
 
@@ -1007,10 +1127,8 @@ extern "C" int ecf8_decode_blocks(const ecf8_plan* plan, void* hip_stream)
     DevDesc* dd = reinterpret_cast<DevDesc*>(ws + desc_offset());
     uint32_t* tables = reinterpret_cast<uint32_t*>(ws + table_offset((int)plan->count));
     auto* status = reinterpret_cast<unsigned long long*>(ws);
-    hipLaunchKernelGGL((ecf8_decode_kernel<kChunk, kLanes>), dim3(plan->grid), dim3(kLanes), 0,
-                       reinterpret_cast<hipStream_t>(hip_stream), dd, (int)plan->count, plan->total_blocks,
-                       tables, status);
-    return hipGetLastError() == hipSuccess ? ECF8_OK : ECF8_ERR_HIP;
+    return launch_decode(plan->chunk_bytes, plan->threads_per_block, plan->grid, reinterpret_cast<hipStream_t>(hip_stream),
+                         dd, (int)plan->count, plan->total_blocks, tables, status);
 }
 
 extern "C" int ecf8_decode_run(const ecf8_plan* plan, void* hip_stream)
@@ -1122,15 +1240,18 @@ extern "C" int ecf8_decode_batched_noalloc(const ecf8_tensor_desc* descs, int co
     if (bad_blocks && !aligned(bad_blocks, 8)) return ECF8_ERR_ARG;
     DevDesc hd[kNoAllocMaxTensors];
     uint64_t blocks = 0;
+    uint32_t C = kChunk, TB = kLanes;
+    int rc = batch_shape(descs, count, &C, &TB);
+    if (rc) return rc;
     for (int i = 0; i < count; ++i) {
-        int rc = fill_desc(descs[i], out_base, blocks, hd[i]);
+        rc = fill_desc(descs[i], out_base, blocks, hd[i]);
         if (rc) return rc;
     }
     unsigned char* ws = nullptr;
-    int rc = noalloc_scratch(&ws);
+    rc = noalloc_scratch(&ws);
     if (rc) return rc;
     DeviceInfo di;
-    rc = device_info(&di);
+    rc = device_info(C, TB, &di);
     if (rc) return rc;
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     auto* status = bad_blocks ? reinterpret_cast<unsigned long long*>(bad_blocks)
@@ -1149,8 +1270,7 @@ extern "C" int ecf8_decode_batched_noalloc(const ecf8_tensor_desc* descs, int co
         hipLaunchKernelGGL(ecf8_table_kernel, dim3(count, kTableSlices), dim3(kTableThreads), 0, st, dd, tables, status);
         uint64_t grid = (uint64_t)di.cus * (uint64_t)di.occupancy;
         if (grid > blocks) grid = blocks;
-        hipLaunchKernelGGL((ecf8_decode_kernel<kChunk, kLanes>), dim3((uint32_t)grid), dim3(kLanes), 0, st, dd, count,
-                           blocks, tables, status);
+        return launch_decode(C, TB, (uint32_t)grid, st, dd, count, blocks, tables, status);
     }
     return hipGetLastError() == hipSuccess ? ECF8_OK : ECF8_ERR_HIP;
 }

@@ -35,7 +35,12 @@ C, TB = 16, 256
 K_WIN = 11
 K_TABLE_MAX = (1 << K_WIN) + ((1 << (16 - K_WIN)) - 1) * 8
 RECORDS, STEP = 20, 4
-OUT_DW = ((8 * C * TB + 15 + 8 + 16) // 8 + 2 + 3) // 4 * 4        # staging dwords in the kernel
+def out_dw(C, TB):
+    """Staging dwords of the kernel's LDS for shape (C, TB)."""
+    return ((8 * C * TB + 15 + 8 + 16) // 8 + 2 + 3) // 4 * 4
+
+
+OUT_DW = out_dw(C, TB)
 
 
 def build_table(lengths):
@@ -74,6 +79,9 @@ def lookup(tab, cd, bits, bitpos):
 
 def model_block(enc, tab, cd, b, quad=False):
     """Returns (staging dwords as python ints, max dword index touched, clear range in dwords, total)."""
+    C, TB = int(enc.meta.chunk_bytes), int(enc.meta.threads_per_block)
+    R0 = 32 * (C // 4 + 2)                        # r = R0 - bit position in the lane's chunk
+    OUT_DW = out_dw(C, TB)
     stream = enc.stream
     T = int(enc.meta.total_bits)
     lens = [int(v) for v in enc.lengths]          # python ints: packets exceed 64 bits
@@ -88,8 +96,8 @@ def model_block(enc, tab, cd, b, quad=False):
         E_ = min(max(leftc - t * 8 * C, 0), 8 * C)
         base = g * C
         raw = np.frombuffer(bytes(stream[base: base + C + 4]) + bytes(64), dtype=np.uint8)
-        lanes.append(dict(bits=np.unpackbits(raw), r=192 - gap, r0=192 - gap, rend=192 - E_, cnt4=0, lastex=0,
-                          rec=[], act=(192 - gap) > (192 - E_)))
+        lanes.append(dict(bits=np.unpackbits(raw), r=R0 - gap, r0=R0 - gap, rend=R0 - E_, cnt4=0, lastex=0,
+                          rec=[], act=(R0 - gap) > (R0 - E_)))
     # count pass: wave-uniform steps, records, then lanes past the records keep walking
     for w0 in range(0, TB, 64):
         wave = lanes[w0:w0 + 64]
@@ -98,7 +106,7 @@ def model_block(enc, tab, cd, b, quad=False):
                 break
             for L in wave:
                 for _ in range(STEP):
-                    e = lookup(tab, cd, L["bits"], 192 - L["r"]) if L["act"] else 0
+                    e = lookup(tab, cd, L["bits"], R0 - L["r"]) if L["act"] else 0
                     em = e if L["act"] else 0
                     if L["act"]:
                         L["lastex"] = e
@@ -110,7 +118,7 @@ def model_block(enc, tab, cd, b, quad=False):
             L["r_rec"] = L["r"]
             L["extra"] = []
             while L["r"] > L["rend"]:
-                e = lookup(tab, cd, L["bits"], 192 - L["r"])
+                e = lookup(tab, cd, L["bits"], R0 - L["r"])
                 L["extra"].append(e)
                 L["lastex"] = e
                 L["r"] -= (e >> 8) & 0xFF
@@ -199,8 +207,19 @@ CASES = {
 @pytest.mark.parametrize("quad", [False, True], ids=["pairs_with_carry", "four_at_a_time"])
 @pytest.mark.parametrize("case", sorted(CASES))
 def test_block_model(case, quad):
+    check_model(case, quad, 16, 256)
+
+
+@pytest.mark.parametrize("shape", [(32, 256), (64, 128), (8, 256)], ids=str)
+@pytest.mark.parametrize("case", ["lowentropy", "two", "fib15"])
+def test_block_model_other_shapes(case, shape):
+    """The same model for other chunk sizes: longer chunks walk well past their 20 records."""
+    check_model(case, False, *shape)
+
+
+def check_model(case, quad, C, TB):
     x, L = CASES[case]()
-    enc = E.encode(x, lengths=L)
+    enc = E.encode(x, lengths=L, chunk_bytes=C, threads_per_block=TB)
     tab, cd, lens = build_table(list(enc.lengths))
     ref = oracle.decode(enc.stream, enc.nibbles, enc.n, enc.lengths)
     assert np.array_equal(ref, x)
@@ -208,7 +227,7 @@ def test_block_model(case, quad):
     for b in sorted({0, 1, nb - 1} & set(range(nb))):
         stage, top, clear_dw, total, a0, lo, hi = model_block(enc, tab, cd, b, quad=quad)
         assert total == hi - lo, ("count", b)
-        assert top < OUT_DW, ("staging dword out of range", top, OUT_DW)
+        assert top < out_dw(C, TB), ("staging dword out of range", top, out_dw(C, TB))
         assert top < clear_dw or all(v == 0 for v in stage[clear_dw:]), ("written past the cleared range", b)
         got = staging_nibbles(stage, a0, hi - lo)
         assert np.array_equal(got, (ref[lo:hi] >> 3) & 15), ("exponents", b)

@@ -86,6 +86,67 @@ def test_small_and_edge_cases_bit_exact(kind, n):
     assert bad.size == 0, "first mismatch at %d of %d (%s)" % (bad[0], n, kind)
 
 
+SHAPES = [(32, 256), (64, 128), (16, 128), (8, 256), (16, 512)]
+SHAPE_CASES = [("stable", 1), ("stable", 4097), ("stable", 1_000_003), ("gauss", 300_001), ("fib15", 200_000),
+               ("long12x6", 100_000), ("two", 150_000), ("single", 200_000), ("bytes", 77_777), ("uniform4", 65_536)]
+
+
+@pytest.mark.parametrize("C,TB", SHAPES, ids=lambda v: str(v))
+@pytest.mark.parametrize("kind,n", SHAPE_CASES, ids=lambda v: str(v))
+def test_other_shapes_bit_exact(C, TB, kind, n):
+    """The decode kernels for other (C, TB) shapes, among them the pages' 64-byte chunks on 128 lanes:
+    every byte equals the oracle's decode of the same stream, canaries intact (1-bit codes fill the
+    staging; 15-bit codes use the long-code table region; long chunks walk past their records)."""
+    d = dev()
+    x, L = make_input(kind, n, n + C + TB)
+    enc = E.encode(x, lengths=L, chunk_bytes=C, threads_per_block=TB)
+    got = decode_with_canaries(enc, d)
+    ref = oracle.decode(enc.stream, enc.nibbles, n, enc.lengths)
+    assert np.array_equal(ref, x)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, "first mismatch at %d of %d (%s, C=%d, TB=%d)" % (bad[0], n, kind, C, TB)
+
+
+@pytest.mark.parametrize("C,TB", SHAPES, ids=lambda v: str(v))
+def test_other_shapes_batched_and_checked(C, TB):
+    """A batched plan of one shape, run twice into a reused buffer; a corrupt gap is flagged exactly as
+    the oracle's count step predicts, and contained."""
+    d = dev()
+    kinds = [("stable", 300_001), ("fib15", 70_000), ("single", 40_000), ("gauss", 1 << 20), ("stable", 5)]
+    xs, encs, offs, off = [], [], [], 0
+    for i, (k, n) in enumerate(kinds):
+        x, L = make_input(k, n, 3000 + i)
+        xs.append(x)
+        encs.append(E.encode(x, lengths=L, chunk_bytes=C, threads_per_block=TB).to(d))
+        offs.append(off)
+        off += (n + 15) // 16 * 16 + 16
+    out = torch.full((off + 64,), CANARY, dtype=torch.uint8, device=d)
+    plan = E.DecodePlan(encs, out=out, offsets=offs)
+    for rep in range(2):
+        plan.run()
+        torch.cuda.synchronize()
+        for i, x in enumerate(xs):
+            assert np.array_equal(plan.view(i).cpu().numpy(), x), (rep, kinds[i])
+    assert plan.status() == 0
+    x, _ = make_input("stable", 400_000, 21)
+    enc = E.encode(x, chunk_bytes=C, threads_per_block=TB)
+    t = TB + 37
+    g0 = (int(enc.gaps[t >> 1]) >> (4 * (t & 1))) & 15
+    for delta in range(1, 16):
+        gaps = enc.gaps.copy()
+        g1 = (g0 + delta) % 16
+        gaps[t >> 1] = (gaps[t >> 1] & (0xF0 if t % 2 == 0 else 0x0F)) | (g1 << (4 * (t & 1)))
+        want_bad = expected_bad_blocks(enc.stream, gaps, enc)
+        if want_bad:
+            break
+    assert want_bad == [1]
+    denc = enc.to(d)
+    denc.gaps.copy_(torch.from_numpy(gaps).to(d))
+    _, bad, buf = decode_plan_with_canaries(denc, d)
+    assert bad == 1
+    check_contained(buf, x, enc, want_bad)
+
+
 def test_all_256_byte_values():
     d = dev()
     x = np.tile(np.arange(256, dtype=np.uint8), 1000)
@@ -319,9 +380,14 @@ def test_out_buffer_checks():
 def test_unsupported_and_misaligned_arguments():
     d = dev()
     x, _ = make_input("stable", 10_000, 8)
+    e12 = E.encode(x, chunk_bytes=12).to(d)
+    with pytest.raises(E.Ecf8Error) as ei:
+        E.decode(e12)
+    assert ei.value.code == -4
+    # tensors of two supported shapes in one batch
     e8 = E.encode(x, chunk_bytes=8).to(d)
     with pytest.raises(E.Ecf8Error) as ei:
-        E.decode(e8)
+        E.DecodePlan([E.encode(x).to(d), e8])
     assert ei.value.code == -4
     e16 = E.encode(x).to(d)
     buf = torch.empty(x.size + 32, dtype=torch.uint8, device=d)
