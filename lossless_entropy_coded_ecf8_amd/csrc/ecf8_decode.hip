@@ -358,13 +358,11 @@ __device__ __forceinline__ int table_index(uint32_t win, int cd)
 template <int TB>
 constexpr int kPitchShift = TB == 64 ? 3 : TB == 128 ? 4 : TB == 256 ? 5 : TB == 512 ? 6 : 7;
 
-// One table lookup at stream position r (r = 32 (S + 1) - bit position within
-// the lane's chunk, S = C / 4 + 1 words per lane): 32-bit window from the
-// lane's two LDS rows, then the index max(prefix11, prefix16 - cd) into the
-// packed table.
+// The 32-bit window at stream position r (r = 32 (S + 1) - bit position
+// within the lane's chunk, S = C / 4 + 1 words per lane), from the lane's two
+// LDS rows.
 template <int TB>
-__device__ __forceinline__ uint32_t lookup(const char* s_stream_b, const uint32_t* s_tx, uint32_t col_addr,
-                                           uint32_t r, int cd)
+__device__ __forceinline__ uint32_t window(const char* s_stream_b, uint32_t col_addr, uint32_t r)
 {
     // a = col_addr + 4 * TB * ((r >> 5) - 2), as one v_and + one v_lshl_add
     static_assert((4 * TB) == (32 << kPitchShift<TB>), "row pitch");
@@ -372,8 +370,28 @@ __device__ __forceinline__ uint32_t lookup(const char* s_stream_b, const uint32_
     asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(a) : "v"(r & ~31u), "i"(kPitchShift<TB>), "v"(col_addr - 2u * 4u * TB));
     const uint32_t w1 = *reinterpret_cast<const uint32_t*>(s_stream_b + a);
     const uint32_t w0 = *reinterpret_cast<const uint32_t*>(s_stream_b + a + 4u * TB);
-    const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, r);
-    return s_tx[table_index(win, cd)];
+    return __builtin_amdgcn_alignbit(w0, w1, r);
+}
+
+// One table lookup at stream position r: the window, then the index
+// max(prefix11, prefix16 - cd) into the packed table.
+template <int TB>
+__device__ __forceinline__ uint32_t lookup(const char* s_stream_b, const uint32_t* s_tx, uint32_t col_addr,
+                                           uint32_t r, int cd)
+{
+    return s_tx[table_index(window<TB>(s_stream_b, col_addr, r), cd)];
+}
+
+// The window after entry e: win << (bits e consumes), as one shift with a
+// byte select.  An entry consumes at most 16 bits, so the shifted window
+// still holds the 16 stream bits a lookup reads (the bits shifted in are
+// zeros, past what the index looks at).
+__device__ __forceinline__ uint32_t window_after(uint32_t win, uint32_t e)
+{
+    uint32_t w;
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD"
+        : "=v"(w) : "v"(e), "v"(win));
+    return w;
 }
 
 // OR the symbols of one table entry, as packed nibbles, into the zeroed
@@ -450,9 +468,14 @@ __device__ __forceinline__ void count_steps(const char* s_stream_b, const uint32
     if constexpr (Q < kRecords / kStep) {
         if (__builtin_amdgcn_ballot_w64(act) == 0) return;
         nq = Q + 1;
+        uint32_t win = 0;
+        // lookups in pairs: the second takes its window from the first's,
+        // shifted by the bits the first consumed (no LDS read of the rows)
 #pragma unroll
         for (int j = 0; j < kStep; ++j) {
-            const uint32_t e = lookup<TB>(s_stream_b, s_tx, col_addr, r, cd);
+            if (j % 2 == 0) win = window<TB>(s_stream_b, col_addr, r);
+            else win = window_after(win, rec[kStep * Q + j - 1]);
+            const uint32_t e = s_tx[table_index(win, cd)];
             const uint32_t em = act ? e : 0u;
             lastex = act ? e : lastex;
             rec[kStep * Q + j] = em;

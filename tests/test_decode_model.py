@@ -2,7 +2,8 @@
 
 The E4M3 decode kernel (ecf8_decode.hip) decodes a block of TB = 256 lanes,
 C = 16 stream bytes each: a count pass in wave-uniform steps of table lookups
-(entries recorded in registers), an exclusive scan of the counts, then a
+(entries recorded in registers; the second lookup of each pair takes the
+first one's window shifted by the bits it consumed), an exclusive scan of the counts, then a
 decode pass that ORs the recorded entries' symbols, two entries at a time,
 into an LDS staging area of packed nibbles, and a write-back of whole
 16-element groups.  This module re-enacts those steps in Python, with the
@@ -68,13 +69,23 @@ def build_table(lengths):
     return tab, cd, lengths
 
 
-def lookup(tab, cd, bits, bitpos):
-    """Entry for the 32-bit window at bitpos of a lane's bit array."""
+def window(bits, bitpos):
+    """The 32-bit window at bitpos of a lane's bit array."""
     w = 0
     for k in range(32):
         w = (w << 1) | int(bits[bitpos + k])
+    return w
+
+
+def entry(tab, cd, w):
+    """Table entry for a 32-bit window."""
     idx = min(max(w >> (32 - K_WIN), (w >> 16) - cd), K_TABLE_MAX - 1)
     return int(tab[idx])
+
+
+def lookup(tab, cd, bits, bitpos):
+    """Entry for the 32-bit window at bitpos of a lane's bit array."""
+    return entry(tab, cd, window(bits, bitpos))
 
 
 def model_block(enc, tab, cd, b, quad=False):
@@ -105,8 +116,14 @@ def model_block(enc, tab, cd, b, quad=False):
             if not any(L["act"] for L in wave):
                 break
             for L in wave:
-                for _ in range(STEP):
-                    e = lookup(tab, cd, L["bits"], R0 - L["r"]) if L["act"] else 0
+                for j in range(STEP):
+                    # pairs: the second lookup's window is the first's shifted
+                    # by the bits the first consumed (zeros shifted in)
+                    if j % 2 == 0:
+                        w = window(L["bits"], R0 - L["r"])
+                    else:
+                        w = (w << ((L["rec"][-1] >> 8) & 0xFF)) & 0xFFFFFFFF
+                    e = entry(tab, cd, w)
                     em = e if L["act"] else 0
                     if L["act"]:
                         L["lastex"] = e
