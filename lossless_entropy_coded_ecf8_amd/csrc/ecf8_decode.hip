@@ -301,9 +301,13 @@ __device__ __forceinline__ uint2 assemble8(uint32_t e, uint32_t nm)
 
 // Write back group g (elements 16g .. 16g+15 of the block-relative range):
 // exponent nibbles from the LDS staging, sign/mantissa nibbles nm from HBM.
-__device__ __forceinline__ void group_bytes(const uint32_t* s_out, uint32_t g, uint2 nm, uint32_t w[4])
+// The staging group is cleared once read (the next block ORs into it); each
+// group is read, and so cleared, by one lane.
+__device__ __forceinline__ void group_bytes(uint32_t* s_out, uint32_t g, uint2 nm, uint32_t w[4])
 {
-    const uint2 ex = reinterpret_cast<const uint2*>(s_out)[g];
+    uint2* const sg = reinterpret_cast<uint2*>(s_out) + g;
+    const uint2 ex = *sg;
+    *sg = make_uint2(0u, 0u);
     const uint2 r0 = assemble8(ex.x, nm.x);
     const uint2 r1 = assemble8(ex.y, nm.y);
     w[0] = r0.x;
@@ -313,7 +317,7 @@ __device__ __forceinline__ void group_bytes(const uint32_t* s_out, uint32_t g, u
 }
 
 // A group fully inside the block's range: one 16-byte store.
-__device__ __forceinline__ void write_full(const uint32_t* s_out, Rsrc out_blk, uint32_t g, uint2 nm)
+__device__ __forceinline__ void write_full(uint32_t* s_out, Rsrc out_blk, uint32_t g, uint2 nm)
 {
     uint32_t w[4];
     group_bytes(s_out, g, nm, w);
@@ -322,7 +326,7 @@ __device__ __forceinline__ void write_full(const uint32_t* s_out, Rsrc out_blk, 
 
 // One of the (at most two) ragged edge groups of a block: store only the
 // bytes inside [a0, endo).
-__device__ __forceinline__ void write_edge(const uint32_t* s_out, Rsrc out_blk, uint32_t g, uint2 nm,
+__device__ __forceinline__ void write_edge(uint32_t* s_out, Rsrc out_blk, uint32_t g, uint2 nm,
                                            uint32_t a0, uint32_t endo)
 {
     uint32_t w[4];
@@ -903,22 +907,22 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(kWavesTarget
         const uint32_t endo = a0 + nw;                 // one past the last valid element, group-relative
         const uint32_t first_full = a0 ? 1u : 0u;
         const uint32_t end_full = endo >> 4;           // groups [first_full, end_full) are whole
-        // assemble prefetched groups four at a time, then issue their stores back to
-        // back: stores share the vector-memory counter with loads, so no wait falls
-        // between them
+        // assemble prefetched groups two at a time, then issue their stores back
+        // to back: stores share the vector-memory counter with loads, so no wait
+        // falls between them.  A lane assembles only groups it stores (a wave
+        // whose lanes have no second group skips it).  Group 0 of a block that
+        // starts mid-group is an edge, written below.
         static_assert(kNibPrefetch % 2 == 0, "write-back batches of two groups");
 #pragma unroll
         for (int k0 = 0; k0 < kNibPrefetch; k0 += 2) {
-            if (tid + k0 * TB >= end_full) break;
+            const uint32_t g0 = tid + k0 * TB, g1 = g0 + TB;
+            if (g0 >= end_full) break;
+            const bool one = g0 >= first_full, two = g1 < end_full;
             uint32_t wb[2][4];
-#pragma unroll
-            for (int k = 0; k < 2; ++k) group_bytes(s_out, tid + (k0 + k) * TB, nv[k0 + k], wb[k]);
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const uint32_t g = tid + (k0 + k) * TB;
-                if (g >= first_full && g < end_full)
-                    bst4(out_blk, 16u * g, wb[k][0], wb[k][1], wb[k][2], wb[k][3]);
-            }
+            if (one) group_bytes(s_out, g0, nv[k0], wb[0]);
+            if (two) group_bytes(s_out, g1, nv[k0 + 1], wb[1]);
+            if (one) bst4(out_blk, 16u * g0, wb[0][0], wb[0][1], wb[0][2], wb[0][3]);
+            if (two) bst4(out_blk, 16u * g1, wb[1][0], wb[1][1], wb[1][2], wb[1][3]);
         }
         for (uint32_t g = tid + kNibPrefetch * TB; g < end_full; g += TB)   // blocks of > 16K elements
             write_full(s_out, out_blk, g, bld2(nib_blk, 8u * g));
@@ -934,13 +938,16 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(kWavesTarget
             write_edge(s_out, out_blk, end_full, nm, a0, endo);
         }
         __builtin_amdgcn_s_setprio(0);
-        // clear the staging the decode wrote: groups [0, zend) cover every
-        // nibble OR-ed in, the codewords a last lane decodes past the end included
-        // (each group is cleared by the lane that read it above)
+        // The write-back read and cleared groups [0, groups).  The decode wrote
+        // groups [0, zend), the codewords a last lane decodes past the end
+        // included (and more or fewer when a corrupt block's count is off):
+        // clear the rest (groups no lane read; the next block writes the
+        // staging only after its barriers).
         {
             const uint32_t zend0 = (a0 + total + 3u + 15u) >> 4;
             const uint32_t zend = zend0 < (uint32_t)(L::kOutDw / 2) ? zend0 : (uint32_t)(L::kOutDw / 2);
-            for (uint32_t g = tid; g < zend; g += TB) reinterpret_cast<uint2*>(s_out)[g] = make_uint2(0u, 0u);
+            for (uint32_t g = groups + tid; g < zend; g += TB)
+                reinterpret_cast<uint2*>(s_out)[g] = make_uint2(0u, 0u);
         }
     }
 }
