@@ -305,9 +305,11 @@ __device__ __forceinline__ uint2 assemble8(uint32_t e, uint32_t nm)
 // group is read, and so cleared, by one lane.
 __device__ __forceinline__ void group_bytes(uint32_t* s_out, uint32_t g, uint2 nm, uint32_t w[4])
 {
-    uint2* const sg = reinterpret_cast<uint2*>(s_out) + g;
-    const uint2 ex = *sg;
-    *sg = make_uint2(0u, 0u);
+    const uint2 ex = reinterpret_cast<const uint2*>(s_out)[g];
+    // two dword stores of one zero register (a 64-bit store would hold a
+    // zero register pair live through the write-back)
+    s_out[2 * g] = 0u;
+    s_out[2 * g + 1] = 0u;
     const uint2 r0 = assemble8(ex.x, nm.x);
     const uint2 r1 = assemble8(ex.y, nm.y);
     w[0] = r0.x;
@@ -907,22 +909,13 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(kWavesTarget
         const uint32_t endo = a0 + nw;                 // one past the last valid element, group-relative
         const uint32_t first_full = a0 ? 1u : 0u;
         const uint32_t end_full = endo >> 4;           // groups [first_full, end_full) are whole
-        // assemble prefetched groups two at a time, then issue their stores back
-        // to back: stores share the vector-memory counter with loads, so no wait
-        // falls between them.  A lane assembles only groups it stores (a wave
-        // whose lanes have no second group skips it).  Group 0 of a block that
-        // starts mid-group is an edge, written below.
-        static_assert(kNibPrefetch % 2 == 0, "write-back batches of two groups");
+        // whole groups of the prefetched range, one store each (group 0 of a
+        // block that starts mid-group is an edge, written below)
 #pragma unroll
-        for (int k0 = 0; k0 < kNibPrefetch; k0 += 2) {
-            const uint32_t g0 = tid + k0 * TB, g1 = g0 + TB;
-            if (g0 >= end_full) break;
-            const bool one = g0 >= first_full, two = g1 < end_full;
-            uint32_t wb[2][4];
-            if (one) group_bytes(s_out, g0, nv[k0], wb[0]);
-            if (two) group_bytes(s_out, g1, nv[k0 + 1], wb[1]);
-            if (one) bst4(out_blk, 16u * g0, wb[0][0], wb[0][1], wb[0][2], wb[0][3]);
-            if (two) bst4(out_blk, 16u * g1, wb[1][0], wb[1][1], wb[1][2], wb[1][3]);
+        for (int k = 0; k < kNibPrefetch; ++k) {
+            const uint32_t g = tid + k * TB;
+            if (g >= end_full) break;
+            if (g >= first_full) write_full(s_out, out_blk, g, nv[k]);
         }
         for (uint32_t g = tid + kNibPrefetch * TB; g < end_full; g += TB)   // blocks of > 16K elements
             write_full(s_out, out_blk, g, bld2(nib_blk, 8u * g));
