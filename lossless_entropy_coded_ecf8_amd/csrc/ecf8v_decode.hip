@@ -106,7 +106,7 @@ struct Entry {
     static constexpr int kSymShift = kFmt == ECF8V_BF16 ? 0 : 2;          // symbol i: (e >> (8 + 8 i + kSymShift))
     static constexpr uint32_t kSym = kFmt == ECF8V_BF16 ? 255u : 31u;     //   & kSym
 };
-static_assert(kRecords % kStep == 0, "records are taken kStep at a time");
+static_assert(kRecords % kStep == 0 && kStep % 2 == 0, "records are taken kStep at a time, looked up in pairs");
 
 // Per-tensor descriptor in the workspace.
 struct DescV {
@@ -674,12 +674,21 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
         for (int q = 0; q < kRecords / kStep; ++q) {
             if (__builtin_amdgcn_ballot_w64(act) == 0) break;
             nq = q + 1;
+            // lookups in pairs: the second takes the first's window shifted by
+            // the bits the first consumed (at most 16, so the 16 bits an index
+            // reads are still stream bits); its rows are not read again
+            uint32_t win = 0;
 #pragma unroll
             for (int j = 0; j < kStep; ++j) {
-                const uint32_t a = col_lo | ((r & 0xE0u) << kPitchShift);   // col_lo < kPitch
-                const uint32_t wlo = *reinterpret_cast<const uint32_t*>(stage + a);
-                const uint32_t whi = *reinterpret_cast<const uint32_t*>(stage + a + kPitch);
-                const uint32_t e = s_tab[tab_index(__builtin_amdgcn_alignbit(whi, wlo, r), cd, last)];
+                if (j % 2 == 0) {
+                    const uint32_t a = col_lo | ((r & 0xE0u) << kPitchShift);   // col_lo < kPitch
+                    const uint32_t wlo = *reinterpret_cast<const uint32_t*>(stage + a);
+                    const uint32_t whi = *reinterpret_cast<const uint32_t*>(stage + a + kPitch);
+                    win = __builtin_amdgcn_alignbit(whi, wlo, r);
+                } else {
+                    win <<= rec[kStep * q + j - 1] & En::kNb & 31u;
+                }
+                const uint32_t e = s_tab[tab_index(win, cd, last)];
                 const uint32_t em = act ? e : 0u;
                 rec[kStep * q + j] = em;
                 lastex = act ? e : lastex;
