@@ -463,16 +463,20 @@ __device__ __forceinline__ uint32_t add_byte0(uint32_t acc, uint32_t e)
 }
 
 // The count pass in wave-uniform steps of kStep lookups, unrolled at compile
-// time so that every record index is static (the records stay in registers).
-// A lane past its end keeps looking up at its final position but records 0
-// (no bits, no symbols); the step loop ends when no lane of the wave is active.
-template <int TB, int Q>
+// time so that every record index is static (the records stay in registers):
+// steps Q .. QEND - 1.  Masked steps: a lane past its end keeps looking up at
+// its final position but records 0 (no bits, no symbols), and the walk ends
+// when no lane of the wave is active.  Unmasked steps are for lookups every
+// lane is sure to take (see kSureSteps).
+template <int TB, int Q, int QEND, bool kMasked>
 __device__ __forceinline__ void count_steps(const char* s_stream_b, const uint32_t* s_tx, uint32_t col_addr, int cd,
                                             uint32_t rend, uint32_t& r, uint32_t& cnt4, uint32_t& lastex, bool& act,
                                             int& nq, uint32_t (&rec)[kRecords])
 {
-    if constexpr (Q < kRecords / kStep) {
-        if (__builtin_amdgcn_ballot_w64(act) == 0) return;
+    if constexpr (Q < QEND) {
+        if constexpr (kMasked) {
+            if (__builtin_amdgcn_ballot_w64(act) == 0) return;
+        }
         nq = Q + 1;
         uint32_t win = 0;
         // lookups in pairs: the second takes its window from the first's,
@@ -482,16 +486,25 @@ __device__ __forceinline__ void count_steps(const char* s_stream_b, const uint32
             if (j % 2 == 0) win = window<TB>(s_stream_b, col_addr, r);
             else win = window_after(win, rec[kStep * Q + j - 1]);
             const uint32_t e = s_tx[table_index(win, cd)];
-            const uint32_t em = act ? e : 0u;
-            lastex = act ? e : lastex;
+            uint32_t em = e;
+            if constexpr (kMasked) {
+                em = act ? e : 0u;
+                lastex = act ? e : lastex;
+            }
             rec[kStep * Q + j] = em;
             r -= (em >> 8) & 0xFFu;
             cnt4 = add_byte0(cnt4, em);
-            act = r > rend;
+            if constexpr (kMasked) act = r > rend;
         }
-        count_steps<TB, Q + 1>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
+        count_steps<TB, Q + 1, QEND, kMasked>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
     }
 }
+
+// Steps every lane takes when its chunk is whole (E = 8C): the walk starts at
+// most 15 bits in and a lookup consumes at most 16 bits, so lookup k starts at
+// most at bit 15 + 16k, before 8C for every k < C / 2.
+template <int C>
+constexpr int kSureSteps = (C / 2 < kRecords ? C / 2 : kRecords) / kStep;
 
 // The decode pass over the recorded entries, two at a time, for the nq steps
 // the count pass took (compile-time unrolled like count_steps).
@@ -814,7 +827,19 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(kWavesTarget
         uint32_t cnt4 = 0, lastex = 0;
         bool act = r > rend;
         int nq = 0;                        // steps taken (wave-uniform)
-        count_steps<TB, 0>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
+        // a wave whose lanes all hold whole chunks takes its sure steps
+        // unmasked (no activity tests); lastex is then the last sure lookup
+        // until a masked step finds a later one
+        constexpr int U = kSureSteps<C>;
+        if (U > 0 && leftc >= 8u * C * 64u * (uint32_t)(wave + 1)) {
+            count_steps<TB, 0, U, false>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
+            lastex = rec[(U > 0 ? U : 1) * kStep - 1];
+            act = r > rend;
+        } else {
+            count_steps<TB, 0, U, true>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
+        }
+        count_steps<TB, U, kRecords / kStep, true>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq,
+                                                   rec);
         const uint32_t r_rec = r;          // where the recorded lookups end
         while (r > rend) {
             const uint32_t e = lookup<TB>(s_stream_b, s_tx, col_addr, r, cd);

@@ -16,6 +16,9 @@ re-walk of lanes with more lookups than records, and checks on every case:
   * every staging dword the decode touches lies below the kernel's staging
     size (the wave sums follow it in LDS), and the clearing range covers
     every dword written;
+  * in a wave whose lanes all hold whole chunks, every lane is active for
+    the first C / 2 lookups (rounded down to whole steps), which the kernel
+    takes without activity tests;
   * the same for a variant that ORs four entries at a time with three
     dwords from one base (+0, +4, +8 bytes), a form once measured and left
     out: the model shows whether its addresses or its packing could explain
@@ -109,14 +112,20 @@ def model_block(enc, tab, cd, b, quad=False):
         raw = np.frombuffer(bytes(stream[base: base + C + 4]) + bytes(64), dtype=np.uint8)
         lanes.append(dict(bits=np.unpackbits(raw), r=R0 - gap, r0=R0 - gap, rend=R0 - E_, cnt4=0, lastex=0,
                           rec=[], act=(R0 - gap) > (R0 - E_)))
-    # count pass: wave-uniform steps, records, then lanes past the records keep walking
+    # count pass: wave-uniform steps, records, then lanes past the records keep walking.
+    # A wave whose lanes all hold whole chunks takes its first `sure` lookups
+    # without activity tests: check that every lane is indeed active there.
+    sure = min(C // 2, RECORDS) // STEP * STEP
     for w0 in range(0, TB, 64):
         wave = lanes[w0:w0 + 64]
+        wave_full = leftc >= 8 * C * (w0 + 64)
         for q in range(RECORDS // STEP):
             if not any(L["act"] for L in wave):
                 break
             for L in wave:
                 for j in range(STEP):
+                    if wave_full and q * STEP + j < sure:
+                        assert L["act"], ("unmasked lookup of an inactive lane", w0, q, j)
                     # pairs: the second lookup's window is the first's shifted
                     # by the bits the first consumed (zeros shifted in)
                     if j % 2 == 0:
