@@ -431,6 +431,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", default="512,2048", help="copycal mode: copy sizes in MiB (comma list)")
     ap.add_argument("--chunk-bytes", type=int, default=16, help="decode mode: stream bytes per lane (C)")
+    ap.add_argument("--max-code-len", type=int, default=11,
+                    help="decode mode: code length limit of the encoding (11: every codeword fits the decode's "
+                         "11-bit table index; 16: plain Huffman)")
     ap.add_argument("--lanes", type=int, default=256, help="decode mode: lanes per block (TB)")
     ap.add_argument("--mode", default="decode", choices=["decode", "pipeline", "alpha", "encode", "variant", "copycal"],
                     help="decode: the batched decode step (default); pipeline: decode-on-use of the "
@@ -475,7 +478,7 @@ def main():
         gen = synth.workload_tensors(wl, device=d)
     names, xs, encs_host, encs = [], [], [], []
     for name, x in gen:
-        h = E.encode(x.cpu(), chunk_bytes=args.chunk_bytes, threads_per_block=args.lanes)
+        h = E.encode(x.cpu(), chunk_bytes=args.chunk_bytes, threads_per_block=args.lanes, max_len=args.max_code_len)
         names.append(name)
         xs.append(x.reshape(-1))
         if wl != "moe256":
@@ -566,7 +569,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[wl], "name": wl, "tensors": len(encs), "elements": n_total,
                    "compressed_bytes": bb["read"], "bits_per_element": round(8.0 * bb["read"] / n_total, 4),
-                   "chunk_bytes": args.chunk_bytes, "lanes_per_block": args.lanes, "launches_per_step": len(plans),
+                   "chunk_bytes": args.chunk_bytes, "lanes_per_block": args.lanes,
+                   "max_code_len": max(max(int(v) for v in e.meta.cb.len) for e in encs),
+                   "code_length_limit": args.max_code_len,
+                   "short_code_form": all(int(p.plan.short_codes) for p in plans), "launches_per_step": len(plans),
                    "grid": int(max(p.plan.grid for p in plans))},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

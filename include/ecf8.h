@@ -136,6 +136,11 @@ typedef struct {
                                 compute units to kernels on other streams: every
                                 workgroup walks blocks grid apart, so all blocks are
                                 decoded whatever the value */
+    uint32_t short_codes;    /* 1: every tensor's code is complete with no codeword longer
+                                than 11 bits, and the decode indexes its tables with the
+                                11-bit prefix alone (set by ecf8_decode_prepare; a tensor
+                                that does not qualify is not decoded under 1 and its blocks
+                                are counted by ecf8_decode_status) */
 } ecf8_plan;
 
 /* ---------------------------- host side ------------------------------- */
@@ -148,9 +153,13 @@ int ecf8_histogram(const uint8_t* fp8, uint64_t n, uint64_t freq[ECF8_NSYM]);
 /* ECF8 blog §3.1.1 steps 2-3: Huffman code lengths from a histogram, ties
  * broken on (weight, node id) with leaves numbered by symbol and merged nodes
  * numbered 16, 17, ... in creation order; one present symbol gets length 1.
- * max_len: the length limit, 15 or 16 (a 16-symbol Huffman tree is at most
- * 15 deep, so the limit of 16 never binds); a smaller limit that the Huffman
- * code exceeds returns ECF8_ERR_UNSUPPORTED.  out: host. */
+ * max_len: the length limit, 1..16 (a 16-symbol Huffman tree is at most 15
+ * deep, so 15 and 16 never bind).  When the Huffman code is deeper than
+ * max_len, the lengths are the optimal ones no longer than max_len
+ * (package-merge, as ecf8v_code_lengths).  A limit of 11 or less lets the
+ * decode index its tables with one shift (ecf8_plan.short_codes).
+ * ECF8_ERR_UNSUPPORTED if 2^max_len is below the number of present symbols.
+ * out: host. */
 int ecf8_codebook_from_freq(const uint64_t freq[ECF8_NSYM], uint32_t max_len, ecf8_codebook* out);
 
 /* ecf8_histogram + ecf8_codebook_from_freq ("build once, freeze", ECF8 blog §5.1). */

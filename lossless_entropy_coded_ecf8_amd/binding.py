@@ -61,7 +61,7 @@ class Plan(ctypes.Structure):
     _fields_ = [("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
                 ("total_blocks", ctypes.c_uint64), ("count", ctypes.c_uint32),
                 ("chunk_bytes", ctypes.c_uint32), ("threads_per_block", ctypes.c_uint32),
-                ("grid", ctypes.c_uint32)]
+                ("grid", ctypes.c_uint32), ("short_codes", ctypes.c_uint32)]
 
 
 MAXSYM_V = 256

@@ -349,15 +349,24 @@ __device__ __forceinline__ void write_edge(uint32_t* s_out, Rsrc out_blk, uint32
 // decodes nothing (every built entry consumes at least one bit), so a
 // corrupted single-symbol stream still ends each walk and is counted by the
 // block check.  prefix11 <= 2047 < kTableMax - 1, so the clamp is one
-// v_med3_i32 in place of the v_max_i32.
+// v_med3_i32 in place of the v_max_i32.  kShort: the code has no codeword
+// longer than kWin bits (see kShortCd), and the index is prefix11.
+template <bool kShort = false>
 __device__ __forceinline__ int table_index(uint32_t win, int cd)
 {
     const int a = (int)(win >> (32 - kWin));
+    if constexpr (kShort) return a;
     const int b = (int)(win >> 16) - cd;
     int m;
     asm("v_med3_i32 %0, %1, %2, %3" : "=v"(m) : "v"(a), "v"(b), "v"(kTableMax - 1));
     return m;
 }
+
+// cdelta of a complete code with no codeword longer than kWin bits (every
+// 11-bit prefix short): its second region is empty and max(prefix11,
+// prefix16 - cd) is prefix11, so table_index<true> (one shift) gives the
+// same entry as the general form.
+constexpr int kShortCd = ((1 << (16 - kWin)) - 1) << kWin;
 
 // log2 of TB / 8: (r & ~31) << kPitchShift<TB> = (r >> 5) * (4 * TB), the byte
 // offset of row r >> 5 in rows of TB dwords
@@ -468,7 +477,7 @@ __device__ __forceinline__ uint32_t add_byte0(uint32_t acc, uint32_t e)
 // its final position but records 0 (no bits, no symbols), and the walk ends
 // when no lane of the wave is active.  Unmasked steps are for lookups every
 // lane is sure to take (see kSureSteps).
-template <int TB, int Q, int QEND, bool kMasked>
+template <int TB, int Q, int QEND, bool kMasked, bool kShort>
 __device__ __forceinline__ void count_steps(const char* s_stream_b, const uint32_t* s_tx, uint32_t col_addr, int cd,
                                             uint32_t rend, uint32_t& r, uint32_t& cnt4, uint32_t& lastex, bool& act,
                                             int& nq, uint32_t (&rec)[kRecords])
@@ -485,7 +494,7 @@ __device__ __forceinline__ void count_steps(const char* s_stream_b, const uint32
         for (int j = 0; j < kStep; ++j) {
             if (j % 2 == 0) win = window<TB>(s_stream_b, col_addr, r);
             else win = window_after(win, rec[kStep * Q + j - 1]);
-            const uint32_t e = s_tx[table_index(win, cd)];
+            const uint32_t e = s_tx[table_index<kShort>(win, cd)];
             uint32_t em = e;
             if constexpr (kMasked) {
                 em = act ? e : 0u;
@@ -496,7 +505,8 @@ __device__ __forceinline__ void count_steps(const char* s_stream_b, const uint32
             cnt4 = add_byte0(cnt4, em);
             if constexpr (kMasked) act = r > rend;
         }
-        count_steps<TB, Q + 1, QEND, kMasked>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
+        count_steps<TB, Q + 1, QEND, kMasked, kShort>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq,
+                                                      rec);
     }
 }
 
@@ -505,6 +515,26 @@ __device__ __forceinline__ void count_steps(const char* s_stream_b, const uint32
 // most at bit 15 + 16k, before 8C for every k < C / 2.
 template <int C>
 constexpr int kSureSteps = (C / 2 < kRecords ? C / 2 : kRecords) / kStep;
+
+// The recorded part of the count pass.  A wave whose lanes all hold whole
+// chunks (wave_full) takes its sure steps unmasked (no activity tests);
+// lastex is then the last sure lookup until a masked step finds a later one.
+template <int C, int TB, bool kShort>
+__device__ __forceinline__ void count_recorded(const char* s_stream_b, const uint32_t* s_tx, uint32_t col_addr, int cd,
+                                               uint32_t rend, bool wave_full, uint32_t& r, uint32_t& cnt4,
+                                               uint32_t& lastex, bool& act, int& nq, uint32_t (&rec)[kRecords])
+{
+    constexpr int U = kSureSteps<C>;
+    if (U > 0 && wave_full) {
+        count_steps<TB, 0, U, false, kShort>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
+        lastex = rec[(U > 0 ? U : 1) * kStep - 1];
+        act = r > rend;
+    } else {
+        count_steps<TB, 0, U, true, kShort>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
+    }
+    count_steps<TB, U, kRecords / kStep, true, kShort>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act,
+                                                       nq, rec);
+}
 
 // The decode pass over the recorded entries, two at a time, for the nq steps
 // the count pass took (compile-time unrolled like count_steps).
@@ -680,7 +710,10 @@ constexpr int kWavesTarget = [] {
     return w < 1 ? 1 : (w < ECF8_MIN_WAVES ? w : ECF8_MIN_WAVES);
 }();
 
-template <int C, int TB>
+// kShort: every tensor's code is complete with no codeword longer than kWin
+// bits (the host launches this form only then; a tensor whose table says
+// otherwise is not decoded and its blocks are counted as bad).
+template <int C, int TB, bool kShort>
 __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(kWavesTarget<C, TB>))) void ecf8_decode_kernel(const DevDesc* __restrict__ descs, int count,
                                                          uint64_t total_blocks,
                                                          const uint32_t* __restrict__ tables,
@@ -754,7 +787,8 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(kWavesTarget
             c_out = d->out;
             c_cd = d->cdelta;
             uint32_t ne = d->entries;
-            c_ok = ne != 0;                       // 0: tables were never built for this plan
+            c_ok = ne != 0 && (!kShort || c_cd == kShortCd);   // 0: tables never built for this plan, or a
+                                                               // code the short form cannot index
             ne = ne < (uint32_t)kTableMax ? ne : (uint32_t)kTableMax;
             const uint32_t* tx = tables + (uint64_t)ptens * kTabStride;
             // (every lane left the previous decode pass at its closing barrier,
@@ -827,19 +861,8 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(kWavesTarget
         uint32_t cnt4 = 0, lastex = 0;
         bool act = r > rend;
         int nq = 0;                        // steps taken (wave-uniform)
-        // a wave whose lanes all hold whole chunks takes its sure steps
-        // unmasked (no activity tests); lastex is then the last sure lookup
-        // until a masked step finds a later one
-        constexpr int U = kSureSteps<C>;
-        if (U > 0 && leftc >= 8u * C * 64u * (uint32_t)(wave + 1)) {
-            count_steps<TB, 0, U, false>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
-            lastex = rec[(U > 0 ? U : 1) * kStep - 1];
-            act = r > rend;
-        } else {
-            count_steps<TB, 0, U, true>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
-        }
-        count_steps<TB, U, kRecords / kStep, true>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq,
-                                                   rec);
+        const bool wave_full = leftc >= 8u * C * 64u * (uint32_t)(wave + 1);
+        count_recorded<C, TB, kShort>(s_stream_b, s_tx, col_addr, cd, rend, wave_full, r, cnt4, lastex, act, nq, rec);
         const uint32_t r_rec = r;          // where the recorded lookups end
         while (r > rend) {
             const uint32_t e = lookup<TB>(s_stream_b, s_tx, col_addr, r, cd);
@@ -988,29 +1011,48 @@ int shape_index(uint32_t C, uint32_t TB)
     return -1;
 }
 
-const void* decode_kernel_ptr(int shape)
+const void* decode_kernel_ptr(int shape, bool short_codes)
 {
     int i = 0;
-#define ECF8_X(c, t) \
-    if (shape == i) return reinterpret_cast<const void*>(ecf8_decode_kernel<c, t>); \
+#define ECF8_X(c, t)                                                                                         \
+    if (shape == i)                                                                                          \
+        return short_codes ? reinterpret_cast<const void*>(ecf8_decode_kernel<c, t, true>)                   \
+                           : reinterpret_cast<const void*>(ecf8_decode_kernel<c, t, false>);                 \
     ++i;
     ECF8_DECODE_SHAPES(ECF8_X)
 #undef ECF8_X
     return nullptr;
 }
 
-int launch_decode(uint32_t C, uint32_t TB, uint32_t grid, hipStream_t st, const DevDesc* dd, int count,
-                  uint64_t blocks, const uint32_t* tables, unsigned long long* status)
+int launch_decode(uint32_t C, uint32_t TB, bool short_codes, uint32_t grid, hipStream_t st, const DevDesc* dd,
+                  int count, uint64_t blocks, const uint32_t* tables, unsigned long long* status)
 {
 #define ECF8_X(c, t)                                                                                          \
     if (C == (c) && TB == (t)) {                                                                              \
-        hipLaunchKernelGGL((ecf8_decode_kernel<c, t>), dim3(grid), dim3(t), 0, st, dd, count, blocks, tables, \
-                           status);                                                                           \
+        if (short_codes)                                                                                      \
+            hipLaunchKernelGGL((ecf8_decode_kernel<c, t, true>), dim3(grid), dim3(t), 0, st, dd, count, blocks, \
+                               tables, status);                                                               \
+        else                                                                                                  \
+            hipLaunchKernelGGL((ecf8_decode_kernel<c, t, false>), dim3(grid), dim3(t), 0, st, dd, count,     \
+                               blocks, tables, status);                                                       \
         return hipGetLastError() == hipSuccess ? ECF8_OK : ECF8_ERR_HIP;                                      \
     }
     ECF8_DECODE_SHAPES(ECF8_X)
 #undef ECF8_X
     return ECF8_ERR_UNSUPPORTED;
+}
+
+// A complete code with no codeword longer than kWin bits: the tables of such
+// tensors are indexed by the 11-bit prefix alone (the short kernel form).
+bool short_code(const ecf8_codebook& cb)
+{
+    uint32_t units = 0;                          // 11-bit prefixes covered
+    for (int s = 0; s < 16; ++s) {
+        const uint32_t l = cb.len[s];
+        if (l > (uint32_t)kWin) return false;
+        if (l) units += 1u << (kWin - l);
+    }
+    return units == (1u << kWin);
 }
 
 constexpr int kShapes = 6;
@@ -1021,9 +1063,9 @@ struct DeviceInfo {
 
 constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
-DeviceInfo g_dev[kMaxDevices][kShapes];   // fixed size: the decode paths allocate no host memory either
+DeviceInfo g_dev[kMaxDevices][kShapes][2];   // fixed size: the decode paths allocate no host memory either
 
-int device_info(uint32_t C, uint32_t TB, DeviceInfo* out)
+int device_info(uint32_t C, uint32_t TB, bool short_codes, DeviceInfo* out)
 {
     const int shape = shape_index(C, TB);
     if (shape < 0 || shape >= kShapes) return ECF8_ERR_UNSUPPORTED;
@@ -1031,12 +1073,13 @@ int device_info(uint32_t C, uint32_t TB, DeviceInfo* out)
     if (hipGetDevice(&dev) != hipSuccess) return ECF8_ERR_HIP;
     if (dev < 0 || dev >= kMaxDevices) return ECF8_ERR_HIP;
     std::lock_guard<std::mutex> lk(g_dev_mu);
-    DeviceInfo& di = g_dev[dev][shape];
+    DeviceInfo& di = g_dev[dev][shape][short_codes ? 1 : 0];
     if (di.cus == 0) {
         int cus = 0, occ = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return ECF8_ERR_HIP;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_kernel_ptr(shape), (int)TB, 0) != hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_kernel_ptr(shape, short_codes), (int)TB, 0) !=
+            hipSuccess)
             return ECF8_ERR_HIP;
         di.cus = cus > 0 ? cus : 1;
         di.occupancy = occ > 0 ? occ : 1;
@@ -1118,15 +1161,17 @@ extern "C" int ecf8_decode_prepare(const ecf8_tensor_desc* descs, int count, uin
     uint32_t C = kChunk, TB = kLanes;
     int rc = batch_shape(descs, count, &C, &TB);
     if (rc) return rc;
+    bool short_codes = true;
     for (int i = 0; i < count; ++i) {
         rc = fill_desc(descs[i], out_base, blocks, hd[i]);
         if (rc) return rc;
+        short_codes = short_codes && short_code(descs[i].meta.cb);
     }
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     if (hipMemcpyAsync(workspace, host.data(), host.size(), hipMemcpyHostToDevice, st) != hipSuccess)
         return ECF8_ERR_HIP;
     DeviceInfo di;
-    rc = device_info(C, TB, &di);
+    rc = device_info(C, TB, short_codes, &di);
     if (rc) return rc;
     uint64_t grid = (uint64_t)di.cus * (uint64_t)di.occupancy;
     if (grid > blocks) grid = blocks;
@@ -1137,6 +1182,7 @@ extern "C" int ecf8_decode_prepare(const ecf8_tensor_desc* descs, int count, uin
     plan->chunk_bytes = C;
     plan->threads_per_block = TB;
     plan->grid = (uint32_t)grid;
+    plan->short_codes = short_codes ? 1u : 0u;
     return ECF8_OK;
 }
 
@@ -1175,8 +1221,9 @@ extern "C" int ecf8_decode_blocks(const ecf8_plan* plan, void* hip_stream)
     DevDesc* dd = reinterpret_cast<DevDesc*>(ws + desc_offset());
     uint32_t* tables = reinterpret_cast<uint32_t*>(ws + table_offset((int)plan->count));
     auto* status = reinterpret_cast<unsigned long long*>(ws);
-    return launch_decode(plan->chunk_bytes, plan->threads_per_block, plan->grid, reinterpret_cast<hipStream_t>(hip_stream),
-                         dd, (int)plan->count, plan->total_blocks, tables, status);
+    return launch_decode(plan->chunk_bytes, plan->threads_per_block, plan->short_codes != 0, plan->grid,
+                         reinterpret_cast<hipStream_t>(hip_stream), dd, (int)plan->count, plan->total_blocks, tables,
+                         status);
 }
 
 extern "C" int ecf8_decode_run(const ecf8_plan* plan, void* hip_stream)
@@ -1291,15 +1338,17 @@ extern "C" int ecf8_decode_batched_noalloc(const ecf8_tensor_desc* descs, int co
     uint32_t C = kChunk, TB = kLanes;
     int rc = batch_shape(descs, count, &C, &TB);
     if (rc) return rc;
+    bool short_codes = true;
     for (int i = 0; i < count; ++i) {
         rc = fill_desc(descs[i], out_base, blocks, hd[i]);
         if (rc) return rc;
+        short_codes = short_codes && short_code(descs[i].meta.cb);
     }
     unsigned char* ws = nullptr;
     rc = noalloc_scratch(&ws);
     if (rc) return rc;
     DeviceInfo di;
-    rc = device_info(C, TB, &di);
+    rc = device_info(C, TB, short_codes, &di);
     if (rc) return rc;
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     auto* status = bad_blocks ? reinterpret_cast<unsigned long long*>(bad_blocks)
@@ -1318,7 +1367,7 @@ extern "C" int ecf8_decode_batched_noalloc(const ecf8_tensor_desc* descs, int co
         hipLaunchKernelGGL(ecf8_table_kernel, dim3(count, kTableSlices), dim3(kTableThreads), 0, st, dd, tables, status);
         uint64_t grid = (uint64_t)di.cus * (uint64_t)di.occupancy;
         if (grid > blocks) grid = blocks;
-        return launch_decode(C, TB, (uint32_t)grid, st, dd, count, blocks, tables, status);
+        return launch_decode(C, TB, short_codes, (uint32_t)grid, st, dd, count, blocks, tables, status);
     }
     return hipGetLastError() == hipSuccess ? ECF8_OK : ECF8_ERR_HIP;
 }

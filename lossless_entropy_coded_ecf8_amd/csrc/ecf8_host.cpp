@@ -10,6 +10,7 @@
 // chunk of the bitstream plus a stored gap (offset of its first codeword), so
 // the encoder records those gaps and the per-block output offsets.
 #include "ecf8.h"
+#include "ecf8v.h"
 #include "host_threads.h"
 
 #include <algorithm>
@@ -207,8 +208,14 @@ extern "C" int ecf8_codebook_from_freq(const uint64_t freq[ECF8_NSYM], uint32_t 
         longest = std::max(longest, d);
     }
     if (longest > (int)max_len) {
+        // deeper than the limit: the optimal lengths no longer than max_len
+        // (package-merge, the same routine as the other float formats)
         std::memset(out, 0, sizeof(*out));
-        return ECF8_ERR_UNSUPPORTED;
+        if ((1u << max_len) < (uint32_t)nleaf) return ECF8_ERR_UNSUPPORTED;
+        uint8_t len[kNsym];
+        const int rc = ecf8v_code_lengths(freq, kNsym, max_len, len);
+        if (rc) return rc;
+        for (int s = 0; s < kNsym; ++s) out->len[s] = len[s];
     }
     return ECF8_OK;
 }

@@ -234,6 +234,53 @@ def test_split_calls_and_decode_without_tables():
         assert np.array_equal(b[offs[i]:offs[i] + x.size], x), kinds[i]
 
 
+def test_short_code_form_selection_and_parity():
+    """The plan picks the one-shift table index (short_codes) exactly when every tensor's code is
+    complete with no codeword longer than 11 bits; both forms decode every tensor exactly."""
+    d = dev()
+    cases = [("stable", 400_001, 11),      # 0: codes limited to 11 bits
+             ("gauss", 300_000, 11),       # 1: codes limited to 11 bits
+             ("uniform4", 262_147, 16),    # 2: all 4 bits
+             ("fib15", 200_000, 16),       # 3: codewords of 15 bits
+             ("single", 70_000, 16),       # 4: one symbol, an incomplete code
+             ("stable", 300_000, 16)]      # 5: the same kind of data with 13-bit codes
+    xs, hosts, encs = [], [], []
+    for i, (k, n, ml) in enumerate(cases):
+        x, L = make_input(k, n, 3000 + i)
+        xs.append(x)
+        hosts.append(E.encode(x, lengths=L, max_len=ml))
+        encs.append(hosts[-1].to(d))
+    for i in (0, 1, 2):
+        assert max(hosts[i].lengths) <= 11 and oracle.kraft_sum(hosts[i].lengths) == 1.0
+    assert max(hosts[3].lengths) > 11 and max(hosts[5].lengths) > 11
+    for batch, want_short in (([0, 1, 2], 1), ([0, 1, 2, 3], 0), ([4], 0), ([5], 0), ([2, 5, 0], 0)):
+        plan = E.DecodePlan([encs[i] for i in batch])
+        assert int(plan.plan.short_codes) == want_short, batch
+        plan.out.fill_(CANARY)
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.status() == 0
+        for j, i in enumerate(batch):
+            assert np.array_equal(plan.view(j).cpu().numpy(), xs[i]), (batch, i)
+
+
+def test_short_code_form_refuses_long_codes():
+    """A plan forced to the short form on a code with longer codewords decodes nothing wrong
+    silently: every block is flagged and no byte outside the tensor is written."""
+    d = dev()
+    x, L = make_input("long12x6", 300_000, 3020)
+    denc = E.encode(x, lengths=L).to(d)
+    n = x.size
+    buf = torch.full((n + 64,), CANARY, dtype=torch.uint8, device=d)
+    plan = E.DecodePlan([denc], out=buf[16:16 + n], offsets=[0])
+    assert int(plan.plan.short_codes) == 0
+    plan.plan.short_codes = 1
+    plan.run()
+    assert plan.status() == int(plan.plan.total_blocks)
+    b = buf.cpu().numpy()
+    assert (b[:16] == CANARY).all() and (b[16 + n:] == CANARY).all()
+
+
 def test_corrupt_block_offset_is_flagged_and_contained():
     """Checked mode: a wrong blk_off entry is reported, and no byte outside [0, n) is written."""
     d = dev()
@@ -415,13 +462,13 @@ def test_empty_tensor_is_a_no_op():
 
 # ---------------------------------------------------------------- full-size workloads
 
-def encode_workload(workload, d, experts=None):
+def encode_workload(workload, d, experts=None, max_len=16):
     """Generate on the GPU, encode on the host, upload.  Returns (names, xs_gpu, device encs)."""
     names, xs, encs = [], [], []
     for name, x in synth.workload_tensors(workload, device=d, experts=experts):
         names.append(name)
         xs.append(x.reshape(-1))
-        encs.append(E.encode(x.cpu()).to(d))
+        encs.append(E.encode(x.cpu(), max_len=max_len).to(d))
     return names, xs, encs
 
 
@@ -443,9 +490,9 @@ def sampled_oracle_check(enc_dev, out_view, rng, blocks=2):
         assert np.array_equal(out_view[lo:hi].cpu().numpy(), ref), ("block", b)
 
 
-def run_batched(workload, experts=None, check_blocks=2):
+def run_batched(workload, experts=None, check_blocks=2, max_len=16):
     d = dev()
-    names, xs, encs = encode_workload(workload, d, experts)
+    names, xs, encs = encode_workload(workload, d, experts, max_len)
     plan = E.DecodePlan(encs)
     plan.out.fill_(CANARY)
     plan.run()
@@ -473,6 +520,12 @@ def test_llama8b_one_launch_per_tensor():
 
 def test_llama70b_block_batched():
     run_batched("llama70b")
+
+
+def test_llama70b_block_batched_short_codes():
+    """The block with codes limited to 11 bits (the bench's encoding): the one-shift form."""
+    plan = run_batched("llama70b", max_len=11)
+    assert int(plan.plan.short_codes) == 1
 
 
 def test_dit14b_block_batched():

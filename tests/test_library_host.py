@@ -54,11 +54,37 @@ def test_codebook_matches_oracle_including_ties(seed):
 def test_fibonacci_depth_15_and_length_limit():
     freq = [1, 1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144, 233, 377, 610, 987]
     assert max(E.codebook_from_freq(freq, 15)) == 15
+    # a binding limit gives the optimal limited code (the oracle's package-merge)
+    L14 = E.codebook_from_freq(freq, 14)
+    assert L14.tolist() == oracle.v_package_merge(freq, 14).tolist() and max(L14) == 14
+    assert oracle.kraft_sum(L14) == 1.0
+    L4 = E.codebook_from_freq(freq, 4)
+    assert L4.tolist() == [4] * 16                      # 16 symbols in 4 bits: the only code
     with pytest.raises(E.Ecf8Error) as ei:
-        E.codebook_from_freq(freq, 14)
+        E.codebook_from_freq(freq, 3)                   # 2^3 < 16 present symbols
     assert ei.value.code == -4
     with pytest.raises(E.Ecf8Error):
         E.codebook_from_freq(freq, 17)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_length_limited_codebook_matches_oracle(seed):
+    """E4M3 codes under a length limit (the decode's one-shift table index needs codes of at most 11
+    bits): the Huffman lengths when the tree is no deeper than the limit, otherwise the oracle's
+    optimal length-limited lengths (package-merge, pinned by brute force on small alphabets)."""
+    rng = np.random.default_rng(100 + seed)
+    k = int(rng.integers(2, 17))
+    freq = np.zeros(16, dtype=np.uint64)
+    freq[rng.choice(16, k, replace=False)] = (10 ** rng.uniform(0, 9, k)).astype(np.uint64) + 1
+    huff = oracle.huffman_lengths(freq)
+    for limit in (16, 13, 11, 8, 5):
+        if (1 << limit) < k:
+            continue
+        got = E.codebook_from_freq(freq, limit)
+        want = huff if max(huff) <= limit else oracle.v_package_merge(freq, limit)
+        assert got.tolist() == want.tolist(), (limit, freq.tolist())
+        assert max(got) <= limit
+        assert oracle.code_cost(freq, got) == oracle.code_cost(freq, want)
 
 
 @pytest.mark.parametrize("lengths", [None, [4] * 16, list(range(1, 16)) + [15]])
