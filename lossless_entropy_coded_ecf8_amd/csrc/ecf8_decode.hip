@@ -261,18 +261,17 @@ __global__ __launch_bounds__(kTableThreads) void ecf8_table_kernel(DevDesc* __re
 }
 
 // ------------------------------------------------------------ helpers
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane)
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v)
 {
-    // Hillis-Steele inside each 16-lane DPP row, then carry row totals with readlane.
+    // Hillis-Steele inside each 16-lane DPP row, then the row totals carried
+    // with the row broadcasts: lane 15 of rows 0 and 2 into rows 1 and 3,
+    // then lane 31 into rows 2 and 3 (rows a broadcast does not write add 0).
     v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xF, 0xF, true);   // row_shr:1
     v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xF, 0xF, true);   // row_shr:2
     v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, true);   // row_shr:4
     v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xF, 0xF, true);   // row_shr:8
-    const uint32_t r0 = __builtin_amdgcn_readlane(v, 15);
-    const uint32_t r1 = __builtin_amdgcn_readlane(v, 31);
-    const uint32_t r2 = __builtin_amdgcn_readlane(v, 47);
-    const int row = lane >> 4;
-    v += (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1 and 3
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2 and 3
     return v;
 }
 
@@ -409,6 +408,15 @@ __device__ __forceinline__ uint32_t window_after(uint32_t win, uint32_t e)
     return w;
 }
 
+// acc + (e & 0xFF) as one byte-select add
+__device__ __forceinline__ uint32_t add_byte0(uint32_t acc, uint32_t e)
+{
+    uint32_t r;
+    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD"
+        : "=v"(r) : "v"(e), "v"(acc));
+    return r;
+}
+
 // OR the symbols of one table entry, as packed nibbles, into the zeroed
 // staging at bit offset ob (two dwords: the entry's 16 symbol bits may
 // straddle a dword boundary).
@@ -420,8 +428,9 @@ __device__ __forceinline__ void emit_symbols(uint32_t* s_out, uint32_t ob, uint3
     atomicOr(&s_out[wa + 1], (uint32_t)(v >> 32));
 }
 
-// OR the symbols of two consecutive table entries of a lane (an entry of 0
-// contributes nothing) into the staging at bit offset ob: their packets joined
+// OR the symbols of two consecutive records of a lane (the entries of a pair
+// of lookups; the second's byte 0 holds the pair's nibble count, and records
+// of a lane past its end are 0) into the staging at bit offset ob: their packets joined
 // into one bit string of at most 32 bits, which covers dword ob / 32 and, when
 // it crosses, part of the next.  Only the first of those dwords is written
 // here, together with `carry`, the spill of the previous pair into this same
@@ -443,12 +452,8 @@ __device__ __forceinline__ uint32_t emit_pair(uint32_t* s_out, uint32_t ob, uint
     const uint64_t v = (uint64_t)p01 << (ob & 31u);
     atomicOr(&s_out[ob >> 5], (uint32_t)v | carry);
     carry = (uint32_t)(v >> 32);
-    // ob + (4 * symbols of e0) + (4 * symbols of e1), with byte selects
-    uint32_t nob;
-    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD\n\t"
-        "v_add_u32_sdwa %0, %3, %0 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD"
-        : "=&v"(nob) : "v"(e0), "v"(ob), "v"(e1));
-    return nob;
+    // ob + 4 * symbols of the pair: byte 0 of the second record holds it
+    return add_byte0(ob, e1);
 }
 
 // ------------------------------------------------------------ decode kernel
@@ -461,15 +466,6 @@ constexpr int kRecords = ECF8_RECORDS;   // table entries recorded per lane by t
 #endif
 constexpr int kStep = ECF8_STEP;         // lookups per wave-uniform step of the count pass
 static_assert(kRecords % kStep == 0 && kStep % 2 == 0, "records are taken a step at a time, emitted in pairs");
-
-// acc + (e & 0xFF) as one byte-select add
-__device__ __forceinline__ uint32_t add_byte0(uint32_t acc, uint32_t e)
-{
-    uint32_t r;
-    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD"
-        : "=v"(r) : "v"(e), "v"(acc));
-    return r;
-}
 
 // The count pass in wave-uniform steps of kStep lookups, unrolled at compile
 // time so that every record index is static (the records stay in registers):
@@ -500,9 +496,16 @@ __device__ __forceinline__ void count_steps(const char* s_stream_b, const uint32
                 em = act ? e : 0u;
                 lastex = act ? e : lastex;
             }
-            rec[kStep * Q + j] = em;
             r -= (em >> 8) & 0xFFu;
-            cnt4 = add_byte0(cnt4, em);
+            if (j % 2 == 0) {
+                rec[kStep * Q + j] = em;
+            } else {
+                // the pair's second record carries the pair's nibble count in
+                // its byte 0 (4 * symbols of both, at most 32: no carry into
+                // the bit count), which the decode pass adds in one step
+                rec[kStep * Q + j] = add_byte0(em, rec[kStep * Q + j - 1]);
+                cnt4 = add_byte0(cnt4, rec[kStep * Q + j]);
+            }
             if constexpr (kMasked) act = r > rend;
         }
         count_steps<TB, Q + 1, QEND, kMasked, kShort>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq,
@@ -527,7 +530,9 @@ __device__ __forceinline__ void count_recorded(const char* s_stream_b, const uin
     constexpr int U = kSureSteps<C>;
     if (U > 0 && wave_full) {
         count_steps<TB, 0, U, false, kShort>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
-        lastex = rec[(U > 0 ? U : 1) * kStep - 1];
+        // the last sure record is a pair's second: take back its own count
+        constexpr int kLast = (U > 0 ? U : 1) * kStep - 1;
+        lastex = rec[kLast] - (rec[kLast - 1] & 0xFFu);
         act = r > rend;
     } else {
         count_steps<TB, 0, U, true, kShort>(s_stream_b, s_tx, col_addr, cd, rend, r, cnt4, lastex, act, nq, rec);
@@ -900,7 +905,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(kWavesTarget
         asm volatile("" ::"v"(nx.sv[0]), "v"(nx.la), "v"(nx.gb), "v"((uint32_t)nx.off));
 
         // ---- phase 3: block-wide exclusive scan of the counts
-        const uint32_t incl = wave_inclusive_scan(cnt, lane);
+        const uint32_t incl = wave_inclusive_scan(cnt);
         if (lane == 63) s_wsum[wave] = incl;
         __syncthreads();
         uint32_t before = 0, total = 0;

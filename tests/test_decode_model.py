@@ -111,7 +111,7 @@ def model_block(enc, tab, cd, b, quad=False):
         base = g * C
         raw = np.frombuffer(bytes(stream[base: base + C + 4]) + bytes(64), dtype=np.uint8)
         lanes.append(dict(bits=np.unpackbits(raw), r=R0 - gap, r0=R0 - gap, rend=R0 - E_, cnt4=0, lastex=0,
-                          rec=[], act=(R0 - gap) > (R0 - E_)))
+                          rec=[], raw=[], act=(R0 - gap) > (R0 - E_)))
     # count pass: wave-uniform steps, records, then lanes past the records keep walking.
     # A wave whose lanes all hold whole chunks takes its first `sure` lookups
     # without activity tests: check that every lane is indeed active there.
@@ -136,9 +136,15 @@ def model_block(enc, tab, cd, b, quad=False):
                     em = e if L["act"] else 0
                     if L["act"]:
                         L["lastex"] = e
-                    L["rec"].append(em)
+                    L["raw"].append(em)
                     L["r"] -= (em >> 8) & 0xFF
-                    L["cnt4"] += em & 0xFF
+                    if j % 2 == 0:
+                        L["rec"].append(em)
+                    else:
+                        # a pair's second record carries the pair's nibble count in byte 0
+                        L["rec"].append(em + (L["rec"][-1] & 0xFF))
+                        assert (L["rec"][-1] & 0xFF) <= 32
+                        L["cnt4"] += L["rec"][-1] & 0xFF
                     L["act"] = L["r"] > L["rend"]
         for L in wave:
             L["r_rec"] = L["r"]
@@ -174,7 +180,7 @@ def model_block(enc, tab, cd, b, quad=False):
     for L in lanes:
         ob = (a0 + pos) * 4
         pos += L["cnt"]
-        rec = L["rec"]
+        rec = L["raw"] if quad else L["rec"]
         if quad:
             for k in range(0, len(rec) - 3, 4):
                 pk, n = 0, 0
@@ -199,7 +205,7 @@ def model_block(enc, tab, cd, b, quad=False):
                 v = p << (ob & 31)
                 OR(ob >> 5, v | carry)
                 carry = v >> 32
-                ob += (rec[k] & 0xFF) + (rec[k + 1] & 0xFF)
+                ob += rec[k + 1] & 0xFF
             if rec:
                 OR(ob >> 5, carry)
         for e in L["extra"]:
