@@ -234,6 +234,15 @@ int ecf8_decode_run(const ecf8_plan* plan, void* hip_stream);
 int ecf8_build_tables(const ecf8_plan* plan, void* hip_stream);
 int ecf8_decode_blocks(const ecf8_plan* plan, void* hip_stream);
 
+/* For measurement (the pages time the decode as a whole, ECF8 blog §4; this
+ * times the kernel): ecf8_decode_blocks with HIP events attached to the
+ * dispatch itself, so that they hold its start and end times (hipEvent_t
+ * handles created by the caller with timing enabled; either may be NULL).
+ * Events recorded on the stream around an ordinary launch also hold the
+ * dispatch's launch and completion latency.  Same errors as
+ * ecf8_decode_blocks. */
+int ecf8_decode_blocks_timed(const ecf8_plan* plan, void* hip_stream, void* start_event, void* stop_event);
+
 /* ECF8 blog §3.3 (data-centre mode: every weight resident, decoded in
  * batches) and §3.2.2 (one preallocated output pool, reused, no allocation);
  * DFloat11 blog §3.3 (the weights of a whole transformer block decoded

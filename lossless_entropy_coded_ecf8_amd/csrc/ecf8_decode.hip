@@ -47,6 +47,7 @@
 //     all blocks of all tensors of a batch at 6 workgroups per CU;
 //   * wave priority rises through a block (count 1, scan and decode 2,
 //     write-back 3), so the wave of a SIMD nearest its stores issues first.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -1029,21 +1030,31 @@ const void* decode_kernel_ptr(int shape, bool short_codes)
     return nullptr;
 }
 
+// The decode dispatch; with events, they are attached to the dispatch itself
+// and take its start and end times.
 int launch_decode(uint32_t C, uint32_t TB, bool short_codes, uint32_t grid, hipStream_t st, const DevDesc* dd,
-                  int count, uint64_t blocks, const uint32_t* tables, unsigned long long* status)
+                  int count, uint64_t blocks, const uint32_t* tables, unsigned long long* status,
+                  hipEvent_t start = nullptr, hipEvent_t stop = nullptr)
 {
+#define ECF8_LAUNCH(k)                                                                                        \
+    do {                                                                                                      \
+        if (start || stop)                                                                                    \
+            hipExtLaunchKernelGGL((k), dim3(grid), dim3(TB), 0, st, start, stop, 0, dd, count, blocks, tables, \
+                                  status);                                                                    \
+        else                                                                                                  \
+            hipLaunchKernelGGL((k), dim3(grid), dim3(TB), 0, st, dd, count, blocks, tables, status);          \
+    } while (0)
 #define ECF8_X(c, t)                                                                                          \
     if (C == (c) && TB == (t)) {                                                                              \
         if (short_codes)                                                                                      \
-            hipLaunchKernelGGL((ecf8_decode_kernel<c, t, true>), dim3(grid), dim3(t), 0, st, dd, count, blocks, \
-                               tables, status);                                                               \
+            ECF8_LAUNCH((ecf8_decode_kernel<c, t, true>));                                                    \
         else                                                                                                  \
-            hipLaunchKernelGGL((ecf8_decode_kernel<c, t, false>), dim3(grid), dim3(t), 0, st, dd, count,     \
-                               blocks, tables, status);                                                       \
+            ECF8_LAUNCH((ecf8_decode_kernel<c, t, false>));                                                   \
         return hipGetLastError() == hipSuccess ? ECF8_OK : ECF8_ERR_HIP;                                      \
     }
     ECF8_DECODE_SHAPES(ECF8_X)
 #undef ECF8_X
+#undef ECF8_LAUNCH
     return ECF8_ERR_UNSUPPORTED;
 }
 
@@ -1229,6 +1240,19 @@ extern "C" int ecf8_decode_blocks(const ecf8_plan* plan, void* hip_stream)
     return launch_decode(plan->chunk_bytes, plan->threads_per_block, plan->short_codes != 0, plan->grid,
                          reinterpret_cast<hipStream_t>(hip_stream), dd, (int)plan->count, plan->total_blocks, tables,
                          status);
+}
+
+extern "C" int ecf8_decode_blocks_timed(const ecf8_plan* plan, void* hip_stream, void* start_event, void* stop_event)
+{
+    int rc = check_plan(plan);
+    if (rc || plan->count == 0 || plan->total_blocks == 0) return rc;
+    unsigned char* ws = static_cast<unsigned char*>(plan->workspace);
+    DevDesc* dd = reinterpret_cast<DevDesc*>(ws + desc_offset());
+    uint32_t* tables = reinterpret_cast<uint32_t*>(ws + table_offset((int)plan->count));
+    auto* status = reinterpret_cast<unsigned long long*>(ws);
+    return launch_decode(plan->chunk_bytes, plan->threads_per_block, plan->short_codes != 0, plan->grid,
+                         reinterpret_cast<hipStream_t>(hip_stream), dd, (int)plan->count, plan->total_blocks, tables,
+                         status, reinterpret_cast<hipEvent_t>(start_event), reinterpret_cast<hipEvent_t>(stop_event));
 }
 
 extern "C" int ecf8_decode_run(const ecf8_plan* plan, void* hip_stream)

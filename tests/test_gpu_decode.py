@@ -281,6 +281,28 @@ def test_short_code_form_refuses_long_codes():
     assert (b[:16] == CANARY).all() and (b[16 + n:] == CANARY).all()
 
 
+def test_decode_blocks_with_dispatch_events():
+    """ecf8_decode_blocks_timed: the same decode, with the events attached to the dispatch holding
+    its start and end (a positive duration, no longer than events recorded around the launch)."""
+    d = dev()
+    x, _ = make_input("stable", 2_000_003, 3030)
+    plan = E.DecodePlan([E.encode(x, max_len=11).to(d)])
+    plan.out.fill_(CANARY)
+    plan.build_tables()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    o0, o1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for ev in (a, b):
+        ev.record()
+    o0.record()
+    plan.decode_blocks(events=(a, b))
+    o1.record()
+    torch.cuda.synchronize()
+    assert plan.status() == 0
+    assert np.array_equal(plan.view(0).cpu().numpy(), x)
+    inner, outer = a.elapsed_time(b), o0.elapsed_time(o1)
+    assert 0 < inner <= outer * 1.001 + 1e-3, (inner, outer)
+
+
 def test_corrupt_block_offset_is_flagged_and_contained():
     """Checked mode: a wrong blk_off entry is reported, and no byte outside [0, n) is written."""
     d = dev()
