@@ -85,6 +85,7 @@ struct EncArgs {
     const uint64_t* tile_off;  // tiles + 1 entries; tile_off[tiles] = T
     const uint64_t* tile_chunk;   // per tile and for T: chunk holding bit tile_off & ~31, and its block
     const uint2* pairs;        // codeword-pair table, 256 entries
+    uint32_t* side;            // per tile: its partial first and last stream words, first and last gap words
     uint64_t m_chunk;          // ceil(2^40 / chunk_bits)
     uint64_t m_tb;             // ceil(2^40 / tb)
 };
@@ -551,32 +552,40 @@ __global__ __launch_bounds__(256) void ecf8_encode_kernel(EncArgs a)
     // tile image -> stream (bytes MSB-first: each big-endian word
     // byte-swapped); words past the stream (metadata that undercounts T) are
     // dropped
+    // A word the tile shares with its neighbour (the stream word holding a
+    // tile boundary, the gap word holding chunks of both tiles) goes to the
+    // tile's side slots instead; ecf8_boundary_kernel ORs the two tiles' parts
+    // into it afterwards (global atomics here were 45% of the pass).  A tile
+    // spans at least 4096 bits, so it shares a word with each neighbour at
+    // most and no word has more than two tiles' bits.
     const bool last_tile = tile + 1 == a.tiles;
     const bool first_shared = (P0 & 31) != 0;
     const bool last_shared = (P1 & 31) != 0 && !last_tile;
+    uint32_t* const side = a.side + 4 * tile;
     const uint32_t nout = W0 >= a.stream_words ? 0u
                           : (a.stream_words - W0 < (uint64_t)nwords ? (uint32_t)(a.stream_words - W0) : nwords);
     for (uint32_t i = tid; i < nout; i += kEncLanes) {
         const uint32_t v = __builtin_bswap32(img[i]);
-        if ((i == 0 && first_shared) || (i == nwords - 1 && last_shared)) {
-            if (v) atomicOr(&a.stream[W0 + i], v);
-        } else {
-            a.stream[W0 + i] = v;
-        }
+        if (i == 0 && first_shared) side[0] = v;
+        else if (i == nwords - 1 && last_shared) side[1] = v;
+        else a.stream[W0 + i] = v;
     }
     // gap image -> gaps: the words of chunks C0 + 1 .. C1 (those starting in
-    // (P0, P1]); the first and last may hold other tiles' chunks and are
-    // OR-ed into the cleared gap array
+    // (P0, P1]); the first is shared when chunk C0 (the previous tile's) is
+    // in it, the last when chunk C1 + 1 (the next tile's) is
+    const bool gfirst_shared = tile > 0 && ((C0 + 1) & 7) != 0;
+    const bool glast_shared = !last_tile && (C1 & 7) != 7;
     for (uint32_t j = g_lo + tid; j < g_hi; j += kEncLanes) {
         const uint64_t g = (C0 >> 3) + j;
         if (g >= a.gap_words) break;
         const uint32_t v = gimg[j];
-        if (j == g_lo || j + 1 == g_hi) {
-            if (v) atomicOr(&a.gaps[g], v);
-        } else {
-            a.gaps[g] = v;
-        }
+        if (j == g_lo && gfirst_shared) side[2] = v;
+        else if (j + 1 == g_hi && glast_shared) side[3] = v;
+        else a.gaps[g] = v;
     }
+    // a tile with no chunk start (the last, if it is shorter than a chunk)
+    // still shares the previous tile's gap word: its part is empty
+    if (tid == 0 && g_lo >= g_hi) side[2] = 0u;
     if (last_tile) {                                      // zero padding after T
         for (uint64_t g = W0 + nwords + tid; g < a.stream_words; g += kEncLanes) a.stream[g] = 0u;
         if (tid == 0) {
@@ -584,6 +593,25 @@ __global__ __launch_bounds__(256) void ecf8_encode_kernel(EncArgs a)
             a.blk_off[a.n_blocks] = a.n;
         }
     }
+}
+
+// Pass 4: the words two tiles share, one lane per tile boundary t (between
+// tiles t and t + 1, at bit P = tile_off[t + 1]): the stream word holding P
+// when P is not word-aligned, and the gap word holding chunks C1 = P / (8C)
+// (tile t's last) and C1 + 1 (tile t + 1's first) when they share one.
+__global__ __launch_bounds__(256) void ecf8_boundary_kernel(const uint64_t* __restrict__ tile_off, uint64_t tiles,
+                                                            const uint32_t* __restrict__ side, uint32_t chunk_bits,
+                                                            uint32_t* __restrict__ stream, uint64_t stream_words,
+                                                            uint32_t* __restrict__ gaps, uint64_t gap_words)
+{
+    const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t + 1 >= tiles) return;
+    const uint64_t P = tile_off[t + 1];
+    const uint32_t* s0 = side + 4 * t;
+    const uint32_t* s1 = side + 4 * (t + 1);
+    if ((P & 31) != 0 && (P >> 5) < stream_words) stream[P >> 5] = s0[1] | s1[0];
+    const uint64_t c1 = P / chunk_bits;
+    if ((c1 & 7) != 7 && (c1 >> 3) < gap_words) gaps[c1 >> 3] = s0[3] | s1[2];
 }
 
 int check(hipError_t e) { return e == hipSuccess ? ECF8_OK : ECF8_ERR_HIP; }
@@ -614,7 +642,7 @@ int resident_slots(int which, const void* kernel, uint32_t* out)
 // u64) | per-tile chunk and block (2 x u64) | group totals/offsets (u64) |
 // codeword-pair table (2 KB), each part 256-byte aligned.
 struct EncWorkspace {
-    uint64_t tiles, groups, off_off, chunk_off, group_off, pair_off, bytes;
+    uint64_t tiles, groups, off_off, chunk_off, group_off, pair_off, side_off, bytes;
 };
 
 EncWorkspace enc_workspace(uint64_t n)
@@ -627,7 +655,8 @@ EncWorkspace enc_workspace(uint64_t n)
     w.chunk_off = w.off_off + round((w.tiles + 1) * 8);
     w.group_off = w.chunk_off + round((w.tiles + 1) * 16);
     w.pair_off = w.group_off + round(w.groups * 8);
-    w.bytes = w.pair_off + 256 * 8 + 256;
+    w.side_off = w.pair_off + 256 * 8 + 256;
+    w.bytes = w.side_off + round(w.tiles * 16);
     return w;
 }
 
@@ -700,6 +729,7 @@ extern "C" int ecf8_encode_device(const uint8_t* fp8, const ecf8_meta* meta, uin
     uint64_t* tile_chunk = reinterpret_cast<uint64_t*>(ws + W.chunk_off);
     uint64_t* group = reinterpret_cast<uint64_t*>(ws + W.group_off);
     uint2* pairs = reinterpret_cast<uint2*>(ws + W.pair_off);
+    uint32_t* side = reinterpret_cast<uint32_t*>(ws + W.side_off);
     EncArgs a;
     a.fp8 = fp8;
     a.n = n;
@@ -717,6 +747,7 @@ extern "C" int ecf8_encode_device(const uint8_t* fp8, const ecf8_meta* meta, uin
     a.tile_off = tile_off;
     a.tile_chunk = tile_chunk;
     a.pairs = pairs;
+    a.side = side;
     a.m_chunk = ((1ull << 40) + a.chunk_bits - 1) / a.chunk_bits;
     a.m_tb = ((1ull << 40) + a.tb - 1) / a.tb;
 
@@ -730,5 +761,8 @@ extern "C" int ecf8_encode_device(const uint8_t* fp8, const ecf8_meta* meta, uin
     hipLaunchKernelGGL(ecf8_tile_off_kernel, dim3((uint32_t)W.groups), dim3(kScanLanes), 0, st, counts, L, W.tiles,
                        group, tile_off, tile_chunk, a.chunk_bits, a.tb, a.stream, a.stream_words);
     hipLaunchKernelGGL(ecf8_encode_kernel, dim3((uint32_t)W.tiles), dim3(kEncLanes), 0, st, a);
+    if (W.tiles > 1)
+        hipLaunchKernelGGL(ecf8_boundary_kernel, dim3((uint32_t)((W.tiles - 1 + 255) / 256)), dim3(256), 0, st,
+                           tile_off, W.tiles, side, a.chunk_bits, a.stream, a.stream_words, a.gaps, a.gap_words);
     return check(hipGetLastError());
 }
