@@ -588,6 +588,11 @@ __global__ __launch_bounds__(256) void ecf8_encode_kernel(EncArgs a)
     if (tid == 0 && g_lo >= g_hi) side[2] = 0u;
     if (last_tile) {                                      // zero padding after T
         for (uint64_t g = W0 + nwords + tid; g < a.stream_words; g += kEncLanes) a.stream[g] = 0u;
+        // and the gap words past the tile's own (the last block's lanes that
+        // hold no chunk; a tile with no chunk start wrote none: from the word
+        // of chunk C0 + 1 on, which for tile 0 holds chunk 0)
+        const uint64_t gz = C1 > C0 ? (C1 >> 3) + 1 : (C0 + 1) >> 3;
+        for (uint64_t g = gz + tid; g < a.gap_words; g += kEncLanes) a.gaps[g] = 0u;
         if (tid == 0) {
             a.blk_off[0] = 0;
             a.blk_off[a.n_blocks] = a.n;
@@ -751,10 +756,9 @@ extern "C" int ecf8_encode_device(const uint8_t* fp8, const ecf8_meta* meta, uin
     a.m_chunk = ((1ull << 40) + a.chunk_bits - 1) / a.chunk_bits;
     a.m_tb = ((1ull << 40) + a.tb - 1) / a.tb;
 
-    // gaps are OR-ed nibbles (zero gaps are not written): clear them; every
-    // other output word is written by the kernels
-    hipLaunchKernelGGL(ecf8_zero_kernel, dim3(256), dim3(256), 0, st, reinterpret_cast<uint32_t*>(gaps),
-                       meta->gap_bytes / 4);
+    // every output word is written by the kernels: the gap and stream words a
+    // tile owns by the encode kernel, those two tiles share by the boundary
+    // kernel, the padding after the last chunk by the last tile
     hipLaunchKernelGGL(ecf8_group_sum_kernel, dim3((uint32_t)W.groups), dim3(kScanLanes), 0, st, counts, L, W.tiles,
                        group);
     hipLaunchKernelGGL(ecf8_group_scan_kernel, dim3(1), dim3(kTopLanes), 0, st, group, W.groups, tab, pairs);
