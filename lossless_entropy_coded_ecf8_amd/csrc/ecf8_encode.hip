@@ -48,7 +48,6 @@ constexpr int kTileWords = (int)(kTile * ECF8_MAX_CODE_LEN / 32) + 2;  // LDS bi
 // being >= 32 bits) at most kTileWords + 1 chunk starts, 8 gaps per word.
 constexpr int kGapWords = (kTileWords + 1) / 8 + 3;
 constexpr int kScanLanes = 256;                                        // lanes of the per-group scans
-constexpr int kTopLanes = 1024;                                        // lanes of the group-total scan
 constexpr uint64_t kGroupTiles = 4ull * kScanLanes;                    // tiles per scan group
 constexpr int kCountWords = 8;                                         // per-tile counts: 16 x 16 bits
 constexpr int kHistWaves = 4;                                          // histogram: one tile per wave at a time
@@ -305,55 +304,44 @@ __device__ __forceinline__ uint64_t div_u64(uint64_t x, uint32_t d)
 
 // Pass 2a: total bits of each group of 1024 tiles.
 __global__ __launch_bounds__(kScanLanes) void ecf8_group_sum_kernel(const uint32_t* __restrict__ counts, CountLens L,
-                                                                    uint64_t tiles, uint64_t* __restrict__ gsum)
+                                                                    uint64_t tiles, uint64_t* __restrict__ gsum,
+                                                                    EncTable tab, uint2* __restrict__ pairs)
 {
     __shared__ uint64_t wsum[kScanLanes / 64];
+    if (blockIdx.x == 0) {                                // the codeword-pair table (see lane_pairs)
+        const uint32_t sa = threadIdx.x & 15u, sb = threadIdx.x >> 4;
+        const uint32_t la = tab.len[sa], lb = tab.len[sb];
+        pairs[threadIdx.x] = make_uint2((tab.code[sa] << lb) | tab.code[sb], la | ((la + lb) << 8));
+    }
     uint32_t v[4];
     const uint64_t s = lane_tiles(counts, L, tiles, blockIdx.x * kGroupTiles + 4ull * threadIdx.x, v);
     const uint64_t incl = block_incl_scan<kScanLanes>(s, wsum);
     if (threadIdx.x == kScanLanes - 1) gsum[blockIdx.x] = incl;
 }
 
-// Pass 2b: exclusive scan of the group totals in place (one workgroup; each
-// lane owns a contiguous run of groups); the same launch writes the 256-entry
-// codeword-pair table the encode kernel looks up.
-__global__ __launch_bounds__(kTopLanes) void ecf8_group_scan_kernel(uint64_t* __restrict__ g, uint64_t groups,
-                                                                    EncTable tab, uint2* __restrict__ pairs)
-{
-    __shared__ uint64_t wsum[kTopLanes / 64];
-    if (threadIdx.x < 256) {                              // the codeword-pair table (see lane_pairs)
-        const uint32_t sa = threadIdx.x & 15u, sb = threadIdx.x >> 4;
-        const uint32_t la = tab.len[sa], lb = tab.len[sb];
-        pairs[threadIdx.x] = make_uint2((tab.code[sa] << lb) | tab.code[sb], la | ((la + lb) << 8));
-    }
-    const uint64_t per = (groups + kTopLanes - 1) / kTopLanes;
-    const uint64_t lo = (uint64_t)threadIdx.x * per, hi = lo + per < groups ? lo + per : groups;
-    uint64_t s = 0;
-    for (uint64_t i = lo; i < hi; ++i) s += g[i];
-    uint64_t run = block_incl_scan<kTopLanes>(s, wsum) - s;
-    for (uint64_t i = lo; i < hi; ++i) {
-        const uint64_t x = g[i];
-        g[i] = run;
-        run += x;
-    }
-}
-
-// Pass 2c: tile bit offsets = group offset + exclusive scan inside the group
+// Pass 2b: tile bit offsets = the sum of the earlier groups' totals (each
+// workgroup adds them up itself) + an exclusive scan inside the group
 // (tile_off[tiles] = T), with the chunk and block holding each tile's first
-// stream word; the stream word holding a tile start that is not word aligned
-// is shared by two tiles and is cleared for their atomic ORs.
+// stream word.
 __global__ __launch_bounds__(kScanLanes) void ecf8_tile_off_kernel(const uint32_t* __restrict__ counts, CountLens L,
-                                                                   uint64_t tiles, const uint64_t* __restrict__ goff,
+                                                                   uint64_t tiles, const uint64_t* __restrict__ gsum,
                                                                    uint64_t* __restrict__ tile_off,
                                                                    uint64_t* __restrict__ tile_chunk, uint32_t chunk_bits,
-                                                                   uint32_t tb, uint32_t* __restrict__ stream,
-                                                                   uint64_t stream_words)
+                                                                   uint32_t tb)
 {
     __shared__ uint64_t wsum[kScanLanes / 64];
+    __shared__ uint64_t s_goff;
+    // this group's offset: the earlier groups' totals, summed lane-strided
+    uint64_t before = 0;
+    for (uint64_t i = threadIdx.x; i < blockIdx.x; i += kScanLanes) before += gsum[i];
+    before = block_incl_scan<kScanLanes>(before, wsum);
+    if (threadIdx.x == kScanLanes - 1) s_goff = before;
+    __syncthreads();
+    const uint64_t goff = s_goff;
     uint32_t v[4];
     const uint64_t t0 = blockIdx.x * kGroupTiles + 4ull * threadIdx.x;
     const uint64_t s = lane_tiles(counts, L, tiles, t0, v);
-    uint64_t run = goff[blockIdx.x] + block_incl_scan<kScanLanes>(s, wsum) - s;
+    uint64_t run = goff + block_incl_scan<kScanLanes>(s, wsum) - s;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         if (t0 + k < tiles) {
@@ -361,7 +349,6 @@ __global__ __launch_bounds__(kScanLanes) void ecf8_tile_off_kernel(const uint32_
             const uint64_t c = div_u64(run & ~31ull, chunk_bits);
             tile_chunk[2 * (t0 + k)] = c;
             tile_chunk[2 * (t0 + k) + 1] = div_u64(c, tb);
-            if ((run & 31) && (run >> 5) < stream_words) stream[run >> 5] = 0u;
         }
         run += v[k];
         if (t0 + k + 1 == tiles) {
@@ -644,8 +631,9 @@ int resident_slots(int which, const void* kernel, uint32_t* out)
 }
 
 // Workspace: per-tile counts (32 B per tile) | tile bit offsets (tiles + 1,
-// u64) | per-tile chunk and block (2 x u64) | group totals/offsets (u64) |
-// codeword-pair table (2 KB), each part 256-byte aligned.
+// u64) | per-tile chunk and block (2 x u64) | group totals (u64) |
+// codeword-pair table (2 KB) | per-tile side slots of the shared words
+// (16 B per tile), each part 256-byte aligned.
 struct EncWorkspace {
     uint64_t tiles, groups, off_off, chunk_off, group_off, pair_off, side_off, bytes;
 };
@@ -760,10 +748,9 @@ extern "C" int ecf8_encode_device(const uint8_t* fp8, const ecf8_meta* meta, uin
     // tile owns by the encode kernel, those two tiles share by the boundary
     // kernel, the padding after the last chunk by the last tile
     hipLaunchKernelGGL(ecf8_group_sum_kernel, dim3((uint32_t)W.groups), dim3(kScanLanes), 0, st, counts, L, W.tiles,
-                       group);
-    hipLaunchKernelGGL(ecf8_group_scan_kernel, dim3(1), dim3(kTopLanes), 0, st, group, W.groups, tab, pairs);
+                       group, tab, pairs);
     hipLaunchKernelGGL(ecf8_tile_off_kernel, dim3((uint32_t)W.groups), dim3(kScanLanes), 0, st, counts, L, W.tiles,
-                       group, tile_off, tile_chunk, a.chunk_bits, a.tb, a.stream, a.stream_words);
+                       group, tile_off, tile_chunk, a.chunk_bits, a.tb);
     hipLaunchKernelGGL(ecf8_encode_kernel, dim3((uint32_t)W.tiles), dim3(kEncLanes), 0, st, a);
     if (W.tiles > 1)
         hipLaunchKernelGGL(ecf8_boundary_kernel, dim3((uint32_t)((W.tiles - 1 + 255) / 256)), dim3(256), 0, st,
