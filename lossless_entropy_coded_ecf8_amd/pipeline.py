@@ -92,17 +92,21 @@ class ECF8Linear(torch.nn.Module):
     """
 
     def __init__(self, weight_u8: torch.Tensor, scale: float, bias: Optional[torch.Tensor] = None,
-                 device="cuda", checked: bool = False):
+                 device="cuda", checked: bool = False, max_code_len: int = 11):
         """checked: after each decode into the layer's own buffer, synchronize
         and raise if the decode's block check flagged a block (a corrupt
-        stream, gap or block offset) instead of feeding the GEMM."""
+        stream, gap or block offset) instead of feeding the GEMM.
+        max_code_len: the code length limit of the weight's encoding; at 11
+        every codeword fits the decode table's 11-bit index, so the decode
+        takes its one-shift form (the limit costs a few hundredths of a
+        percent of the stream on typical weights); 16 is plain Huffman."""
         super().__init__()
         self.checked = checked
         if weight_u8.dim() != 2 or weight_u8.dtype != torch.uint8:
             raise ValueError("weight_u8 must be a 2-D uint8 tensor of FP8 E4M3 bytes")
         self.out_features, self.in_features = (int(s) for s in weight_u8.shape)
         self.device = torch.device(device)
-        self.enc = binding.encode(weight_u8.contiguous().cpu()).to(self.device)
+        self.enc = binding.encode(weight_u8.contiguous().cpu(), max_len=max_code_len).to(self.device)
         self.register_buffer("w_scale", torch.tensor(float(scale), dtype=torch.float32, device=self.device))
         self.bias = None if bias is None else bias.detach().to(self.device)
         self._own: Optional[torch.Tensor] = None
