@@ -9,26 +9,28 @@
 // codes MSB-first, nibble plane (s << 3) | m with the even element low, 4-bit
 // gaps with T counted as a codeword start, uint64 block offsets.
 //
-// Two passes over the input, in tiles of 4096 elements (256 lanes x 16):
-//   1. histogram: per tile, the count of each of the 16 exponent symbols
-//      (kept in the workspace as 16-bit fields) and the tensor's totals;
+// Two passes over the input:
+//   1. histogram, in count tiles of 4096 elements: per tile, the count of
+//      each of the 16 exponent symbols (kept in the workspace as 16-bit
+//      fields) and the tensor's totals;
 //   -- the host turns the totals into code lengths and sizes --
-//   2. three small launches turn the per-tile counts and the code lengths
-//      into 64-bit tile bit offsets (tile bits = sum of count x length;
-//      group totals over 1024 tiles, one workgroup scanning the group
-//      totals, each group rescanning its tiles), clear the stream words that
-//      two tiles share, and write a 256-entry table of codeword pairs;
-//   3. encode, one workgroup per tile: a lane looks up its 8 element pairs
-//      in the pair table, lane and workgroup scans give the bit positions,
-//      each pair is OR-ed into an LDS image of the tile's bit range, and the
-//      image goes out as 32-bit words (the first and last word of the tile,
-//      when shared with a neighbouring tile, with a global atomic OR on the
-//      cleared word); each chunk start inside a lane's bit range gives that
-//      chunk's gap (next codeword start - chunk start) into an LDS gap image,
-//      written out as whole words, and a block start the block offset; the
-//      nibble plane is written per lane.  Chunks are at least 32 bits and
-//      codewords at most 16, so an element's bit interval holds at most one
-//      chunk start.
+//   2. two small launches turn the per-tile counts and the code lengths into
+//      64-bit tile bit offsets (tile bits = sum of count x length; group
+//      totals over 1024 tiles, then each group adds up the totals before it
+//      and scans its tiles) with the chunk and block of each tile's first
+//      stream word, and write a 256-entry table of codeword pairs;
+//   3. encode, one workgroup per 8192 elements (32 per lane): a lane looks up
+//      its 16 element pairs in the pair table, lane and workgroup scans give
+//      the bit positions, each pair is OR-ed into an LDS image of the
+//      workgroup's bit range, and the image goes out in 16-byte stores; the
+//      first and last stream word, when shared with a neighbouring
+//      workgroup, go to side slots that a fourth launch ORs together.  Each
+//      chunk start inside a lane's bit range gives that chunk's gap (next
+//      codeword start - chunk start) into an LDS gap image, written out as
+//      whole words (shared words through the side slots too), and a block
+//      start the block offset; the nibble plane is written per lane.
+//      Chunks are at least 32 bits and codewords at most 16, so an element's
+//      bit interval holds at most one chunk start.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -41,17 +43,25 @@
 namespace {
 
 constexpr int kEncLanes = 256;
-constexpr int kEncPerLane = 16;
-constexpr uint64_t kTile = (uint64_t)kEncLanes * kEncPerLane;          // 4096 elements
-constexpr int kTileWords = (int)(kTile * ECF8_MAX_CODE_LEN / 32) + 2;  // LDS bit image
-// LDS gap image: a tile's bits span at most kTileWords * 32 bits, so (chunks
-// being >= 32 bits) at most kTileWords + 1 chunk starts, 8 gaps per word.
-constexpr int kGapWords = (kTileWords + 1) / 8 + 3;
+constexpr uint64_t kTile = 4096;                                       // elements per count tile
+constexpr int kHistPerLane = 16;                                       // histogram: bytes per lane and load
+constexpr int kEncPerLane = 32;                                        // encode: elements per lane
+constexpr int kPairs = kEncPerLane / 2;                                // codeword pairs per lane
+constexpr uint64_t kWgElems = (uint64_t)kEncLanes * kEncPerLane;       // 8192 elements per encode workgroup
+constexpr uint64_t kWgTiles = kWgElems / kTile;                        // count tiles per encode workgroup
+// LDS bit image of a workgroup's stream words: its bits (at most 16 per
+// element), the offset of its first bit in a 16-byte aligned group of words
+// (up to 3 words and 31 bits), the last window's spill word; whole quads.
+constexpr int kImgWords = ((int)(kWgElems * ECF8_MAX_CODE_LEN / 32) + 1 + 3 + 1 + 3) / 4 * 4;
+// LDS gap image: the bits span at most kImgWords * 32 bits, so (chunks being
+// >= 32 bits) at most kImgWords + 1 chunk starts, 8 gaps per word; whole quads.
+constexpr int kGapWords = ((kImgWords + 1) / 8 + 3 + 3) / 4 * 4;
 constexpr int kScanLanes = 256;                                        // lanes of the per-group scans
 constexpr uint64_t kGroupTiles = 4ull * kScanLanes;                    // tiles per scan group
 constexpr int kCountWords = 8;                                         // per-tile counts: 16 x 16 bits
 constexpr int kHistWaves = 4;                                          // histogram: one tile per wave at a time
-constexpr int kHistLoads = (int)(kTile / 64 / 16);                     // 16-byte loads per lane per tile
+constexpr int kHistLoads = (int)(kTile / 64 / kHistPerLane);           // 16-byte loads per lane per tile
+static_assert(kWgElems % kTile == 0, "an encode workgroup covers whole count tiles");
 
 // Symbol counted by 16-bit field f (0 = low half) of per-tile count word d.
 __host__ __device__ constexpr int count_symbol(int d, int f) { return (d >> 1) + 4 * (2 * (d & 1) + f); }
@@ -71,6 +81,7 @@ struct EncArgs {
     const uint8_t* fp8;
     uint64_t n;
     uint64_t tiles;
+    uint64_t n_wg;             // encode workgroups: ceil(n / kWgElems)
     uint64_t n_blocks;
     uint32_t chunk_bits;       // 8 * C
     uint32_t tb;               // chunks per block
@@ -84,9 +95,11 @@ struct EncArgs {
     const uint64_t* tile_off;  // tiles + 1 entries; tile_off[tiles] = T
     const uint64_t* tile_chunk;   // per tile and for T: chunk holding bit tile_off & ~31, and its block
     const uint2* pairs;        // codeword-pair table, 256 entries
-    uint32_t* side;            // per tile: its partial first and last stream words, first and last gap words
+    uint32_t* side;            // per workgroup: its partial first and last stream words, first and last gap words
     uint64_t m_chunk;          // ceil(2^40 / chunk_bits)
     uint64_t m_tb;             // ceil(2^40 / tb)
+    uint32_t stream_quads;     // stream is 16-byte aligned: whole quads of words go out as one store
+    uint32_t nibble_quads;     // nibbles is 16-byte aligned
 };
 
 // x / d for x < 2^20 and d <= 1024 through m = ceil(2^40 / d): the product's
@@ -96,7 +109,7 @@ __device__ __forceinline__ uint32_t div_small(uint32_t x, uint64_t m) { return (
 // The lane's 16 bytes (elements e0 .. e0 + 15) as 4 little-endian words, zero past n.
 __device__ __forceinline__ void load16(const uint8_t* p, uint64_t e0, uint64_t n, uint32_t (&w)[4])
 {
-    if (e0 + kEncPerLane <= n && ((uintptr_t)(p + e0) & 15) == 0) {
+    if (e0 + 16 <= n && ((uintptr_t)(p + e0) & 15) == 0) {
         const uint4 v = *reinterpret_cast<const uint4*>(p + e0);
         w[0] = v.x;
         w[1] = v.y;
@@ -203,14 +216,14 @@ __global__ __launch_bounds__(256) void ecf8_hist_kernel(const uint8_t* __restric
     const uint64_t stride = (uint64_t)gridDim.x * kHistWaves;
     const uint64_t first = (uint64_t)blockIdx.x * kHistWaves + wave;
     const uint64_t full = ((uintptr_t)fp8 & 15) == 0 ? n / kTile : 0;   // tiles read with plain vector loads
-    const uint32_t lane_off = (uint32_t)lane * kEncPerLane;
+    const uint32_t lane_off = (uint32_t)lane * kHistPerLane;
     uint64_t t = first;
     uint4 nx[kHistLoads];
     auto load_full = [&](uint64_t tt) {
         const uint64_t s = tt < full ? tt : 0;            // past the last full tile: tile 0 again (discarded)
 #pragma unroll
         for (int k = 0; k < kHistLoads; ++k)
-            nx[k] = *reinterpret_cast<const uint4*>(fp8 + s * kTile + k * (64 * kEncPerLane) + lane_off);
+            nx[k] = *reinterpret_cast<const uint4*>(fp8 + s * kTile + k * (64 * kHistPerLane) + lane_off);
     };
     if (t < full) load_full(t);
     for (; t < full; t += stride) {
@@ -233,9 +246,9 @@ __global__ __launch_bounds__(256) void ecf8_hist_kernel(const uint8_t* __restric
         uint32_t pad = 0;
 #pragma unroll
         for (int k = 0; k < kHistLoads; ++k) {
-            const uint64_t e0 = t * kTile + (uint64_t)k * (64 * kEncPerLane) + lane_off;
+            const uint64_t e0 = t * kTile + (uint64_t)k * (64 * kHistPerLane) + lane_off;
             load16(fp8, e0, n, w[k]);
-            pad += e0 >= n ? kEncPerLane : (e0 + kEncPerLane > n ? (uint32_t)(e0 + kEncPerLane - n) : 0u);
+            pad += e0 >= n ? kHistPerLane : (e0 + kHistPerLane > n ? (uint32_t)(e0 + kHistPerLane - n) : 0u);
         }
         uint32_t c[kCountWords];
         tile_hist(w, pad, c);
@@ -311,7 +324,8 @@ __global__ __launch_bounds__(kScanLanes) void ecf8_group_sum_kernel(const uint32
     if (blockIdx.x == 0) {                                // the codeword-pair table (see lane_pairs)
         const uint32_t sa = threadIdx.x & 15u, sb = threadIdx.x >> 4;
         const uint32_t la = tab.len[sa], lb = tab.len[sb];
-        pairs[threadIdx.x] = make_uint2((tab.code[sa] << lb) | tab.code[sb], la | ((la + lb) << 8));
+        const uint32_t pc = (tab.code[sa] << lb) | tab.code[sb];          // la + lb <= 32 bits
+        pairs[threadIdx.x] = make_uint2(la + lb ? pc << (32 - la - lb) : 0u, (la + lb) | (la << 16));
     }
     uint32_t v[4];
     const uint64_t s = lane_tiles(counts, L, tiles, blockIdx.x * kGroupTiles + 4ull * threadIdx.x, v);
@@ -361,65 +375,70 @@ __global__ __launch_bounds__(kScanLanes) void ecf8_tile_off_kernel(const uint32_
 }
 
 // Inclusive scan over the 64 lanes of the wave: DPP row shifts inside each
-// 16-lane row, then the earlier rows' totals through readlane.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane)
+// 16-lane row, then row_bcast:15 adds row r's total into row r + 1 and
+// row_bcast:31 the first two rows' total into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v)
 {
     v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xF, 0xF, true);   // row_shr:1
     v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xF, 0xF, true);   // row_shr:2
     v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, true);   // row_shr:4
     v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xF, 0xF, true);   // row_shr:8
-    const uint32_t r0 = __builtin_amdgcn_readlane(v, 15);
-    const uint32_t r1 = __builtin_amdgcn_readlane(v, 31);
-    const uint32_t r2 = __builtin_amdgcn_readlane(v, 47);
-    const int row = lane >> 4;
-    return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+    return v;
 }
 
-// A tile's metadata, one 64-bit word per lane: lane 0 tile_off[tile], 1
-// tile_off[tile + 1], 2..4 its chunk C0, block B0 and the next tile's chunk C1.
-__device__ __forceinline__ uint64_t tile_meta(const EncArgs& a, uint64_t tile, int lane)
+// The lane's 32 bytes (elements e0 .. e0 + 31) as 8 little-endian words, zero past n.
+__device__ __forceinline__ void load32(const uint8_t* p, uint64_t e0, uint64_t n, uint32_t (&w)[8])
 {
-    if (lane >= 5) return 0;
-    const uint64_t* p = lane < 2 ? a.tile_off + tile + lane : a.tile_chunk + 2 * tile + (lane - 2);
-    return *p;
+    uint32_t a[4], b[4];
+    load16(p, e0, n, a);
+    load16(p, e0 + 16, n, b);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        w[q] = a[q];
+        w[4 + q] = b[q];
+    }
 }
 
-__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l)
+// Nibble plane of 16 bytes: (s << 3) | m of each byte, element 0 in the low
+// nibble.  Per word, a bit select (bitop3 with table 0xE4: the third operand
+// picks the first where it is 1, else the second) puts the sign (bit 7,
+// shifted to bit 3) beside the mantissa in each byte's low nibble (the high
+// nibble is left dirty), a second select packs the low nibbles of bytes 2k
+// and 2k + 1 into byte 2k, and a byte permute gathers bytes 0 and 2 of two
+// words.
+__device__ __forceinline__ uint32_t bit_select(uint32_t ones, uint32_t zeros, uint32_t mask)
 {
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
-    return ((uint64_t)hi << 32) | lo;
+    return __builtin_amdgcn_bitop3_b32(ones, zeros, mask, 0xE4);
 }
 
-// Nibble plane of one lane's 16 bytes: (s << 3) | m of each byte, element 0
-// in the low nibble (SWAR: each byte's nibble, then two halvings).
-__device__ __forceinline__ uint2 nibbles16(const uint32_t (&w)[4])
+__device__ __forceinline__ uint2 nibbles16(const uint32_t* w)
 {
     uint32_t h[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        uint32_t x = ((w[q] >> 4) & 0x08080808u) | (w[q] & 0x07070707u);   // nibble in the low half of each byte
-        x = (x | (x >> 4)) & 0x00FF00FFu;                                  // bytes 0 and 2: two nibbles each
-        h[q] = (x | (x >> 8)) & 0xFFFFu;                                   // four nibbles, element 4q lowest
+        const uint32_t x = bit_select(w[q], w[q] >> 4, 0x07070707u);   // low nibble: sign | mantissa
+        h[q] = bit_select(x, x >> 4, 0x0F0F0F0Fu);                      // byte 2k: nibbles 2k, 2k + 1
     }
-    return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    return make_uint2(__builtin_amdgcn_perm(h[1], h[0], 0x06040200u), __builtin_amdgcn_perm(h[3], h[2], 0x06040200u));
 }
 
-// Codeword pairs of one lane's 16 elements from the pair table `tbl`: entry
-// s_a + 16 s_b holds pc = code(s_a) followed by code(s_b) (at most 32 bits)
-// and pl = len(s_a) | (len(s_a) + len(s_b)) << 8.  The entry's byte offset
-// 8 s_a + 128 s_b comes straight from the exponent bits (byte & 0x78 = 8 s).
-// Elements at or past `valid` (ragged tail) get length 0.
+// Codeword pairs of one lane's 32 elements from the pair table `tbl`: entry
+// s_a + 16 s_b holds pc = code(s_a) followed by code(s_b), left-aligned in 32
+// bits, and pl = (len(s_a) + len(s_b)) | len(s_a) << 16.  The entry's byte
+// offset 8 s_a + 128 s_b comes straight from the exponent bits (byte & 0x78
+// = 8 s).  Elements at or past `valid` (ragged tail) get length 0.
 template <bool kFull>
-__device__ __forceinline__ void lane_pairs(const uint32_t (&w)[4], uint32_t valid, const uint2* tbl,
-                                           uint32_t (&pc)[8], uint32_t (&pl)[8])
+__device__ __forceinline__ void lane_pairs(const uint32_t (&w)[8], uint32_t valid, const uint2* tbl,
+                                           uint32_t (&pc)[kPairs], uint32_t (&pl)[kPairs])
 {
     const uint8_t* base = reinterpret_cast<const uint8_t*>(tbl);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t m = w[j >> 1] & 0x78787878u;
-        const uint32_t ia = (m >> (16 * (j & 1))) & 0x78u, ib = (m >> (16 * (j & 1) + 8)) & 0x78u;
-        const uint2 e = *reinterpret_cast<const uint2*>(base + ia + (ib << 4));
+    for (int j = 0; j < kPairs; ++j) {
+        const uint32_t h = w[j >> 1] >> (16 * (j & 1));
+        const uint32_t off = (h & 0x78u) | ((h >> 4) & 0x780u);
+        const uint2 e = *reinterpret_cast<const uint2*>(base + off);
         pc[j] = e.x;
         pl[j] = e.y;
         if (!kFull) {
@@ -427,158 +446,182 @@ __device__ __forceinline__ void lane_pairs(const uint32_t (&w)[4], uint32_t vali
                 pc[j] = 0u;
                 pl[j] = 0u;
             } else if ((uint32_t)(2 * j + 1) >= valid) {  // first codeword only
-                pc[j] = e.x >> ((e.y >> 8) - (e.y & 255u));
-                pl[j] = (e.y & 255u) * 257u;
+                const uint32_t la = e.y >> 16;
+                pc[j] = e.x & ~(0xFFFFFFFFu >> la);
+                pl[j] = la * 0x10001u;
             }
         }
     }
 }
 
-// Pass 3: encode, one workgroup per tile.
-//   * The workgroup copies the pair table into LDS (one entry per lane).
-//   * The tile's image words and gap words are cleared before the scan
-//     barrier.
-//   * A lane's 8 pairs are OR-ed into the LDS image at their bit positions,
-//     each as a 64-bit window over two words.
-//   * The chunk starts inside a lane's bit range (p, p + acc] are visited
-//     one by one (most lanes have none): the pair holding one is found from
-//     the cumulative pair ends E, its gap is the next codeword start after
-//     it (the end of the pair's first codeword, or of the pair) minus the
-//     chunk start, OR-ed into an LDS gap image (gap words from C0 / 8 on),
-//     and a block start also stores the block offset.
-//   * Chunk, block and position bookkeeping is 32-bit, relative to the
-//     tile's chunk C0 and block B0.
-__global__ __launch_bounds__(256) void ecf8_encode_kernel(EncArgs a)
+// Pass 3: encode, one workgroup per 8192 elements (two count tiles), 32 per
+// lane.
+//   * The workgroup copies the pair table into LDS (one entry per lane); its
+//     bit range, chunk and block come from the offsets of its first tile and
+//     of the next workgroup's, read once (uniform).
+//   * The bit image in LDS starts at the 16-byte aligned group of stream
+//     words that holds the workgroup's first bit; it and the gap image are
+//     cleared in quads before the scan barrier.
+//   * A lane's 16 codeword pairs are OR-ed into the image at their bit
+//     positions: the left-aligned pair shifted right by the position's offset
+//     in its word, and the bits that spill into the next word (alignbit).
+//   * The chunk starts inside a lane's bit range (p, p + acc] are visited one
+//     by one (most lanes have none, a few one): the gap is the smallest
+//     distance from the chunk start to a codeword start at or after it (the
+//     starts of the pairs and of their second codewords, and the lane's end),
+//     taken as a minimum of unsigned differences (starts before the chunk
+//     wrap around to large values); it is OR-ed into the gap image (gap words
+//     from C0 / 8 on), and a block start also stores the block offset: the
+//     element whose codeword starts there, the count of codeword starts
+//     before it.
+//   * The image goes out in quads of words (one 16-byte store each; the
+//     quads holding a word shared with a neighbouring workgroup word by word).
+// Uniform state of one encode workgroup and its LDS.
+struct WgState {
+    uint64_t wg, e0, P0, P1, C0, B0, C1, W0, Wq;
+    uint32_t o, nwords, g_lo, g_hi, valid;
+    uint32_t* img;
+    uint32_t* gimg;
+    uint32_t* wsum;
+    const uint2* pair;
+};
+
+// Everything after the pair-table barrier: kFull when all 8192 elements of
+// the workgroup lie below n (no length-0 padding).
+template <bool kFull>
+__device__ __forceinline__ void encode_body(const EncArgs& a, const WgState& S, const uint32_t (&w)[8])
 {
-    __shared__ uint32_t img[kTileWords];
-    __shared__ uint32_t gimg[kGapWords];                  // gap words from word C0 / 8 on
-    __shared__ uint32_t wsum[4];
-    __shared__ uint2 s_pair[256];                         // the pair table
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint64_t tile = blockIdx.x;
-    const uint64_t e0 = tile * kTile + (uint64_t)tid * kEncPerLane;
-    uint32_t w[4];
-    load16(a.fp8, e0, a.n, w);
-    const uint64_t tm = tile_meta(a, tile, lane);
-    s_pair[tid] = a.pairs[tid];
-    const uint64_t P0 = lane_u64(tm, 0), P1 = lane_u64(tm, 1), C0 = lane_u64(tm, 2), B0 = lane_u64(tm, 3),
-                   C1 = lane_u64(tm, 4);
-    const uint64_t W0 = P0 >> 5;                          // first stream word of the tile
-    const uint64_t nw = P1 > P0 ? ((P1 + 31) >> 5) - W0 : 0;
-    const uint32_t nwords = (uint32_t)(nw < (uint64_t)kTileWords - 1 ? nw : (uint64_t)kTileWords - 1);
-    const uint32_t g_lo = (uint32_t)(((C0 + 1) >> 3) - (C0 >> 3));
-    const uint64_t g_hi64 = C1 > C0 ? (C1 >> 3) - (C0 >> 3) + 1 : 0;
-    const uint32_t g_hi = (uint32_t)(g_hi64 < (uint64_t)kGapWords ? g_hi64 : (uint64_t)kGapWords);
-    for (uint32_t i = tid; i < nwords + 1; i += kEncLanes) img[i] = 0u;   // + 1: the last window's spill word
-    for (uint32_t i = tid; i < g_hi; i += kEncLanes) gimg[i] = 0u;
-    __syncthreads();                                      // pair table
-
-    const uint32_t valid = e0 >= a.n ? 0u : (a.n - e0 >= (uint64_t)kEncPerLane ? 16u : (uint32_t)(a.n - e0));
-    uint32_t pc[8], pl[8], E[8];
-    if ((tile + 1) * kTile <= a.n)
-        lane_pairs<true>(w, 16u, s_pair, pc, pl);
-    else
-        lane_pairs<false>(w, valid, s_pair, pc, pl);
-    uint32_t acc = 0;
+    uint32_t pc[kPairs], pl[kPairs];
+    lane_pairs<kFull>(w, S.valid, S.pair, pc, pl);
+    uint32_t sum = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        acc += pl[j] >> 8;
-        E[j] = acc;                                       // end of pair j, from the lane's first bit
+    for (int j = 0; j < kPairs; ++j) sum += pl[j];
+    const uint32_t acc = sum & 0xFFFFu;                   // the lane's bits (at most 512: no carry into bit 16)
+    if (kFull || S.valid) {
+        uint8_t* nib = a.nibbles + (S.e0 >> 1);
+        const uint2 lo = nibbles16(w), hi = nibbles16(w + 4);
+        if ((kFull || S.valid > 16) && a.nibble_quads) {
+            *reinterpret_cast<uint4*>(nib) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+            *reinterpret_cast<uint2*>(nib) = lo;
+            if (kFull || S.valid > 16) *reinterpret_cast<uint2*>(nib + 8) = hi;
+        }
     }
-    if (valid) *reinterpret_cast<uint2*>(a.nibbles + (e0 >> 1)) = nibbles16(w);
 
-    const uint32_t incl = wave_incl_scan(acc, lane);
-    if (lane == 63) wsum[wave] = incl;
+    const uint32_t incl = wave_incl_scan(acc);
+    if (lane == 63) S.wsum[wave] = incl;
     __syncthreads();                                      // wsum; images cleared
     uint32_t before = 0;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) before += v < wave ? wsum[v] : 0u;
-    const uint32_t rel = (uint32_t)(P0 & 31) + before + incl - acc;   // bit offset inside the tile image
+    for (int v = 0; v < 4; ++v) before += v < wave ? S.wsum[v] : 0u;
+    const uint32_t pre = before + incl - acc;             // the lane's first bit - P0
+    const uint32_t ib = (uint32_t)(S.P0 & 127) + pre;     // ... in the image
 
-    // codeword pairs into the image: the pair's bits left-aligned in a 64-bit
-    // window starting at its word (offset + length <= 63)
+    // codeword pairs into the image: bits [q, q + 32) of the pair at image
+    // position q go to word q / 32 (shifted right by q % 32) and the next word
+    // (the spill; zero when q % 32 = 0)
+    uint32_t q[kPairs + 1];
+    q[0] = ib;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t pos = rel + (j ? E[j - 1] : 0u), L = pl[j] >> 8;
-        const uint64_t v = (uint64_t)pc[j] << ((64u - (pos & 31u) - L) & 63u);
-        atomicOr(&img[pos >> 5], (uint32_t)(v >> 32));
-        atomicOr(&img[(pos >> 5) + 1], (uint32_t)v);
+    for (int j = 0; j < kPairs; ++j) {
+        q[j + 1] = q[j] + (pl[j] & 0xFFFFu);
+        atomicOr(&S.img[q[j] >> 5], pc[j] >> (q[j] & 31u));
+        atomicOr(&S.img[(q[j] >> 5) + 1], __builtin_amdgcn_alignbit(pc[j], 0u, q[j]));
     }
 
-    // chunk starts in (p, p + acc]: d = their offsets from the lane's first bit
-    const uint32_t x = (uint32_t)((P0 & ~31ull) - C0 * a.chunk_bits) + rel;
+    // chunk starts in (p, p + acc]: d = their offsets from the lane's first
+    // bit, D = ib + d their image positions
+    const uint32_t x = (uint32_t)(S.P0 - S.C0 * a.chunk_bits) + pre;   // from the start of chunk C0
     const uint32_t dt = div_small(x, a.m_chunk);
-    uint32_t u = (uint32_t)(C0 & 7) + dt;                 // chunk of the lane's first bit - 8 * (C0 / 8)
-    const uint32_t tbx = (uint32_t)(C0 - B0 * a.tb) + dt;
+    uint32_t u = (uint32_t)(S.C0 & 7) + dt;               // chunk of the lane's first bit - 8 * (C0 / 8)
+    const uint32_t tbx = (uint32_t)(S.C0 - S.B0 * a.tb) + dt;
     uint32_t bk = div_small(tbx, a.m_tb);                 // its block - B0
     uint32_t tbp = tbx - bk * a.tb;                       // its place in the block
     for (uint32_t d = a.chunk_bits - (x - dt * a.chunk_bits); d <= acc; d += a.chunk_bits) {
-        uint32_t st = 0, en = E[0], la = pl[0] & 255u, jj = 0;   // pair jj: E[jj - 1] < d <= E[jj]
+        uint32_t D = ib + d;
+        asm volatile("" : "+v"(D));                       // one subtraction per codeword start and chunk start
+        uint32_t gap = q[kPairs] - D;                     // the lane's end is the next lane's first start
 #pragma unroll
-        for (int k = 0; k < 7; ++k) {
-            const bool past = E[k] < d;
-            st = past ? E[k] : st;
-            en = past ? E[k + 1] : en;
-            la = past ? (pl[k + 1] & 255u) : la;
-            jj += past ? 1u : 0u;
+        for (int j = 0; j < kPairs; ++j) {
+            const uint32_t t = q[j] - D;                  // the pair's start; + len(s_a): its second codeword's
+            gap = min(gap, min(t, t + (pl[j] >> 16)));
         }
-        const uint32_t mid = st + la;                     // end of the pair's first codeword
-        const bool in_a = d <= mid;
-        const uint32_t gap = (in_a ? mid : en) - d;
         ++u;
         if (++tbp == a.tb) {
             tbp = 0;
             ++bk;
-            const uint64_t blk = B0 + bk;
-            if (blk <= a.n_blocks) a.blk_off[blk] = e0 + 2 * jj + (in_a ? 1 : 2);
+            const uint64_t blk = S.B0 + bk;
+            if (blk <= a.n_blocks) {
+                uint32_t before_d = 0;                    // codeword starts before the chunk start
+#pragma unroll
+                for (int j = 0; j < kPairs; ++j)
+                    before_d += (q[j] < D ? 1u : 0u) + (q[j] + (pl[j] >> 16) < D ? 1u : 0u);
+                asm volatile("" : "+v"(before_d));        // a 32-bit count, added to e0 once
+                a.blk_off[blk] = S.e0 + before_d;
+            }
         }
-        if (gap && (u >> 3) < g_hi) atomicOr(&gimg[u >> 3], gap << (4 * (u & 7)));
+        if (gap && (u >> 3) < S.g_hi) atomicOr(&S.gimg[u >> 3], gap << (4 * (u & 7)));
     }
     __syncthreads();                                      // images complete
 
-    // tile image -> stream (bytes MSB-first: each big-endian word
-    // byte-swapped); words past the stream (metadata that undercounts T) are
-    // dropped
-    // A word the tile shares with its neighbour (the stream word holding a
-    // tile boundary, the gap word holding chunks of both tiles) goes to the
-    // tile's side slots instead; ecf8_boundary_kernel ORs the two tiles' parts
-    // into it afterwards (global atomics here were 45% of the pass).  A tile
-    // spans at least 4096 bits, so it shares a word with each neighbour at
-    // most and no word has more than two tiles' bits.
-    const bool last_tile = tile + 1 == a.tiles;
-    const bool first_shared = (P0 & 31) != 0;
-    const bool last_shared = (P1 & 31) != 0 && !last_tile;
-    uint32_t* const side = a.side + 4 * tile;
-    const uint32_t nout = W0 >= a.stream_words ? 0u
-                          : (a.stream_words - W0 < (uint64_t)nwords ? (uint32_t)(a.stream_words - W0) : nwords);
-    for (uint32_t i = tid; i < nout; i += kEncLanes) {
-        const uint32_t v = __builtin_bswap32(img[i]);
-        if (i == 0 && first_shared) side[0] = v;
-        else if (i == nwords - 1 && last_shared) side[1] = v;
-        else a.stream[W0 + i] = v;
+    // image -> stream (bytes MSB-first: each big-endian word byte-swapped);
+    // words past the stream (metadata that undercounts T) are dropped.  A
+    // word the workgroup shares with its neighbour (the stream word holding a
+    // workgroup boundary, the gap word holding chunks of both) goes to the
+    // workgroup's side slots instead; ecf8_boundary_kernel ORs the two parts
+    // into it afterwards.  A workgroup other than the last spans at least
+    // 8192 bits, so it shares a word with each neighbour at most and no word
+    // has more than two workgroups' bits.
+    const bool last_wg = S.wg + 1 == a.n_wg;
+    const bool first_shared = (S.P0 & 31) != 0;
+    const bool last_shared = (S.P1 & 31) != 0 && !last_wg;
+    uint32_t* const side = a.side + 4 * S.wg;
+    const uint32_t nwords = S.nwords, o = S.o;
+    const uint32_t nout = S.W0 >= a.stream_words ? 0u
+                          : (a.stream_words - S.W0 < (uint64_t)nwords ? (uint32_t)(a.stream_words - S.W0) : nwords);
+    // image words [lo, hi) are the workgroup's own
+    const uint32_t lo = o + (first_shared ? 1u : 0u);
+    const uint32_t hi = o + (last_shared && nout == nwords ? nwords - 1 : nout);
+    for (uint32_t k = tid; 4 * k < o + nout; k += kEncLanes) {
+        const uint4 v = reinterpret_cast<const uint4*>(S.img)[k];
+        const uint32_t val[4] = {__builtin_bswap32(v.x), __builtin_bswap32(v.y), __builtin_bswap32(v.z),
+                                 __builtin_bswap32(v.w)};
+        const uint32_t j0 = 4 * k;
+        if (a.stream_quads && j0 >= lo && j0 + 4 <= hi) {
+            *reinterpret_cast<uint4*>(a.stream + S.Wq + j0) = make_uint4(val[0], val[1], val[2], val[3]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t j = j0 + i;
+                if (j >= lo && j < hi) a.stream[S.Wq + j] = val[i];
+                else if (j == o && first_shared) side[0] = val[i];
+                else if (j + 1 == o + nwords && last_shared && nout == nwords) side[1] = val[i];
+            }
+        }
     }
     // gap image -> gaps: the words of chunks C0 + 1 .. C1 (those starting in
-    // (P0, P1]); the first is shared when chunk C0 (the previous tile's) is
-    // in it, the last when chunk C1 + 1 (the next tile's) is
-    const bool gfirst_shared = tile > 0 && ((C0 + 1) & 7) != 0;
-    const bool glast_shared = !last_tile && (C1 & 7) != 7;
-    for (uint32_t j = g_lo + tid; j < g_hi; j += kEncLanes) {
-        const uint64_t g = (C0 >> 3) + j;
+    // (P0, P1]); the first is shared when chunk C0 (the previous workgroup's)
+    // is in it, the last when chunk C1 + 1 (the next workgroup's) is
+    const bool gfirst_shared = S.wg > 0 && ((S.C0 + 1) & 7) != 0;
+    const bool glast_shared = !last_wg && (S.C1 & 7) != 7;
+    for (uint32_t j = S.g_lo + tid; j < S.g_hi; j += kEncLanes) {
+        const uint64_t g = (S.C0 >> 3) + j;
         if (g >= a.gap_words) break;
-        const uint32_t v = gimg[j];
-        if (j == g_lo && gfirst_shared) side[2] = v;
-        else if (j + 1 == g_hi && glast_shared) side[3] = v;
+        const uint32_t v = S.gimg[j];
+        if (j == S.g_lo && gfirst_shared) side[2] = v;
+        else if (j + 1 == S.g_hi && glast_shared) side[3] = v;
         else a.gaps[g] = v;
     }
-    // a tile with no chunk start (the last, if it is shorter than a chunk)
-    // still shares the previous tile's gap word: its part is empty
-    if (tid == 0 && g_lo >= g_hi) side[2] = 0u;
-    if (last_tile) {                                      // zero padding after T
-        for (uint64_t g = W0 + nwords + tid; g < a.stream_words; g += kEncLanes) a.stream[g] = 0u;
-        // and the gap words past the tile's own (the last block's lanes that
-        // hold no chunk; a tile with no chunk start wrote none: from the word
-        // of chunk C0 + 1 on, which for tile 0 holds chunk 0)
-        const uint64_t gz = C1 > C0 ? (C1 >> 3) + 1 : (C0 + 1) >> 3;
+    // a workgroup with no chunk start (the last, if it is shorter than a
+    // chunk) still shares the previous one's gap word: its part is empty
+    if (tid == 0 && S.g_lo >= S.g_hi) side[2] = 0u;
+    if (last_wg) {                                        // zero padding after T
+        for (uint64_t g = S.W0 + nwords + tid; g < a.stream_words; g += kEncLanes) a.stream[g] = 0u;
+        // and the gap words past the workgroup's own (the last block's lanes
+        // that hold no chunk; a workgroup with no chunk start wrote none: from
+        // the word of chunk C0 + 1 on, which for workgroup 0 holds chunk 0)
+        const uint64_t gz = S.C1 > S.C0 ? (S.C1 >> 3) + 1 : (S.C0 + 1) >> 3;
         for (uint64_t g = gz + tid; g < a.gap_words; g += kEncLanes) a.gaps[g] = 0u;
         if (tid == 0) {
             a.blk_off[0] = 0;
@@ -587,18 +630,65 @@ __global__ __launch_bounds__(256) void ecf8_encode_kernel(EncArgs a)
     }
 }
 
-// Pass 4: the words two tiles share, one lane per tile boundary t (between
-// tiles t and t + 1, at bit P = tile_off[t + 1]): the stream word holding P
-// when P is not word-aligned, and the gap word holding chunks C1 = P / (8C)
-// (tile t's last) and C1 + 1 (tile t + 1's first) when they share one.
-__global__ __launch_bounds__(256) void ecf8_boundary_kernel(const uint64_t* __restrict__ tile_off, uint64_t tiles,
+// 7 workgroups per compute unit (72 VGPRs; 7 x 20.5 KB of LDS)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7))) void ecf8_encode_kernel(EncArgs a)
+{
+    __shared__ __align__(16) uint32_t img[kImgWords];
+    __shared__ __align__(16) uint32_t gimg[kGapWords];     // gap words from word C0 / 8 on
+    __shared__ uint32_t wsum[4];
+    __shared__ uint2 s_pair[256];                         // the pair table
+    const int tid = threadIdx.x;
+    WgState S;
+    S.wg = blockIdx.x;
+    const uint64_t t0 = S.wg * kWgTiles;
+    const uint64_t t1 = t0 + kWgTiles < a.tiles ? t0 + kWgTiles : a.tiles;
+    // uniform metadata: bit range [P0, P1), the chunk C0 and block B0 holding
+    // word P0 / 32, the chunk C1 holding word P1 / 32
+    S.P0 = a.tile_off[t0];
+    S.P1 = a.tile_off[t1];
+    S.C0 = a.tile_chunk[2 * t0];
+    S.B0 = a.tile_chunk[2 * t0 + 1];
+    S.C1 = a.tile_chunk[2 * t1];
+    S.e0 = S.wg * kWgElems + (uint64_t)tid * kEncPerLane;
+    uint32_t w[8];
+    load32(a.fp8, S.e0, a.n, w);
+    s_pair[tid] = a.pairs[tid];
+    S.W0 = S.P0 >> 5;                                     // first stream word of the workgroup
+    S.Wq = S.W0 & ~3ull;                                  // image word 0 = stream word Wq
+    S.o = (uint32_t)(S.W0 - S.Wq);
+    const uint64_t nw = S.P1 > S.P0 ? ((S.P1 + 31) >> 5) - S.W0 : 0;
+    S.nwords = (uint32_t)(nw < (uint64_t)kImgWords - 8 ? nw : (uint64_t)kImgWords - 8);
+    S.g_lo = (uint32_t)(((S.C0 + 1) >> 3) - (S.C0 >> 3));
+    const uint64_t g_hi64 = S.C1 > S.C0 ? (S.C1 >> 3) - (S.C0 >> 3) + 1 : 0;
+    S.g_hi = (uint32_t)(g_hi64 < (uint64_t)kGapWords ? g_hi64 : (uint64_t)kGapWords);
+    S.valid = S.e0 >= a.n ? 0u : (a.n - S.e0 >= (uint64_t)kEncPerLane ? 32u : (uint32_t)(a.n - S.e0));
+    S.img = img;
+    S.gimg = gimg;
+    S.wsum = wsum;
+    S.pair = s_pair;
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+    for (uint32_t k = tid; 4 * k < S.o + S.nwords + 1; k += kEncLanes) reinterpret_cast<uint4*>(img)[k] = z4;
+    for (uint32_t k = tid; 4 * k < S.g_hi; k += kEncLanes) reinterpret_cast<uint4*>(gimg)[k] = z4;
+    __syncthreads();                                      // pair table
+    if ((S.wg + 1) * kWgElems <= a.n)
+        encode_body<true>(a, S, w);
+    else
+        encode_body<false>(a, S, w);
+}
+
+// Pass 4: the words two workgroups share, one lane per boundary t (between
+// workgroups t and t + 1, at bit P = tile_off[(t + 1) * kWgTiles]): the stream
+// word holding P when P is not word-aligned, and the gap word holding chunks
+// C1 = P / (8C) (workgroup t's last) and C1 + 1 (workgroup t + 1's first) when
+// they share one.
+__global__ __launch_bounds__(256) void ecf8_boundary_kernel(const uint64_t* __restrict__ tile_off, uint64_t n_wg,
                                                             const uint32_t* __restrict__ side, uint32_t chunk_bits,
                                                             uint32_t* __restrict__ stream, uint64_t stream_words,
                                                             uint32_t* __restrict__ gaps, uint64_t gap_words)
 {
     const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t + 1 >= tiles) return;
-    const uint64_t P = tile_off[t + 1];
+    if (t + 1 >= n_wg) return;
+    const uint64_t P = tile_off[(t + 1) * kWgTiles];
     const uint32_t* s0 = side + 4 * t;
     const uint32_t* s1 = side + 4 * (t + 1);
     if ((P & 31) != 0 && (P >> 5) < stream_words) stream[P >> 5] = s0[1] | s1[0];
@@ -632,8 +722,8 @@ int resident_slots(int which, const void* kernel, uint32_t* out)
 
 // Workspace: per-tile counts (32 B per tile) | tile bit offsets (tiles + 1,
 // u64) | per-tile chunk and block (2 x u64) | group totals (u64) |
-// codeword-pair table (2 KB) | per-tile side slots of the shared words
-// (16 B per tile), each part 256-byte aligned.
+// codeword-pair table (2 KB) | per-encode-workgroup side slots of the shared words
+// (16 B each, sized per tile), each part 256-byte aligned.
 struct EncWorkspace {
     uint64_t tiles, groups, off_off, chunk_off, group_off, pair_off, side_off, bytes;
 };
@@ -727,6 +817,7 @@ extern "C" int ecf8_encode_device(const uint8_t* fp8, const ecf8_meta* meta, uin
     a.fp8 = fp8;
     a.n = n;
     a.tiles = W.tiles;
+    a.n_wg = (n + kWgElems - 1) / kWgElems;
     a.n_blocks = meta->n_blocks;
     a.chunk_bits = 8u * meta->chunk_bytes;
     a.tb = meta->threads_per_block;
@@ -743,17 +834,19 @@ extern "C" int ecf8_encode_device(const uint8_t* fp8, const ecf8_meta* meta, uin
     a.side = side;
     a.m_chunk = ((1ull << 40) + a.chunk_bits - 1) / a.chunk_bits;
     a.m_tb = ((1ull << 40) + a.tb - 1) / a.tb;
+    a.stream_quads = ((uintptr_t)stream & 15) == 0;
+    a.nibble_quads = ((uintptr_t)nibbles & 15) == 0;
 
     // every output word is written by the kernels: the gap and stream words a
-    // tile owns by the encode kernel, those two tiles share by the boundary
-    // kernel, the padding after the last chunk by the last tile
+    // workgroup owns by the encode kernel, those two workgroups share by the boundary
+    // kernel, the padding after the last chunk by the last workgroup
     hipLaunchKernelGGL(ecf8_group_sum_kernel, dim3((uint32_t)W.groups), dim3(kScanLanes), 0, st, counts, L, W.tiles,
                        group, tab, pairs);
     hipLaunchKernelGGL(ecf8_tile_off_kernel, dim3((uint32_t)W.groups), dim3(kScanLanes), 0, st, counts, L, W.tiles,
                        group, tile_off, tile_chunk, a.chunk_bits, a.tb);
-    hipLaunchKernelGGL(ecf8_encode_kernel, dim3((uint32_t)W.tiles), dim3(kEncLanes), 0, st, a);
-    if (W.tiles > 1)
-        hipLaunchKernelGGL(ecf8_boundary_kernel, dim3((uint32_t)((W.tiles - 1 + 255) / 256)), dim3(256), 0, st,
-                           tile_off, W.tiles, side, a.chunk_bits, a.stream, a.stream_words, a.gaps, a.gap_words);
+    hipLaunchKernelGGL(ecf8_encode_kernel, dim3((uint32_t)a.n_wg), dim3(kEncLanes), 0, st, a);
+    if (a.n_wg > 1)
+        hipLaunchKernelGGL(ecf8_boundary_kernel, dim3((uint32_t)((a.n_wg - 1 + 255) / 256)), dim3(256), 0, st,
+                           tile_off, a.n_wg, side, a.chunk_bits, a.stream, a.stream_words, a.gaps, a.gap_words);
     return check(hipGetLastError());
 }

@@ -50,17 +50,20 @@ def make_input(kind, n, seed):
     return x.astype(np.uint8), L
 
 
-def canary_buffers(meta, d):
-    """Device buffers of meta's sizes inside larger canary-filled allocations."""
-    def buf(nbytes):
-        whole = torch.full((int(nbytes) + PAD,), CANARY, dtype=torch.uint8, device=d)
-        return whole, whole[:int(nbytes)]
-    parts = [buf(meta.stream_bytes), buf(meta.nibble_bytes), buf(meta.gap_bytes), buf(8 * (meta.n_blocks + 1))]
+def canary_buffers(meta, d, out_offsets=(0, 0, 0, 0)):
+    """Device buffers of meta's sizes inside larger canary-filled allocations, each starting
+    out_offsets[i] bytes into its allocation (the ABI's least alignments: stream 4, nibbles 8,
+    gaps 4, blk_off 8)."""
+    def buf(nbytes, off):
+        whole = torch.full((int(nbytes) + PAD + off,), CANARY, dtype=torch.uint8, device=d)
+        return whole[off:], whole[off:off + int(nbytes)]
+    sizes = [meta.stream_bytes, meta.nibble_bytes, meta.gap_bytes, 8 * (meta.n_blocks + 1)]
+    parts = [buf(n, off) for n, off in zip(sizes, out_offsets)]
     enc = B.DeviceEncoded(meta, parts[0][1], parts[1][1], parts[2][1], parts[3][1].view(torch.int64))
     return enc, [p[0] for p in parts]
 
 
-def encode_on_device(x_np, lengths, C, TB, d, offset=0):
+def encode_on_device(x_np, lengths, C, TB, d, offset=0, out_offsets=(0, 0, 0, 0)):
     """Device encode of x_np (uploaded at byte `offset` of a larger buffer) into canary buffers."""
     n = x_np.size
     up = torch.zeros(n + offset + 16, dtype=torch.uint8, device=d)
@@ -71,14 +74,14 @@ def encode_on_device(x_np, lengths, C, TB, d, offset=0):
     if lengths is None:
         lengths = B.codebook_from_freq(freq.astype(np.uint64)) if n else [0] * 16
     m = B.meta_from_freq(freq.astype(np.uint64), n, lengths, C, TB)
-    enc, wholes = canary_buffers(m, d)
+    enc, wholes = canary_buffers(m, d, out_offsets)
     B.encode_into(x, enc, ws)
     torch.cuda.synchronize()
     return enc, wholes, freq
 
 
-def assert_equal_to_oracle(x_np, lengths, C, TB, d, offset=0):
-    enc, wholes, freq = encode_on_device(x_np, lengths, C, TB, d, offset)
+def assert_equal_to_oracle(x_np, lengths, C, TB, d, offset=0, out_offsets=(0, 0, 0, 0)):
+    enc, wholes, freq = encode_on_device(x_np, lengths, C, TB, d, offset, out_offsets)
     assert np.array_equal(freq.astype(np.uint64), oracle.histogram(x_np).astype(np.uint64))
     ref = oracle.encode(x_np, lengths=lengths, chunk_bytes=C, tb=TB)
     assert int(enc.meta.total_bits) == ref["total_bits"]
@@ -92,7 +95,7 @@ def assert_equal_to_oracle(x_np, lengths, C, TB, d, offset=0):
     return enc
 
 
-EDGE = [("stable", n) for n in (1, 2, 15, 16, 17, 31, 4095, 4096, 4097, 8191, 65537, 1_000_003)] + \
+EDGE = [("stable", n) for n in (1, 2, 15, 16, 17, 31, 4095, 4096, 4097, 8191, 8193, 16385, 65537, 1_000_003)] + \
        [("uniform4", 8192 * 3), ("fib15", 200_000), ("long12x6", 200_000), ("two", 65536 + 7),
         ("single", 300_000), ("bytes", 123_457)]
 PARAMS = [(16, 256), (4, 64), (12, 192), (64, 1024), (8, 128)]
@@ -121,6 +124,16 @@ def test_encode_device_unaligned_input(offset):
     d = dev()
     x, _ = make_input("stable", 100_003, offset)
     assert_equal_to_oracle(x, None, 16, 256, d, offset)
+
+
+@pytest.mark.parametrize("n", [8192 * 5 + 100, 300_001])
+def test_encode_device_outputs_at_least_alignment(n):
+    """Stream and gaps 4 bytes, nibbles and blk_off 8 bytes past a 16-byte boundary: the
+    encode's 16-byte stores fall back to narrower ones, same bytes."""
+    d = dev()
+    x, _ = make_input("stable", n, 7)
+    assert_equal_to_oracle(x, None, 16, 256, d, out_offsets=(4, 8, 4, 8))
+    assert_equal_to_oracle(x, None, 8, 128, d, out_offsets=(12, 8, 4, 8))
 
 
 def test_encode_device_empty():
