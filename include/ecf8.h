@@ -340,12 +340,39 @@ uint64_t ecf8_encode_workspace_bytes(uint64_t n);
  * buffers or the workspace.  n = 0 writes the 16 zero bytes of the stream and
  * blk_off[0] = 0 only (fp8, nibbles, gaps and workspace may be NULL).
  * Alignment: stream and gaps 4 B, nibbles and blk_off 8 B, workspace 256 B.
- * Asynchronous on hip_stream: gap clear, three scan launches, encode.
+ * Asynchronous on hip_stream: two scan launches (group totals, tile
+ * offsets), the encode, and one launch for the words two encode workgroups
+ * share.  The same as ecf8_encode_batched_device with one job.
  * Errors: ECF8_ERR_ARG (NULL or misaligned), ECF8_ERR_META,
- * ECF8_ERR_WORKSPACE, ECF8_ERR_SIZE (n >= 2^44), ECF8_ERR_HIP. */
+ * ECF8_ERR_WORKSPACE, ECF8_ERR_SIZE (n >= 2^37), ECF8_ERR_HIP. */
 int ecf8_encode_device(const uint8_t* fp8, const ecf8_meta* meta, uint8_t* stream, uint8_t* nibbles,
                        uint8_t* gaps, uint64_t* blk_off, void* workspace, uint64_t workspace_bytes,
                        void* hip_stream);
+
+/* One tensor of ecf8_encode_batched_device: the arguments of
+ * ecf8_encode_device, with the metadata by value. */
+typedef struct {
+    const uint8_t* fp8;        /* device, meta.n bytes */
+    ecf8_meta meta;            /* from ecf8_meta_from_freq (or ecf8_encode_sizes) for this data */
+    uint8_t* stream;           /* device outputs of at least meta's sizes */
+    uint8_t* nibbles;
+    uint8_t* gaps;
+    uint64_t* blk_off;
+    void* workspace;           /* the workspace ecf8_histogram_device filled for this data */
+    uint64_t workspace_bytes;
+} ecf8_encode_job;
+
+/* ECF8 blog §3.1.1 / §3.2.1 on the GPU, for several tensors at once (a
+ * layer re-encoded after its weights change, DFloat11 §5 "dynamic codebook
+ * update"): jobs[0 .. count) encoded as ecf8_encode_device would encode each
+ * (same bytes, same alignment and workspace rules), eight tensors per set of
+ * four launches instead of four launches per tensor.  jobs is host memory,
+ * read before the call returns; the tensors' buffers must not overlap.  Every
+ * job is checked before anything is launched: on an error nothing is
+ * written.  Asynchronous on hip_stream.
+ * Errors: ECF8_ERR_ARG (count < 0, jobs NULL with count > 0, or a job's
+ * pointers NULL or misaligned), and per job as ecf8_encode_device. */
+int ecf8_encode_batched_device(const ecf8_encode_job* jobs, int count, void* hip_stream);
 
 /* ------------------------- weight statistics --------------------------- */
 

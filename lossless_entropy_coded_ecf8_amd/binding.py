@@ -57,6 +57,12 @@ class TensorDesc(ctypes.Structure):
     _fields_ = [("s", Stream), ("meta", Meta), ("out_offset", ctypes.c_uint64)]
 
 
+class EncodeJob(ctypes.Structure):
+    _fields_ = [("fp8", ctypes.c_void_p), ("meta", Meta), ("stream", ctypes.c_void_p), ("nibbles", ctypes.c_void_p),
+                ("gaps", ctypes.c_void_p), ("blk_off", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_uint64)]
+
+
 class Plan(ctypes.Structure):
     _fields_ = [("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
                 ("total_blocks", ctypes.c_uint64), ("count", ctypes.c_uint32),
@@ -97,7 +103,7 @@ EXPORTS = ["ecf8_histogram", "ecf8_codebook_from_freq", "ecf8_build_codebook", "
            "ecf8_decode_prepare", "ecf8_decode_run", "ecf8_build_tables", "ecf8_decode_blocks",
            "ecf8_decode_blocks_timed", "ecf8_decode_batched", "ecf8_decode", "ecf8_decode_batched_noalloc",
            "ecf8_decode_status", "ecf8_histogram_device", "ecf8_meta_from_freq", "ecf8_encode_workspace_bytes",
-           "ecf8_encode_device", "ecf8_alpha_hat", "ecf8_exponent_entropy_bound", "ecf8_hbm_copy",
+           "ecf8_encode_device", "ecf8_encode_batched_device", "ecf8_alpha_hat", "ecf8_exponent_entropy_bound", "ecf8_hbm_copy",
            "ecf8_strerror", "ecf8_version"]
 
 _lib = None
@@ -142,6 +148,7 @@ def lib() -> ctypes.CDLL:
                                     ctypes.POINTER(Meta)]),
         "ecf8_encode_workspace_bytes": (ctypes.c_uint64, [ctypes.c_uint64]),
         "ecf8_encode_device": (i, [vp, ctypes.POINTER(Meta), vp, vp, vp, vp, vp, ctypes.c_uint64, vp]),
+        "ecf8_encode_batched_device": (i, [ctypes.POINTER(EncodeJob), i, vp]),
         "ecf8_alpha_hat": (i, [vp, ctypes.c_uint64, ctypes.c_double, ctypes.POINTER(ctypes.c_double)]),
         "ecf8_exponent_entropy_bound": (ctypes.c_double, [ctypes.c_double]),
         "ecf8_hbm_copy": (i, [vp, vp, ctypes.c_uint64, vp]),
@@ -439,6 +446,22 @@ def encode_into(x, enc: DeviceEncoded, workspace, stream=None) -> DeviceEncoded:
                                     ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                     _stream_handle(stream)), "ecf8_encode_device")
     return enc
+
+
+def encode_batched_into(xs, encs, workspaces, stream=None):
+    """Encode several device byte tensors at once (ecf8_encode_batched_device): xs[i] into encs[i]'s buffers
+    under encs[i].meta, workspaces[i] being the one a histogram_device of xs[i] filled."""
+    if not (len(xs) == len(encs) == len(workspaces)):
+        raise ValueError("xs, encs and workspaces differ in length")
+    jobs = (EncodeJob * max(len(xs), 1))()
+    keep = []
+    for k, (x, enc, ws) in enumerate(zip(xs, encs, workspaces)):
+        x = x.contiguous().view(-1)
+        keep.append(x)
+        jobs[k] = EncodeJob(x.data_ptr(), enc.meta, enc.stream.data_ptr(), enc.nibbles.data_ptr(),
+                            enc.gaps.data_ptr(), enc.blk_off.data_ptr(), ws.data_ptr(), ws.numel())
+    _check(lib().ecf8_encode_batched_device(jobs, len(xs), _stream_handle(stream)), "ecf8_encode_batched_device")
+    return encs
 
 
 def encode_device(x, lengths=None, chunk_bytes: int = DEFAULT_CHUNK_BYTES,

@@ -62,45 +62,62 @@ constexpr int kCountWords = 8;                                         // per-ti
 constexpr int kHistWaves = 4;                                          // histogram: one tile per wave at a time
 constexpr int kHistLoads = (int)(kTile / 64 / kHistPerLane);           // 16-byte loads per lane per tile
 static_assert(kWgElems % kTile == 0, "an encode workgroup covers whole count tiles");
+constexpr uint64_t kMaxGrid = 1ull << 24;                              // workgroups of 256 lanes per launch
 
 // Symbol counted by 16-bit field f (0 = low half) of per-tile count word d.
 __host__ __device__ constexpr int count_symbol(int d, int f) { return (d >> 1) + 4 * (2 * (d & 1) + f); }
 
-// Code table for the encode kernel: length and MSB-first code per symbol.
-struct EncTable {
-    uint32_t code[ECF8_NSYM];
-    uint32_t len[ECF8_NSYM];
-};
-
-// Code length of the symbol of each count field: v[2d + f] for word d, half f.
-struct CountLens {
-    uint32_t v[2 * kCountWords];
-};
-
-struct EncArgs {
+// One tensor of an encode launch: its input, outputs, workspace parts and
+// code.  Up to kBatch tensors go to each launch by value (kernel argument).
+struct EncJob {
     const uint8_t* fp8;
     uint64_t n;
-    uint64_t tiles;
+    uint64_t tiles;            // count tiles: ceil(n / kTile)
     uint64_t n_wg;             // encode workgroups: ceil(n / kWgElems)
     uint64_t n_blocks;
-    uint32_t chunk_bits;       // 8 * C
-    uint32_t tb;               // chunks per block
-    uint64_t gap_count;        // chunks with a gap entry (n_blocks * TB)
     uint64_t gap_words;        // gap_bytes / 4
     uint64_t stream_words;     // stream_bytes / 4
     uint32_t* stream;
     uint8_t* nibbles;
     uint32_t* gaps;            // 4-byte words of the gap array
     uint64_t* blk_off;
-    const uint64_t* tile_off;  // tiles + 1 entries; tile_off[tiles] = T
-    const uint64_t* tile_chunk;   // per tile and for T: chunk holding bit tile_off & ~31, and its block
-    const uint2* pairs;        // codeword-pair table, 256 entries
+    const uint32_t* counts;    // per-tile symbol counts (the histogram pass)
+    uint64_t* group;           // per group of kGroupTiles tiles: its total bits
+    uint64_t* tile_off;        // tiles + 1 entries; tile_off[tiles] = T
+    uint64_t* tile_chunk;      // per tile and for T: chunk holding bit tile_off & ~31, and its block
+    uint2* pairs;              // codeword-pair table, 256 entries
     uint32_t* side;            // per workgroup: its partial first and last stream words, first and last gap words
     uint64_t m_chunk;          // ceil(2^40 / chunk_bits)
     uint64_t m_tb;             // ceil(2^40 / tb)
+    uint32_t chunk_bits;       // 8 * C
+    uint32_t tb;               // chunks per block
     uint32_t stream_quads;     // stream is 16-byte aligned: whole quads of words go out as one store
     uint32_t nibble_quads;     // nibbles is 16-byte aligned
+    uint16_t code[ECF8_NSYM];  // MSB-first canonical code per symbol
+    uint8_t len[ECF8_NSYM];    // code length per symbol
+    uint8_t count_len[2 * kCountWords];   // code length of the symbol of count field 2d + f
 };
+
+constexpr int kBatch = 8;
+
+// The tensors of one launch and, per kernel, the first block of each tensor
+// (start[count] = the grid).
+struct EncBatch {
+    EncJob job[kBatch];
+    uint32_t grp_start[kBatch + 1];   // group-sum and tile-offset kernels
+    uint32_t wg_start[kBatch + 1];    // encode kernel
+    uint32_t bnd_start[kBatch + 1];   // boundary kernel
+    uint32_t count;
+};
+
+// The tensor whose blocks hold block b (uniform): start[j] <= b < start[j + 1].
+__device__ __forceinline__ int job_of(const uint32_t* start, uint32_t count, uint32_t b)
+{
+    int j = 0;
+#pragma unroll
+    for (int k = 1; k < kBatch; ++k) j += (k < (int)count && b >= start[k]) ? 1 : 0;
+    return j;
+}
 
 // x / d for x < 2^20 and d <= 1024 through m = ceil(2^40 / d): the product's
 // error is below x / 2^40 < 1 / d, so the quotient is exact.
@@ -266,19 +283,19 @@ __global__ __launch_bounds__(256) void ecf8_hist_kernel(const uint8_t* __restric
 }
 
 // Code bits of one tile from its counts.
-__device__ __forceinline__ uint32_t tile_bits(const uint32_t* __restrict__ counts, uint64_t tile, const CountLens& L)
+__device__ __forceinline__ uint32_t tile_bits(const uint32_t* __restrict__ counts, uint64_t tile, const uint8_t* L)
 {
     const uint4 a = reinterpret_cast<const uint4*>(counts)[2 * tile];
     const uint4 b = reinterpret_cast<const uint4*>(counts)[2 * tile + 1];
     const uint32_t c[kCountWords] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     uint32_t s = 0;
 #pragma unroll
-    for (int d = 0; d < kCountWords; ++d) s += (c[d] & 0xFFFFu) * L.v[2 * d] + (c[d] >> 16) * L.v[2 * d + 1];
+    for (int d = 0; d < kCountWords; ++d) s += (c[d] & 0xFFFFu) * L[2 * d] + (c[d] >> 16) * L[2 * d + 1];
     return s;
 }
 
 // Bits of the four tiles a scan lane owns (zero past the last tile).
-__device__ __forceinline__ uint32_t lane_tiles(const uint32_t* __restrict__ counts, const CountLens& L, uint64_t tiles,
+__device__ __forceinline__ uint32_t lane_tiles(const uint32_t* __restrict__ counts, const uint8_t* L, uint64_t tiles,
                                                uint64_t t0, uint32_t (&v)[4])
 {
     uint32_t s = 0;
@@ -315,61 +332,63 @@ __device__ __forceinline__ uint64_t div_u64(uint64_t x, uint32_t d)
     return q;
 }
 
-// Pass 2a: total bits of each group of 1024 tiles.
-__global__ __launch_bounds__(kScanLanes) void ecf8_group_sum_kernel(const uint32_t* __restrict__ counts, CountLens L,
-                                                                    uint64_t tiles, uint64_t* __restrict__ gsum,
-                                                                    EncTable tab, uint2* __restrict__ pairs)
+// Pass 2a: total bits of each group of 1024 tiles; the first group of each
+// tensor also writes the tensor's codeword-pair table (see lane_pairs).
+__global__ __launch_bounds__(kScanLanes) void ecf8_group_sum_kernel(const EncBatch B)
 {
     __shared__ uint64_t wsum[kScanLanes / 64];
-    if (blockIdx.x == 0) {                                // the codeword-pair table (see lane_pairs)
+    const int jb = job_of(B.grp_start, B.count, blockIdx.x);
+    const EncJob& J = B.job[jb];
+    const uint32_t g = blockIdx.x - B.grp_start[jb];
+    if (g == 0) {
         const uint32_t sa = threadIdx.x & 15u, sb = threadIdx.x >> 4;
-        const uint32_t la = tab.len[sa], lb = tab.len[sb];
-        const uint32_t pc = (tab.code[sa] << lb) | tab.code[sb];          // la + lb <= 32 bits
-        pairs[threadIdx.x] = make_uint2(la + lb ? pc << (32 - la - lb) : 0u, (la + lb) | (la << 16));
+        const uint32_t la = J.len[sa], lb = J.len[sb];
+        const uint32_t pc = ((uint32_t)J.code[sa] << lb) | J.code[sb];    // la + lb <= 32 bits
+        J.pairs[threadIdx.x] = make_uint2(la + lb ? pc << (32 - la - lb) : 0u, (la + lb) | (la << 16));
     }
     uint32_t v[4];
-    const uint64_t s = lane_tiles(counts, L, tiles, blockIdx.x * kGroupTiles + 4ull * threadIdx.x, v);
+    const uint64_t s = lane_tiles(J.counts, J.count_len, J.tiles, g * kGroupTiles + 4ull * threadIdx.x, v);
     const uint64_t incl = block_incl_scan<kScanLanes>(s, wsum);
-    if (threadIdx.x == kScanLanes - 1) gsum[blockIdx.x] = incl;
+    if (threadIdx.x == kScanLanes - 1) J.group[g] = incl;
 }
 
 // Pass 2b: tile bit offsets = the sum of the earlier groups' totals (each
 // workgroup adds them up itself) + an exclusive scan inside the group
 // (tile_off[tiles] = T), with the chunk and block holding each tile's first
 // stream word.
-__global__ __launch_bounds__(kScanLanes) void ecf8_tile_off_kernel(const uint32_t* __restrict__ counts, CountLens L,
-                                                                   uint64_t tiles, const uint64_t* __restrict__ gsum,
-                                                                   uint64_t* __restrict__ tile_off,
-                                                                   uint64_t* __restrict__ tile_chunk, uint32_t chunk_bits,
-                                                                   uint32_t tb)
+__global__ __launch_bounds__(kScanLanes) void ecf8_tile_off_kernel(const EncBatch B)
 {
     __shared__ uint64_t wsum[kScanLanes / 64];
     __shared__ uint64_t s_goff;
+    const int jb = job_of(B.grp_start, B.count, blockIdx.x);
+    const EncJob& J = B.job[jb];
+    const uint32_t g = blockIdx.x - B.grp_start[jb];
+    const uint64_t tiles = J.tiles;
     // this group's offset: the earlier groups' totals, summed lane-strided
     uint64_t before = 0;
-    for (uint64_t i = threadIdx.x; i < blockIdx.x; i += kScanLanes) before += gsum[i];
+    for (uint64_t i = threadIdx.x; i < g; i += kScanLanes) before += J.group[i];
     before = block_incl_scan<kScanLanes>(before, wsum);
     if (threadIdx.x == kScanLanes - 1) s_goff = before;
     __syncthreads();
     const uint64_t goff = s_goff;
     uint32_t v[4];
-    const uint64_t t0 = blockIdx.x * kGroupTiles + 4ull * threadIdx.x;
-    const uint64_t s = lane_tiles(counts, L, tiles, t0, v);
+    const uint64_t t0 = g * kGroupTiles + 4ull * threadIdx.x;
+    const uint64_t s = lane_tiles(J.counts, J.count_len, tiles, t0, v);
     uint64_t run = goff + block_incl_scan<kScanLanes>(s, wsum) - s;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         if (t0 + k < tiles) {
-            tile_off[t0 + k] = run;
-            const uint64_t c = div_u64(run & ~31ull, chunk_bits);
-            tile_chunk[2 * (t0 + k)] = c;
-            tile_chunk[2 * (t0 + k) + 1] = div_u64(c, tb);
+            J.tile_off[t0 + k] = run;
+            const uint64_t c = div_u64(run & ~31ull, J.chunk_bits);
+            J.tile_chunk[2 * (t0 + k)] = c;
+            J.tile_chunk[2 * (t0 + k) + 1] = div_u64(c, J.tb);
         }
         run += v[k];
         if (t0 + k + 1 == tiles) {
-            tile_off[tiles] = run;
-            const uint64_t c = div_u64(run & ~31ull, chunk_bits);
-            tile_chunk[2 * tiles] = c;
-            tile_chunk[2 * tiles + 1] = div_u64(c, tb);
+            J.tile_off[tiles] = run;
+            const uint64_t c = div_u64(run & ~31ull, J.chunk_bits);
+            J.tile_chunk[2 * tiles] = c;
+            J.tile_chunk[2 * tiles + 1] = div_u64(c, J.tb);
         }
     }
 }
@@ -489,7 +508,7 @@ struct WgState {
 // Everything after the pair-table barrier: kFull when all 8192 elements of
 // the workgroup lie below n (no length-0 padding).
 template <bool kFull>
-__device__ __forceinline__ void encode_body(const EncArgs& a, const WgState& S, const uint32_t (&w)[8])
+__device__ __forceinline__ void encode_body(const EncJob& a, const WgState& S, const uint32_t (&w)[8])
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t pc[kPairs], pl[kPairs];
@@ -631,15 +650,17 @@ __device__ __forceinline__ void encode_body(const EncArgs& a, const WgState& S, 
 }
 
 // 7 workgroups per compute unit (72 VGPRs; 7 x 20.5 KB of LDS)
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7))) void ecf8_encode_kernel(EncArgs a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7))) void ecf8_encode_kernel(const EncBatch B)
 {
     __shared__ __align__(16) uint32_t img[kImgWords];
     __shared__ __align__(16) uint32_t gimg[kGapWords];     // gap words from word C0 / 8 on
     __shared__ uint32_t wsum[4];
     __shared__ uint2 s_pair[256];                         // the pair table
     const int tid = threadIdx.x;
+    const int jb = job_of(B.wg_start, B.count, blockIdx.x);
+    const EncJob& a = B.job[jb];
     WgState S;
-    S.wg = blockIdx.x;
+    S.wg = blockIdx.x - B.wg_start[jb];
     const uint64_t t0 = S.wg * kWgTiles;
     const uint64_t t1 = t0 + kWgTiles < a.tiles ? t0 + kWgTiles : a.tiles;
     // uniform metadata: bit range [P0, P1), the chunk C0 and block B0 holding
@@ -681,19 +702,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7))) void e
 // word holding P when P is not word-aligned, and the gap word holding chunks
 // C1 = P / (8C) (workgroup t's last) and C1 + 1 (workgroup t + 1's first) when
 // they share one.
-__global__ __launch_bounds__(256) void ecf8_boundary_kernel(const uint64_t* __restrict__ tile_off, uint64_t n_wg,
-                                                            const uint32_t* __restrict__ side, uint32_t chunk_bits,
-                                                            uint32_t* __restrict__ stream, uint64_t stream_words,
-                                                            uint32_t* __restrict__ gaps, uint64_t gap_words)
+__global__ __launch_bounds__(256) void ecf8_boundary_kernel(const EncBatch B)
 {
-    const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t + 1 >= n_wg) return;
-    const uint64_t P = tile_off[(t + 1) * kWgTiles];
-    const uint32_t* s0 = side + 4 * t;
-    const uint32_t* s1 = side + 4 * (t + 1);
-    if ((P & 31) != 0 && (P >> 5) < stream_words) stream[P >> 5] = s0[1] | s1[0];
-    const uint64_t c1 = P / chunk_bits;
-    if ((c1 & 7) != 7 && (c1 >> 3) < gap_words) gaps[c1 >> 3] = s0[3] | s1[2];
+    const int jb = job_of(B.bnd_start, B.count, blockIdx.x);
+    const EncJob& J = B.job[jb];
+    const uint64_t t = (uint64_t)(blockIdx.x - B.bnd_start[jb]) * blockDim.x + threadIdx.x;
+    if (t + 1 >= J.n_wg) return;
+    const uint64_t P = J.tile_off[(t + 1) * kWgTiles];
+    const uint32_t* s0 = J.side + 4 * t;
+    const uint32_t* s1 = J.side + 4 * (t + 1);
+    if ((P & 31) != 0 && (P >> 5) < J.stream_words) J.stream[P >> 5] = s0[1] | s1[0];
+    const uint64_t c1 = P / J.chunk_bits;
+    if ((c1 & 7) != 7 && (c1 >> 3) < J.gap_words) J.gaps[c1 >> 3] = s0[3] | s1[2];
 }
 
 int check(hipError_t e) { return e == hipSuccess ? ECF8_OK : ECF8_ERR_HIP; }
@@ -771,82 +791,142 @@ extern "C" int ecf8_histogram_device(const uint8_t* fp8, uint64_t n, uint64_t* f
     return check(hipGetLastError());
 }
 
-extern "C" int ecf8_encode_device(const uint8_t* fp8, const ecf8_meta* meta, uint8_t* stream, uint8_t* nibbles,
-                                  uint8_t* gaps, uint64_t* blk_off, void* workspace, uint64_t workspace_bytes,
-                                  void* hip_stream)
+namespace {
+
+// Checks one tensor's arguments and fills its job (n > 0), or sets `empty`
+// (n = 0: the caller writes the 16 zero bytes of stream padding and
+// blk_off[0] = 0).
+int make_job(const ecf8_encode_job& in, EncJob& J, bool& empty)
 {
-    if (!meta) return ECF8_ERR_ARG;
+    const ecf8_meta* meta = &in.meta;
     int rc = ecf8_validate_meta(meta);
     if (rc) return rc;
     const uint64_t n = meta->n;
-    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
-    if (!stream || !blk_off || ((uintptr_t)stream & 3) || ((uintptr_t)blk_off & 7)) return ECF8_ERR_ARG;
-    if (n == 0) {      // the 16 zero bytes of stream padding and blk_off[0] = 0
-        hipLaunchKernelGGL(ecf8_zero_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<uint32_t*>(stream),
-                           meta->stream_bytes / 4);
-        hipLaunchKernelGGL(ecf8_zero_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<uint32_t*>(blk_off),
-                           (uint64_t)2);
-        return check(hipGetLastError());
-    }
-    if (!fp8 || !nibbles || !gaps || !workspace || ((uintptr_t)nibbles & 7) || ((uintptr_t)gaps & 3))
+    if (!in.stream || !in.blk_off || ((uintptr_t)in.stream & 3) || ((uintptr_t)in.blk_off & 7)) return ECF8_ERR_ARG;
+    empty = n == 0;
+    if (empty) return ECF8_OK;
+    if (!in.fp8 || !in.nibbles || !in.gaps || !in.workspace || ((uintptr_t)in.nibbles & 7) ||
+        ((uintptr_t)in.gaps & 3))
         return ECF8_ERR_ARG;
     const EncWorkspace W = enc_workspace(n);
-    if (workspace_bytes < W.bytes || ((uintptr_t)workspace & 255)) return ECF8_ERR_WORKSPACE;
-    if (W.tiles > 0xFFFFFFFFull) return ECF8_ERR_SIZE;
+    if (in.workspace_bytes < W.bytes || ((uintptr_t)in.workspace & 255)) return ECF8_ERR_WORKSPACE;
+    const uint64_t n_wg = (n + kWgElems - 1) / kWgElems;
+    if (n_wg >= kMaxGrid) return ECF8_ERR_SIZE;
 
     ecf8_codebook cb = meta->cb;
     uint32_t code[ECF8_NSYM];
     rc = ecf8_canonical_codes(&cb, code);
     if (rc) return rc;
-    EncTable tab;
+    std::memset(&J, 0, sizeof(J));
     for (int s = 0; s < ECF8_NSYM; ++s) {
-        tab.code[s] = code[s];
-        tab.len[s] = cb.len[s];
+        J.code[s] = (uint16_t)code[s];
+        J.len[s] = cb.len[s];
     }
-    CountLens L;
     for (int d = 0; d < kCountWords; ++d)
-        for (int f = 0; f < 2; ++f) L.v[2 * d + f] = cb.len[count_symbol(d, f)];
-    uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
-    const uint32_t* counts = reinterpret_cast<const uint32_t*>(ws);
-    uint64_t* tile_off = reinterpret_cast<uint64_t*>(ws + W.off_off);
-    uint64_t* tile_chunk = reinterpret_cast<uint64_t*>(ws + W.chunk_off);
-    uint64_t* group = reinterpret_cast<uint64_t*>(ws + W.group_off);
-    uint2* pairs = reinterpret_cast<uint2*>(ws + W.pair_off);
-    uint32_t* side = reinterpret_cast<uint32_t*>(ws + W.side_off);
-    EncArgs a;
-    a.fp8 = fp8;
-    a.n = n;
-    a.tiles = W.tiles;
-    a.n_wg = (n + kWgElems - 1) / kWgElems;
-    a.n_blocks = meta->n_blocks;
-    a.chunk_bits = 8u * meta->chunk_bytes;
-    a.tb = meta->threads_per_block;
-    a.gap_count = meta->n_blocks * meta->threads_per_block;
-    a.gap_words = meta->gap_bytes / 4;
-    a.stream_words = meta->stream_bytes / 4;   // C and TB are multiples of 4 and 64: a whole number of words
-    a.stream = reinterpret_cast<uint32_t*>(stream);
-    a.nibbles = nibbles;
-    a.gaps = reinterpret_cast<uint32_t*>(gaps);
-    a.blk_off = blk_off;
-    a.tile_off = tile_off;
-    a.tile_chunk = tile_chunk;
-    a.pairs = pairs;
-    a.side = side;
-    a.m_chunk = ((1ull << 40) + a.chunk_bits - 1) / a.chunk_bits;
-    a.m_tb = ((1ull << 40) + a.tb - 1) / a.tb;
-    a.stream_quads = ((uintptr_t)stream & 15) == 0;
-    a.nibble_quads = ((uintptr_t)nibbles & 15) == 0;
+        for (int f = 0; f < 2; ++f) J.count_len[2 * d + f] = cb.len[count_symbol(d, f)];
+    uint8_t* ws = reinterpret_cast<uint8_t*>(in.workspace);
+    J.fp8 = in.fp8;
+    J.n = n;
+    J.tiles = W.tiles;
+    J.n_wg = n_wg;
+    J.n_blocks = meta->n_blocks;
+    J.gap_words = meta->gap_bytes / 4;
+    J.stream_words = meta->stream_bytes / 4;   // C and TB are multiples of 4 and 64: a whole number of words
+    J.stream = reinterpret_cast<uint32_t*>(in.stream);
+    J.nibbles = in.nibbles;
+    J.gaps = reinterpret_cast<uint32_t*>(in.gaps);
+    J.blk_off = in.blk_off;
+    J.counts = reinterpret_cast<const uint32_t*>(ws);
+    J.group = reinterpret_cast<uint64_t*>(ws + W.group_off);
+    J.tile_off = reinterpret_cast<uint64_t*>(ws + W.off_off);
+    J.tile_chunk = reinterpret_cast<uint64_t*>(ws + W.chunk_off);
+    J.pairs = reinterpret_cast<uint2*>(ws + W.pair_off);
+    J.side = reinterpret_cast<uint32_t*>(ws + W.side_off);
+    J.chunk_bits = 8u * meta->chunk_bytes;
+    J.tb = meta->threads_per_block;
+    J.m_chunk = ((1ull << 40) + J.chunk_bits - 1) / J.chunk_bits;
+    J.m_tb = ((1ull << 40) + J.tb - 1) / J.tb;
+    J.stream_quads = ((uintptr_t)in.stream & 15) == 0;
+    J.nibble_quads = ((uintptr_t)in.nibbles & 15) == 0;
+    return ECF8_OK;
+}
 
-    // every output word is written by the kernels: the gap and stream words a
-    // workgroup owns by the encode kernel, those two workgroups share by the boundary
-    // kernel, the padding after the last chunk by the last workgroup
-    hipLaunchKernelGGL(ecf8_group_sum_kernel, dim3((uint32_t)W.groups), dim3(kScanLanes), 0, st, counts, L, W.tiles,
-                       group, tab, pairs);
-    hipLaunchKernelGGL(ecf8_tile_off_kernel, dim3((uint32_t)W.groups), dim3(kScanLanes), 0, st, counts, L, W.tiles,
-                       group, tile_off, tile_chunk, a.chunk_bits, a.tb);
-    hipLaunchKernelGGL(ecf8_encode_kernel, dim3((uint32_t)a.n_wg), dim3(kEncLanes), 0, st, a);
-    if (a.n_wg > 1)
-        hipLaunchKernelGGL(ecf8_boundary_kernel, dim3((uint32_t)((a.n_wg - 1 + 255) / 256)), dim3(256), 0, st,
-                           tile_off, a.n_wg, side, a.chunk_bits, a.stream, a.stream_words, a.gaps, a.gap_words);
+// The four launches of up to kBatch tensors (every output word is written by
+// them: the gap and stream words a workgroup owns by the encode kernel, those
+// two workgroups share by the boundary kernel, the padding after the last
+// chunk by the last workgroup).
+int launch_batch(EncBatch& B, hipStream_t st)
+{
+    B.grp_start[0] = B.wg_start[0] = B.bnd_start[0] = 0;
+    for (uint32_t j = 0; j < B.count; ++j) {
+        const EncJob& J = B.job[j];
+        B.grp_start[j + 1] = B.grp_start[j] + (uint32_t)((J.tiles + kGroupTiles - 1) / kGroupTiles);
+        B.wg_start[j + 1] = B.wg_start[j] + (uint32_t)J.n_wg;
+        B.bnd_start[j + 1] = B.bnd_start[j] + (uint32_t)((J.n_wg - 1 + 255) / 256);
+    }
+    for (uint32_t j = B.count + 1; j <= (uint32_t)kBatch; ++j)
+        B.grp_start[j] = B.wg_start[j] = B.bnd_start[j] = 0xFFFFFFFFu;
+    const uint32_t c = B.count;
+    hipLaunchKernelGGL(ecf8_group_sum_kernel, dim3(B.grp_start[c]), dim3(kScanLanes), 0, st, B);
+    hipLaunchKernelGGL(ecf8_tile_off_kernel, dim3(B.grp_start[c]), dim3(kScanLanes), 0, st, B);
+    hipLaunchKernelGGL(ecf8_encode_kernel, dim3(B.wg_start[c]), dim3(kEncLanes), 0, st, B);
+    if (B.bnd_start[c]) hipLaunchKernelGGL(ecf8_boundary_kernel, dim3(B.bnd_start[c]), dim3(256), 0, st, B);
     return check(hipGetLastError());
+}
+
+}  // namespace
+
+extern "C" int ecf8_encode_batched_device(const ecf8_encode_job* jobs, int count, void* hip_stream)
+{
+    if (count < 0 || (count > 0 && !jobs)) return ECF8_ERR_ARG;
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    std::vector<EncJob> J(count > 0 ? (size_t)count : 1);
+    std::vector<char> empty(count > 0 ? (size_t)count : 1, 0);
+    for (int i = 0; i < count; ++i) {           // every job checked before anything is launched
+        bool e = false;
+        const int rc = make_job(jobs[i], J[i], e);
+        if (rc) return rc;
+        empty[i] = e;
+    }
+    for (int i = 0; i < count; ++i) {
+        if (!empty[i]) continue;
+        hipLaunchKernelGGL(ecf8_zero_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<uint32_t*>(jobs[i].stream),
+                           jobs[i].meta.stream_bytes / 4);
+        hipLaunchKernelGGL(ecf8_zero_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<uint32_t*>(jobs[i].blk_off),
+                           (uint64_t)2);
+    }
+    EncBatch B;
+    B.count = 0;
+    uint64_t wgs = 0;
+    for (int i = 0; i <= count; ++i) {
+        const bool flush = i == count || B.count == (uint32_t)kBatch || (!empty[i] && wgs + J[i].n_wg >= kMaxGrid);
+        if (flush && B.count) {
+            const int rc = launch_batch(B, st);
+            if (rc) return rc;
+            B.count = 0;
+            wgs = 0;
+        }
+        if (i == count) break;
+        if (empty[i]) continue;
+        B.job[B.count++] = J[i];
+        wgs += J[i].n_wg;
+    }
+    return check(hipGetLastError());
+}
+
+extern "C" int ecf8_encode_device(const uint8_t* fp8, const ecf8_meta* meta, uint8_t* stream, uint8_t* nibbles,
+                                  uint8_t* gaps, uint64_t* blk_off, void* workspace, uint64_t workspace_bytes,
+                                  void* hip_stream)
+{
+    if (!meta) return ECF8_ERR_ARG;
+    ecf8_encode_job job;
+    job.fp8 = fp8;
+    job.meta = *meta;
+    job.stream = stream;
+    job.nibbles = nibbles;
+    job.gaps = gaps;
+    job.blk_off = blk_off;
+    job.workspace = workspace;
+    job.workspace_bytes = workspace_bytes;
+    return ecf8_encode_batched_device(&job, 1, hip_stream);
 }

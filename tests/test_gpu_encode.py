@@ -209,6 +209,71 @@ def test_one_histogram_serves_several_encodes():
         assert np.array_equal(enc.blk_off.cpu().numpy().view(np.uint64), ref["blk_off"])
 
 
+BATCH_CASES = [("stable", 100_003, 16, 256), ("stable", 0, 16, 256), ("stable", 1, 4, 64),
+               ("fib15", 200_000, 12, 192), ("stable", 8193, 64, 1024), ("two", 65536 + 7, 8, 128),
+               ("stable", 4097, 16, 256), ("single", 300_000, 4, 64), ("long12x6", 50_000, 16, 256),
+               ("stable", 16385, 8, 128), ("bytes", 123_457, 16, 256), ("uniform4", 8192 * 3, 12, 192),
+               ("stable", 31, 64, 1024), ("stable", 1_000_003, 16, 256), ("stable", 2, 16, 256),
+               ("fib15", 70_001, 4, 64), ("stable", 8192, 16, 256), ("stable", 0, 8, 128),
+               ("stable", 250_000, 16, 256)]
+
+
+def prepare_job(kind, n, C, TB, seed, d):
+    x_np, L = make_input(kind, n, seed)
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).to(d)
+    ws = B.encode_workspace(max(n, 1), d)
+    freq = B.histogram_device(x, workspace=ws).cpu().numpy().astype(np.uint64)
+    if L is None:
+        L = B.codebook_from_freq(freq) if n else [0] * 16
+    m = B.meta_from_freq(freq, n, L, C, TB)
+    enc, wholes = canary_buffers(m, d)
+    return x_np, L, x, ws, enc, wholes
+
+
+def check_against_oracle(x_np, L, C, TB, enc, wholes):
+    ref = oracle.encode(x_np, lengths=L, chunk_bytes=C, tb=TB)
+    assert int(enc.meta.total_bits) == ref["total_bits"]
+    for whole, key in zip(wholes, ["stream", "nibbles", "gaps", "blk_off"]):
+        got = whole.cpu().numpy()
+        want = np.ascontiguousarray(ref[key]).view(np.uint8)
+        k = want.size
+        assert (got[k:] == CANARY).all(), "%s: write past the end" % key
+        bad = np.nonzero(got[:k] != want)[0]
+        assert bad.size == 0, "%s: first mismatch at byte %d of %d" % (key, bad[0], k)
+
+
+def test_encode_batched_bytes_equal_oracle():
+    """19 tensors of mixed sizes (two empty), symbol sets and (C, TB) in one batched call (eight
+    tensors per set of launches, so three sets): every buffer equals the oracle's encode."""
+    d = dev()
+    jobs = [prepare_job(kind, n, C, TB, 11 * i + 5, d) for i, (kind, n, C, TB) in enumerate(BATCH_CASES)]
+    B.encode_batched_into([j[2] for j in jobs], [j[4] for j in jobs], [j[3] for j in jobs])
+    torch.cuda.synchronize()
+    for (kind, n, C, TB), (x_np, L, x, ws, enc, wholes) in zip(BATCH_CASES, jobs):
+        check_against_oracle(x_np, L, C, TB, enc, wholes)
+
+
+def test_encode_batched_checks_every_job_first():
+    """A misaligned stream in the third job: the call fails and no job's buffers are written."""
+    d = dev()
+    jobs = [prepare_job("stable", 50_000 + i, 16, 256, i, d) for i in range(4)]
+    encs = [j[4] for j in jobs]
+    whole = torch.full((int(encs[2].meta.stream_bytes) + PAD + 2,), CANARY, dtype=torch.uint8, device=d)
+    encs[2].stream = whole[2:2 + int(encs[2].meta.stream_bytes)]
+    with pytest.raises(E.Ecf8Error):
+        B.encode_batched_into([j[2] for j in jobs], encs, [j[3] for j in jobs])
+    torch.cuda.synchronize()
+    for j in jobs:
+        for w in j[5]:
+            assert (w.cpu().numpy() == CANARY).all()
+    assert (whole.cpu().numpy() == CANARY).all()
+
+
+def test_encode_batched_empty_list():
+    dev()
+    assert B.encode_batched_into([], [], []) == []
+
+
 def test_encode_device_rejects_bad_arguments():
     d = dev()
     x = torch.from_numpy(make_input("stable", 10_000, 1)[0]).to(d)
