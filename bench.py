@@ -378,7 +378,7 @@ def variant_bench(args):
     for name, x in synth.workload_tensors_as(args.workload, fmt, device=d):
         names.append(name)
         xs.append(x.reshape(-1).view(torch.int16) if fmt == "bf16" else x.reshape(-1))
-        hs.append(B.v_encode(fmt, x.cpu()))
+        hs.append(B.v_encode(fmt, x.cpu(), max_len=args.variant_max_code_len))
         log("encoded %-12s n=%d  %.3f code bits/element, max_len %d" % (name, hs[-1].n,
                                                                         hs[-1].meta.total_bits / hs[-1].n,
                                                                         hs[-1].meta.max_len))
@@ -418,7 +418,9 @@ def variant_bench(args):
            "config": {"workload": WORKLOAD_TEXT[args.workload] + ", cast to " + fmt, "format": fmt,
                       "tensors": len(hs), "elements": n, "compressed_bytes": read,
                       "compressed_ratio": round(read / written, 4), "chunk_bytes": 16, "lanes_per_block": 256,
-                      "grid": int(plan.plan.grid)},
+                      "grid": int(plan.plan.grid), "code_length_limit": args.variant_max_code_len,
+                      "max_code_len": max(int(h.meta.max_len) for h in hs),
+                      "short_code_form": bool(plan.plan.short_codes)},
            "roofline": {"bound": "hbm", "achieved": round((read + written) / (st["mean"] * 1e-3) / 1e9, 2),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round((read + written) / (st["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -443,6 +445,9 @@ def main():
     ap.add_argument("--max-code-len", type=int, default=11,
                     help="decode mode: code length limit of the encoding (11: every codeword fits the decode's "
                          "11-bit table index; 16: plain Huffman)")
+    ap.add_argument("--variant-max-code-len", type=int, default=10,
+                    help="variant mode: code length limit of the encoding (10: every codeword fits the variant "
+                         "decode's 10-bit table index; 16: the library default)")
     ap.add_argument("--lanes", type=int, default=256, help="decode mode: lanes per block (TB)")
     ap.add_argument("--mode", default="decode", choices=["decode", "pipeline", "alpha", "encode", "variant", "copycal"],
                     help="decode: the batched decode step (default); pipeline: decode-on-use of the "

@@ -125,7 +125,8 @@ typedef struct {
     uint32_t threads_per_block;
     uint32_t grid;            /* persistent workgroups; may be lowered (>= 1) */
     uint32_t table_entries;   /* LDS decode-table entries: the plan's largest table */
-    uint32_t reserved;
+    uint32_t short_codes;     /* 1: no code of the batch is longer than 10 bits, and the decode
+                                 indexes its tables with one shift (chosen by ecf8v_decode_prepare) */
 } ecf8v_plan;
 
 /* Device workspace bytes for a batched decode of `count` tensors (256-byte

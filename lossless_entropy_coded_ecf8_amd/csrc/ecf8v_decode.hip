@@ -21,7 +21,9 @@
 // last) with cdelta = 63 * p_long: one branch-free expression picks the
 // region, and the clamp sends any window past the codes to an entry that
 // decodes nothing.  As w >> 22 < 1024 <= last, the two bounds are one
-// median-of-three.  Codewords longer than 10 bits cover at most 1/8 of the
+// median-of-three.  When no code of a batch is longer than 10 bits there is no
+// region 2 and the index is w >> 22 alone (the kernel's short form, chosen
+// when the plan is prepared).  Codewords longer than 10 bits cover at most 1/8 of the
 // space when there are at most 256 symbols, so a table has at most 9089
 // entries.
 // An entry holds the bits consumed (1 for no codeword), the whole codewords
@@ -42,8 +44,9 @@
 //     reads and a funnel shift;
 //   * counting walk: lookups in wave-uniform steps of four, each entry
 //     recorded in statically indexed registers (lanes past their chunk end
-//     record 0); a lane's last lookup may decode codewords starting past its
-//     chunk, which are taken off its count;
+//     record 0; an E5M2 wave whose chunks are all whole takes its first two
+//     steps without that test); a lane's last lookup may decode codewords
+//     starting past its chunk, which are taken off its count;
 //   * block scan of the counts (checked against the block offsets);
 //   * replay: each recorded entry's symbol bytes are OR-ed into the cleared
 //     LDS stage at the scanned position (two dword ORs).  Codewords a lane
@@ -107,6 +110,8 @@ struct Entry {
     static constexpr uint32_t kSym = kFmt == ECF8V_BF16 ? 255u : 31u;     //   & kSym
 };
 static_assert(kRecords % kStep == 0 && kStep % 2 == 0, "records are taken kStep at a time, looked up in pairs");
+constexpr int kSureSteps = (kChunkBits / 16) / kStep;   // steps whose lookups all start inside a whole chunk
+static_assert(kSureSteps * kStep <= kRecords && 15 + 16 * (kSureSteps * kStep - 1) < kChunkBits, "sure steps");
 
 // Per-tensor descriptor in the workspace.
 struct DescV {
@@ -532,15 +537,26 @@ __device__ __forceinline__ uint32_t reg_window(const uint32_t (&w)[5], uint32_t 
 }
 
 // min(max(a, b), last) for a = win >> 22 <= 1023 < last: the median of the
-// three (one instruction).
+// three (one instruction).  kShort: every code of the batch is at most 10
+// bits long (no region 2), so a is the index itself: one shift.  (With an
+// incomplete code the prefixes past the codes are entries that decode
+// nothing in either form.)
+template <bool kShort>
 __device__ __forceinline__ uint32_t tab_index(uint32_t win, int cd, int last)
 {
-    const int a = (int)(win >> (32 - kWin));
+    int a = (int)(win >> (32 - kWin));
+    if (kShort) {
+        // kept opaque, so that the entry's address is one shift-and-add of it
+        // (not a shift, a mask and an add of the window)
+        asm volatile("" : "+v"(a));
+        return (uint32_t)a;
+    }
     const int b = (int)(win >> 16) - cd;
     int m;
     asm("v_med3_i32 %0, %1, %2, %3" : "=v"(m) : "v"(b), "v"(a), "s"(last));
     return (uint32_t)m;
 }
+
 
 // Waves per SIMD the register allocation must allow (measured best with 256
 // lanes: BF16 keeps its 16 raw-plane registers per lane unspilled at 5 (at 6
@@ -560,7 +576,7 @@ struct StageLds {
     uint8_t stage[kStageBytes];
     uint32_t wsum[kWaves];
 };
-template <int kFmt, int kTB>
+template <int kFmt, int kTB, bool kShort>
 __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<kFmt, kTB>))) void ecf8v_decode_kernel(
     const DescV* __restrict__ descs, int count, const uint32_t* __restrict__ tables, uint64_t total_blocks,
     unsigned long long* __restrict__ status, uint32_t tab_n)
@@ -670,13 +686,44 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
         uint32_t r = r0, cnt = 0, inv = 0, lastex = 0;
         bool act = r > rend;
         int nq = 0;                           // four-lookup steps taken (wave-uniform)
+        // An E5M2 wave whose 64 chunks all lie below T takes its first
+        // kSureSteps steps without activity tests: a lookup consumes at most
+        // 16 bits and the walk starts at most 15 bits in, so each of the first
+        // 8 lookups starts inside the 128-bit chunk.  (BF16 keeps one path:
+        // at 5 waves per SIMD the second one would spill records.)
+        constexpr int kSure = kFmt == ECF8V_E5M2 ? kSureSteps : 0;
+        const bool wave_full =
+            c_T >= (b * kTB + (uint64_t)((__builtin_amdgcn_readfirstlane(tid) & ~63) + 64)) * (uint64_t)kChunkBits;
 #pragma unroll
         for (int q = 0; q < kRecords / kStep; ++q) {
-            if (__builtin_amdgcn_ballot_w64(act) == 0) break;
-            nq = q + 1;
             // lookups in pairs: the second takes the first's window shifted by
             // the bits the first consumed (at most 16, so the 16 bits an index
             // reads are still stream bits); its rows are not read again
+            if (q < kSure && wave_full) {
+                nq = q + 1;
+                uint32_t win = 0;
+#pragma unroll
+                for (int j = 0; j < kStep; ++j) {
+                    if (j % 2 == 0) {
+                        const uint32_t a = col_lo | ((r & 0xE0u) << kPitchShift);   // col_lo < kPitch
+                        const uint32_t wlo = *reinterpret_cast<const uint32_t*>(stage + a);
+                        const uint32_t whi = *reinterpret_cast<const uint32_t*>(stage + a + kPitch);
+                        win = __builtin_amdgcn_alignbit(whi, wlo, r);
+                    } else {
+                        win <<= rec[kStep * q + j - 1] & En::kNb & 31u;
+                    }
+                    const uint32_t e = s_tab[tab_index<kShort>(win, cd, last)];
+                    rec[kStep * q + j] = e;
+                    r -= e & En::kNb;
+                    cnt += (e >> En::kCnt) & 3u;
+                    if (j % 2) inv |= rec[kStep * q + j - 1] | e;
+                }
+                lastex = rec[kStep * q + kStep - 1];
+                act = r > rend;
+                continue;
+            }
+            if (__builtin_amdgcn_ballot_w64(act) == 0) break;
+            nq = q + 1;
             uint32_t win = 0;
 #pragma unroll
             for (int j = 0; j < kStep; ++j) {
@@ -688,13 +735,13 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
                 } else {
                     win <<= rec[kStep * q + j - 1] & En::kNb & 31u;
                 }
-                const uint32_t e = s_tab[tab_index(win, cd, last)];
+                const uint32_t e = s_tab[tab_index<kShort>(win, cd, last)];
                 const uint32_t em = act ? e : 0u;
                 rec[kStep * q + j] = em;
                 lastex = act ? e : lastex;
                 r -= em & En::kNb;
                 cnt += (em >> En::kCnt) & 3u;
-                inv |= em;
+                if (j % 2) inv |= rec[kStep * q + j - 1] | em;
                 act = r > rend;
             }
         }
@@ -703,7 +750,7 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
             const uint32_t a = col_lo | ((r & 0xE0u) << kPitchShift);
             const uint32_t wlo = *reinterpret_cast<const uint32_t*>(stage + a);
             const uint32_t whi = *reinterpret_cast<const uint32_t*>(stage + a + kPitch);
-            const uint32_t e = s_tab[tab_index(__builtin_amdgcn_alignbit(whi, wlo, r), cd, last)];
+            const uint32_t e = s_tab[tab_index<kShort>(__builtin_amdgcn_alignbit(whi, wlo, r), cd, last)];
             lastex = e;
             r -= e & En::kNb;
             cnt += (e >> En::kCnt) & 3u;
@@ -788,7 +835,7 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
                                        bswap(bld(rs, tid * kChunk + kChunk))};
                 uint32_t r2 = r_rec;
                 while (r2 > rend) {
-                    const uint32_t e = s_tab[tab_index(reg_window(w, 160u - r2), cd, last)];
+                    const uint32_t e = s_tab[tab_index<kShort>(reg_window(w, 160u - r2), cd, last)];
                     emit_entry(stage32, ob, e);
                     ob += (e >> En::kCnt) & 3u;
                     r2 -= e & En::kNb;
@@ -819,7 +866,7 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
                 if (pos < base + lim && pos + cnt > base) {
                     uint32_t p = gap, k = pos;
                     while (p < E && k < base + lim) {
-                        const uint32_t e = s_tab[tab_index(reg_window(w, p), cd, last)];
+                        const uint32_t e = s_tab[tab_index<kShort>(reg_window(w, p), cd, last)];
                         const uint32_t ns = (e >> En::kCnt) & 3u;
                         for (uint32_t i = 0; i < ns; ++i, ++k)
                             if (k >= base && k < base + lim && k < pos + cnt)
@@ -842,40 +889,42 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
 int check(hipError_t e) { return e == hipSuccess ? ECF8_OK : ECF8_ERR_HIP; }
 
 template <int kFmt, int kTB>
-const void* decode_kernel_ptr()
+const void* decode_kernel_ptr(bool short_codes)
 {
-    return reinterpret_cast<const void*>(ecf8v_decode_kernel<kFmt, kTB>);
+    return short_codes ? reinterpret_cast<const void*>(ecf8v_decode_kernel<kFmt, kTB, true>)
+                       : reinterpret_cast<const void*>(ecf8v_decode_kernel<kFmt, kTB, false>);
 }
 
-const void* pick_kernel(uint32_t fmt, uint32_t tb)
+const void* pick_kernel(uint32_t fmt, uint32_t tb, bool short_codes)
 {
     if (fmt == ECF8V_BF16) {
-        if (tb == 64) return decode_kernel_ptr<ECF8V_BF16, 64>();
-        if (tb == 128) return decode_kernel_ptr<ECF8V_BF16, 128>();
-        if (tb == 256) return decode_kernel_ptr<ECF8V_BF16, 256>();
+        if (tb == 64) return decode_kernel_ptr<ECF8V_BF16, 64>(short_codes);
+        if (tb == 128) return decode_kernel_ptr<ECF8V_BF16, 128>(short_codes);
+        if (tb == 256) return decode_kernel_ptr<ECF8V_BF16, 256>(short_codes);
     } else if (fmt == ECF8V_E5M2) {
-        if (tb == 64) return decode_kernel_ptr<ECF8V_E5M2, 64>();
-        if (tb == 128) return decode_kernel_ptr<ECF8V_E5M2, 128>();
-        if (tb == 256) return decode_kernel_ptr<ECF8V_E5M2, 256>();
+        if (tb == 64) return decode_kernel_ptr<ECF8V_E5M2, 64>(short_codes);
+        if (tb == 128) return decode_kernel_ptr<ECF8V_E5M2, 128>(short_codes);
+        if (tb == 256) return decode_kernel_ptr<ECF8V_E5M2, 256>(short_codes);
     }
     return nullptr;
 }
 
 std::mutex g_mu;
-std::map<std::tuple<int, uint32_t, uint32_t, uint32_t>, uint32_t> g_slots;   // (device, fmt, tb, lds): workgroups
+std::map<std::tuple<int, uint32_t, uint32_t, uint32_t, bool>, uint32_t> g_slots;   // (device, fmt, tb, lds, form)
 
 // Resident decode workgroups of the current device for a kernel and its dynamic LDS.
-int kernel_slots(uint32_t fmt, uint32_t tb, uint32_t lds, uint32_t* out)
+int kernel_slots(uint32_t fmt, uint32_t tb, uint32_t lds, bool short_codes, uint32_t* out)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return ECF8_ERR_HIP;
     std::lock_guard<std::mutex> lk(g_mu);
-    const auto key = std::make_tuple(dev, fmt, tb, lds);
+    const auto key = std::make_tuple(dev, fmt, tb, lds, short_codes);
     auto it = g_slots.find(key);
     if (it == g_slots.end()) {
         int cus = 0, occ = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return ECF8_ERR_HIP;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, pick_kernel(fmt, tb), (int)tb, lds) != hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, pick_kernel(fmt, tb, short_codes), (int)tb, lds) !=
+            hipSuccess)
             return ECF8_ERR_HIP;
         it = g_slots.emplace(key, (uint32_t)((cus > 0 ? cus : 1) * (occ > 0 ? occ : 1))).first;
     }
@@ -906,12 +955,13 @@ extern "C" int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, u
     uint64_t blocks = 0;
     uint32_t tab_n = kTabMin;
     uint32_t fmt = count ? descs[0].meta.format : ECF8V_BF16, tb = count ? descs[0].meta.threads_per_block : 256;
+    bool short_codes = true;              // no codeword longer than 10 bits in any tensor: the one-shift index
     for (int i = 0; i < count; ++i) {
         const ecf8v_tensor_desc& t = descs[i];
         int rc = ecf8v_validate_meta(&t.meta);
         if (rc) return rc;
         if (t.meta.format != fmt || t.meta.threads_per_block != tb) return ECF8_ERR_ARG;
-        if (t.meta.chunk_bytes != (uint32_t)kChunk || !pick_kernel(fmt, tb)) return ECF8_ERR_UNSUPPORTED;
+        if (t.meta.chunk_bytes != (uint32_t)kChunk || !pick_kernel(fmt, tb, false)) return ECF8_ERR_UNSUPPORTED;
         if (t.meta.n && (!t.stream || !t.raw || !t.gaps || !t.blk_off)) return ECF8_ERR_ARG;
         if (!aligned(t.stream, 16) || !aligned(t.blk_off, 8) || (t.out_offset & 15) ||
             !aligned(t.raw, fmt == ECF8V_BF16 ? 16 : 8))
@@ -936,6 +986,7 @@ extern "C" int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, u
         d.entries = g.entries;
         std::memcpy(d.len, t.meta.len, sizeof(d.len));
         if (t.meta.n && g.entries > tab_n) tab_n = g.entries;
+        if (t.meta.n && g.long_units) short_codes = false;
     }
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     if (count && hipMemcpy(ws + desc_offset(), dv.data(), sizeof(DescV) * count, hipMemcpyHostToDevice) != hipSuccess)
@@ -956,9 +1007,10 @@ extern "C" int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, u
     plan->format = fmt;
     plan->threads_per_block = tb;
     plan->table_entries = tab_n;
+    plan->short_codes = short_codes ? 1u : 0u;
     uint32_t slots = 1;
     if (blocks) {
-        int rc = kernel_slots(fmt, tb, decode_lds_bytes(tab_n), &slots);
+        int rc = kernel_slots(fmt, tb, decode_lds_bytes(tab_n), short_codes, &slots);
         if (rc) return rc;
     }
     plan->grid = (uint32_t)(blocks < slots ? (blocks ? blocks : 1) : slots);
@@ -976,7 +1028,7 @@ extern "C" int ecf8v_decode_run(const ecf8v_plan* plan, void* hip_stream)
     hipLaunchKernelGGL(ecf8v_clear_kernel, dim3(1), dim3(64), 0, st, status, 1u);
     if (plan->count == 0 || plan->total_blocks == 0) return check(hipGetLastError());
     const uint32_t tb = plan->threads_per_block;
-    const void* k = pick_kernel(plan->format, tb);
+    const void* k = pick_kernel(plan->format, tb, plan->short_codes != 0);
     if (!k) return ECF8_ERR_UNSUPPORTED;
     int count = (int)plan->count;
     uint64_t total = plan->total_blocks;

@@ -95,6 +95,41 @@ def test_length_limits_and_long_codes(max_len):
     assert np.array_equal(as_elems("bf16", got), x)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "e5m2"])
+@pytest.mark.parametrize("kind,max_len", [("heavy", 16), ("heavy", 10), ("normal", 9), ("single", 16),
+                                          ("all_exponents", 10)])
+def test_short_code_form_selected_and_bit_exact(fmt, kind, max_len):
+    """Plans whose codes are all at most 10 bits long take the one-shift table index (short_codes = 1),
+    others the general one; both decode bit-exactly (the single-symbol code is incomplete: its unused
+    prefixes decode nothing in either form)."""
+    d = dev()
+    x = make(fmt, 300_001, 13 + max_len, kind)
+    h = B.v_encode(fmt, x, max_len=max_len)
+    want_short = int(max(int(v) for v in h.lengths) <= 10)
+    if kind == "heavy" and max_len == 16:
+        assert not want_short, "the heavy-tailed case should need codes longer than 10 bits"
+    (got,), plan = decode_checked([h], d)
+    assert int(plan.plan.short_codes) == want_short
+    ref = oracle.v_decode(fmt, h.stream, h.raw, h.n, h.lengths)
+    assert np.array_equal(ref, x)
+    bad = np.nonzero(as_elems(fmt, got) != ref)[0]
+    assert bad.size == 0, "first mismatch at %d of %d" % (bad[0], h.n)
+
+
+def test_short_form_needs_every_tensor_short():
+    """One tensor with a code longer than 10 bits keeps the whole batch on the general form."""
+    d = dev()
+    hs = [B.v_encode("e5m2", make("e5m2", 200_000, 3, "normal"), max_len=10),
+          B.v_encode("e5m2", make("e5m2", 200_000, 4, "heavy"))]
+    assert max(int(v) for v in hs[1].lengths) > 10
+    outs, plan = decode_checked(hs, d)
+    assert int(plan.plan.short_codes) == 0
+    for h, got in zip(hs, outs):
+        assert np.array_equal(got, oracle.v_decode("e5m2", h.stream, h.raw, h.n, h.lengths))
+    outs, plan = decode_checked(hs[:1], d)
+    assert int(plan.plan.short_codes) == 1
+
+
 def test_batched_mixed_formats_rejected_and_mixed_codebooks_ok():
     d = dev()
     hs = [B.v_encode("bf16", make("bf16", n, n, k)) for n, k in [(100_000, "normal"), (3, "normal"),
