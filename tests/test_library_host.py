@@ -276,6 +276,35 @@ def test_encode_device_argument_checks_need_no_gpu():
     assert L.ecf8_histogram_device(P(0x100000), 5, P(0x100000), P(0x600000), 255, None) == -7
 
 
+def test_encode_batched_checks_every_job_before_any_launch():
+    """ecf8_encode_batched_device rejects a batch on the host when any job is bad (fake device pointers,
+    so a launch would fail with a HIP error instead of the argument error)."""
+    x = synth.small_stable(10_000, 1.8, 3)
+    m = E.encode(x).meta
+    L = E.lib()
+    ws_need = E.encode_workspace_bytes(m.n)
+
+    def job(k, **kw):
+        base = 0x1000000 * (k + 1)
+        a = dict(fp8=base, stream=base + 0x100000, nib=base + 0x200000, gaps=base + 0x300000,
+                 blk=base + 0x400000, ws=base + 0x500000, ws_bytes=ws_need, meta=m)
+        a.update(kw)
+        return B.EncodeJob(a["fp8"], a["meta"], a["stream"], a["nib"], a["gaps"], a["blk"], a["ws"], a["ws_bytes"])
+
+    def call(jobs, count=None):
+        arr = (B.EncodeJob * max(len(jobs), 1))(*jobs)
+        return L.ecf8_encode_batched_device(arr, len(jobs) if count is None else count, None)
+    assert L.ecf8_encode_batched_device(None, 2, None) == -1
+    assert call([job(0)], count=-1) == -1
+    assert call([job(0), job(1, stream=0x2100002)]) == -1
+    assert call([job(0), job(1), job(2, nib=0x3200004)]) == -1
+    assert call([job(0), job(1, ws_bytes=ws_need - 1)]) == -7
+    bad = B.Meta.from_buffer_copy(m)
+    bad.total_bits += 1 << 20
+    assert call([job(0), job(1, meta=bad)]) == -3
+    assert call([job(k) for k in range(9)] + [job(9, fp8=0)]) == -1
+
+
 # ---------------------------------------------------------------- alpha statistics
 
 def test_alpha_hat_matches_oracle():
