@@ -105,6 +105,34 @@ def copy_ceiling(torch, d, gib: float = 1.0, reps: int = 10):
     return 2.0 * n / (st["median"] * 1e-3) / 1e9
 
 
+def stream_ceiling(torch, d, read_bytes: int, write_bytes: int, reps: int = 10):
+    """The library's plain stream of the same byte mix (ecf8_hbm_stream): read_bytes read once and write_bytes
+    written, rounded down to 16-byte units; median per-dispatch time in ms after a 1 GiB read."""
+    from lossless_entropy_coded_ecf8_amd import binding as B
+    rb, wb = read_bytes // 16 * 16, write_bytes // 16 * 16
+    if rb == 0 or rb > wb:
+        return None
+    src = torch.randint(0, 256, (rb,), dtype=torch.uint8, device=d)
+    dst = torch.empty(wb, dtype=torch.uint8, device=d)
+    for _ in range(3):
+        B.hbm_stream(src, rb, dst, wb)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for s, e in ev:
+        s.record()
+        B.hbm_stream(src, rb, dst, wb)
+        e.record()
+    torch.cuda.synchronize()
+    u = (rb // 16 << 32) // (wb // 16)
+    i = torch.tensor([0, wb // 16 // 2, wb // 16 - 1], dtype=torch.int64)
+    j = (i * u) >> 32                                  # spot check of the mapping
+    ok = all(torch.equal(dst[16 * int(a):16 * int(a) + 16], src[16 * int(b):16 * int(b) + 16]) for a, b in zip(i, j))
+    del src, dst
+    if not ok:
+        raise RuntimeError("stream kernel mismatch")
+    return dispatch_stats([s.elapsed_time(e) for s, e in ev])["median"]
+
+
 def cpu_baseline(encs_host, seconds: float):
     """Time the C oracle decoding whole blocks of the largest tensor: all host cores (thread pool), then
     one core, each on a bounded sample sized to about `seconds` / 2 of wall time."""
@@ -565,6 +593,8 @@ def main():
     del scratch
 
     copy_gbs = copy_ceiling(torch, d)
+    bbs = batch_bytes(encs)
+    stream_ms = stream_ceiling(torch, d, bbs["read"], bbs["written"])
     bb = batch_bytes(encs)
     n_total = bb["written"]
     value = n_total / (step_ms * 1e-3) / 1e9
@@ -599,6 +629,11 @@ def main():
                      "frac_median": round(gbs(st["median"]) / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes": bb["total"], "kernel_sha": khash,
                      "copy_ceiling_gbs": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4),
+                     "stream_mix_ms": None if stream_ms is None else round(stream_ms, 5),
+                     "frac_of_stream_mix": None if stream_ms is None else round(stream_ms / st["mean"], 4),
+                     "stream_mix_note": "ecf8_hbm_stream: the same bytes read and written by a plain stream "
+                                        "(no decode work); frac_of_stream_mix = its median time / the mean "
+                                        "decode time",
                      "cache": ("every byte the decode reads and writes fits the 256 MB Infinity Cache: cache-resident "
                                "timings" if wl in CACHE_RESIDENT else
                                "kernel_ms*: back-to-back steps (part of one step's data stays in the 256 MB Infinity "

@@ -402,6 +402,19 @@ double ecf8_exponent_entropy_bound(double alpha);
  * Errors: ECF8_ERR_ARG (NULL or misaligned with bytes > 0), ECF8_ERR_HIP. */
 int ecf8_hbm_copy(const void* src, void* dst, uint64_t bytes, void* hip_stream);
 
+/* A plain stream with a decode's byte mix: write_bytes to dst while reading
+ * read_bytes (<= write_bytes) from src, each byte once: output 16-byte unit i
+ * takes input unit (i * m) >> 32, m = floor(2^32 * read_units / write_units),
+ * so neighbouring lanes share input units and their cache lines.  Same grid,
+ * loads, stores and hints as ecf8_hbm_copy.  Not part of the method: the rate
+ * a decode moving the same bytes could reach with no work of its own (a
+ * tighter ceiling than the copy, whose reads and writes are equal).  Both
+ * sizes multiples of 16, both pointers 16-byte aligned, write_bytes / 16 <
+ * 2^32.  Asynchronous on hip_stream.
+ * Errors: ECF8_ERR_ARG (NULL, misaligned, sizes not multiples of 16, read
+ * 0 or more than written), ECF8_ERR_SIZE, ECF8_ERR_HIP. */
+int ecf8_hbm_stream(const void* src, uint64_t read_bytes, void* dst, uint64_t write_bytes, void* hip_stream);
+
 /* Human-readable name of an error code (static string). */
 const char* ecf8_strerror(int code);
 

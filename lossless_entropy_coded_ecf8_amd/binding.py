@@ -103,7 +103,7 @@ EXPORTS = ["ecf8_histogram", "ecf8_codebook_from_freq", "ecf8_build_codebook", "
            "ecf8_decode_prepare", "ecf8_decode_run", "ecf8_build_tables", "ecf8_decode_blocks",
            "ecf8_decode_blocks_timed", "ecf8_decode_batched", "ecf8_decode", "ecf8_decode_batched_noalloc",
            "ecf8_decode_status", "ecf8_histogram_device", "ecf8_meta_from_freq", "ecf8_encode_workspace_bytes",
-           "ecf8_encode_device", "ecf8_encode_batched_device", "ecf8_alpha_hat", "ecf8_exponent_entropy_bound", "ecf8_hbm_copy",
+           "ecf8_encode_device", "ecf8_encode_batched_device", "ecf8_alpha_hat", "ecf8_exponent_entropy_bound", "ecf8_hbm_copy", "ecf8_hbm_stream",
            "ecf8_strerror", "ecf8_version"]
 
 _lib = None
@@ -152,6 +152,7 @@ def lib() -> ctypes.CDLL:
         "ecf8_alpha_hat": (i, [vp, ctypes.c_uint64, ctypes.c_double, ctypes.POINTER(ctypes.c_double)]),
         "ecf8_exponent_entropy_bound": (ctypes.c_double, [ctypes.c_double]),
         "ecf8_hbm_copy": (i, [vp, vp, ctypes.c_uint64, vp]),
+        "ecf8_hbm_stream": (i, [vp, ctypes.c_uint64, vp, ctypes.c_uint64, vp]),
         "ecf8_strerror": (ctypes.c_char_p, [i]),
         "ecf8_version": (i, []),
     }
@@ -609,6 +610,16 @@ class DecodePlan:
 
     def view(self, i: int):
         return self.out[self.offsets[i]: self.offsets[i] + self.encs[i].n]
+
+
+def hbm_stream(src, read_bytes: int, dst, write_bytes: int, stream=None):
+    """A plain stream with a decode's byte mix (ecf8_hbm_stream): write_bytes to dst, reading read_bytes of src
+    once; output 16-byte unit i takes input unit (i * m) >> 32, m = floor(2^32 * read_units / write_units)."""
+    if src.numel() * src.element_size() < read_bytes or dst.numel() * dst.element_size() < write_bytes:
+        raise ValueError("buffers smaller than the sizes")
+    _check(lib().ecf8_hbm_stream(ctypes.c_void_p(src.data_ptr()), int(read_bytes), ctypes.c_void_p(dst.data_ptr()),
+                                 int(write_bytes), _stream_handle(stream)), "ecf8_hbm_stream")
+    return dst
 
 
 def hbm_copy(src, dst, stream=None):

@@ -305,6 +305,21 @@ def test_encode_batched_checks_every_job_before_any_launch():
     assert call([job(k) for k in range(9)] + [job(9, fp8=0)]) == -1
 
 
+def test_measurement_kernels_reject_bad_arguments_without_a_gpu():
+    L = E.lib()
+    P = lambda v: ctypes.c_void_p(v)
+    assert L.ecf8_hbm_copy(P(0), P(0x200000), 16, None) == -1
+    assert L.ecf8_hbm_copy(P(0x100008), P(0x200000), 16, None) == -1
+    assert L.ecf8_hbm_copy(P(0), P(0), 0, None) == 0
+    assert L.ecf8_hbm_stream(P(0x100000), 32, P(0x200000), 16, None) == -1       # reads more than it writes
+    assert L.ecf8_hbm_stream(P(0x100000), 0, P(0x200000), 16, None) == -1
+    assert L.ecf8_hbm_stream(P(0x100000), 24, P(0x200000), 32, None) == -1       # not whole 16-byte units
+    assert L.ecf8_hbm_stream(P(0x100004), 16, P(0x200000), 32, None) == -1       # misaligned
+    assert L.ecf8_hbm_stream(P(0), 16, P(0x200000), 32, None) == -1
+    assert L.ecf8_hbm_stream(P(0x100000), 16, P(0x200000), 16 << 32, None) == -2
+    assert L.ecf8_hbm_stream(P(0), 0, P(0), 0, None) == 0
+
+
 # ---------------------------------------------------------------- alpha statistics
 
 def test_alpha_hat_matches_oracle():
