@@ -767,9 +767,6 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(kWavesTarget
     load_block<C, TB>(nt, blk, tid, nx);
     int ptens = nt.t;                  // tensor of the prefetched block
     const uint32_t cap = 8u * C * TB;  // staging capacity in elements
-    // wait for the first block's loads here, so that at the loop head only the
-    // back edge has loads in flight and the compiler can count them exactly
-    asm volatile("" ::"v"(nx.sv[0]), "v"(nx.la), "v"(nx.gb), "v"((uint32_t)nx.off));
 
     // fields of the tensor being decoded
     int cur = -1;
@@ -779,35 +776,43 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(kWavesTarget
     uint8_t* c_out = nullptr;
     int c_cd = 0;
     uint32_t c_ok = 0;
+    // Takes tensor t's fields and copies its decode table into LDS: 16-byte
+    // loads, at most 3 per lane (each load waits for every memory operation in
+    // flight, the previous block's stores too, so fewer, wider loads cost fewer
+    // round trips: 3% faster than dword loads).
+    auto take_tensor = [&](int t) {
+        const DevDesc* d = descs + t;
+        c_begin = d->block_begin;
+        c_n = d->n;
+        c_T = d->total_bits;
+        c_lenpack = d->lenpack;
+        c_nib = d->nibbles;
+        c_stream = d->stream;
+        c_out = d->out;
+        c_cd = d->cdelta;
+        uint32_t ne = d->entries;
+        c_ok = ne != 0 && (!kShort || c_cd == kShortCd);   // 0: tables never built for this plan, or a
+                                                           // code the short form cannot index
+        ne = ne < (uint32_t)kTableMax ? ne : (uint32_t)kTableMax;
+        const uint32_t* tx = tables + (uint64_t)t * kTabStride;
+        const uint32_t n4 = (ne + 3) / 4;
+        const Rsrc rt = make_rsrc(tx, 16ull * n4);
+        for (uint32_t i = tid; i < n4; i += TB)
+            reinterpret_cast<u32x4*>(s_tx)[i] = __builtin_amdgcn_raw_buffer_load_b128(rt, 16u * i, 0, 0);
+        cur = t;
+    };
+    // the first tensor's table is requested together with the first block's
+    // inputs, so the two latencies overlap
+    take_tensor(ptens);
+    // wait for the first block's loads here, so that at the loop head only the
+    // back edge has loads in flight and the compiler can count them exactly
+    asm volatile("" ::"v"(nx.sv[0]), "v"(nx.la), "v"(nx.gb), "v"((uint32_t)nx.off));
 
     for (; blk < total_blocks; blk += gridDim.x) {
         const BlockIn<C> in = nx;
-        if (ptens != cur) {
-            const DevDesc* d = descs + ptens;
-            c_begin = d->block_begin;
-            c_n = d->n;
-            c_T = d->total_bits;
-            c_lenpack = d->lenpack;
-            c_nib = d->nibbles;
-            c_stream = d->stream;
-            c_out = d->out;
-            c_cd = d->cdelta;
-            uint32_t ne = d->entries;
-            c_ok = ne != 0 && (!kShort || c_cd == kShortCd);   // 0: tables never built for this plan, or a
-                                                               // code the short form cannot index
-            ne = ne < (uint32_t)kTableMax ? ne : (uint32_t)kTableMax;
-            const uint32_t* tx = tables + (uint64_t)ptens * kTabStride;
-            // (every lane left the previous decode pass at its closing barrier,
-            // so the old table is no longer read).  16-byte loads, at most 3 per
-            // lane: each load waits for every memory operation in flight (the
-            // previous block's stores too), so fewer, wider loads cost fewer
-            // round trips (3% faster than dword loads).
-            const uint32_t n4 = (ne + 3) / 4;
-            const Rsrc rt = make_rsrc(tx, 16ull * n4);
-            for (uint32_t i = tid; i < n4; i += TB)
-                reinterpret_cast<u32x4*>(s_tx)[i] = __builtin_amdgcn_raw_buffer_load_b128(rt, 16u * i, 0, 0);
-            cur = ptens;
-        }
+        // (every lane left the previous decode pass at its closing barrier, so
+        // the old table is no longer read)
+        if (ptens != cur) take_tensor(ptens);
         // the table is in place and every lane has finished the previous block's
         // write-back, whose staging memory the stream rows reuse
         __syncthreads();
