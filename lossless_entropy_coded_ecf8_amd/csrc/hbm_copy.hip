@@ -71,7 +71,7 @@ __global__ void hbm_copy_tail_kernel(const uint8_t* __restrict__ src, uint8_t* _
 // copy.
 __global__ __launch_bounds__(kCopyLanes) void hbm_stream_kernel(const uint8_t* __restrict__ src,
                                                                 uint8_t* __restrict__ dst, uint64_t out_units,
-                                                                uint64_t in_units, uint64_t m)
+                                                                uint64_t m)
 {
     constexpr uint64_t kStep = (uint64_t)kCopyLanes * kCopyUnroll;
     const uint64_t steps = (out_units + kStep - 1) / kStep;
@@ -93,7 +93,6 @@ __global__ __launch_bounds__(kCopyLanes) void hbm_stream_kernel(const uint8_t* _
         for (int k = 0; k < kCopyUnroll; ++k)
             __builtin_amdgcn_raw_buffer_store_b128(v[k], rd, 16u * (threadIdx.x + k * kCopyLanes), 0, kNonTemporal);
     }
-    (void)in_units;
 }
 
 uint32_t copy_grid(uint64_t units, int cus)
@@ -122,7 +121,7 @@ extern "C" int ecf8_hbm_stream(const void* src, uint64_t read_bytes, void* dst, 
     const uint64_t m = (uint64_t)(((unsigned __int128)in_units << 32) / out_units);   // <= 2^32
     hipLaunchKernelGGL(hbm_stream_kernel, dim3(copy_grid(out_units, cus)), dim3(kCopyLanes), 0,
                        reinterpret_cast<hipStream_t>(hip_stream), static_cast<const uint8_t*>(src),
-                       static_cast<uint8_t*>(dst), out_units, in_units, m);
+                       static_cast<uint8_t*>(dst), out_units, m);
     return hipGetLastError() == hipSuccess ? ECF8_OK : ECF8_ERR_HIP;
 }
 
