@@ -202,14 +202,19 @@ int ecf8_validate_meta(const ecf8_meta* meta);
 /* Workspace bytes a decode of `count` tensors needs (256-byte aligned
  * device memory, owned by the caller, sized once and reused across calls, as
  * ECF8 blog §3.2.2 sizes its pool once): a 256-byte block-check counter,
- * 128 bytes of descriptor and 9,216 bytes of decode table per tensor.
- * Returns 0 for count < 0. */
+ * 144 bytes of descriptor per tensor (rounded up to a multiple of 256 in
+ * all) and 9,216 bytes of decode table per tensor.  Returns 0 for
+ * count < 0. */
 uint64_t ecf8_workspace_bytes(int count);
 
 /* Batched-decode setup (ECF8 blog §3.3, "resident weights + batched decode"):
  * validates every descriptor on the host, writes the device descriptor table
- * into the workspace (one small host-to-device copy on hip_stream) and fills
- * *plan.  All tensors must share (C, TB).  out_base: device, receives tensor i
+ * into the workspace (one small host-to-device copy on hip_stream), launches
+ * on hip_stream the table kernel that builds each tensor's canonical decode
+ * table from its 16 code lengths into the workspace (ECF8 blog §3.1.2; once
+ * per plan, since a tensor's codebook does not change) and fills *plan.  The
+ * workspace's block-check counter starts at 0.  All tensors must share
+ * (C, TB).  out_base: device, receives tensor i
  * at out_base + descs[i].out_offset (n_i bytes).  The plan stays valid while
  * the workspace and the tensors' buffers do.
  * Errors: ECF8_ERR_ARG/SIZE/META/UNSUPPORTED/WORKSPACE/HIP. */
@@ -217,31 +222,25 @@ int ecf8_decode_prepare(const ecf8_tensor_desc* descs, int count, uint8_t* out_b
                         void* workspace, uint64_t workspace_bytes, void* hip_stream,
                         ecf8_plan* plan);
 
-/* One batched decode of a prepared plan: a table kernel builds each tensor's
- * canonical decode table from its 16 code lengths (ECF8 blog §3.1.2), then one
- * persistent decode dispatch covers every block of every tensor (ECF8 blog
- * §3.2.1 phases: chunk load, gap-based symbol count, block-wide exclusive
- * scan, cooperative decode into LDS, coalesced write-back).  Asynchronous on
- * hip_stream; the return code covers launch errors only. */
+/* One batched decode of a prepared plan: one persistent dispatch over every
+ * block of every tensor, running the ECF8 blog §3.2.1 phases on each block
+ * (chunk load, gap-based symbol count, block-wide exclusive scan,
+ * cooperative decode into LDS, coalesced write-back) with the decode table
+ * of the block's tensor (ECF8 blog §3.1.2, built by ecf8_decode_prepare)
+ * copied into LDS by each workgroup when its tensor changes.  Must follow the
+ * plan's ecf8_decode_prepare on the same stream, or on a stream ordered
+ * after it.  Asynchronous on hip_stream; the return code covers launch errors
+ * only (ECF8_ERR_ARG/WORKSPACE/HIP). */
 int ecf8_decode_run(const ecf8_plan* plan, void* hip_stream);
 
-/* The two launches of ecf8_decode_run, for callers that schedule or time
- * them separately: ecf8_build_tables (grid = tensors x 9 workgroups, one per
- * 256-entry slice of a tensor's table, ECF8 blog §3.1.2; it also restarts the
- * workspace's block-check counter) must precede ecf8_decode_blocks (the
- * persistent decode dispatch, ECF8 blog §3.2.1) on the same stream.  Same
- * arguments and errors as ecf8_decode_run. */
-int ecf8_build_tables(const ecf8_plan* plan, void* hip_stream);
-int ecf8_decode_blocks(const ecf8_plan* plan, void* hip_stream);
-
 /* For measurement (the pages time the decode as a whole, ECF8 blog §4; this
- * times the kernel): ecf8_decode_blocks with HIP events attached to the
+ * times the kernel): ecf8_decode_run with HIP events attached to the
  * dispatch itself, so that they hold its start and end times (hipEvent_t
  * handles created by the caller with timing enabled; either may be NULL).
  * Events recorded on the stream around an ordinary launch also hold the
  * dispatch's launch and completion latency.  Same errors as
- * ecf8_decode_blocks. */
-int ecf8_decode_blocks_timed(const ecf8_plan* plan, void* hip_stream, void* start_event, void* stop_event);
+ * ecf8_decode_run. */
+int ecf8_decode_run_timed(const ecf8_plan* plan, void* hip_stream, void* start_event, void* stop_event);
 
 /* ECF8 blog §3.3 (data-centre mode: every weight resident, decoded in
  * batches) and §3.2.2 (one preallocated output pool, reused, no allocation);
@@ -274,10 +273,10 @@ int ecf8_decode(const ecf8_stream* s, const ecf8_meta* meta, uint8_t* out_fp8, u
  * synchronisation): every decoded block compares the sum of its threads'
  * symbol counts (each counted from the thread's stored gap) with its stored
  * offsets blk_off[b + 1] - blk_off[b].  This call synchronizes hip_stream,
- * reads the workspace's counter of disagreeing blocks for the last run (the
- * table launch of each run restarts it; a plan whose tables were never built
- * flags every block) into *bad_blocks (host) and returns ECF8_ERR_CORRUPT if
- * it is non-zero.  A corrupt stream, gap or offset that keeps every block's
+ * reads the workspace's counter of disagreeing blocks into *bad_blocks
+ * (host), restarts it, and returns ECF8_ERR_CORRUPT if it was non-zero.  The
+ * counter covers every run on the workspace since ecf8_decode_prepare wrote
+ * it (cleared) or since the previous call of this function.  A corrupt stream, gap or offset that keeps every block's
  * count is not detected (the format carries no checksum); whatever the
  * corruption, no byte outside each tensor's output range is written.
  * Errors: ECF8_ERR_ARG (NULL), ECF8_ERR_HIP. */
@@ -287,7 +286,7 @@ int ecf8_decode_status(const void* workspace, void* hip_stream, uint64_t* bad_bl
  * capture, serving loops and harnesses that forbid hipMalloc): the same
  * decode as ecf8_decode_batched, with no workspace argument.  Its block-check
  * counter, descriptors and decode tables live in a fixed device array of the
- * library, 149,760 bytes per GPU, held by each GPU the library runs on until
+ * library, 150,016 bytes per GPU, held by each GPU the library runs on until
  * the process ends; it holds at most 16 tensors (count > 16 returns
  * ECF8_ERR_WORKSPACE).  The descriptors reach the device as kernel arguments,
  * so the call allocates nothing, copies nothing and issues no memset:

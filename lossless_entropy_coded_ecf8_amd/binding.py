@@ -100,8 +100,7 @@ EXPORTS_V = ["ecf8v_nsym", "ecf8v_histogram", "ecf8v_code_lengths", "ecf8v_canon
 
 EXPORTS = ["ecf8_histogram", "ecf8_codebook_from_freq", "ecf8_build_codebook", "ecf8_canonical_codes",
            "ecf8_encode_sizes", "ecf8_encode", "ecf8_validate_meta", "ecf8_workspace_bytes",
-           "ecf8_decode_prepare", "ecf8_decode_run", "ecf8_build_tables", "ecf8_decode_blocks",
-           "ecf8_decode_blocks_timed", "ecf8_decode_batched", "ecf8_decode", "ecf8_decode_batched_noalloc",
+           "ecf8_decode_prepare", "ecf8_decode_run", "ecf8_decode_run_timed", "ecf8_decode_batched", "ecf8_decode", "ecf8_decode_batched_noalloc",
            "ecf8_decode_status", "ecf8_histogram_device", "ecf8_meta_from_freq", "ecf8_encode_workspace_bytes",
            "ecf8_encode_device", "ecf8_encode_batched_device", "ecf8_alpha_hat", "ecf8_exponent_entropy_bound", "ecf8_hbm_copy", "ecf8_hbm_stream",
            "ecf8_strerror", "ecf8_version"]
@@ -135,9 +134,7 @@ def lib() -> ctypes.CDLL:
         "ecf8_decode_prepare": (i, [ctypes.POINTER(TensorDesc), i, vp, vp, ctypes.c_uint64, vp,
                                     ctypes.POINTER(Plan)]),
         "ecf8_decode_run": (i, [ctypes.POINTER(Plan), vp]),
-        "ecf8_build_tables": (i, [ctypes.POINTER(Plan), vp]),
-        "ecf8_decode_blocks": (i, [ctypes.POINTER(Plan), vp]),
-        "ecf8_decode_blocks_timed": (i, [ctypes.POINTER(Plan), vp, vp, vp]),
+        "ecf8_decode_run_timed": (i, [ctypes.POINTER(Plan), vp, vp, vp]),
         "ecf8_decode_batched": (i, [ctypes.POINTER(TensorDesc), i, vp, vp, ctypes.c_uint64, vp]),
         "ecf8_decode": (i, [ctypes.POINTER(Stream), ctypes.POINTER(Meta), vp, ctypes.c_uint64, vp,
                             ctypes.c_uint64, vp]),
@@ -574,33 +571,28 @@ class DecodePlan:
             self._synced.add(s.cuda_stream)
         return ctypes.c_void_p(s.cuda_stream)
 
-    def run(self, stream=None):
-        _check(lib().ecf8_decode_run(ctypes.byref(self.plan), self._launch_stream(stream)), "ecf8_decode_run")
-        return self.out
-
-    def build_tables(self, stream=None):
-        _check(lib().ecf8_build_tables(ctypes.byref(self.plan), self._launch_stream(stream)), "ecf8_build_tables")
-
-    def decode_blocks(self, stream=None, events=None):
-        """The decode dispatch.  events: optional (start, stop) torch.cuda.Event pair (timing
-        enabled) attached to the dispatch itself (ecf8_decode_blocks_timed), so that
-        start.elapsed_time(stop) is the kernel's own duration."""
-        if events is None:
-            _check(lib().ecf8_decode_blocks(ctypes.byref(self.plan), self._launch_stream(stream)),
-                   "ecf8_decode_blocks")
-            return self.out
+    def run(self, stream=None, events=None):
+        """The decode dispatch (each workgroup builds its tensor's table in LDS).  events:
+        optional (start, stop) torch.cuda.Event pair (timing enabled) attached to the dispatch
+        itself (ecf8_decode_run_timed), so that start.elapsed_time(stop) is the kernel's own
+        duration."""
         st = self._launch_stream(stream)
+        if events is None:
+            _check(lib().ecf8_decode_run(ctypes.byref(self.plan), st), "ecf8_decode_run")
+            return self.out
         handles = []
         for ev in events:
             if not ev.cuda_event:                  # torch creates its event on the first record
                 ev.record()
             handles.append(ctypes.c_void_p(ev.cuda_event))
-        _check(lib().ecf8_decode_blocks_timed(ctypes.byref(self.plan), st, handles[0], handles[1]),
-               "ecf8_decode_blocks_timed")
+        _check(lib().ecf8_decode_run_timed(ctypes.byref(self.plan), st, handles[0], handles[1]),
+               "ecf8_decode_run_timed")
         return self.out
 
     def status(self, stream=None) -> int:
-        """Synchronize and return the number of blocks whose counts disagreed with blk_off."""
+        """Synchronize and return the number of blocks whose counts disagreed with blk_off in
+        the runs since the plan was prepared or since the previous status() (which restarts
+        the count)."""
         bad = ctypes.c_uint64(0)
         rc = lib().ecf8_decode_status(ctypes.c_void_p(self.workspace.data_ptr()), _stream_handle(stream),
                                       ctypes.byref(bad))

@@ -18,9 +18,11 @@
 //     weight distributions of interest.  Codes longer than 11 bits (rare) live
 //     in a second region indexed by the next 16 bits; one branch-free
 //     max(prefix11, prefix16 - c) picks the region (canonical codes put every
-//     long code at the top of the code space).  The table is built per tensor
-//     on the GPU from the 16 code lengths by a small kernel and copied to LDS
-//     by each persistent workgroup when its tensor changes.
+//     long code at the top of the code space).  Each tensor's table is built
+//     from its 16 code lengths once per plan (the codebooks are fixed), in LDS
+//     by a small kernel (a first-symbol table of the 11-bit windows, chained)
+//     that stores it; each persistent decode workgroup copies it into LDS
+//     when its tensor changes, so a decode run is one dispatch.
 //   * chunks: 16 bytes per lane, 256 lanes (4 wave64s) per block; the lane's
 //     chunk plus one look-ahead dword are byte-swapped into LDS in word-major
 //     order (word k of every lane is one contiguous row), so the window reads
@@ -66,7 +68,6 @@ constexpr uint32_t kTabStride = 2304;                               // entries p
 constexpr int kChunk = 16;                                          // the tuned shape: C
 constexpr int kLanes = 256;                                         // and TB
 constexpr uint64_t kStatusBytes = 256;
-constexpr int kTableThreads = 256;
 constexpr int kNibPrefetch = 4;                                     // write-back groups prefetched per lane
 
 // Device descriptor of one tensor (workspace resident).
@@ -81,15 +82,15 @@ struct alignas(16) DevDesc {
     uint64_t block_begin;     // first global block of this tensor in the batch
     uint64_t block_end;       // one past its last global block
     uint8_t len[16];
-    // derived on the GPU by the table kernel
+    // derived from len[] on the host when the plan is prepared
     uint64_t lenpack;         // 4 bits per symbol: code length - 1
     uint32_t p_long;          // first 11-bit prefix of a code longer than 11 bits
     int32_t cdelta;           // 31 * p_long (second-region offset)
     uint32_t entries;         // table entries in use
-    uint32_t pad0;
-    uint64_t pad1[2];
+    uint16_t start[16];       // canonical code of each symbol, left-justified to 16 bits
+    uint32_t pad;
 };
-static_assert(sizeof(DevDesc) == 128, "descriptor layout");
+static_assert(sizeof(DevDesc) == 144, "descriptor layout");
 
 uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
@@ -156,109 +157,6 @@ __device__ __forceinline__ void bst4(Rsrc r, uint32_t off, uint32_t a, uint32_t 
 __device__ __forceinline__ void bst1(Rsrc r, uint32_t off, uint8_t v)
 {
     __builtin_amdgcn_raw_buffer_store_b8(v, r, off, 0, 0);
-}
-
-// ------------------------------------------------------------ table kernel
-// Grid (tensors, kTableSlices): workgroup (i, j) builds entries
-// [256 j, 256 j + 256) of tensor i's table, one entry per lane.  Canonical
-// codes occupy consecutive ranges of the left-justified 16-bit code space in
-// (length, symbol) order, so symbol s starts at the sum of 2^(16 - len) over
-// the symbols before it; each of 16 lanes computes one symbol's range.
-// Entry layout (one dword, so a lookup is a single 4-byte LDS read):
-//   bits  7..0   4 * symbols decoded (0..16): the nibble count of the entry's
-//                output, also usable directly as a shift amount (bits 4..0)
-//   bits 15..8   bits consumed (1..16)
-//   bits 31..16  the symbols as nibbles, first symbol in bits 19..16.
-constexpr int kTableSlices = (kTableMax + kTableThreads - 1) / kTableThreads;   // 9
-
-__global__ __launch_bounds__(kTableThreads) void ecf8_table_kernel(DevDesc* __restrict__ descs,
-                                                                   uint32_t* __restrict__ tables,
-                                                                   unsigned long long* __restrict__ status)
-{
-    // each run's block check counts from zero (the decode dispatch that follows
-    // on the same stream adds to it)
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0ull;
-    __shared__ uint32_t s_start[16];   // canonical order: left-justified start of the k-th codeword range
-    __shared__ uint32_t s_len[16];
-    __shared__ uint32_t s_sym[16];
-    __shared__ uint32_t s_k;
-    DevDesc* d = descs + blockIdx.x;
-    const int tid = threadIdx.x;
-    if (tid < 16) {
-        const uint32_t l = d->len[tid];
-        uint32_t rank = 0, start = 0, k = 0, plong_units = 0;
-        for (int u = 0; u < 16; ++u) {
-            const uint32_t lu = d->len[u];
-            if (!lu) continue;
-            k++;
-            if (lu <= (uint32_t)kWin) plong_units += 1u << (16 - lu);
-            if (l && (lu < l || (lu == l && u < tid))) {
-                rank++;
-                start += 1u << (16 - lu);
-            }
-        }
-        if (l) {
-            s_start[rank] = start;
-            s_len[rank] = l;
-            s_sym[rank] = tid;
-        }
-        if (tid == 0) {
-            s_k = k;
-            // every code of at most kWin bits precedes the long ones, so the
-            // first long prefix is the total space of the short codes
-            const uint32_t p_long = plong_units >> (16 - kWin);
-            uint32_t cdelta = ((1u << (16 - kWin)) - 1) * p_long;
-            uint32_t entries = 65536u - cdelta;      // <= kTableMax for every complete code
-            if (entries > (uint32_t)kTableMax) entries = kTableMax;
-            if (blockIdx.y == 0) {
-                uint64_t lenpack = 0;
-                for (int u = 0; u < 16; ++u)
-                    if (d->len[u]) lenpack |= (uint64_t)((d->len[u] - 1) & 15) << (4 * u);
-                d->lenpack = lenpack;
-                d->p_long = p_long;
-                d->cdelta = (int32_t)cdelta;
-                d->entries = entries;
-            }
-        }
-    }
-    __syncthreads();
-    const int k = (int)s_k;
-    uint32_t plong_units = 0;
-    for (int u = 0; u < 16; ++u) {
-        const uint32_t lu = d->len[u];
-        if (lu && lu <= (uint32_t)kWin) plong_units += 1u << (16 - lu);
-    }
-    const uint32_t p_long = plong_units >> (16 - kWin);
-    const uint32_t cdelta = ((1u << (16 - kWin)) - 1) * p_long;
-    uint32_t entries = 65536u - cdelta;
-    if (entries > (uint32_t)kTableMax) entries = kTableMax;
-    const uint32_t idx = blockIdx.y * kTableThreads + tid;
-    if (idx >= entries) return;
-    uint32_t v, known;
-    if (idx < p_long) {
-        v = idx << (16 - kWin);
-        known = kWin;
-    } else {
-        v = idx + cdelta;
-        known = 16;
-    }
-    uint32_t pos = 0, ns = 0, sy = 0;
-    while (k > 0 && ns < (uint32_t)kMaxSymPerEntry && pos < known) {
-        const uint32_t x = (v << pos) & 0xFFFFu;
-        int lo = 0, hi = k;
-        while (hi - lo > 1) {
-            int mid = (lo + hi) >> 1;
-            if (s_start[mid] <= x) lo = mid;
-            else hi = mid;
-        }
-        const uint32_t l = s_len[lo];
-        if (x >= s_start[lo] + (1u << (16 - l))) break;   // outside an incomplete code
-        if (pos + l > known) break;                          // codeword not fully visible
-        sy |= s_sym[lo] << (4 * ns);
-        ns++;
-        pos += l;
-    }
-    tables[(uint64_t)blockIdx.x * kTabStride + idx] = (4 * ns) | ((pos ? pos : 1u) << 8) | (sy << 16);
 }
 
 // ------------------------------------------------------------ helpers
@@ -703,6 +601,162 @@ __device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l)
     return ((uint64_t)hi << 32) | lo;
 }
 
+// ------------------------------------------------------------ decode table
+// Builds tensor d's packed table in LDS from its code lengths (ECF8 blog
+// §3.1.2 table-driven decode; the codes are canonical, so the lengths fix
+// them).  Canonical codes in (length, symbol) order occupy consecutive,
+// size-aligned ranges of the left-justified 16-bit code space; d->start holds
+// each symbol's first code, summed from the lengths when the plan was
+// prepared.  Entries:
+//   bits  7..0   4 * symbols decoded (0..16): the nibble count of the entry's
+//                output, also usable directly as a shift amount (bits 4..0)
+//   bits 15..8   bits consumed (1..16)
+//   bits 31..16  the symbols as nibbles, first symbol in bits 19..16.
+// Entry w < p_long (an 11-bit window whose first codeword has at most kWin
+// bits) decodes greedily the whole codewords inside the window, at most
+// kMaxSymPerEntry; entry i in [p_long, entries) stands for the 16-bit value
+// i + cdelta (a codeword longer than kWin bits, or no codeword of an
+// incomplete code, which consumes one bit and decodes nothing).
+// Steps: (1) each short symbol's window range is scattered into a
+// first-symbol table F (one 16-bit word per 11-bit window: length | symbol
+// << 8; windows of no short codeword get length 16, which never fits), at
+// most one store per lane and symbol; (2) each lane chains F over its windows
+// (the next codeword starts at the window shifted by the bits consumed so
+// far); (3) after a barrier, since F shares the table area, the entries are
+// stored, and the long region is searched directly.  Called by every lane of
+// a workgroup of kBuildThreads lanes (it holds barriers); a barrier of the
+// caller orders the stores before any read of the table.
+constexpr int kFirstOff = (int)kTabStride - (1 << kWin) / 2;   // F: the last 1024 dwords of the table area
+static_assert(kFirstOff >= 0 && kFirstOff % 4 == 0, "first-symbol table inside the table area");
+constexpr int kBuildThreads = 256;
+
+__device__ __forceinline__ void build_table(const DevDesc* __restrict__ d, uint32_t* s_tx, int tid)
+{
+    constexpr int TB = kBuildThreads;
+    constexpr int kPer = (1 << kWin) / TB;                  // windows per lane
+    static_assert(kPer * TB == (1 << kWin), "windows split evenly over the lanes");
+    static_assert(TB >= 64, "the first wave holds a lane per window of the 9..kWin-bit codes");
+    const uint32_t* lp = reinterpret_cast<const uint32_t*>(d->len);
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(d->start);
+    uint32_t lw[4], sw[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lw[i] = __builtin_amdgcn_readfirstlane(gld(lp + i));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sw[i] = __builtin_amdgcn_readfirstlane(gld(sp + i));
+    const uint32_t p_long = __builtin_amdgcn_readfirstlane(gld(&d->p_long));
+    auto len_of = [&](int u) -> uint32_t { return (lw[u >> 2] >> (8 * (u & 3))) & 0xFFu; };
+    auto start_of = [&](int u) -> uint32_t { return (sw[u >> 1] >> (16 * (u & 1))) & 0xFFFFu; };
+
+    // (1) symbol s of length l <= kWin covers the 2^(kWin - l) windows from
+    // its first one.  Lengths 1..8 cover whole groups of 8 windows, at most
+    // 256 groups in all: the lane of a group finds the symbol covering it
+    // (ranges are disjoint) and stores the group in one 16-byte store.
+    // Lengths 9..kWin cover 4, 2 or 1 windows: lane 4 s + j of the first wave
+    // stores window j of symbol s.
+    uint16_t* const F = reinterpret_cast<uint16_t*>(s_tx + kFirstOff);
+    const uint32_t t = (uint32_t)tid;
+#pragma unroll
+    for (int g0 = 0; g0 < (1 << (kWin - 3)); g0 += TB) {
+        const uint32_t w = 8u * (t + (uint32_t)g0);
+        uint32_t v = 0;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const uint32_t ls = len_of(s);
+            const uint32_t span = ls - 1u < 8u ? 1u << (kWin - ls) : 0u;
+            v = w - (start_of(s) >> (16 - kWin)) < span ? ls | ((uint32_t)s << 8) : v;
+        }
+        if (v) {   // (no range reaches past window 2^kWin - 1)
+            const uint32_t v2 = v | (v << 16);
+            *reinterpret_cast<uint4*>(F + w) = make_uint4(v2, v2, v2, v2);
+        }
+    }
+    if (t < 64) {
+        const uint32_t s = t >> 2, j = t & 3;
+        const uint32_t lq = s < 8 ? (s < 4 ? lw[0] : lw[1]) : (s < 12 ? lw[2] : lw[3]);
+        const uint32_t ls = (lq >> (8 * (s & 3))) & 0xFFu;
+        const uint32_t sq = s < 8 ? (s < 4 ? (s < 2 ? sw[0] : sw[1]) : (s < 6 ? sw[2] : sw[3]))
+                                  : (s < 12 ? (s < 10 ? sw[4] : sw[5]) : (s < 14 ? sw[6] : sw[7]));
+        const uint32_t st = (sq >> (16 * (s & 1))) & 0xFFFFu;
+        if (ls - 9u < (uint32_t)kWin - 8u && j < (1u << (kWin - ls)))
+            F[(st >> (16 - kWin)) + j] = (uint16_t)(ls | (s << 8));
+    }
+    if (p_long < (1u << kWin))
+        for (uint32_t w = p_long + t; w < (1u << kWin); w += TB) F[w] = (uint16_t)16u;
+    __syncthreads();
+
+    // (2) the short entries, chained over F
+    uint32_t ent[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const uint32_t w = t + (uint32_t)(TB * k);
+        const uint32_t f1 = F[w];
+        const uint32_t c1 = f1 & 0xFFu;
+        const uint32_t f2 = F[(w << (c1 & 31)) & 0x7FFu];
+        const uint32_t c2 = c1 + (f2 & 0xFFu);
+        const uint32_t f3 = F[(w << (c2 & 31)) & 0x7FFu];
+        const uint32_t c3 = c2 + (f3 & 0xFFu);
+        const uint32_t f4 = F[(w << (c3 & 31)) & 0x7FFu];
+        const uint32_t c4 = c3 + (f4 & 0xFFu);
+        // lengths are >= 1, so c2 < c3 < c4: the kept symbols are a prefix
+        const bool k2 = c2 <= (uint32_t)kWin, k3 = c3 <= (uint32_t)kWin, k4 = c4 <= (uint32_t)kWin;
+        const uint32_t n4 = k4 ? 16u : k3 ? 12u : k2 ? 8u : 4u;      // 4 * symbols
+        const uint32_t bits = k4 ? c4 : k3 ? c3 : k2 ? c2 : c1;
+        const uint32_t sy = (f1 >> 8) | ((f2 >> 4) & 0xF0u) | (f3 & 0xF00u) | ((f4 << 4) & 0xF000u);
+        const uint32_t keep = (1u << n4) - 1u;
+        ent[k] = n4 | (bits << 8) | ((sy & keep) << 16);
+    }
+    __syncthreads();
+
+    // (3) store; the long region from the canonical ranges directly
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const uint32_t w = t + (uint32_t)(TB * k);
+        if (w < p_long) s_tx[w] = ent[k];
+    }
+    {
+        const uint32_t ne = __builtin_amdgcn_readfirstlane(gld(&d->entries));
+        const uint32_t cd = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)gld(&d->cdelta));
+        for (uint32_t i = p_long + t; i < ne; i += TB) {
+            const uint32_t v = i + cd;
+            uint32_t pos = 0, ns = 0, sy = 0;
+            while (ns < (uint32_t)kMaxSymPerEntry && pos < 16u) {
+                const uint32_t x = (v << pos) & 0xFFFFu;
+                uint32_t fl = 0, fs = 0;
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const uint32_t lu = len_of(u);
+                    const uint32_t span = lu ? 1u << (16 - lu) : 0u;
+                    const bool in = x - start_of(u) < span;
+                    fl = in ? lu : fl;
+                    fs = in ? (uint32_t)u : fs;
+                }
+                if (fl == 0 || pos + fl > 16u) break;
+                sy |= fs << (4 * ns);
+                ns++;
+                pos += fl;
+            }
+            s_tx[i] = (4 * ns) | ((pos ? pos : 1u) << 8) | (sy << 16);
+        }
+    }
+}
+
+// One workgroup per tensor builds its table in LDS (the general form, valid
+// for both index forms) and writes it to the workspace, once per plan: the
+// codebooks are fixed, and each decode workgroup copies the table of the
+// tensor it works on into its LDS (a 9 KB copy from L2 costs a decode
+// workgroup less than the build, whose chained LDS reads conflict).
+__global__ __launch_bounds__(kBuildThreads) void ecf8_table_kernel(const DevDesc* __restrict__ descs,
+                                                                    uint32_t* __restrict__ tables)
+{
+    __shared__ __align__(16) uint32_t s_tab[kTabStride];
+    const DevDesc* d = descs + blockIdx.x;
+    build_table(d, s_tab, (int)threadIdx.x);
+    __syncthreads();
+    const uint32_t n4 = (gld(&d->entries) + 3) / 4;
+    uint4* dst = reinterpret_cast<uint4*>(tables + (uint64_t)blockIdx.x * kTabStride);
+    for (uint32_t i = threadIdx.x; i < n4; i += kBuildThreads) dst[i] = reinterpret_cast<const uint4*>(s_tab)[i];
+}
+
 #ifndef ECF8_MIN_WAVES
 #define ECF8_MIN_WAVES 6
 #endif
@@ -790,13 +844,9 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(kWavesTarget
         c_stream = d->stream;
         c_out = d->out;
         c_cd = d->cdelta;
-        uint32_t ne = d->entries;
-        c_ok = ne != 0 && (!kShort || c_cd == kShortCd);   // 0: tables never built for this plan, or a
-                                                           // code the short form cannot index
-        ne = ne < (uint32_t)kTableMax ? ne : (uint32_t)kTableMax;
-        const uint32_t* tx = tables + (uint64_t)t * kTabStride;
-        const uint32_t n4 = (ne + 3) / 4;
-        const Rsrc rt = make_rsrc(tx, 16ull * n4);
+        c_ok = !kShort || c_cd == kShortCd;   // 0: a code the short form cannot index
+        const uint32_t n4 = (d->entries + 3) / 4;
+        const Rsrc rt = make_rsrc(tables + (uint64_t)t * kTabStride, 16ull * n4);
         for (uint32_t i = tid; i < n4; i += TB)
             reinterpret_cast<u32x4*>(s_tx)[i] = __builtin_amdgcn_raw_buffer_load_b128(rt, 16u * i, 0, 0);
         cur = t;
@@ -1138,6 +1188,28 @@ int fill_desc(const ecf8_tensor_desc& td, uint8_t* out_base, uint64_t& blocks, D
     blocks += m.n_blocks;
     dd.block_end = blocks;
     for (int s = 0; s < 16; ++s) dd.len[s] = m.cb.len[s];
+    // the table's split point: every code of at most kWin bits precedes the
+    // long ones, so the first long 11-bit prefix is the short codes' space
+    uint32_t short_units = 0;
+    for (int s = 0; s < 16; ++s) {
+        const uint32_t l = m.cb.len[s];
+        if (!l) continue;
+        dd.lenpack |= (uint64_t)((l - 1) & 15) << (4 * s);
+        if (l <= (uint32_t)kWin) short_units += 1u << (16 - l);
+    }
+    dd.p_long = short_units >> (16 - kWin);
+    for (int s = 0; s < 16; ++s) {
+        const uint32_t l = m.cb.len[s];
+        uint32_t st = 0;
+        for (int u = 0; u < 16 && l; ++u) {
+            const uint32_t lu = m.cb.len[u];
+            if (lu && (lu < l || (lu == l && u < s))) st += 1u << (16 - lu);
+        }
+        dd.start[s] = (uint16_t)st;   // < 2^16: the code space before a used symbol is not full
+    }
+    dd.cdelta = (int32_t)(((1u << (16 - kWin)) - 1) * dd.p_long);
+    const uint32_t entries = 65536u - (uint32_t)dd.cdelta;      // <= kTableMax for every complete code
+    dd.entries = entries < (uint32_t)kTableMax ? entries : (uint32_t)kTableMax;
     return ECF8_OK;
 }
 
@@ -1176,7 +1248,7 @@ extern "C" int ecf8_decode_prepare(const ecf8_tensor_desc* descs, int count, uin
     std::memset(plan, 0, sizeof(*plan));
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < ecf8_workspace_bytes(count))
         return ECF8_ERR_WORKSPACE;
-    std::vector<unsigned char> host(table_offset(count) - 0, 0);   // status + descriptors
+    std::vector<unsigned char> host(table_offset(count), 0);   // cleared status + descriptors
     DevDesc* hd = reinterpret_cast<DevDesc*>(host.data() + desc_offset());
     uint64_t blocks = 0;
     uint32_t C = kChunk, TB = kLanes;
@@ -1191,6 +1263,14 @@ extern "C" int ecf8_decode_prepare(const ecf8_tensor_desc* descs, int count, uin
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     if (hipMemcpyAsync(workspace, host.data(), host.size(), hipMemcpyHostToDevice, st) != hipSuccess)
         return ECF8_ERR_HIP;
+    if (count > 0) {
+        // each tensor's decode table, once per plan (the codebooks are fixed)
+        unsigned char* ws = static_cast<unsigned char*>(workspace);
+        hipLaunchKernelGGL(ecf8_table_kernel, dim3(count), dim3(kBuildThreads), 0, st,
+                           reinterpret_cast<const DevDesc*>(ws + desc_offset()),
+                           reinterpret_cast<uint32_t*>(ws + table_offset(count)));
+        if (hipGetLastError() != hipSuccess) return ECF8_ERR_HIP;
+    }
     DeviceInfo di;
     rc = device_info(C, TB, short_codes, &di);
     if (rc) return rc;
@@ -1221,50 +1301,32 @@ int check_plan(const ecf8_plan* plan)
 
 }  // namespace
 
-extern "C" int ecf8_build_tables(const ecf8_plan* plan, void* hip_stream)
-{
-    int rc = check_plan(plan);
-    if (rc || plan->count == 0 || plan->total_blocks == 0) return rc;
-    unsigned char* ws = static_cast<unsigned char*>(plan->workspace);
-    DevDesc* dd = reinterpret_cast<DevDesc*>(ws + desc_offset());
-    uint32_t* tables = reinterpret_cast<uint32_t*>(ws + table_offset((int)plan->count));
-    auto* status = reinterpret_cast<unsigned long long*>(ws);
-    hipLaunchKernelGGL(ecf8_table_kernel, dim3(plan->count, kTableSlices), dim3(kTableThreads), 0,
-                       reinterpret_cast<hipStream_t>(hip_stream), dd, tables, status);
-    return hipGetLastError() == hipSuccess ? ECF8_OK : ECF8_ERR_HIP;
-}
+namespace {
 
-extern "C" int ecf8_decode_blocks(const ecf8_plan* plan, void* hip_stream)
+int run_plan(const ecf8_plan* plan, void* hip_stream, hipEvent_t start, hipEvent_t stop)
 {
     int rc = check_plan(plan);
     if (rc || plan->count == 0 || plan->total_blocks == 0) return rc;
     unsigned char* ws = static_cast<unsigned char*>(plan->workspace);
     DevDesc* dd = reinterpret_cast<DevDesc*>(ws + desc_offset());
-    uint32_t* tables = reinterpret_cast<uint32_t*>(ws + table_offset((int)plan->count));
     auto* status = reinterpret_cast<unsigned long long*>(ws);
+    const uint32_t* tables = reinterpret_cast<const uint32_t*>(ws + table_offset((int)plan->count));
     return launch_decode(plan->chunk_bytes, plan->threads_per_block, plan->short_codes != 0, plan->grid,
                          reinterpret_cast<hipStream_t>(hip_stream), dd, (int)plan->count, plan->total_blocks, tables,
-                         status);
+                         status, start, stop);
 }
 
-extern "C" int ecf8_decode_blocks_timed(const ecf8_plan* plan, void* hip_stream, void* start_event, void* stop_event)
-{
-    int rc = check_plan(plan);
-    if (rc || plan->count == 0 || plan->total_blocks == 0) return rc;
-    unsigned char* ws = static_cast<unsigned char*>(plan->workspace);
-    DevDesc* dd = reinterpret_cast<DevDesc*>(ws + desc_offset());
-    uint32_t* tables = reinterpret_cast<uint32_t*>(ws + table_offset((int)plan->count));
-    auto* status = reinterpret_cast<unsigned long long*>(ws);
-    return launch_decode(plan->chunk_bytes, plan->threads_per_block, plan->short_codes != 0, plan->grid,
-                         reinterpret_cast<hipStream_t>(hip_stream), dd, (int)plan->count, plan->total_blocks, tables,
-                         status, reinterpret_cast<hipEvent_t>(start_event), reinterpret_cast<hipEvent_t>(stop_event));
-}
+}  // namespace
 
 extern "C" int ecf8_decode_run(const ecf8_plan* plan, void* hip_stream)
 {
-    int rc = ecf8_build_tables(plan, hip_stream);
-    if (rc) return rc;
-    return ecf8_decode_blocks(plan, hip_stream);
+    return run_plan(plan, hip_stream, nullptr, nullptr);
+}
+
+extern "C" int ecf8_decode_run_timed(const ecf8_plan* plan, void* hip_stream, void* start_event, void* stop_event)
+{
+    return run_plan(plan, hip_stream, reinterpret_cast<hipEvent_t>(start_event),
+                    reinterpret_cast<hipEvent_t>(stop_event));
 }
 
 extern "C" int ecf8_decode_batched(const ecf8_tensor_desc* descs, int count, uint8_t* out_base,
@@ -1296,6 +1358,11 @@ extern "C" int ecf8_decode_status(const void* workspace, void* hip_stream, uint6
     unsigned long long v = 0;
     if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return ECF8_ERR_HIP;
     *bad_blocks = v;
+    if (v) {   // restart the count
+        const unsigned long long zero = 0;
+        if (hipMemcpy(const_cast<void*>(workspace), &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+            return ECF8_ERR_HIP;
+    }
     return v ? ECF8_ERR_CORRUPT : ECF8_OK;
 }
 
@@ -1312,20 +1379,20 @@ constexpr int kNoAllocMaxTensors = 16;
 constexpr int kSetupDescs = 8;                          // descriptors per setup launch (1 KiB of arguments)
 constexpr uint64_t kNoAllocScratchBytes =
     kStatusBytes + (kNoAllocMaxTensors * sizeof(DevDesc) + 255) / 256 * 256 + kNoAllocMaxTensors * kTableBytes;
-static_assert(kNoAllocScratchBytes == 149760, "scratch size stated in the header");
+static_assert(kNoAllocScratchBytes == 150016, "scratch size stated in the header");
 
 struct SetupArgs {
     DevDesc d[kSetupDescs];
 };
 
-// Copies n descriptors from the kernel arguments to dst (one dword per lane)
+// Copies n descriptors from the kernel arguments to dst (dwords spread over the lanes)
 // and, with clear set, zeroes the block-check counter.
 __global__ __launch_bounds__(256) void ecf8_noalloc_setup_kernel(SetupArgs a, int n, DevDesc* __restrict__ dst,
                                                                  unsigned long long* __restrict__ status, int clear)
 {
     constexpr int kDw = (int)(sizeof(DevDesc) / 4);
     const int t = threadIdx.x;
-    if (t < n * kDw) reinterpret_cast<uint32_t*>(dst)[t] = reinterpret_cast<const uint32_t*>(a.d)[t];
+    for (int i = t; i < n * kDw; i += 256) reinterpret_cast<uint32_t*>(dst)[i] = reinterpret_cast<const uint32_t*>(a.d)[i];
     if (clear && t == 0) *status = 0ull;
 }
 
@@ -1398,7 +1465,7 @@ extern "C" int ecf8_decode_batched_noalloc(const ecf8_tensor_desc* descs, int co
         if (count == 0) break;
     }
     if (blocks > 0) {
-        hipLaunchKernelGGL(ecf8_table_kernel, dim3(count, kTableSlices), dim3(kTableThreads), 0, st, dd, tables, status);
+        hipLaunchKernelGGL(ecf8_table_kernel, dim3(count), dim3(kBuildThreads), 0, st, dd, tables);
         uint64_t grid = (uint64_t)di.cus * (uint64_t)di.occupancy;
         if (grid > blocks) grid = blocks;
         return launch_decode(C, TB, short_codes, (uint32_t)grid, st, dd, count, blocks, tables, status);

@@ -196,11 +196,12 @@ def test_batched_mixed_tensors_and_buffer_reuse():
     assert plan2.status() == 0
 
 
-def test_split_calls_and_decode_without_tables():
-    """ecf8_build_tables then ecf8_decode_blocks equals ecf8_decode_run, on a batch whose tensors'
-    tables differ in size (each workgroup reloads its LDS table, in 16-byte loads, whenever its
-    next block belongs to another tensor); ecf8_decode_blocks on a plan whose tables were never
-    built flags every block, ends, and writes nothing outside the tensors' ranges."""
+def test_tables_switched_per_tensor_in_one_dispatch():
+    """One dispatch over tensors whose tables differ in size and form (11-bit codes, 12-bit
+    codes, 15-bit codes, two symbols, all 4-bit, 11-bit codes again): each workgroup copies the
+    table of its next block's tensor into LDS whenever that tensor changes, at several workgroup
+    counts (1 workgroup walks every tensor in turn); every tensor decodes exactly and no byte
+    outside the tensors' ranges is written."""
     d = dev()
     kinds = [("stable", 500_001), ("long12x6", 300_000), ("fib15", 200_003), ("two", 150_000),
              ("uniform4", 262_144), ("gauss", 400_000)]
@@ -214,24 +215,35 @@ def test_split_calls_and_decode_without_tables():
     inside = np.zeros(off + 64, dtype=bool)
     for o, (_, n) in zip(offs, kinds):
         inside[o:o + n] = True
-    # tables never built: every block is flagged, no byte outside the ranges is touched
-    out0 = torch.full((off + 64,), CANARY, dtype=torch.uint8, device=d)
-    plan0 = E.DecodePlan(encs, out=out0, offsets=offs)
-    plan0.decode_blocks()
-    assert plan0.status() == int(plan0.plan.total_blocks)
-    b0 = out0.cpu().numpy()
-    assert (b0[~inside] == CANARY).all()
-    # the two calls in order decode every tensor exactly
-    out = torch.full((off + 64,), CANARY, dtype=torch.uint8, device=d)
-    plan = E.DecodePlan(encs, out=out, offsets=offs)
-    plan.build_tables()
-    plan.decode_blocks()
-    torch.cuda.synchronize()
+    for wgs in (None, 37, 1):
+        out = torch.full((off + 64,), CANARY, dtype=torch.uint8, device=d)
+        plan = E.DecodePlan(encs, out=out, offsets=offs, workgroups=wgs)
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.status() == 0, wgs
+        b = out.cpu().numpy()
+        assert (b[~inside] == CANARY).all(), wgs
+        for i, x in enumerate(xs):
+            assert np.array_equal(b[offs[i]:offs[i] + x.size], x), (kinds[i], wgs)
+
+
+def test_status_counts_until_read():
+    """The block-check counter adds over runs and restarts when read: two runs on a corrupt
+    offset report twice one run's count, the next read reports 0."""
+    d = dev()
+    x, _ = make_input("stable", 400_000, 2100)
+    enc = E.encode(x)
+    denc = enc.to(d)
+    denc.blk_off[1] += 5
+    plan = E.DecodePlan([denc])
+    plan.run()
+    one = plan.status()
+    assert one >= 1
     assert plan.status() == 0
-    b = out.cpu().numpy()
-    assert (b[~inside] == CANARY).all()
-    for i, x in enumerate(xs):
-        assert np.array_equal(b[offs[i]:offs[i] + x.size], x), kinds[i]
+    plan.run()
+    plan.run()
+    assert plan.status() == 2 * one
+    assert plan.status() == 0
 
 
 def test_short_code_form_selection_and_parity():
@@ -281,20 +293,19 @@ def test_short_code_form_refuses_long_codes():
     assert (b[:16] == CANARY).all() and (b[16 + n:] == CANARY).all()
 
 
-def test_decode_blocks_with_dispatch_events():
-    """ecf8_decode_blocks_timed: the same decode, with the events attached to the dispatch holding
+def test_decode_run_with_dispatch_events():
+    """ecf8_decode_run_timed: the same decode, with the events attached to the dispatch holding
     its start and end (a positive duration, no longer than events recorded around the launch)."""
     d = dev()
     x, _ = make_input("stable", 2_000_003, 3030)
     plan = E.DecodePlan([E.encode(x, max_len=11).to(d)])
     plan.out.fill_(CANARY)
-    plan.build_tables()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     o0, o1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for ev in (a, b):
         ev.record()
     o0.record()
-    plan.decode_blocks(events=(a, b))
+    plan.run(events=(a, b))
     o1.record()
     torch.cuda.synchronize()
     assert plan.status() == 0
