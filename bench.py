@@ -9,11 +9,13 @@ output buffer; the one-tensor-per-launch workloads make one such dispatch
 per tensor.  The decoded output is checked bit-exact against the original
 bytes before timing.
 
-Prints ONE JSON line: value = decoded FP8 GB/s of the whole step (K steps of
-plain launches between two events); roofline = algorithmic HBM bytes of the
-decode kernel (compressed bytes read + FP8 bytes written) over its average
-duration, from events attached to each dispatch in another K steps;
-cpu_baseline = the plain C oracle decoding a bounded sample on the host cores.
+Prints ONE JSON line: value = decoded FP8 GB/s of the whole step (K timed
+steps between two events); roofline = algorithmic HBM bytes of the decode
+kernel (compressed bytes read + FP8 bytes written) over its average duration,
+from events attached to the dispatch of each timed step (one-dispatch-per-
+tensor workloads: of K more steps, since attached events would add launch
+work to each of their dispatches); cpu_baseline = the plain C oracle decoding
+a bounded sample on the host cores.
 """
 from __future__ import annotations
 
@@ -471,6 +473,8 @@ def main():
     ap.add_argument("--workload", default="llama70b", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settled", action="store_true",
+                    help="also time K decode steps after about 0.2 s of continuous decoding (kernel_ms_settled)")
     ap.add_argument("--copy-mib", default="512,2048", help="copycal mode: copy sizes in MiB (comma list)")
     ap.add_argument("--chunk-bytes", type=int, default=16, help="decode mode: stream bytes per lane (C)")
     ap.add_argument("--max-code-len", type=int, default=11,
@@ -556,7 +560,7 @@ def main():
     def step(evs=None):
         # with events, they are attached to each decode dispatch itself (ecf8_decode_run_timed): they
         # hold the kernel's start and end, not the launch and completion latency of events recorded
-        # around it (the timed steps that give `value` carry none: attached events add launch work)
+        # around it
         for i, p in enumerate(plans):
             p.run(events=None if evs is None else evs[i])
 
@@ -567,26 +571,47 @@ def main():
             b.record()
         return ev
 
+    # The timed region: K steps between two events.  A batched step is one dispatch, and its
+    # attached events (about 10 us of launch work a step) are in the timed region, so `value` and
+    # the kernel time come from the same steps.  A one-dispatch-per-tensor step would carry one
+    # pair per tensor (about 18 us each): its K timed steps are plain launches, and the kernel
+    # time comes from the K steps that follow, with events attached.
+    separate = wl in PER_TENSOR
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     K = args.steps
+    ev = [new_events() for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for k in range(K):
-        step()
+        step(None if separate else ev[k])
     end.record()
     torch.cuda.synchronize()
     step_ms = start.elapsed_time(end) / K
-    # the kernel's own time: the same K steps again, events attached to every dispatch
-    ev = [new_events() for _ in range(K)]
-    torch.cuda.synchronize()
-    for k in range(K):
-        step(ev[k])
-    torch.cuda.synchronize()
+    if separate:
+        for k in range(K):
+            step(ev[k])
+        torch.cuda.synchronize()
     dec = [sum(a.elapsed_time(b) for a, b in e) for e in ev]      # decode time of each step
     st = dispatch_stats(dec)
+
+    # --settled: the same decode once the device has run it without a pause for about 0.2 s (its
+    # clocks have then left the start-up transient that a short timed region falls in); off by
+    # default, so that a profiler's average over the run's dispatches is the timed region's
+    sts = None
+    if args.settled:
+        t_end = time.time() + 0.2
+        while time.time() < t_end:
+            for _ in range(20):
+                step()
+            torch.cuda.synchronize()
+        evs_ = [new_events() for _ in range(K)]
+        for k in range(K):
+            step(evs_[k])
+        torch.cuda.synchronize()
+        sts = dispatch_stats([sum(a.elapsed_time(b) for a, b in e) for e in evs_])
 
     # the same decode with a 1 GiB read before each step: the 256 MB Infinity Cache then holds only
     # clean lines of that buffer (a write would leave dirty lines for the decode to write back)
@@ -649,6 +674,15 @@ def main():
                      "kernel_ms_cache_evicted": stc["mean"], "kernel_ms_cache_evicted_median": stc["median"],
                      "kernel_ms_cache_evicted_min": stc["min"], "kernel_ms_cache_evicted_max": stc["max"],
                      "frac_cache_evicted": round(gbs(stc["mean"]) / HBM_PEAK_GBS, 4),
+                     "kernel_timing": ("a second series of K steps, events attached to each dispatch (the K "
+                                       "timed steps are plain launches)" if separate else
+                                       "events attached to the dispatch of each of the K timed steps"),
+                     **({} if sts is None else {
+                         "kernel_ms_settled": sts["mean"], "kernel_ms_settled_median": sts["median"],
+                         "frac_settled": round(gbs(sts["mean"]) / HBM_PEAK_GBS, 4),
+                         "settled_note": "--settled: K more steps after about 0.2 s of continuous decoding (the "
+                                         "device leaves its start-up clock transient; context, not the "
+                                         "headline)"}),
                      "decode_us_per_step": [round(1000 * t, 1) for t in dec[:50]]},
     }
     if not args.no_cpu_baseline:
