@@ -148,13 +148,23 @@ int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, uint8_t* out
 
 /* DFloat11 article §3.2 / ECF8 blog §3.2.1: the decode of a prepared plan,
  * asynchronous on hip_stream: one persistent dispatch over all tensors'
- * blocks (the workspace must still hold what prepare put there). */
+ * blocks (the workspace must still hold what prepare put there).  Errors:
+ * ECF8_ERR_ARG (NULL plan or workspace, grid 0, a bad table size),
+ * ECF8_ERR_UNSUPPORTED, ECF8_ERR_HIP (launch). */
 int ecf8v_decode_run(const ecf8v_plan* plan, void* hip_stream);
+
+/* For measurement: ecf8v_decode_run with HIP events attached to the
+ * dispatch itself (hipEvent_t handles created by the caller with timing
+ * enabled; either may be NULL), so that they hold its start and end times.
+ * Same errors as ecf8v_decode_run. */
+int ecf8v_decode_run_timed(const ecf8v_plan* plan, void* hip_stream, void* start_event, void* stop_event);
 
 /* Synchronize hip_stream and report the blocks whose decoded symbol count
  * disagreed with blk_off, or whose stream held a window that is no codeword
  * (those blocks are not written), in *bad_blocks; returns ECF8_ERR_CORRUPT
- * if non-zero.  The counter is cleared by each run. */
+ * if non-zero.  The count covers every run on the workspace since
+ * ecf8v_decode_prepare cleared it or since the previous call of this
+ * function, which restarts it. */
 int ecf8v_decode_status(const void* workspace, void* hip_stream, uint64_t* bad_blocks);
 
 #ifdef __cplusplus

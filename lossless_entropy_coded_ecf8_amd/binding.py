@@ -96,7 +96,7 @@ class PlanV(ctypes.Structure):
 
 EXPORTS_V = ["ecf8v_nsym", "ecf8v_histogram", "ecf8v_code_lengths", "ecf8v_canonical_codes", "ecf8v_encode_sizes",
              "ecf8v_encode", "ecf8v_validate_meta", "ecf8v_workspace_bytes", "ecf8v_decode_prepare",
-             "ecf8v_decode_run", "ecf8v_decode_status"]
+             "ecf8v_decode_run", "ecf8v_decode_run_timed", "ecf8v_decode_status"]
 
 EXPORTS = ["ecf8_histogram", "ecf8_codebook_from_freq", "ecf8_build_codebook", "ecf8_canonical_codes",
            "ecf8_encode_sizes", "ecf8_encode", "ecf8_validate_meta", "ecf8_workspace_bytes",
@@ -167,6 +167,7 @@ def lib() -> ctypes.CDLL:
         "ecf8v_decode_prepare": (i, [ctypes.POINTER(TensorDescV), i, vp, vp, ctypes.c_uint64, vp,
                                      ctypes.POINTER(PlanV)]),
         "ecf8v_decode_run": (i, [ctypes.POINTER(PlanV), vp]),
+        "ecf8v_decode_run_timed": (i, [ctypes.POINTER(PlanV), vp, vp, vp]),
         "ecf8v_decode_status": (i, [vp, vp, u64p]),
     })
     for name, (res, args) in sig.items():
@@ -852,11 +853,25 @@ class DecodePlanV:
 
     _launch_stream = DecodePlan._launch_stream
 
-    def run(self, stream=None):
-        _check(lib().ecf8v_decode_run(ctypes.byref(self.plan), self._launch_stream(stream)), "ecf8v_decode_run")
+    def run(self, stream=None, events=None):
+        """The decode dispatch.  events: optional (start, stop) torch.cuda.Event pair (timing
+        enabled) attached to the dispatch itself (ecf8v_decode_run_timed)."""
+        st = self._launch_stream(stream)
+        if events is None:
+            _check(lib().ecf8v_decode_run(ctypes.byref(self.plan), st), "ecf8v_decode_run")
+            return self.out
+        handles = []
+        for ev in events:
+            if not ev.cuda_event:                  # torch creates its event on the first record
+                ev.record()
+            handles.append(ctypes.c_void_p(ev.cuda_event))
+        _check(lib().ecf8v_decode_run_timed(ctypes.byref(self.plan), st, handles[0], handles[1]),
+               "ecf8v_decode_run_timed")
         return self.out
 
     def status(self, stream=None) -> int:
+        """Synchronize and return the bad blocks of the runs since prepare or the previous
+        status() (which restarts the count)."""
         bad = ctypes.c_uint64(0)
         rc = lib().ecf8v_decode_status(ctypes.c_void_p(self.workspace.data_ptr()), _stream_handle(stream),
                                        ctypes.byref(bad))

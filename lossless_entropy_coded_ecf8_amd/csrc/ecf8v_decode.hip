@@ -65,6 +65,7 @@
 // slower path: rounds of 16384 symbols, each lane walking its chunk again.
 // Wave priority rises through a block (walk 1, scan and replay 2, write-back
 // 3), so the wave of a SIMD nearest its stores issues first.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -1017,7 +1018,9 @@ extern "C" int ecf8v_decode_prepare(const ecf8v_tensor_desc* descs, int count, u
     return ECF8_OK;
 }
 
-extern "C" int ecf8v_decode_run(const ecf8v_plan* plan, void* hip_stream)
+namespace {
+
+int run_plan(const ecf8v_plan* plan, void* hip_stream, hipEvent_t start, hipEvent_t stop)
 {
     if (!plan || !plan->workspace || plan->grid == 0) return ECF8_ERR_ARG;
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
@@ -1025,8 +1028,7 @@ extern "C" int ecf8v_decode_run(const ecf8v_plan* plan, void* hip_stream)
     auto* status = reinterpret_cast<unsigned long long*>(ws);
     const DescV* descs = reinterpret_cast<const DescV*>(ws + desc_offset());
     uint32_t* tables = reinterpret_cast<uint32_t*>(ws + table_offset((int)plan->count));
-    hipLaunchKernelGGL(ecf8v_clear_kernel, dim3(1), dim3(64), 0, st, status, 1u);
-    if (plan->count == 0 || plan->total_blocks == 0) return check(hipGetLastError());
+    if (plan->count == 0 || plan->total_blocks == 0) return ECF8_OK;
     const uint32_t tb = plan->threads_per_block;
     const void* k = pick_kernel(plan->format, tb, plan->short_codes != 0);
     if (!k) return ECF8_ERR_UNSUPPORTED;
@@ -1035,9 +1037,25 @@ extern "C" int ecf8v_decode_run(const ecf8v_plan* plan, void* hip_stream)
     uint32_t tab_n = plan->table_entries;
     if (tab_n < (uint32_t)kTabMin || tab_n > (uint32_t)kTabMax || (tab_n & 3)) return ECF8_ERR_ARG;
     void* args[] = {(void*)&descs, (void*)&count, (void*)&tables, (void*)&total, (void*)&status, (void*)&tab_n};
-    if (hipLaunchKernel(k, dim3(plan->grid), dim3(tb), args, decode_lds_bytes(tab_n), st) != hipSuccess)
-        return ECF8_ERR_HIP;
+    const hipError_t e = start || stop
+                             ? hipExtLaunchKernel(k, dim3(plan->grid), dim3(tb), args, decode_lds_bytes(tab_n), st,
+                                                  start, stop, 0)
+                             : hipLaunchKernel(k, dim3(plan->grid), dim3(tb), args, decode_lds_bytes(tab_n), st);
+    if (e != hipSuccess) return ECF8_ERR_HIP;
     return check(hipGetLastError());
+}
+
+}  // namespace
+
+extern "C" int ecf8v_decode_run(const ecf8v_plan* plan, void* hip_stream)
+{
+    return run_plan(plan, hip_stream, nullptr, nullptr);
+}
+
+extern "C" int ecf8v_decode_run_timed(const ecf8v_plan* plan, void* hip_stream, void* start_event, void* stop_event)
+{
+    return run_plan(plan, hip_stream, reinterpret_cast<hipEvent_t>(start_event),
+                    reinterpret_cast<hipEvent_t>(stop_event));
 }
 
 extern "C" int ecf8v_decode_status(const void* workspace, void* hip_stream, uint64_t* bad_blocks)
@@ -1048,5 +1066,10 @@ extern "C" int ecf8v_decode_status(const void* workspace, void* hip_stream, uint
     unsigned long long v[2] = {0, 0};
     if (hipMemcpy(v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return ECF8_ERR_HIP;
     *bad_blocks = v[0] + v[1];
+    if (*bad_blocks) {   // restart the count
+        const unsigned long long zero[2] = {0, 0};
+        if (hipMemcpy(const_cast<void*>(workspace), zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+            return ECF8_ERR_HIP;
+    }
     return *bad_blocks ? ECF8_ERR_CORRUPT : ECF8_OK;
 }

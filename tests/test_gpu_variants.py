@@ -168,6 +168,37 @@ def test_corrupt_block_offset_is_flagged_and_contained():
     assert np.array_equal(got[lo:], x[lo:])      # later blocks unaffected
 
 
+def test_status_counts_until_read_and_timed_run():
+    """The variant block-check counter adds over runs and restarts when read; a run with events
+    attached to its dispatch (ecf8v_decode_run_timed) decodes the same bytes, and its events hold
+    a positive duration no longer than events recorded around the launch."""
+    d = dev()
+    x = make("e5m2", 300_000, 11)
+    h = B.v_encode("e5m2", x, threads_per_block=64)
+    good = B.DecodePlanV([h.to(d)])
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    o0, o1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for ev in (a, b):
+        ev.record()
+    good.out.fill_(CANARY)
+    o0.record()
+    good.run(events=(a, b))
+    o1.record()
+    torch.cuda.synchronize()
+    assert good.status() == 0
+    assert np.array_equal(as_elems("e5m2", good.view(0).cpu().numpy()), x)
+    assert 0 < a.elapsed_time(b) <= o0.elapsed_time(o1) * 1.001 + 1e-3
+    h.blk_off[2] += 5                            # blocks 1 and 2 disagree with their counts
+    bad = B.DecodePlanV([h.to(d)])
+    bad.run()
+    assert bad.status() == 2
+    assert bad.status() == 0
+    bad.run()
+    bad.run()
+    assert bad.status() == 4
+    assert bad.status() == 0
+
+
 def dense_sparse_runs(fmt, n, dense_run, sparse_run, seed):
     """Runs of one exponent (a 1-bit code: 128 codewords per 16-byte chunk) between runs of ~100
     exponents (long codes), so that blocks stay under 16384 symbols while some chunks need more
