@@ -74,8 +74,9 @@ def linear_fp8(x_fp8: torch.Tensor, x_scale: torch.Tensor, w_u8: torch.Tensor, w
 
 
 def check_decode(plan: binding.DecodePlan, stream=None):
-    """Checked mode: synchronize `stream` and raise if the last run of `plan`
-    flagged any block (its decoded symbol count disagreed with blk_off)."""
+    """Checked mode: synchronize `stream` and raise if a run of `plan` since the
+    previous check flagged any block (its decoded symbol count disagreed with
+    blk_off); each check restarts the count."""
     bad = plan.status(stream)
     if bad:
         raise binding.Ecf8Error(-5, "ECF8 decode (%d corrupt blocks)" % bad)
