@@ -227,6 +227,65 @@ def test_tables_switched_per_tensor_in_one_dispatch():
             assert np.array_equal(b[offs[i]:offs[i] + x.size], x), (kinds[i], wgs)
 
 
+def reference_table(lengths):
+    """The decode table by its definition (ECF8 blog §3.1.2, table-driven decode of a canonical
+    code), from the oracle's canonical codes: entry i < p_long stands for the 11-bit window i
+    (11 known bits), entry i >= p_long for the 16-bit value i + 31 p_long (16 known bits, the
+    region of codewords longer than 11 bits); each entry decodes greedily the whole codewords
+    inside its known bits, at most 4, by prefix match.  Entry: 4 * symbols | bits consumed
+    (1 when none) << 8 | symbols as nibbles << 16.  p_long = 11-bit prefixes of the codes of at
+    most 11 bits; entries = min(65536 - 31 p_long, 2296)."""
+    L = [int(v) for v in lengths]
+    codes = oracle.canonical_codes(L)
+    cw = [(int(codes[s]), L[s], s) for s in range(16) if L[s]]
+    p_long = sum(1 << (16 - l) for l in L if 0 < l <= 11) >> 5
+    ne = min(65536 - 31 * p_long, 2296)
+    table = []
+    for i in range(ne):
+        v, known = (i << 5, 11) if i < p_long else (i + 31 * p_long, 16)
+        pos = ns = sy = 0
+        while ns < 4 and pos < known:
+            x = (v << pos) & 0xFFFF
+            hit = next(((l, s) for c, l, s in cw if x >> (16 - l) == c), None)
+            if hit is None or pos + hit[0] > known:
+                break
+            sy |= hit[1] << (4 * ns)
+            ns += 1
+            pos += hit[0]
+        table.append(4 * ns | max(pos, 1) << 8 | sy << 16)
+    return np.array(table, dtype=np.uint32)
+
+
+def test_decode_tables_match_definition():
+    """The table kernel (run by ecf8_decode_prepare) writes, for each tensor of a plan, every
+    entry the decode can index exactly as reference_table defines it: codes limited to 11 bits,
+    all 4-bit, two 1-bit codes, 12- and 15-bit codewords (the 16-bit region), a single symbol
+    (an incomplete code, 2296 entries) and plain Huffman codes of weight-like data.  The
+    workspace holds a 256-byte counter, 144 bytes of descriptor per tensor rounded up to 256
+    bytes in all, then 9216 bytes of table per tensor."""
+    d = dev()
+    kinds = [("stable", 11), ("uniform4", 16), ("two", 16), ("long12x6", 16), ("fib15", 16),
+             ("single", 16), ("gauss", 16), ("stable", 16)]
+    encs, lens = [], []
+    for i, (k, ml) in enumerate(kinds):
+        x, L = make_input(k, 40_000, 4000 + i)
+        h = E.encode(x, lengths=L, max_len=ml) if L is not None else E.encode(x, max_len=ml)
+        encs.append(h.to(d))
+        lens.append(list(h.lengths))
+    plan = E.DecodePlan(encs)
+    torch.cuda.synchronize()
+    ws = plan.workspace.cpu().numpy()
+    off = 256 + (144 * len(encs) + 255) // 256 * 256
+    for t, L in enumerate(lens):
+        want = reference_table(L)
+        got = ws[off + t * 9216: off + t * 9216 + 4 * want.size].view("<u4")
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, (kinds[t], L, bad[:5], got[bad[:5]], want[bad[:5]])
+    # and the plan decodes every tensor exactly with those tables
+    plan.run()
+    assert plan.status() == 0
+
+
 def test_status_counts_until_read():
     """The block-check counter adds over runs and restarts when read: two runs on a corrupt
     offset report twice one run's count, the next read reports 0."""
