@@ -49,7 +49,8 @@
 //     starting past its chunk, which are taken off its count;
 //   * block scan of the counts (checked against the block offsets);
 //   * replay: each recorded entry's symbol bytes are OR-ed into the cleared
-//     LDS stage at the scanned position (two dword ORs).  Codewords a lane
+//     LDS stage at the scanned position (one dword OR per entry; the part
+//     that crosses into the next dword is carried to the next entry's OR).  Codewords a lane
 //     decodes past its chunk end are the next lane's first ones, at the same
 //     positions, so OR-ing them twice is exact.  Lanes with more lookups than
 //     records walk the rest from registers;
@@ -526,6 +527,20 @@ __device__ __forceinline__ void emit_entry(uint32_t* stage32, uint32_t ob, uint3
     atomicOr(w + 1, (uint32_t)(v >> 32));
 }
 
+// The same for consecutive entries of a lane, one LDS atomic each: the
+// entry's bytes cover dword ob / 4 and, when they cross, part of the next.
+// Only the first is OR-ed here, together with `carry`, the previous entry's
+// spill into this same dword; this entry's spill is returned in `carry` for
+// the next entry (or the final flush).  An entry adds at most 3 bytes, so the
+// next one starts in this dword or the next, and a spill is non-zero only if
+// it starts in the next: the carry lands in the dword it belongs to.
+__device__ __forceinline__ void emit_entry_carry(uint32_t* stage32, uint32_t ob, uint32_t e, uint32_t& carry)
+{
+    const uint64_t v = (uint64_t)(e >> 8) << (8 * (ob & 3));
+    atomicOr(stage32 + (ob >> 2), (uint32_t)v | carry);
+    carry = (uint32_t)(v >> 32);
+}
+
 // Window at chunk bit p from the lane's words in registers (w[4] the look-ahead).
 __device__ __forceinline__ uint32_t reg_window(const uint32_t (&w)[5], uint32_t p)
 {
@@ -816,17 +831,20 @@ __global__ __launch_bounds__(kTB) __attribute__((amdgpu_waves_per_eu(kMinWaves<k
             const uint2 tail_raw = load_raw_unit(rr, tail_lane ? end_full : 0x0FFFFFFFu);
             // ---- replay into the stage
             uint32_t ob = geo.a0 + pos;
+            uint32_t carry = 0;
 #pragma unroll
             for (int q = 0; q < kRecords / kStep; ++q) {
                 if (q < nq) {                             // no early exit: the records keep static indices
 #pragma unroll
                     for (int j = 0; j < kStep; ++j) {
                         const uint32_t e = rec[kStep * q + j];
-                        emit_entry(stage32, ob, e);
+                        emit_entry_carry(stage32, ob, e, carry);
                         ob += (e >> En::kCnt) & 3u;
                     }
                 }
             }
+            // the last entry's spill belongs to ob's dword (zero if it did not cross)
+            if (nq) atomicOr(stage32 + (ob >> 2), carry);
             if (r_rec > rend) {
                 // lanes with more lookups than records: the rest from registers
                 // (the rows are stage memory now; the chunk is L2-resident)
