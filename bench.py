@@ -542,8 +542,8 @@ def main():
             log("encoded %-12s n=%d  %.3f bits/exponent" % (name, h.n, h.meta.total_bits / max(h.n, 1)))
     log("setup %.1f s, %d tensors" % (time.time() - t0, len(encs)))
 
-    # one step: one batched dispatch of all tensors, or one dispatch per tensor (each workgroup builds
-    # its tensor's decode table in LDS, so a decode is one launch)
+    # one step: one batched dispatch of all tensors, or one dispatch per tensor (the decode tables are
+    # built once per plan, so a run is one dispatch)
     plans = [E.DecodePlan([e]) for e in encs] if wl in PER_TENSOR else [E.DecodePlan(encs)]
     for p in plans:
         p.run()
