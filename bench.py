@@ -3,9 +3,9 @@
 
 One step = one batched decode of a whole workload (default: the Llama-3-70B
 transformer block, 7 FP8 E4M3 tensors, 855,638,016 elements) with every
-input resident in HBM: one persistent decode dispatch (each workgroup builds
-its tensor's decode table in LDS from the code lengths) into one reused
-output buffer; the one-tensor-per-launch workloads make one such dispatch
+input resident in HBM: one persistent decode dispatch (the decode tables are
+built once when the plan is prepared; each workgroup copies its tensor's
+table into LDS) into one reused output buffer; the one-tensor-per-launch workloads make one such dispatch
 per tensor.  The decoded output is checked bit-exact against the original
 bytes before timing.
 
@@ -487,6 +487,10 @@ def main():
                     help="variant mode: code length limit of the encoding (10: every codeword fits the variant "
                          "decode's 10-bit table index; 16: the library default)")
     ap.add_argument("--lanes", type=int, default=256, help="decode mode: lanes per block (TB)")
+    ap.add_argument("--experts", type=int, default=0,
+                    help="decode mode, moe256: the first N experts only (a shorter dispatch of the same layer)")
+    ap.add_argument("--claim-blocks", type=int, default=-1,
+                    help="decode mode: block order (0 static, k >= 2 claims of k blocks; default: the library's choice)")
     ap.add_argument("--mode", default="decode", choices=["decode", "pipeline", "alpha", "encode", "variant", "copycal"],
                     help="decode: the batched decode step (default); pipeline: decode-on-use of the "
                          "block's layers beside FP8 GEMMs, against resident FP8 weights")
@@ -526,6 +530,8 @@ def main():
     wl = args.workload
     if wl == "moe8":
         gen = synth.workload_tensors("moe256", device=d, experts=synth.moe_routing())
+    elif wl == "moe256" and args.experts:
+        gen = synth.workload_tensors(wl, device=d, experts=list(range(args.experts)))
     else:
         gen = synth.workload_tensors(wl, device=d)
     names, xs, encs_host, encs = [], [], [], []
@@ -544,7 +550,9 @@ def main():
 
     # one step: one batched dispatch of all tensors, or one dispatch per tensor (the decode tables are
     # built once per plan, so a run is one dispatch)
-    plans = [E.DecodePlan([e]) for e in encs] if wl in PER_TENSOR else [E.DecodePlan(encs)]
+    claim = None if args.claim_blocks < 0 else args.claim_blocks
+    plans = ([E.DecodePlan([e], claim_blocks=claim) for e in encs] if wl in PER_TENSOR
+             else [E.DecodePlan(encs, claim_blocks=claim)])
     for p in plans:
         p.run()
     torch.cuda.synchronize()
@@ -651,13 +659,19 @@ def main():
         "vs_baseline": None,
         "dtype": "u8",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[wl], "name": wl, "tensors": len(encs), "elements": n_total,
+        "config": {"workload": (WORKLOAD_TEXT[wl] if not (wl == "moe256" and args.experts) else
+                                "MoE layer, the first %d of its 256 experts x (gate, up 7168x2048; down 2048x7168), "
+                                "FP8 E4M3, alpha ~ U[1.5,2.0] per expert, per-expert codebooks, one batched dispatch"
+                                % args.experts),
+                   "name": wl if not (wl == "moe256" and args.experts) else "moe256_first%d" % args.experts,
+                   "tensors": len(encs), "elements": n_total,
                    "compressed_bytes": bb["read"], "bits_per_element": round(8.0 * bb["read"] / n_total, 4),
                    "chunk_bytes": args.chunk_bytes, "lanes_per_block": args.lanes,
                    "max_code_len": max(max(int(v) for v in e.meta.cb.len) for e in encs),
                    "code_length_limit": args.max_code_len,
                    "short_code_form": all(int(p.plan.short_codes) for p in plans), "launches_per_step": len(plans),
-                   "grid": int(max(p.plan.grid for p in plans))},
+                   "grid": int(max(p.plan.grid for p in plans)),
+                   "claim_blocks": int(max(p.plan.claim_blocks for p in plans))},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "ecf8_decode_kernel", "kernel_ms": st["mean"], "kernel_ms_median": st["median"],

@@ -141,6 +141,16 @@ typedef struct {
                                 11-bit prefix alone (set by ecf8_decode_prepare; a tensor
                                 that does not qualify is not decoded under 1 and its blocks
                                 are counted by ecf8_decode_status) */
+    uint32_t claim_blocks;   /* block order of a run.  0: workgroup g decodes blocks g,
+                                g + grid, g + 2 grid, ...  k (2..1024): workgroups take
+                                claims of k consecutive blocks, the first one each by
+                                its index and the rest from a counter in the workspace,
+                                which keeps the blocks in flight close together over a
+                                long dispatch.  ecf8_decode_prepare sets 4 when the
+                                plan has at least 96 blocks per workgroup, else 0; the
+                                caller may change it before a run (total_blocks + grid *
+                                claim_blocks must stay below 2^32).  Runs of one plan
+                                must not overlap in time: they share the counter */
 } ecf8_plan;
 
 /* ---------------------------- host side ------------------------------- */

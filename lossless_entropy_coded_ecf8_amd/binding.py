@@ -67,7 +67,8 @@ class Plan(ctypes.Structure):
     _fields_ = [("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
                 ("total_blocks", ctypes.c_uint64), ("count", ctypes.c_uint32),
                 ("chunk_bytes", ctypes.c_uint32), ("threads_per_block", ctypes.c_uint32),
-                ("grid", ctypes.c_uint32), ("short_codes", ctypes.c_uint32)]
+                ("grid", ctypes.c_uint32), ("short_codes", ctypes.c_uint32),
+                ("claim_blocks", ctypes.c_uint32)]
 
 
 MAXSYM_V = 256
@@ -521,10 +522,13 @@ class DecodePlan:
     """
 
     def __init__(self, encs: Sequence[DeviceEncoded], out=None, offsets: Optional[List[int]] = None,
-                 workspace=None, stream=None, workgroups: Optional[int] = None):
+                 workspace=None, stream=None, workgroups: Optional[int] = None,
+                 claim_blocks: Optional[int] = None):
         """workgroups: upper bound on the persistent decode's workgroups (default:
         every compute unit at full occupancy); a smaller grid leaves compute units
-        to kernels running concurrently on other streams."""
+        to kernels running concurrently on other streams.  claim_blocks: the block
+        order (ecf8_plan.claim_blocks: 0 static, 2..1024 blocks per claim; default:
+        the library's choice)."""
         import torch
         self.encs = list(encs)
         dev = self.encs[0].stream.device if self.encs else torch.device("cuda")
@@ -558,6 +562,8 @@ class DecodePlan:
                "ecf8_decode_prepare")
         if workgroups is not None:
             self.plan.grid = max(1, min(int(self.plan.grid), int(workgroups)))
+        if claim_blocks is not None:
+            self.plan.claim_blocks = int(claim_blocks)
         # the descriptor upload is ordered on the prepare stream; a launch on
         # another stream first waits for it (once per stream)
         self._prep_stream = _torch_stream(stream)
@@ -573,7 +579,8 @@ class DecodePlan:
         return ctypes.c_void_p(s.cuda_stream)
 
     def run(self, stream=None, events=None):
-        """The decode dispatch (each workgroup builds its tensor's table in LDS).  events:
+        """The decode dispatch (each workgroup copies its tensor's decode table, built when the
+        plan was prepared, into LDS).  events:
         optional (start, stop) torch.cuda.Event pair (timing enabled) attached to the dispatch
         itself (ecf8_decode_run_timed), so that start.elapsed_time(stop) is the kernel's own
         duration."""

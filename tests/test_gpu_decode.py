@@ -196,6 +196,57 @@ def test_batched_mixed_tensors_and_buffer_reuse():
     assert plan2.status() == 0
 
 
+@pytest.mark.parametrize("claim,workgroups", [(2, 7), (3, 5), (5, None), (16, 13), (16, None), (1024, 3),
+                                               (2, 1), (40, 64)], ids=lambda v: str(v))
+def test_claimed_block_order_bit_exact(claim, workgroups):
+    """The claimed block order (ecf8_plan.claim_blocks): tensors with different codebooks, claims
+    of 2 to 1024 blocks, grids from 1 workgroup to full (some with more workgroups x claim than
+    blocks), three runs into a reused buffer: every byte exact, canaries intact, no block flagged,
+    and the claim counters back at zero after each run."""
+    d = dev()
+    kinds = [("stable", 1_300_001), ("fib15", 70_000), ("single", 40_000), ("bytes", 99_999),
+             ("two", 33_333), ("gauss", 1 << 20), ("stable", 5), ("long12x6", 250_000)]
+    xs, encs, offs, off = [], [], [], 0
+    for i, (k, n) in enumerate(kinds):
+        x, L = make_input(k, n, 5000 + i)
+        xs.append(x)
+        encs.append(E.encode(x, lengths=L).to(d))
+        offs.append(off)
+        off += (n + 15) // 16 * 16 + 16 * (i % 3)
+    out = torch.full((off + 64,), CANARY, dtype=torch.uint8, device=d)
+    plan = E.DecodePlan(encs, out=out, offsets=offs, workgroups=workgroups, claim_blocks=claim)
+    assert int(plan.plan.claim_blocks) == claim
+    for rep in range(3):
+        out[:off].fill_(0)
+        plan.run()
+        torch.cuda.synchronize()
+        for i, x in enumerate(xs):
+            assert np.array_equal(plan.view(i).cpu().numpy(), x), (rep, i, kinds[i])
+        assert (out[off:].cpu().numpy() == CANARY).all()
+        assert int(plan.workspace[64:72].cpu().view(torch.int64)[0]) == 0, "claim counters not reset"
+    assert plan.status() == 0
+
+
+def test_claimed_order_on_the_llama70b_block():
+    """The Llama-3-70B block (codes limited to 11 bits, as benchmarked) decoded in claims of 16
+    blocks (the library keeps this block in the static order), twice: every tensor equals its
+    input, sampled blocks equal the oracle's decode."""
+    d = dev()
+    names, xs, encs = encode_workload("llama70b", d, max_len=11)
+    assert E.DecodePlan(encs).plan.claim_blocks == 0
+    plan = E.DecodePlan(encs, claim_blocks=16)
+    rng = np.random.default_rng(5)
+    for rep in range(2):
+        plan.out.fill_(CANARY)
+        plan.run()
+        torch.cuda.synchronize()
+        for i, (nm, x) in enumerate(zip(names, xs)):
+            assert torch.equal(plan.view(i), x), (rep, nm)
+    assert plan.status() == 0
+    for i in range(len(encs)):
+        sampled_oracle_check(encs[i], plan.view(i), rng, 1)
+
+
 def test_tables_switched_per_tensor_in_one_dispatch():
     """One dispatch over tensors whose tables differ in size and form (11-bit codes, 12-bit
     codes, 15-bit codes, two symbols, all 4-bit, 11-bit codes again): each workgroup copies the
@@ -637,7 +688,12 @@ def test_moe_full_layer_batched():
     names, xs, encs = encode_workload("moe256", d)
     plan = E.DecodePlan(encs)
     assert plan.out.numel() > 2 ** 32
-    plan.run()
+    # a dispatch this long (515 blocks per workgroup) takes the claimed block order; two runs, the
+    # second from the counters
+    # the first left at zero
+    assert int(plan.plan.claim_blocks) == 4
+    for rep in range(2):
+        plan.run()
     torch.cuda.synchronize()
     assert plan.status() == 0
     rng = np.random.default_rng(3)

@@ -346,3 +346,17 @@ def test_entropy_bound_matches_oracle():
     for a in (0.5, 1.0, 1.5, 1.9, 2.0):
         assert abs(E.exponent_entropy_bound(a) - oracle.entropy_bound(a)) < 1e-15
     assert np.isnan(E.exponent_entropy_bound(0.0))
+
+
+def test_plan_block_order_checks_need_no_gpu():
+    """ecf8_decode_run checks a plan's claim size before any launch: 1 and more than 1024 blocks
+    per claim, and a claim counter that could pass 2^32, are argument errors."""
+    ws = (ctypes.c_uint8 * 256)()
+    base = dict(workspace=ctypes.cast(ws, ctypes.c_void_p), workspace_bytes=1 << 20, total_blocks=1000, count=1,
+                chunk_bytes=16, threads_per_block=256, grid=100, short_codes=1)
+    for claim, blocks, grid in ((1, 1000, 100), (1025, 1000, 100), (16, (1 << 32) - 100 * 16, 100),
+                                (1024, 1 << 20, (1 << 22) + 1)):
+        p = B.Plan(**dict(base, total_blocks=blocks, grid=grid))
+        p.claim_blocks = claim
+        assert B.lib().ecf8_decode_run(ctypes.byref(p), None) == -1, (claim, blocks, grid)  # ECF8_ERR_ARG
+    assert ctypes.sizeof(B.Plan) == 48
