@@ -147,7 +147,7 @@ typedef struct {
                                 its index and the rest from a counter in the workspace,
                                 which keeps the blocks in flight close together over a
                                 long dispatch.  ecf8_decode_prepare sets 4 when the
-                                plan has at least 96 blocks per workgroup, else 0; the
+                                plan has at least 64 blocks per workgroup, else 0; the
                                 caller may change it before a run (total_blocks + grid *
                                 claim_blocks must stay below 2^32).  Runs of one plan
                                 must not overlap in time: they share the counter */

@@ -76,13 +76,13 @@ constexpr uint64_t kStatusBytes = 256;
 // each run leaves them zero).
 constexpr uint64_t kSchedOffset = 64;
 // The claimed order: blocks per claim, and the blocks per workgroup from which
-// a plan takes it (measured on MoE layers of 64 to 256 experts, 131 to 515
-// blocks per workgroup: 6-10% faster than the static order in claims of 4;
-// 2 blocks per claim queue on the counter; the Llama-3-70B block, 38 blocks
-// per workgroup, is 3% slower in claims).
+// a plan takes it (measured on MoE layers of 32 to 256 experts, 66 to 515
+// blocks per workgroup: 3-10% faster than the static order in claims of 4;
+// claims of 2 queue on the counter; the Llama-3-70B block, 38 blocks per
+// workgroup, is 4% slower in claims).
 constexpr uint32_t kClaimBlocks = 4;
 constexpr uint32_t kClaimBlocksMax = 1024;
-constexpr uint64_t kClaimMinBlocksPerWg = 96;
+constexpr uint64_t kClaimMinBlocksPerWg = 64;
 constexpr int kNibPrefetch = 4;                                     // write-back groups prefetched per lane
 
 // Device descriptor of one tensor (workspace resident).
