@@ -211,7 +211,8 @@ int ecf8_validate_meta(const ecf8_meta* meta);
 
 /* Workspace bytes a decode of `count` tensors needs (256-byte aligned
  * device memory, owned by the caller, sized once and reused across calls, as
- * ECF8 blog §3.2.2 sizes its pool once): a 256-byte block-check counter,
+ * ECF8 blog §3.2.2 sizes its pool once): a 256-byte status area (the
+ * block-check counter, and at byte 64 the claimed block order's two counters),
  * 144 bytes of descriptor per tensor (rounded up to a multiple of 256 in
  * all) and 9,216 bytes of decode table per tensor.  Returns 0 for
  * count < 0. */
